@@ -1,0 +1,72 @@
+"""Pins for the oracle dequant-matmul (CPU only)."""
+
+import numpy as np
+import pytest
+
+from oracle import (dequantize, linear64, linear_naive, pack_codes, quantize_groups,
+                    quantize_pack, QuantConfig)
+
+
+def _w(N, K, seed):
+    return (np.random.default_rng(seed).standard_normal((N, K)) * 0.02).astype(np.float16)
+
+
+def test_one_hot_rows_select_dequantized_columns():
+    """X = identity: Y[k][n] must equal deq[n][k] exactly (catches a transposed
+    operand or a wrong group index)."""
+    N, K, g = 24, 256, 64
+    W = _w(N, K, 1)
+    q, sc, zr = quantize_groups(W, g)
+    qw = pack_codes(q)
+    X = np.eye(K, dtype=np.float16)
+    Y = linear64(X, qw, sc, zr, g)
+    assert np.array_equal(Y, dequantize(q, sc, zr, g).T)
+
+
+def test_naive_loop_agrees():
+    M, N, K, g = 3, 5, 256, 128
+    W = _w(N, K, 2)
+    X = np.random.default_rng(3).standard_normal((M, K)).astype(np.float16)
+    q, sc, zr = quantize_groups(W, g)
+    Y = linear64(X, pack_codes(q), sc, zr, g)
+    Yn = linear_naive(X, q, sc, zr, g)
+    assert np.max(np.abs(Y - Yn)) <= 1e-12 * np.max(np.abs(Yn))
+
+
+def test_lossless_grid_gives_exact_xwt():
+    rng = np.random.default_rng(5)
+    M, N, K, g = 4, 7, 256, 128
+    q = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    q[:, ::g] = 0
+    q[:, 1::g] = 15
+    W = ((q.astype(np.float64) - 3) * 2.0 ** -5).astype(np.float16)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    qw, sc, zr = quantize_pack(W, QuantConfig(group_size=g))
+    Y = linear64(X, qw, sc, zr, g)
+    assert np.array_equal(Y, X.astype(np.float64) @ W.astype(np.float64).T)
+
+
+def test_sampled_rows_and_cols_match_full():
+    M, N, K, g = 6, 40, 256, 128
+    W = _w(N, K, 6)
+    X = np.random.default_rng(7).standard_normal((M, K)).astype(np.float16)
+    qw, sc, zr = quantize_pack(W, QuantConfig(group_size=g))
+    full = linear64(X, qw, sc, zr, g)
+    rows = np.array([0, 5, 2])
+    cols = np.array([39, 0, 17, 17])
+    part = linear64(X, qw, sc, zr, g, rows=rows, cols=cols)
+    assert np.array_equal(part, full[np.ix_(rows, cols)])
+
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_error_vs_unquantized_is_small(g):
+    """The quantized layer approximates X*W^T: relative Frobenius error of a
+    16-level grid on Gaussian weights is a few percent, far from 1."""
+    M, N, K = 8, 64, 512
+    W = _w(N, K, 8)
+    X = np.random.default_rng(9).standard_normal((M, K)).astype(np.float16)
+    qw, sc, zr = quantize_pack(W, QuantConfig(group_size=g))
+    Y = linear64(X, qw, sc, zr, g)
+    Yr = X.astype(np.float64) @ W.astype(np.float64).T
+    rel = np.linalg.norm(Y - Yr) / np.linalg.norm(Yr)
+    assert 0.01 < rel < 0.2
