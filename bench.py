@@ -1,0 +1,377 @@
+#!/usr/bin/env python3
+"""Throughput of the AWQ W4A16 hot path on one MI355X.
+
+Headline (the JSON line's `value`): decode GEMV weight bandwidth at M=1 over the
+three 7B-class projections (K,N) = (4096,4096), (4096,11008), (11008,4096),
+int4 g128 with zero points, fp16 activations.  One step = one pass over the
+three layers (three GEMV launches).  Weight copies rotate over >= 512 MB so
+every launch streams its weights from HBM rather than the 256 MB Infinity
+Cache.  Inputs are seeded synthetic tensors (workloads/), resident in HBM
+before the timed region.
+
+Also measured after the timed region ("rows"): quantize/pack, GEMV at M=4,
+GEMM at M=1 (for the GEMV-vs-GEMM comparison), batched GEMM at M=16/64/256
+(13B-class MLP, g64 and g128), prefill GEMM at M=4096 (70B-class, fp16 and
+bf16) and the full alpha search on a 4096^3 layer.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows all|none]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA, 2.5 PFLOP/s
+ROTATE_BYTES = 512 << 20         # >= 2x the 256 MB Infinity Cache
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=300)
+    p.add_argument("--warmup", type=int, default=30)
+    p.add_argument("--rows", choices=("all", "none"), default="all")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class Launcher:
+    """Direct ctypes calls with pre-marshalled arguments (no per-call tensor checks)."""
+
+    def __init__(self, awq, torch):
+        self.awq = awq
+        self.torch = torch
+        self.lib = awq.lib
+
+    def linear(self, X, packed, Y, g, kernel):
+        qw, sc, zr = packed
+        M, K = X.shape
+        N = qw.shape[0]
+        st = self.lib.awq_linear_ex(
+            ctypes.c_void_p(X.data_ptr()), 0 if X.dtype == self.torch.float16 else 1,
+            ctypes.c_void_p(qw.data_ptr()), ctypes.c_void_p(sc.data_ptr()),
+            ctypes.c_void_p(zr.data_ptr()), M, N, K, self.awq.config(g),
+            ctypes.c_void_p(Y.data_ptr()),
+            {self.torch.float16: 0, self.torch.bfloat16: 1, self.torch.float32: 2}[Y.dtype],
+            kernel, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(self.lib.awq_last_error().decode())
+
+
+def make_graph(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                                  # warm the launch path outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def copies_for(nbytes):
+    return max(2, -(-ROTATE_BYTES // max(1, nbytes)))
+
+
+def packed_copies(awq, torch, W_np, g, R):
+    W = torch.from_numpy(W_np).cuda()
+    base = awq.awq_quantize_pack(W, g)
+    torch.cuda.synchronize()
+    del W
+    out = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
+    torch.cuda.synchronize()
+    return out
+
+
+def time_graph(torch, g, reps, launches_per_replay):
+    """Average GPU time per launch (seconds) from HIP events around graph replays."""
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * launches_per_replay)
+
+
+def cpu_baseline(layers):
+    """The CPU oracle on one M=1 pass over the three decode layers (unpack,
+    fp64 dequant and product, as the oracle stands), repeated until ~10 s."""
+    from threadpoolctl import threadpool_info
+    from oracle import linear64
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    total_bytes = 0
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        for (X, qw, sc, zr, nbytes) in layers:
+            linear64(X, qw, sc, zr, 128)
+            total_bytes += nbytes
+        passes += 1
+        if time.perf_counter() - t0 > 10.0 or passes >= 20:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{passes} pass(es) of the M=1 decode step over the three layers "
+                      f"(unpack + fp64 dequant + fp64 GEMV), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              f"(this build has no multi-GPU path; run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_weight_only_quantize_amd as awq
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    L = Launcher(awq, torch)
+
+    # ---- headline workload: M=1 decode over three 7B-class layers --------------
+    cases = wl.gemv_cases(Ms=(1,))
+    per_step_bytes = sum(c.weight_bytes for c in cases)
+    R = copies_for(per_step_bytes)
+    log(f"decode GEMV: {len(cases)} layers, {per_step_bytes / 1e6:.2f} MB/step, {R} weight copies")
+    layers = []
+    host_layers = []
+    for c in cases:
+        W = c.weight()
+        X = c.activation()
+        copies = packed_copies(awq, torch, W, 128, R)
+        Xd = torch.from_numpy(X).cuda()
+        Yd = torch.empty((1, c.N), dtype=torch.float16, device="cuda")
+        layers.append((c, Xd, copies, Yd))
+        if not args.no_cpu_baseline:
+            qw, sc, zr = (t.cpu().numpy() for t in copies[0])
+            host_layers.append((X, qw.view(np.uint32), sc, zr, c.weight_bytes))
+        del W
+
+    def step_fn(r):
+        def f():
+            for (c, Xd, copies, Yd) in layers:
+                L.linear(Xd, copies[r], Yd, 128, awq.AWQ_KERNEL_AUTO)
+        return f
+
+    graphs = [make_graph(torch, step_fn(r)) for r in range(R)]
+
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        graphs[(args.warmup + i) % R].replay()
+    starts[args.steps].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_step = starts[0].elapsed_time(starts[args.steps]) * 1e-3 / args.steps
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = per_step_bytes * args.steps / wall / 1e9
+    achieved = per_step_bytes / gpu_step / 1e9
+    log(f"decode step: wall {ms_per_step * 1e3:.2f} us, GPU {gpu_step * 1e6:.2f} us per step")
+
+    # per-layer kernel time (graph of R launches on rotating copies)
+    per_layer = []
+    for (c, Xd, copies, Yd) in layers:
+        def f(c=c, Xd=Xd, copies=copies, Yd=Yd):
+            for r in range(R):
+                L.linear(Xd, copies[r], Yd, 128, awq.AWQ_KERNEL_AUTO)
+        g = make_graph(torch, f)
+        t = time_graph(torch, g, 10, R)
+        per_layer.append({"layer": c.name, "us": round(t * 1e6, 3),
+                          "GB/s": round(c.weight_bytes / t / 1e9, 1)})
+
+    rows = {"decode_gemv_m1_layers": per_layer}
+    if args.rows == "all":
+        rows.update(measure_rows(awq, torch, wl, L, layers, R))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(host_layers)
+
+    out = {
+        "metric": "W4A16 GEMV weight GB/s (M=1) & GEMM TFLOP/s (M>=256), % of MI355X roofline",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode GEMV, M=1, 7B-class layers (K,N)=(4096,4096),(4096,11008),"
+                        "(11008,4096), int4 g128 zero-point, fp16 activations, fp16 out",
+            "global_batch": 1,
+            "weight_bytes_per_step": per_step_bytes,
+            "rotating_copies": R,
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def measure_rows(awq, torch, wl, L, decode_layers, R_dec):
+    rows = {}
+
+    # GEMV at M=4 and GEMM at M=1 on the decode layers
+    for M, kernel, key in ((4, awq.AWQ_KERNEL_AUTO, "decode_gemv_m4"),
+                           (1, awq.AWQ_KERNEL_GEMM, "decode_gemm_kernel_m1")):
+        tot_b, tot_t = 0, 0.0
+        per = []
+        for (c, _, copies, _) in decode_layers:
+            Xd = torch.from_numpy(c.activation(M=M)).cuda()
+            Yd = torch.empty((M, c.N), dtype=torch.float16, device="cuda")
+
+            def f(Xd=Xd, Yd=Yd, copies=copies):
+                for r in range(R_dec):
+                    L.linear(Xd, copies[r], Yd, 128, kernel)
+            t = time_graph(torch, make_graph(torch, f), 10, R_dec)
+            tot_b += c.weight_bytes
+            tot_t += t
+            per.append({"layer": c.name, "us": round(t * 1e6, 3)})
+        rows[key] = {"GB/s": round(tot_b / tot_t / 1e9, 1),
+                     "frac_hbm": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4), "layers": per}
+        log(key, rows[key]["GB/s"], "GB/s")
+
+    # quantize/pack of the 4096x11008 layer: 2 B read + 0.5 B + 3/g B written per weight
+    c = wl.gemv_cases(Ms=(1,))[1]
+    Wd = [torch.from_numpy(c.weight()).cuda()]
+    qbytes = c.N * c.K * 2 + c.weight_bytes
+    Rq = copies_for(qbytes)
+    Wd += [Wd[0].clone() for _ in range(Rq - 1)]
+    outs = [awq.empty_packed(c.N, c.K, 128, "cuda") for _ in range(Rq)]
+
+    def fq():
+        for r in range(Rq):
+            awq.awq_quantize_pack(Wd[r], 128, out=outs[r])
+    t = time_graph(torch, make_graph(torch, fq), 5, Rq)
+    rows["quantize_pack_4096x11008"] = {"us": round(t * 1e6, 2), "GB/s": round(qbytes / t / 1e9, 1),
+                                        "frac_hbm": round(qbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+    log("quantize", rows["quantize_pack_4096x11008"])
+    del Wd, outs
+
+    # batched GEMM (13B-class MLP) at M = 16, 64, 256, g64 and g128
+    gemm = []
+    for case in wl.gemm_cases():
+        key = (case.K, case.N, case.group_size)
+        gemm.append(case)
+    cache = {}
+    res = []
+    for case in gemm:
+        key = (case.K, case.N, case.group_size)
+        if key not in cache:
+            Rg = copies_for(case.weight_bytes)
+            cache.clear()
+            cache[key] = (packed_copies(awq, torch, case.weight(), case.group_size, Rg), Rg)
+        copies, Rg = cache[key]
+        Xd = torch.from_numpy(case.activation()).cuda()
+        Yd = torch.empty((case.M, case.N), dtype=torch.float16, device="cuda")
+
+        def fg(Xd=Xd, Yd=Yd, copies=copies, Rg=Rg, gs=case.group_size):
+            for r in range(Rg):
+                L.linear(Xd, copies[r], Yd, gs, awq.AWQ_KERNEL_AUTO)
+        t = time_graph(torch, make_graph(torch, fg), 5, Rg)
+        tf = case.flops / t / 1e12
+        gbs = case.weight_bytes / t / 1e9
+        res.append({"layer": case.name, "us": round(t * 1e6, 2), "TFLOP/s": round(tf, 1),
+                    "weight_GB/s": round(gbs, 1),
+                    "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+        log(case.name, res[-1])
+    cache.clear()
+    rows["batched_gemm"] = res
+
+    # prefill GEMM (70B-class) at M=4096, fp16 and bf16 activations
+    res = []
+    for case in wl.prefill_cases():
+        W = torch.from_numpy(case.weight()).cuda()
+        packed = awq.awq_quantize_pack(W, 128)
+        del W
+        X = case.activation()
+        if case.x_dtype == "bf16":
+            Xd = torch.from_numpy(X.view(np.int16)).cuda().view(torch.bfloat16)
+        else:
+            Xd = torch.from_numpy(X).cuda()
+        Yd = torch.empty((case.M, case.N), dtype=torch.float16 if case.x_dtype == "f16"
+                         else torch.bfloat16, device="cuda")
+
+        def fp(Xd=Xd, Yd=Yd, packed=packed):
+            L.linear(Xd, packed, Yd, 128, awq.AWQ_KERNEL_AUTO)
+        t = time_graph(torch, make_graph(torch, fp), 5, 1)
+        tf = case.flops / t / 1e12
+        res.append({"layer": case.name, "us": round(t * 1e6, 1), "TFLOP/s": round(tf, 1),
+                    "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
+        log(case.name, res[-1])
+        del packed, Xd, Yd
+    rows["prefill_gemm"] = res
+
+    # full alpha search, 4096 tokens x 4096 x 4096, 20 alphas
+    case = wl.search_case()
+    Xd = torch.from_numpy(case.activation()).cuda()
+    Wd = torch.from_numpy(case.weight()).cuda()
+    ws = torch.empty(awq.awq_scale_search_workspace_size(case.M, case.N, case.K), dtype=torch.uint8,
+                     device="cuda")
+    awq.awq_scale_search(Xd, Wd, workspace=ws)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        r = awq.awq_scale_search(Xd, Wd, workspace=ws)
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    t = min(ts)
+    flops = 21 * 2 * case.M * case.N * case.K
+    rows["scale_search_4096"] = {"ms": round(t * 1e3, 3), "effective_TFLOP/s": round(flops / t / 1e12, 1),
+                                 "frac_mfma": round(flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                                 "best_index": r["best_index"]}
+    log("search", rows["scale_search_4096"])
+    return rows
+
+
+if __name__ == "__main__":
+    main()

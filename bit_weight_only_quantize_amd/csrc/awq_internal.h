@@ -1,0 +1,59 @@
+// Internal launcher interface between the C ABI (api.cpp) and the HIP kernels.
+// Every launcher assumes its arguments were validated by the caller and
+// returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+enum class XType : int { F16 = 0, BF16 = 1 };
+enum class YType : int { F16 = 0, BF16 = 1, F32 = 2 };
+
+// ---- quantize_pack.hip -----------------------------------------------------
+hipError_t launch_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int gs,
+                                const float *s, uint32_t *qweight,
+                                uint16_t *scales, uint8_t *zeros,
+                                int32_t *nonfinite, hipStream_t st);
+
+// ---- linear_gemv.hip (M <= 16) -------------------------------------------------
+hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,
+                       const uint16_t *scales, const uint8_t *zeros, int64_t M,
+                       int64_t N, int64_t K, int gs, void *Y, YType yt,
+                       hipStream_t st);
+
+// ---- linear_gemm.hip (any M) ---------------------------------------------------
+hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
+                       const uint16_t *scales, const uint8_t *zeros, int64_t M,
+                       int64_t N, int64_t K, int gs, void *Y, YType yt,
+                       hipStream_t st);
+
+// Dense fp16 B (X * W^T with W fp16 [N][K]), fp32 output.
+hipError_t launch_gemm_dense_f32(const uint16_t *X, const uint16_t *W, int64_t M,
+                                 int64_t N, int64_t K, float *Y, hipStream_t st);
+
+// Quantized GEMM whose epilogue accumulates sum (Yref - Y)^2: one fp64
+// partial per workgroup tile into `partials` (gemm_tile_count entries).
+hipError_t launch_gemm_loss(const uint16_t *A, const uint32_t *qweight,
+                            const uint16_t *scales, const uint8_t *zeros,
+                            int64_t M, int64_t N, int64_t K, int gs,
+                            const float *Yref, double *partials, hipStream_t st);
+int64_t gemm_tile_count(int64_t M, int64_t N);
+
+// ---- search.hip ----------------------------------------------------------------
+// xbar[k] = sum_m |X[m][k]| / M in fp64 (exact sum; `units` is K u64 scratch).
+hipError_t launch_mean_abs(const uint16_t *X, int64_t M, int64_t K, uint64_t *units,
+                           double *xbar, hipStream_t st);
+// s_table[j][k] for n_alpha alphas (device fp64 array).
+hipError_t launch_scale_table(const double *xbar, int64_t K, const double *alphas,
+                              int n_alpha, float *s_table, hipStream_t st);
+// A = fp16(fp32(X) / s).
+hipError_t launch_scale_activation(const uint16_t *X, const float *s, int64_t M,
+                                   int64_t K, uint16_t *A, hipStream_t st);
+// losses[j] = sum of partials[j][0..n) in index order; then best index.
+hipError_t launch_reduce_losses(const double *partials, int64_t n_per_alpha,
+                                int n_alpha, double *losses, int32_t *best,
+                                hipStream_t st);
+
+}  // namespace awq

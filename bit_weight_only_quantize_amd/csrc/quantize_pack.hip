@@ -1,0 +1,117 @@
+// Scale + group-quantize + pack for gfx950.
+//
+// Follows the pages' quantizer config ("AWQ Advanced Usage Guide", "Group Size
+// Configuration" and "Zero-Point Quantization": w_bit = 4, q_group_size, an
+// asymmetric grid with a zero point) and the sW side of Y = (X/s)(sW)
+// (ai.lansai.wang explainer, section "AWQ 的四步链路").  Per group of g
+// consecutive input channels of one output row:
+//   v = fp32(s_k * W_nk); lo = min(min v, 0); hi = max(max v, 0)
+//   scale = fp16(max((hi - lo) / 15, 2^-14)); zero = clamp(rint(-lo/scale), 0, 15)
+//   code  = clamp(rint(v / scale) + zero, 0, 15)
+// with IEEE correctly rounded fp32 division and rint half-to-even, so the codes
+// are reproducible bit for bit on any IEEE machine.
+//
+// Mapping: one lane per output word (8 input channels, 16 bytes of W);
+// g/8 consecutive lanes form a group and exchange min/max with lane shuffles.
+// The kernel is bound by HBM traffic (2 bytes in, 0.5 + 3/g bytes out per
+// weight) plus the division chain.
+
+#include "awq_internal.h"
+#include "device_common.h"
+
+namespace awq {
+
+template <int GS>
+__global__ __launch_bounds__(256) void quantize_pack_kernel(
+    const uint16_t *__restrict__ W, int64_t N, int64_t K, const float *__restrict__ s,
+    uint32_t *__restrict__ qweight, uint16_t *__restrict__ scales,
+    uint8_t *__restrict__ zeros, int32_t *__restrict__ nonfinite) {
+  constexpr int kLanesPerGroup = GS / 8;
+  const int64_t words_per_row = K / 8;
+  const int64_t total = N * words_per_row;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  // total is a multiple of kLanesPerGroup and groups start at multiples of
+  // it, so a group is either entirely active or entirely idle.
+  const bool active = t < total;
+
+  float v[8];
+  int bad = 0;
+  if (active) {
+    const int64_t n = t / words_per_row;
+    const int64_t c = t - n * words_per_row;
+    const u32x4 raw = *reinterpret_cast<const u32x4 *>(W + n * K + c * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = half_bits_to_float((uint16_t)(raw[i] & 0xFFFFu));
+      v[2 * i + 1] = half_bits_to_float((uint16_t)(raw[i] >> 16));
+    }
+    if (s != nullptr) {
+      const float4 s0 = *reinterpret_cast<const float4 *>(s + c * 8);
+      const float4 s1 = *reinterpret_cast<const float4 *>(s + c * 8 + 4);
+      v[0] = s0.x * v[0]; v[1] = s0.y * v[1]; v[2] = s0.z * v[2]; v[3] = s0.w * v[3];
+      v[4] = s1.x * v[4]; v[5] = s1.y * v[5]; v[6] = s1.z * v[6]; v[7] = s1.w * v[7];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bad += !__builtin_isfinite(v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+
+  float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    lo = fminf(lo, v[i]);
+    hi = fmaxf(hi, v[i]);
+  }
+#pragma unroll
+  for (int off = 1; off < kLanesPerGroup; off <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, off, 64));
+    hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+  }
+
+  const float step = (hi - lo) / 15.0f;
+  const _Float16 sh = (_Float16)fmaxf(step, 0x1p-14f);
+  const float sf = (float)sh;
+  const float zf = fminf(fmaxf(__builtin_rintf(-lo / sf), 0.0f), 15.0f);
+
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float qf = fminf(fmaxf(__builtin_rintf(v[i] / sf) + zf, 0.0f), 15.0f);
+    word |= ((uint32_t)qf) << (4 * nibble_of_channel(i));
+  }
+
+  if (active) {
+    qweight[t] = word;
+    const int64_t n = t / words_per_row;
+    const int64_t c = t - n * words_per_row;
+    if ((c % kLanesPerGroup) == 0) {
+      const int64_t G = K / GS;
+      const int64_t gi = n * G + c / kLanesPerGroup;
+      scales[gi] = __builtin_bit_cast(uint16_t, sh);
+      zeros[gi] = (uint8_t)zf;
+    }
+  }
+
+  if (nonfinite != nullptr) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off, 64);
+    if ((threadIdx.x & 63) == 0 && bad) atomicAdd(nonfinite, bad);
+  }
+}
+
+hipError_t launch_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int gs,
+                                const float *s, uint32_t *qweight, uint16_t *scales,
+                                uint8_t *zeros, int32_t *nonfinite, hipStream_t st) {
+  const int64_t total = N * (K / 8);
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (gs == 128)
+    quantize_pack_kernel<128><<<grid, 256, 0, st>>>(W, N, K, s, qweight, scales, zeros, nonfinite);
+  else
+    quantize_pack_kernel<64><<<grid, 256, 0, st>>>(W, N, K, s, qweight, scales, zeros, nonfinite);
+  return hipGetLastError();
+}
+
+}  // namespace awq

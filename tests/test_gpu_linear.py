@@ -1,0 +1,181 @@
+"""GPU parity: awq_linear / awq_linear_ex against the fp64 oracle."""
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from gpu_common import (assert_close, dev, out_to_f64, say, to_dev, to_np, torch_mod)
+from oracle import (QuantConfig, bf16_bits_to_f32, dequantize, linear64, quantize_pack,
+                    unpack_codes)
+
+pytestmark = pytest.mark.gpu
+
+GEMV, GEMM = 1, 2
+
+
+def _awq():
+    import bit_weight_only_quantize_amd as awq
+    return awq
+
+
+def _packed(W, g, chunk=4096):
+    """Oracle-packed weights (row chunks bound host memory), plus GPU copies."""
+    parts = [quantize_pack(W[r:r + chunk], QuantConfig(group_size=g))
+             for r in range(0, W.shape[0], chunk)]
+    qw, sc, zr = (np.concatenate([p[i] for p in parts]) for i in range(3))
+    return qw, sc, zr, (to_dev(qw), to_dev(sc), to_dev(zr))
+
+
+_PREFILL_CACHE = {}
+
+
+def _x_f64(X, dt):
+    return bf16_bits_to_f32(X).astype(np.float64) if dt == "bf16" else X.astype(np.float64)
+
+
+def _run(X, dt, packed_dev, g, kernel, out_dtype=None):
+    awq = _awq()
+    Xd = to_dev(X, bf16=(dt == "bf16"))
+    Y = awq.awq_linear_ex(Xd, *packed_dev, kernel=kernel, group_size=g, out_dtype=out_dtype)
+    torch_mod().cuda.synchronize()
+    return Y
+
+
+# --- exactness pin: one-hot activations reproduce dequantized weights -------------
+
+@pytest.mark.parametrize("kernel", [GEMV, GEMM])
+@pytest.mark.parametrize("g", [64, 128])
+def test_one_hot_rows_are_exact(kernel, g):
+    """X = rows of the identity: Y[r][n] = deq[n][k_r] exactly in fp32, since
+    the B operand is the exact integer q - z and the scale is applied once."""
+    torch = torch_mod()
+    N, K = 80, 512
+    W = wl.gen_weight(N, K, 17)
+    qw, sc, zr, pd = _packed(W, g)
+    deq = dequantize(unpack_codes(qw, K), sc, zr, g)
+    ks = np.arange(0, K, 37) if kernel == GEMV else np.arange(K)
+    for k0 in range(0, len(ks), 16 if kernel == GEMV else len(ks)):
+        sel = ks[k0:k0 + (16 if kernel == GEMV else len(ks))]
+        X = np.zeros((len(sel), K), np.float16)
+        X[np.arange(len(sel)), sel] = 1.0
+        say("one-hot", "gemv" if kernel == GEMV else "gemm", g, len(sel))
+        Y = out_to_f64(_run(X, "f16", pd, g, kernel, torch.float32))
+        assert np.array_equal(Y, deq[:, sel].T)
+
+
+# --- small and ragged shapes: full element-by-element comparison -------------------
+
+RAGGED = [
+    (1, 77, 320, 64, "f16"), (3, 200, 384, 128, "f16"), (16, 48, 256, 128, "bf16"),
+    (5, 130, 1024, 64, "bf16"), (33, 77, 320, 64, "f16"), (77, 200, 384, 128, "f16"),
+    (130, 260, 640, 64, "bf16"), (257, 129, 1152, 128, "f16"), (1, 512, 512, 128, "f16"),
+    (8, 512, 512, 128, "f16"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g,dt", RAGGED)
+def test_ragged_shapes(M, N, K, g, dt):
+    torch = torch_mod()
+    W = wl.gen_weight(N, K, 40 + N)
+    X = wl.gen_activation(M, K, 50 + M, 51, dt)
+    qw, sc, zr, pd = _packed(W, g)
+    ref = linear64(_x_f64(X, dt), qw, sc, zr, g)
+    kernels = [GEMM] + ([GEMV] if M <= 16 else [])
+    for kern in kernels:
+        say("ragged", M, N, K, g, dt, "gemv" if kern == GEMV else "gemm")
+        Y32 = out_to_f64(_run(X, dt, pd, g, kern, torch.float32))
+        assert_close(Y32, ref, f"{M}x{N}x{K} fp32 out")
+        Y16 = out_to_f64(_run(X, dt, pd, g, kern))          # same dtype as X
+        assert_close(Y16, ref, f"{M}x{N}x{K} 16-bit out")
+        # the 16-bit output is the fp32 result rounded once
+        want = torch.from_numpy(Y32).to(torch.float16 if dt == "f16" else torch.bfloat16)
+        assert np.array_equal(Y16, want.float().numpy().astype(np.float64))
+
+
+def test_tiny_layer_config():
+    """Tiny single layer: W 512x512, g128, X at M=1 and M=8 with 5 outlier channels."""
+    torch = torch_mod()
+    for case in wl.tiny_cases():
+        W = case.weight()
+        X = case.activation()
+        qw, sc, zr, pd = _packed(W, 128)
+        ref = linear64(X, qw, sc, zr, 128)
+        say("tiny", case.name)
+        Y = out_to_f64(_run(X, "f16", pd, 128, 0))
+        assert_close(Y, ref, case.name)
+        Yg = out_to_f64(_run(X, "f16", pd, 128, GEMM, torch.float32))
+        Yv = out_to_f64(_run(X, "f16", pd, 128, GEMV, torch.float32))
+        assert_close(Yg, ref, case.name + " gemm")
+        assert_close(Yv, ref, case.name + " gemv")
+
+
+# --- the decode, batched and prefill layer shapes ------------------------------------
+
+@pytest.mark.parametrize("case", wl.gemv_cases(), ids=lambda c: c.name)
+def test_decode_gemv_layers(case):
+    W = case.weight()
+    X = case.activation()
+    qw, sc, zr, pd = _packed(W, 128)
+    ref = linear64(X, qw, sc, zr, 128)
+    say("gemv layer", case.name)
+    assert_close(out_to_f64(_run(X, "f16", pd, 128, 0)), ref, case.name)
+
+
+@pytest.mark.parametrize("case", wl.gemm_cases(), ids=lambda c: c.name)
+def test_batched_gemm_layers(case):
+    W = case.weight()
+    X = case.activation()
+    qw, sc, zr, pd = _packed(W, case.group_size)
+    ref = linear64(X, qw, sc, zr, case.group_size)
+    say("gemm layer", case.name)
+    assert_close(out_to_f64(_run(X, "f16", pd, case.group_size, 0)), ref, case.name)
+
+
+@pytest.mark.parametrize("case", wl.prefill_cases(), ids=lambda c: c.name)
+def test_prefill_layers_sampled(case):
+    """M=4096 prefill on 70B-class layers: every output is computed on the GPU;
+    the oracle evaluates 96 sampled rows x 384 sampled columns (plus the last
+    row and column) one by one."""
+    torch = torch_mod()
+    key = (case.K, case.N)
+    if key not in _PREFILL_CACHE:
+        _PREFILL_CACHE.clear()
+        _PREFILL_CACHE[key] = _packed(case.weight(), 128)
+    qw, sc, zr, pd = _PREFILL_CACHE[key]
+    X = case.activation()
+    out_dtype = torch.float16 if case.x_dtype == "f16" else torch.float32
+    say("prefill layer", case.name)
+    Y = _run(X, case.x_dtype, pd, 128, 0, out_dtype)
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[case.M - 1], rng.choice(case.M, 96, replace=False)]))
+    cols = np.unique(np.concatenate([[case.N - 1], rng.choice(case.N, 384, replace=False)]))
+    ref = linear64(_x_f64(X, case.x_dtype), qw, sc, zr, 128, rows=rows, cols=cols)
+    got = out_to_f64(Y)[np.ix_(rows, cols)]
+    assert_close(got, ref, case.name)
+    assert np.isfinite(out_to_f64(Y)).all()
+    if case.x_dtype == "bf16":
+        # bf16 output is the fp32 result rounded once to bf16
+        Yb = _run(X, "bf16", pd, 128, 0, torch.bfloat16)
+        assert torch.equal(Yb, Y.to(torch.bfloat16))
+
+
+def test_gemv_and_gemm_agree_at_batch_one():
+    case = wl.gemv_cases(Ms=(1,))[1]
+    W = case.weight()
+    X = case.activation()
+    torch = torch_mod()
+    _, _, _, pd = _packed(W, 128)
+    say("gemv vs gemm", case.name)
+    a = out_to_f64(_run(X, "f16", pd, 128, GEMV, torch.float32))
+    b = out_to_f64(_run(X, "f16", pd, 128, GEMM, torch.float32))
+    assert np.max(np.abs(a - b)) <= 1e-4 * np.max(np.abs(b))
+
+
+def test_empty_inputs():
+    awq = _awq()
+    torch = torch_mod()
+    W = wl.gen_weight(32, 256, 1)
+    _, _, _, pd = _packed(W, 128)
+    X = torch.empty((0, 256), dtype=torch.float16, device=dev())
+    Y = awq.awq_linear(X, *pd, group_size=128)
+    assert Y.shape == (0, 32)
