@@ -53,6 +53,13 @@ class AwqError(RuntimeError):
 
 
 def _load():
+    # torch bundles its own HIP runtime under the same soname
+    # (libamdhip64.so.7).  Importing torch first maps that runtime, and the
+    # dynamic loader then resolves this library's dependency to the same copy,
+    # so torch's streams and allocations are valid here.  Loading this library
+    # first would map /opt/rocm's runtime and torch would add a second one.
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m bit_weight_only_quantize_amd.build`")

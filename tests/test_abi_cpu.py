@@ -111,3 +111,11 @@ def test_search_workspace_and_validation():
     assert call(ws_ptr=ctypes.c_void_p(0x10010)) == binding.AWQ_ERR_INVALID_ARG  # not 256-aligned
     assert call(M=0) == binding.AWQ_ERR_INVALID_ARG
     assert best.value == -1      # nothing written on error
+
+
+def test_single_hip_runtime_in_process():
+    """torch bundles a HIP runtime with the same soname; the binding must bind
+    the library to that copy, never map a second runtime next to it."""
+    maps = open("/proc/self/maps").read()
+    runtimes = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(runtimes) == 1, runtimes
