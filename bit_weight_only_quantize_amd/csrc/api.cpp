@@ -75,6 +75,9 @@ awq_status check_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,
     return fail(AWQ_ERR_INVALID_ARG, "GEMV kernel serves M <= %d, got M=%lld", AWQ_GEMV_MAX_M,
                 (long long)M);
   if (M == 0 || N == 0) return AWQ_OK;
+  if (!awq::gemm_supported(N, K, false))
+    return fail(AWQ_ERR_UNSUPPORTED, "layer of %lld x %lld exceeds 2 GiB of packed weights",
+                (long long)N, (long long)K);
   if (!X || !qweight || !scales || !zeros || !Y)
     return fail(AWQ_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(X, 16) || !aligned(qweight, 16))
@@ -129,6 +132,9 @@ awq_status check_search(int64_t M, int64_t N, int64_t K, awq_config cfg, int32_t
   if (N > ((int64_t)1 << 31)) return fail(AWQ_ERR_INVALID_ARG, "N too large");
   if (n_alpha < 1 || n_alpha > 64)
     return fail(AWQ_ERR_INVALID_ARG, "n_alpha=%d must be in [1, 64]", n_alpha);
+  if (!awq::gemm_supported(N, K, true))
+    return fail(AWQ_ERR_UNSUPPORTED, "search layer of %lld x %lld exceeds 2 GiB of fp16 weights",
+                (long long)N, (long long)K);
   return AWQ_OK;
 }
 
@@ -186,7 +192,11 @@ awq_status awq_linear_ex(const void *X, int32_t x_dtype, const uint32_t *qweight
   const awq::YType yt = y_dtype == AWQ_F16    ? awq::YType::F16
                         : y_dtype == AWQ_BF16 ? awq::YType::BF16
                                               : awq::YType::F32;
-  const bool gemv = kernel == AWQ_KERNEL_GEMV || (kernel == AWQ_KERNEL_AUTO && M <= AWQ_GEMV_MAX_M);
+  const bool gemv_ok = awq::gemv_supported(M, K, cfg.group_size);
+  if (kernel == AWQ_KERNEL_GEMV && !gemv_ok)
+    return fail(AWQ_ERR_UNSUPPORTED, "GEMV kernel cannot serve K=%lld", (long long)K);
+  const bool gemv = kernel == AWQ_KERNEL_GEMV ||
+                    (kernel == AWQ_KERNEL_AUTO && M <= AWQ_GEMV_MAX_M && gemv_ok);
   hipError_t e = gemv ? awq::launch_gemv(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size,
                                          Y, yt, as_stream(stream))
                       : awq::launch_gemm(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size,

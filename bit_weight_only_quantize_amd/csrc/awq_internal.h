@@ -18,6 +18,8 @@ hipError_t launch_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int gs,
                                 int32_t *nonfinite, hipStream_t st);
 
 // ---- linear_gemv.hip (M <= 16) -------------------------------------------------
+// Whether the GEMV kernel can serve this shape (M <= 16, LDS staging fits).
+bool gemv_supported(int64_t M, int64_t K, int gs);
 hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M,
                        int64_t N, int64_t K, int gs, void *Y, YType yt,
@@ -40,6 +42,9 @@ hipError_t launch_gemm_loss(const uint16_t *A, const uint32_t *qweight,
                             int64_t M, int64_t N, int64_t K, int gs,
                             const float *Yref, double *partials, hipStream_t st);
 int64_t gemm_tile_count(int64_t M, int64_t N);
+// Whether a layer fits the kernels' 32-bit buffer offsets (packed weights, or
+// the dense fp16 weights of the search, below 2 GiB).
+bool gemm_supported(int64_t N, int64_t K, bool dense);
 
 // ---- search.hip ----------------------------------------------------------------
 // xbar[k] = sum_m |X[m][k]| / M in fp64 (exact sum; `units` is K u64 scratch).

@@ -9,15 +9,32 @@
 // in fp32, and the group's scale multiplies that fp32 partial.  No dequantized
 // weight is ever rounded to 16 bits.
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile of Y; its four
-// waves each own a 64 x 64 quarter (4 x 4 MFMA tiles of 16 x 16).  K advances
-// in blocks of 128 (one g128 group or two g64 groups).  The activation block
-// (128 rows x 128 channels, 32 KiB fp16) is staged in LDS with a 16-byte row
-// pad (conflict-free 128-bit reads) and prefetched into registers one block
-// ahead.  Packed weights bypass LDS: each lane loads the 16 bytes it needs
-// (32 codes of one column) one block ahead and dequantizes them in registers;
-// each dequantized fragment feeds 4 MFMA tiles.  Block ids are remapped so
-// each XCD works on a contiguous run of tiles that share activation rows.
+// Tiling for the MI355X: a 256-thread workgroup (one wave per SIMD) computes a
+// 256 x 128 tile of Y; each wave owns 128 x 64 (8 x 4 MFMA tiles of 16 x 16).
+// K advances in blocks of 128 channels (one g128 group or two g64 groups).
+//  * Activations: each 256 x 128 fp16 block (64 KiB) goes from global memory
+//    straight to LDS (buffer_load_dwordx4 ... lds, no VGPR staging),
+//    double-buffered in two 64 KiB arrays.  16-byte chunk c of row r is stored
+//    at chunk c ^ (r mod 16): the 16 rows read by one 128-bit LDS access land
+//    in 16 distinct bank groups.
+//  * Per group, a wave reads all its A fragments (8 tiles x 32 channels) from
+//    LDS once; they are MFMA-only operands, so the register allocator may keep
+//    them in AGPRs.  Columns are then walked one 16-wide tile at a time: the
+//    lane dequantizes its 32 codes of that column (16 VGPRs live) and runs 8
+//    MFMA chains (one per M tile) whose fp32 sums are scaled into the
+//    accumulator.  Each dequantized fragment feeds 8 MFMAs.
+//  * Packed weights, scales and zeros bypass LDS and are prefetched one block
+//    ahead into registers.
+//  * All global accesses go through buffer resources: out-of-range reads return
+//    zero and out-of-range writes are dropped by the hardware, so edge tiles
+//    need no clamping or branches around loads.
+//  * One s_barrier per block, after an explicit vmcnt(0): the data waited for
+//    was issued a whole block earlier.  __syncthreads() is avoided in the loop
+//    because its release fence would also drain the prefetches in flight.
+//  * Block ids are remapped so each XCD works on a contiguous run of tiles
+//    along N that share one activation block in that XCD's L2.
+// 32-bit buffer offsets: the launcher slices M so that X, Y and the reference
+// output of one launch stay below 2 GiB.
 
 #include "awq_internal.h"
 #include "device_common.h"
@@ -26,28 +43,38 @@ namespace awq {
 
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 128;
-constexpr int kMT = 4, kNT = 4;        // 16x16 tiles per wave along M and N
-constexpr int kLDA = kBK + 8;          // fp16 elements per LDS row (16-byte pad)
+constexpr int kBM = 256, kBN = 128, kBK = 128;
+constexpr int kMT = 8, kNT = 4;        // 16x16 tiles per wave along M and N
 constexpr int kThreads = 256;
+constexpr uint32_t kNone = 0xFFFFFFFFu; // an offset every range check rejects
 
 enum Epi : int { kEpiStore = 0, kEpiLoss = 1 };
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt with vmcnt = 0 and expcnt / lgkmcnt left at their maxima.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace
 
-template <class XT, int GS, int EPI, bool DENSE>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
-    const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
-    const uint16_t *__restrict__ Wdense, const uint16_t *__restrict__ scales,
-    const uint8_t *__restrict__ zeros, int64_t M, int64_t N, int64_t K,
-    void *__restrict__ Y, int ytype, const float *__restrict__ Yref,
-    double *__restrict__ partials) {
+template <class XT, int GS, int EPI, bool DENSE, int YT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
+                 const uint16_t *__restrict__ Wdense, const uint16_t *__restrict__ scales,
+                 const uint8_t *__restrict__ zeros, int M, int N, int K, void *__restrict__ Y,
+                 const float *__restrict__ Yref, double *__restrict__ partials) {
   constexpr bool kBF16 = __is_same(XT, TagBF16);
   constexpr int kGS = DENSE ? 128 : GS;
   constexpr int kWpl = kGS / 32;        // 8-channel words per lane per group
   constexpr int kGPB = kBK / kGS;       // groups per K block
 
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kBM * kLDA];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[kBM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBM * kBK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -55,67 +82,71 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int c = lane & 15, kq = lane >> 4;
 
-  const int64_t tiles_n = (N + kBN - 1) / kBN;
-  const int64_t tiles_m = (M + kBM - 1) / kBM;
-  const int64_t bid = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
-  const int64_t tm = bid / tiles_n, tn = bid - (bid / tiles_n) * tiles_n;
-  if (tm >= tiles_m) return;
-  const int64_t row0 = tm * kBM, col0 = tn * kBN;
+  const int tiles_n = (N + kBN - 1) / kBN;
+  const int bid = (int)xcd_remap(blockIdx.x, (int64_t)gridDim.x);
+  const int tm = bid / tiles_n, tn = bid - (bid / tiles_n) * tiles_n;
+  const int row0 = tm * kBM, col0 = tn * kBN;
 
-  const int64_t G = K / kGS;
-  const int64_t wrow = K / 8;
-  const int64_t nkb = (K + kBK - 1) / kBK;
+  const int G = K / kGS;
+  const int nkb = (K + kBK - 1) / kBK;
 
-  // ---- activation block: global -> registers -> LDS ------------------------
-  u32x4 apre[8];
-  auto load_a = [&](int64_t kb) {
+  const rsrc_t rX = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+
+  // ---- activation block -> LDS: 16 DMA instructions per wave, 1 KiB each ------
+  // Instruction r of wave w fills rows 4*(16w + r) .. +3; lane l writes row
+  // +l/16 at physical chunk l%16 and so fetches logical chunk (l%16) ^ (row%16).
+  // row%16 = 4*(r%4) + l/16, so four lane offsets cover all sixteen r.
+  uint32_t a_voff[4];
+  {
+    const int lrow = lane >> 4;
+    const uint32_t base = (uint32_t)(row0 + 64 * wave + lrow) * (uint32_t)K * 2u;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int row = (tid >> 4) + 16 * r;
-      const int64_t kk = kb * kBK + (tid & 15) * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row0 + row < M && kk < K)
-        v = *reinterpret_cast<const u32x4 *>(X + (row0 + row) * K + kk);
-      apre[r] = v;
+    for (int q = 0; q < 4; ++q) a_voff[q] = base + ((uint32_t)((lane & 15) ^ (4 * q + lrow)) << 4);
+  }
+  const uint32_t a_rstep = 8u * (uint32_t)K;   // bytes between rows 4 apart
+  auto issue_a = [&](int kb, uint16_t *buf) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t off = a_voff[r & 3] + (uint32_t)r * a_rstep + (uint32_t)kb * (kBK * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rX, (lds_void *)(reinterpret_cast<char *>(buf) + (16 * wave + r) * 1024), 16, off, 0, 0,
+          0);
     }
   };
-  auto store_a = [&]() {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int row = (tid >> 4) + 16 * r;
-      *reinterpret_cast<u32x4 *>(&sA[row * kLDA + (tid & 15) * 8]) = apre[r];
-    }
+
+  // ---- packed weights, scales and zeros of one K block (registers) -------------
+  const uint32_t lane_col = (uint32_t)(wn * 64 + c);
+  const rsrc_t rQ = make_rsrc(qweight, DENSE ? 0u : (uint32_t)N * (uint32_t)K / 2u);
+  const rsrc_t rS = make_rsrc(scales, DENSE ? 0u : (uint32_t)N * (uint32_t)G * 2u);
+  const rsrc_t rZ = make_rsrc(zeros, DENSE ? 0u : (uint32_t)N * (uint32_t)G);
+  const uint32_t q_lane = lane_col * (uint32_t)(K / 2) + (uint32_t)(kq * kWpl * 4);
+  const uint32_t s_lane = lane_col * (uint32_t)G;
+
+  struct BRegs {
+    uint32_t raw[kNT][kGPB][kWpl];
+    uint32_t sc[kNT][kGPB];
+    uint32_t zr[kNT][kGPB];
   };
-
-  // ---- packed weights, scales and zeros for one K block ----------------------
-  int64_t ncol[kNT];
-#pragma unroll
-  for (int j = 0; j < kNT; ++j) ncol[j] = col0 + wn * 64 + j * 16 + c;
-
-  uint32_t braw[kNT][kGPB][kWpl];
-  float bsc[kNT][kGPB];
-  uint32_t bzr[kNT][kGPB];
-  auto load_b = [&](int64_t kb) {
+  auto load_b = [&](int kb, BRegs &r) {
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
+      const uint32_t ncol = (uint32_t)(col0 + j * 16);
 #pragma unroll
       for (int gi = 0; gi < kGPB; ++gi) {
-        const int64_t g = kb * kGPB + gi;
-        const bool ok = ncol[j] < N && g < G;
-        const uint32_t *p = qweight + (ok ? ncol[j] : 0) * wrow + g * (kGS / 8) + kq * kWpl;
+        const uint32_t g = (uint32_t)(kb * kGPB + gi);
+        const uint32_t qo = q_lane + ncol * (uint32_t)(K / 2) + g * (kGS / 2);
         if constexpr (kWpl == 4) {
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (ok) v = *reinterpret_cast<const u32x4 *>(p);
+          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo, 0, 0));
 #pragma unroll
-          for (int w = 0; w < kWpl; ++w) braw[j][gi][w] = v[w];
+          for (int w = 0; w < kWpl; ++w) r.raw[j][gi][w] = v[w];
         } else {
-          u32x2 v = {0u, 0u};
-          if (ok) v = *reinterpret_cast<const u32x2 *>(p);
+          const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rQ, qo, 0, 0));
 #pragma unroll
-          for (int w = 0; w < kWpl; ++w) braw[j][gi][w] = v[w];
+          for (int w = 0; w < kWpl; ++w) r.raw[j][gi][w] = v[w];
         }
-        bsc[j][gi] = ok ? half_bits_to_float(scales[ncol[j] * G + g]) : 0.0f;
-        bzr[j][gi] = ok ? (uint32_t)zeros[ncol[j] * G + g] : 0u;
+        const uint32_t so = s_lane + ncol * (uint32_t)G + g;
+        r.sc[j][gi] = __builtin_amdgcn_raw_buffer_load_b16(rS, so * 2u, 0, 0);
+        r.zr[j][gi] = __builtin_amdgcn_raw_buffer_load_b8(rZ, so, 0, 0);
       }
     }
   };
@@ -126,145 +157,165 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
     for (int j = 0; j < kNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_a(0);
-  if constexpr (!DENSE) load_b(0);
-  store_a();
-  __syncthreads();
+  // A fragment: M tile i, logical 16-byte chunk ch of the block row.
+  auto a_frag = [&](const uint16_t *buf, int i, int ch) {
+    const int row = wm * 128 + i * 16 + c;
+    return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(buf) + row * (kBK * 2) +
+                                            ((ch ^ c) << 4));
+  };
 
-  for (int64_t kb = 0; kb < nkb; ++kb) {
-    const bool more = kb + 1 < nkb;
-    if (more) load_a(kb + 1);
+  const rsrc_t rW = make_rsrc(Wdense, DENSE ? (uint32_t)N * (uint32_t)K * 2u : 0u);
+  const uint32_t w_lane = lane_col * (uint32_t)K * 2u + (uint32_t)(kq * 64);
 
+  auto compute = [&](int kb, const uint16_t *buf, const BRegs &br) {
     if constexpr (DENSE) {
-      // B straight from the fp16 weight rows (used for X * W^T only).
+      u32x4 a[kMT][4];
+#pragma unroll
+      for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) a[i][st] = a_frag(buf, i, kq * 4 + st);
 #pragma unroll
       for (int j = 0; j < kNT; ++j) {
         u32x4 b[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          const int64_t kk = kb * kBK + kq * 32 + 8 * st;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (ncol[j] < N && kk < K)
-            v = *reinterpret_cast<const u32x4 *>(Wdense + ncol[j] * K + kk);
-          b[st] = v;
+          const int kk = kb * kBK + kq * 32 + 8 * st;
+          const uint32_t off = w_lane + (uint32_t)(col0 + j * 16) * (uint32_t)K * 2u +
+                               (uint32_t)(kb * kBK * 2 + st * 16);
+          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0));
+          b[st] = kk < K ? v : u32x4{0u, 0u, 0u, 0u};    // K tail of a g64-aligned K
         }
 #pragma unroll
-        for (int i = 0; i < kMT; ++i) {
-          const uint16_t *ap = &sA[(wm * 64 + i * 16 + c) * kLDA + kq * 32];
+        for (int st = 0; st < 4; ++st)
 #pragma unroll
-          for (int st = 0; st < 4; ++st)
-            acc[i][j] = mfma32<XT>(*reinterpret_cast<const u32x4 *>(ap + 8 * st), b[st], acc[i][j]);
-        }
+          for (int i = 0; i < kMT; ++i) acc[i][j] = mfma32<XT>(a[i][st], b[st], acc[i][j]);
       }
     } else {
-      uint32_t craw[kNT][kGPB][kWpl];
-      float csc[kNT][kGPB];
-      uint32_t czr[kNT][kGPB];
-#pragma unroll
-      for (int j = 0; j < kNT; ++j)
-#pragma unroll
-        for (int gi = 0; gi < kGPB; ++gi) {
-          csc[j][gi] = bsc[j][gi];
-          czr[j][gi] = bzr[j][gi];
-#pragma unroll
-          for (int w = 0; w < kWpl; ++w) craw[j][gi][w] = braw[j][gi][w];
-        }
-      if (more) load_b(kb + 1);
-
 #pragma unroll
       for (int gi = 0; gi < kGPB; ++gi) {
-        if (kb * kGPB + gi >= G) break;
-        u32x4 bq[kNT][kWpl];
+        if (kGPB > 1 && kb * kGPB + gi >= G) break;
+        u32x4 a[kMT][kWpl];
+#pragma unroll
+        for (int i = 0; i < kMT; ++i)
+#pragma unroll
+          for (int w = 0; w < kWpl; ++w) a[i][w] = a_frag(buf, i, gi * (kGS / 8) + kq * kWpl + w);
+        f32x4 rs[kMT];
+        if constexpr (kBF16) {
+#pragma unroll
+          for (int i = 0; i < kMT; ++i) {
+            rs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < kWpl; ++w) rs[i] = mfma32<TagBF16>(a[i][w], bf16_ones(), rs[i]);
+          }
+        }
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
+          u32x4 bq[kWpl];
           if constexpr (!kBF16) {
-            const DeqF16 deq(czr[j][gi]);
+            const DeqF16 deq(br.zr[j][gi]);
 #pragma unroll
-            for (int w = 0; w < kWpl; ++w) bq[j][w] = deq(craw[j][gi][w]);
+            for (int w = 0; w < kWpl; ++w) bq[w] = deq(br.raw[j][gi][w]);
           } else {
             const DeqBF16 deq;
 #pragma unroll
-            for (int w = 0; w < kWpl; ++w) bq[j][w] = deq(craw[j][gi][w]);
+            for (int w = 0; w < kWpl; ++w) bq[w] = deq(br.raw[j][gi][w]);
           }
-        }
+          const float sc = half_bits_to_float((uint16_t)br.sc[j][gi]);
+          f32x4 t[kMT];
 #pragma unroll
-        for (int i = 0; i < kMT; ++i) {
-          const uint16_t *ap = &sA[(wm * 64 + i * 16 + c) * kLDA + gi * kGS + kq * 8 * kWpl];
-          u32x4 a[kWpl];
+          for (int i = 0; i < kMT; ++i) t[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int w = 0; w < kWpl; ++w) a[w] = *reinterpret_cast<const u32x4 *>(ap + 8 * w);
-          f32x4 rs = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (kBF16) {
+          for (int w = 0; w < kWpl; ++w)
 #pragma unroll
-            for (int w = 0; w < kWpl; ++w) rs = mfma32<TagBF16>(a[w], bf16_ones(), rs);
-          }
+            for (int i = 0; i < kMT; ++i) t[i] = mfma32<XT>(a[i][w], bq[w], t[i]);
 #pragma unroll
-          for (int j = 0; j < kNT; ++j) {
-            f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int w = 0; w < kWpl; ++w) t = mfma32<XT>(a[w], bq[j][w], t);
+          for (int i = 0; i < kMT; ++i) {
             if constexpr (kBF16) {
-              const float cz = -(float)(128u + czr[j][gi]);
+              const float cz = -(float)(128u + br.zr[j][gi]);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) t[e] = __builtin_fmaf(cz, rs[e], t[e]);
+              for (int e = 0; e < 4; ++e) t[i][e] = __builtin_fmaf(cz, rs[i][e], t[i][e]);
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(t[e], csc[j][gi], acc[i][j][e]);
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(t[i][e], sc, acc[i][j][e]);
           }
         }
       }
     }
+  };
 
-    __syncthreads();
-    if (more) {
-      store_a();
-      __syncthreads();
-    }
+  // ---- main loop: two static buffers, one barrier per block -------------------
+  // Prefetch indices are clamped to the last block instead of branched on, so
+  // no load sits under a branch; the surplus prefetch of the last iteration
+  // lands in a buffer nobody reads again.
+  BRegs r0, r1;
+  const int last = nkb - 1;
+  issue_a(0, sA0);
+  if constexpr (!DENSE) load_b(0, r0);
+  for (int kb = 0; kb < nkb; kb += 2) {
+    wait_vmem_all();
+    __builtin_amdgcn_s_barrier();
+    issue_a(kb + 1 < last ? kb + 1 : last, sA1);
+    if constexpr (!DENSE) load_b(kb + 1 < last ? kb + 1 : last, r1);
+    __builtin_amdgcn_sched_barrier(0);   // issue the prefetch before the math
+    compute(kb, sA0, r0);
+    if (kb + 1 >= nkb) break;
+
+    wait_vmem_all();
+    __builtin_amdgcn_s_barrier();
+    issue_a(kb + 2 < last ? kb + 2 : last, sA0);
+    if constexpr (!DENSE) load_b(kb + 2 < last ? kb + 2 : last, r0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kb + 1, sA1, r1);
   }
+  wait_vmem_all();
 
   // ---- epilogue -------------------------------------------------------------
+  // Lane (c, kq) holds rows 4*kq + e of column c of every 16x16 tile.
   if constexpr (EPI == kEpiStore) {
+    constexpr int ysz = YT == (int)YType::F32 ? 4 : 2;
+    const rsrc_t rY = make_rsrc(Y, (uint32_t)M * (uint32_t)N * (uint32_t)ysz);
 #pragma unroll
-    for (int i = 0; i < kMT; ++i) {
+    for (int j = 0; j < kNT; ++j) {
+      const int n = col0 + wn * 64 + j * 16 + c;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t m = row0 + wm * 64 + i * 16 + 4 * kq + e;
-        if (m >= M) continue;
+      for (int i = 0; i < kMT; ++i) {
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) {
-          const int64_t n = ncol[j];
-          if (n >= N) continue;
+        for (int e = 0; e < 4; ++e) {
+          const int m = row0 + wm * 128 + i * 16 + 4 * kq + e;
+          const uint32_t o = n < N ? (uint32_t)m * (uint32_t)N + (uint32_t)n : kNone / 4u;
           const float v = acc[i][j][e];
-          const int64_t o = m * N + n;
-          if (ytype == (int)YType::F16)
-            reinterpret_cast<uint16_t *>(Y)[o] = float_to_half_bits(v);
-          else if (ytype == (int)YType::BF16)
-            reinterpret_cast<uint16_t *>(Y)[o] = float_to_bf16_bits(v);
+          if constexpr (YT == (int)YType::F16)
+            __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(v), rY, o * 2u, 0, 0);
+          else if constexpr (YT == (int)YType::BF16)
+            __builtin_amdgcn_raw_buffer_store_b16(float_to_bf16_bits(v), rY, o * 2u, 0, 0);
           else
-            reinterpret_cast<float *>(Y)[o] = v;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rY, o * 4u, 0, 0);
         }
       }
     }
   } else {
+    const rsrc_t rR = make_rsrc(Yref, (uint32_t)M * (uint32_t)N * 4u);
     double sum = 0.0;
 #pragma unroll
-    for (int i = 0; i < kMT; ++i) {
+    for (int j = 0; j < kNT; ++j) {
+      const int n = col0 + wn * 64 + j * 16 + c;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t m = row0 + wm * 64 + i * 16 + 4 * kq + e;
-        if (m >= M) continue;
+      for (int i = 0; i < kMT; ++i) {
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) {
-          const int64_t n = ncol[j];
-          if (n >= N) continue;
-          const double d = (double)Yref[m * N + n] - (double)acc[i][j][e];
+        for (int e = 0; e < 4; ++e) {
+          // rows >= M and columns >= N read 0 and have acc = 0: they add nothing
+          const int m = row0 + wm * 128 + i * 16 + 4 * kq + e;
+          const uint32_t o = n < N ? (uint32_t)m * (uint32_t)N + (uint32_t)n : kNone / 4u;
+          const float ref = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, o * 4u, 0, 0));
+          const double d = (double)ref - (double)acc[i][j][e];
           sum = __builtin_fma(d, d, sum);
         }
       }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    __shared__ double wsum[4];
+    __syncthreads();
+    double *wsum = reinterpret_cast<double *>(sA0);
     if (lane == 0) wsum[wave] = sum;
     __syncthreads();
     if (tid == 0) partials[tm * tiles_n + tn] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
@@ -275,13 +326,55 @@ int64_t gemm_tile_count(int64_t M, int64_t N) {
   return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
 }
 
+// Largest row count per launch that keeps every per-launch buffer below 2 GiB
+// (a multiple of the 256-row tile).
+static int64_t rows_per_launch(int64_t N, int64_t K) {
+  const int64_t lim = ((int64_t)1 << 31) - 1;
+  int64_t r = lim / (K * 2);
+  const int64_t ry = lim / (N * 4);
+  r = r < ry ? r : ry;
+  return (r / kBM) * kBM;
+}
+
+bool gemm_supported(int64_t N, int64_t K, bool dense) {
+  const int64_t lim = ((int64_t)1 << 31) - 1;
+  return (dense ? N * K * 2 : N * K / 2) <= lim && rows_per_launch(N, K) > 0;
+}
+
+template <class XT, int GS, int EPI, bool DENSE, int YT>
+static hipError_t gemm_go1(const uint16_t *X, const uint32_t *qw, const uint16_t *Wd,
+                          const uint16_t *sc, const uint8_t *zr, int64_t M, int64_t N, int64_t K,
+                          void *Y, int yt, const float *Yref, double *partials, hipStream_t st) {
+  const int ysize = yt == (int)YType::F32 ? 4 : 2;
+  const int64_t rows = rows_per_launch(N, K);
+  if (rows <= 0) return hipErrorInvalidValue;
+  int64_t tile_base = 0;
+  for (int64_t m0 = 0; m0 < M; m0 += rows) {
+    const int64_t mm = M - m0 < rows ? M - m0 : rows;
+    const dim3 grid((unsigned)gemm_tile_count(mm, N));
+    gemm_kernel<XT, GS, EPI, DENSE, YT><<<grid, kThreads, 0, st>>>(
+        X + m0 * K, qw, Wd, sc, zr, (int)mm, (int)N, (int)K,
+        Y ? reinterpret_cast<char *>(Y) + m0 * N * ysize : nullptr,
+        Yref ? Yref + m0 * N : nullptr, partials ? partials + tile_base : nullptr);
+    tile_base += gemm_tile_count(mm, N);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <class XT, int GS, int EPI, bool DENSE>
-static void gemm_go(const uint16_t *X, const uint32_t *qw, const uint16_t *Wd,
-                    const uint16_t *sc, const uint8_t *zr, int64_t M, int64_t N, int64_t K,
-                    void *Y, int yt, const float *Yref, double *partials, hipStream_t st) {
-  const dim3 grid((unsigned)gemm_tile_count(M, N));
-  gemm_kernel<XT, GS, EPI, DENSE><<<grid, kThreads, 0, st>>>(X, qw, Wd, sc, zr, M, N, K, Y, yt,
-                                                            Yref, partials);
+static hipError_t gemm_go(const uint16_t *X, const uint32_t *qw, const uint16_t *Wd,
+                          const uint16_t *sc, const uint8_t *zr, int64_t M, int64_t N, int64_t K,
+                          void *Y, int yt, const float *Yref, double *partials, hipStream_t st) {
+  if (EPI == kEpiLoss || yt == (int)YType::F32)
+    return gemm_go1<XT, GS, EPI, DENSE, (int)YType::F32>(X, qw, Wd, sc, zr, M, N, K, Y, yt, Yref,
+                                                         partials, st);
+  if (yt == (int)YType::BF16)
+    return gemm_go1<XT, GS, EPI, DENSE, (int)YType::BF16>(X, qw, Wd, sc, zr, M, N, K, Y, yt, Yref,
+                                                          partials, st);
+  return gemm_go1<XT, GS, EPI, DENSE, (int)YType::F16>(X, qw, Wd, sc, zr, M, N, K, Y, yt, Yref,
+                                                       partials, st);
 }
 
 hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
@@ -290,42 +383,31 @@ hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
   if (M == 0 || N == 0) return hipSuccess;
   const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
   const int y = (int)yt;
-  if (xt == XType::F16) {
-    if (gs == 128)
-      gemm_go<TagF16, 128, kEpiStore, false>(x, qweight, nullptr, scales, zeros, M, N, K, Y, y,
-                                             nullptr, nullptr, st);
-    else
-      gemm_go<TagF16, 64, kEpiStore, false>(x, qweight, nullptr, scales, zeros, M, N, K, Y, y,
-                                            nullptr, nullptr, st);
-  } else {
-    if (gs == 128)
-      gemm_go<TagBF16, 128, kEpiStore, false>(x, qweight, nullptr, scales, zeros, M, N, K, Y, y,
-                                              nullptr, nullptr, st);
-    else
-      gemm_go<TagBF16, 64, kEpiStore, false>(x, qweight, nullptr, scales, zeros, M, N, K, Y, y,
-                                             nullptr, nullptr, st);
-  }
-  return hipGetLastError();
+  if (xt == XType::F16)
+    return gs == 128 ? gemm_go<TagF16, 128, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
+                                                              M, N, K, Y, y, nullptr, nullptr, st)
+                     : gemm_go<TagF16, 64, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
+                                                             M, N, K, Y, y, nullptr, nullptr, st);
+  return gs == 128 ? gemm_go<TagBF16, 128, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
+                                                             M, N, K, Y, y, nullptr, nullptr, st)
+                   : gemm_go<TagBF16, 64, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
+                                                            M, N, K, Y, y, nullptr, nullptr, st);
 }
 
 hipError_t launch_gemm_dense_f32(const uint16_t *X, const uint16_t *W, int64_t M, int64_t N,
                                  int64_t K, float *Y, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  gemm_go<TagF16, 128, kEpiStore, true>(X, nullptr, W, nullptr, nullptr, M, N, K, Y,
-                                        (int)YType::F32, nullptr, nullptr, st);
-  return hipGetLastError();
+  return gemm_go<TagF16, 128, kEpiStore, true>(X, nullptr, W, nullptr, nullptr, M, N, K, Y,
+                                               (int)YType::F32, nullptr, nullptr, st);
 }
 
 hipError_t launch_gemm_loss(const uint16_t *A, const uint32_t *qweight, const uint16_t *scales,
                             const uint8_t *zeros, int64_t M, int64_t N, int64_t K, int gs,
                             const float *Yref, double *partials, hipStream_t st) {
-  if (gs == 128)
-    gemm_go<TagF16, 128, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M, N, K, nullptr, 0,
-                                          Yref, partials, st);
-  else
-    gemm_go<TagF16, 64, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M, N, K, nullptr, 0,
-                                         Yref, partials, st);
-  return hipGetLastError();
+  return gs == 128 ? gemm_go<TagF16, 128, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M,
+                                                           N, K, nullptr, 0, Yref, partials, st)
+                   : gemm_go<TagF16, 64, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M,
+                                                          N, K, nullptr, 0, Yref, partials, st);
 }
 
 }  // namespace awq

@@ -23,64 +23,143 @@
 
 namespace awq {
 
-template <class XT, int GS, int NW, int U>
+namespace {
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+}  // namespace
+
+// LDS layout (dynamic shared memory, byte offsets):
+//   [0, xbytes)              activation rows 0..M-1 (when staged), then one
+//                            zero row that lanes for rows >= M read
+//   [soff, soff + 32*G)      scales of the 16 columns, fp16 bits, [16][G]
+//   [zoff, zoff + 16*G)      zero points of the 16 columns, u8, [16][G]
+// The cross-wave reduction reuses the start of the buffer after the loop.
+struct GemvSmem {
+  uint32_t xrow;     // bytes per staged activation row (K * 2)
+  uint32_t soff, zoff, total;
+};
+
+__host__ __device__ inline GemvSmem gemv_smem(int M, int K, int G, bool stage_x) {
+  GemvSmem L;
+  L.xrow = (uint32_t)K * 2u;
+  const uint32_t xbytes = stage_x ? L.xrow * (uint32_t)(M + 1) : 0u;
+  L.soff = (xbytes + 15u) & ~15u;
+  L.zoff = L.soff + 32u * (uint32_t)G;
+  L.total = L.zoff + 16u * (uint32_t)G;
+  return L;
+}
+
+// Memory instructions are the scarce resource here (each one occupies the
+// CU's address unit for tens of cycles), so per group a wave issues exactly
+// one: the 16-byte packed-weight load of each lane.  Activations (staged by
+// the workgroup once, by DMA, when M*K*2 fits the LDS budget), scales and
+// zero points come from LDS.  All global reads use buffer resources, so rows
+// >= M, columns >= N and groups >= G read zero without branches.
+template <class XT, int GS, int NW, int U, bool STAGE_X>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
-    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M,
-    int64_t N, int64_t K, void *__restrict__ Y, int ytype) {
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
+    void *__restrict__ Y, int ytype) {
   constexpr int kWpl = GS / 32;            // packed words per lane per group
   constexpr bool kBF16 = __is_same(XT, TagBF16);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int c = lane & 15;
   const int kq = lane >> 4;
-  const int64_t n = (int64_t)blockIdx.x * 16 + c;
-  const bool nvalid = n < N;
-  const int64_t G = K / GS;
-  const int64_t wrow = K / 8;
-  const bool mvalid = c < M;               // A-operand row of this lane
+  const int n0 = blockIdx.x * 16;
+  const int n = n0 + c;
+  const int G = K / GS;
+  const GemvSmem L = gemv_smem(M, K, G, STAGE_X);
 
-  const uint32_t *wp = qweight + (nvalid ? n : 0) * wrow + kq * kWpl;
-  const uint16_t *sp = scales + (nvalid ? n : 0) * G;
-  const uint8_t *zp = zeros + (nvalid ? n : 0) * G;
-  const uint16_t *xp = X + (int64_t)(mvalid ? c : 0) * K + kq * 8 * kWpl;
+  const rsrc_t rQ = make_rsrc(qweight, (uint32_t)N * (uint32_t)K / 2u);
+  const rsrc_t rS = make_rsrc(scales, (uint32_t)N * (uint32_t)G * 2u);
+  const rsrc_t rZ = make_rsrc(zeros, (uint32_t)N * (uint32_t)G);
+  const rsrc_t rX = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+
+  // ---- prologue: scales / zeros of the 16 columns (contiguous [16][G]) -------
+  {
+    uint16_t *ss = reinterpret_cast<uint16_t *>(smem + L.soff);
+    uint8_t *zs = reinterpret_cast<uint8_t *>(smem + L.zoff);
+    const uint32_t base = (uint32_t)n0 * (uint32_t)G;
+    for (int i = tid; i < 16 * G; i += 64 * NW) {
+      ss[i] = __builtin_amdgcn_raw_buffer_load_b16(rS, (base + (uint32_t)i) * 2u, 0, 0);
+      zs[i] = __builtin_amdgcn_raw_buffer_load_b8(rZ, base + (uint32_t)i, 0, 0);
+    }
+  }
+  // ---- prologue: activation rows by DMA, plus a zero row --------------------
+  if constexpr (STAGE_X) {
+    const uint32_t rowbytes = L.xrow;
+    const uint32_t chunks = (uint32_t)M * rowbytes / 1024u;     // whole KiB per row set
+    for (uint32_t ch = (uint32_t)wave; ch < chunks; ch += NW) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rX, (__attribute__((address_space(3))) void *)(smem + ch * 1024u), 16,
+          ch * 1024u + (uint32_t)lane * 16u, 0, 0, 0);
+    }
+    // tail of the rows that is not a whole KiB, and the zero row
+    const uint32_t done = chunks * 1024u, total = (uint32_t)M * rowbytes;
+    for (uint32_t b = done + (uint32_t)tid * 16u; b < total; b += 64u * NW * 16u)
+      *reinterpret_cast<u32x4 *>(smem + b) =
+          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, b, 0, 0));
+    for (uint32_t b = total + (uint32_t)tid * 16u; b < total + rowbytes; b += 64u * NW * 16u)
+      *reinterpret_cast<u32x4 *>(smem + b) = u32x4{0u, 0u, 0u, 0u};
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) and lgkmcnt(0): DMA and LDS stores done
+  __syncthreads();
+
+  const uint32_t q_lane = (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(kq * kWpl * 4);
+  // activation row of this lane as the A operand: row c, or the zero row
+  const char *xlds = smem + (uint32_t)(c < M ? c : M) * L.xrow + (uint32_t)(kq * kWpl * 16);
+  const uint32_t x_lane = (uint32_t)c * (uint32_t)K * 2u + (uint32_t)(kq * kWpl * 16);
+  const uint16_t *ss = reinterpret_cast<const uint16_t *>(smem + L.soff) + c * G;
+  const uint8_t *zs = reinterpret_cast<const uint8_t *>(smem + L.zoff) + c * G;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t g0 = wave; g0 < G; g0 += (int64_t)NW * U) {
+  for (int g0 = wave; g0 < G; g0 += NW * U) {
     uint32_t raw[U][kWpl];
     u32x4 a[U][kWpl];
-    float sc[U];
-    uint32_t zr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t g = g0 + (int64_t)u * NW;
-      const bool gv = g < G;
-      if (kWpl == 4) {
-        u32x4 r = {0u, 0u, 0u, 0u};
-        if (gv && nvalid) r = *reinterpret_cast<const u32x4 *>(wp + g * (GS / 8));
+      const int g = g0 + u * NW;
+      // a group past the end reads zeros (whole offset replaced, no wrap)
+      const uint32_t qo = g < G ? q_lane + (uint32_t)g * (GS / 2) : 0xFFFFFFF0u;
+      if constexpr (kWpl == 4) {
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo, 0, 0));
 #pragma unroll
-        for (int j = 0; j < kWpl; ++j) raw[u][j] = r[j];
+        for (int j = 0; j < kWpl; ++j) raw[u][j] = v[j];
       } else {
-        u32x2 r = {0u, 0u};
-        if (gv && nvalid) r = *reinterpret_cast<const u32x2 *>(wp + g * (GS / 8));
+        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rQ, qo, 0, 0));
 #pragma unroll
-        for (int j = 0; j < kWpl; ++j) raw[u][j] = r[j];
+        for (int j = 0; j < kWpl; ++j) raw[u][j] = v[j];
       }
-      sc[u] = (gv && nvalid) ? half_bits_to_float(sp[g]) : 0.0f;
-      zr[u] = (gv && nvalid) ? (uint32_t)zp[g] : 0u;
+      if constexpr (!STAGE_X) {
 #pragma unroll
-      for (int j = 0; j < kWpl; ++j) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (gv && mvalid) x = *reinterpret_cast<const u32x4 *>(xp + g * GS + 8 * j);
-        a[u][j] = x;
+        for (int j = 0; j < kWpl; ++j)
+          a[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rX, x_lane + (uint32_t)g * (GS * 2) + 16u * j, 0, 0));
       }
     }
+    // keep the batch's loads ahead of the math (the scheduler would otherwise
+    // sink each load next to its use and serialize the round trips)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int g = g0 + u * NW;
+      const int gs = g < G ? g : G - 1;
+      if constexpr (STAGE_X) {
+#pragma unroll
+        for (int j = 0; j < kWpl; ++j)
+          a[u][j] = *reinterpret_cast<const u32x4 *>(xlds + (uint32_t)gs * (GS * 2) + 16u * j);
+      }
+      const uint32_t zr = zs[gs];
+      const float sc = g < G ? half_bits_to_float(ss[gs]) : 0.0f;
       f32x4 t = {0.f, 0.f, 0.f, 0.f};
       if constexpr (!kBF16) {
-        const DeqF16 deq(zr[u]);
+        const DeqF16 deq(zr);
 #pragma unroll
         for (int j = 0; j < kWpl; ++j) t = mfma32<TagF16>(a[u][j], deq(raw[u][j]), t);
       } else {
@@ -91,27 +170,28 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
           t = mfma32<TagBF16>(a[u][j], deq(raw[u][j]), t);
           r = mfma32<TagBF16>(a[u][j], bf16_ones(), r);
         }
-        const float cz = -(float)(128u + zr[u]);
+        const float cz = -(float)(128u + zr);
 #pragma unroll
         for (int e = 0; e < 4; ++e) t[e] = __builtin_fmaf(cz, r[e], t[e]);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(t[e], sc[u], acc[e]);
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(t[e], sc, acc[e]);
     }
   }
 
-  __shared__ f32x4 red[NW][64];
-  red[wave][lane] = acc;
+  __syncthreads();
+  f32x4 *red = reinterpret_cast<f32x4 *>(smem);
+  red[wave * 64 + lane] = acc;
   __syncthreads();
   if (wave != 0) return;
-  f32x4 sum = red[0][lane];
+  f32x4 sum = red[lane];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
-    const f32x4 o = red[w][lane];
+    const f32x4 o = red[w * 64 + lane];
 #pragma unroll
     for (int e = 0; e < 4; ++e) sum[e] += o[e];
   }
-  if (!nvalid) return;
+  if (n >= N) return;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int m = 4 * kq + e;
@@ -126,13 +206,34 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
   }
 }
 
+// Activations are staged in LDS when M rows (plus the zero row) fit in
+// 48 KiB; larger M*K streams them from global memory instead.
+constexpr uint32_t kGemvStageBytes = 48u * 1024u;
+
 template <class XT, int GS>
 static void gemv_dispatch(const uint16_t *X, const uint32_t *qw, const uint16_t *sc,
                           const uint8_t *zr, int M, int64_t N, int64_t K, void *Y, YType yt,
                           hipStream_t st) {
   constexpr int NW = 8, U = 4;
   const dim3 grid((unsigned)((N + 15) / 16));
-  gemv_kernel<XT, GS, NW, U><<<grid, 64 * NW, 0, st>>>(X, qw, sc, zr, M, N, K, Y, (int)yt);
+  const int G = (int)(K / GS);
+  const bool stage = (uint64_t)(M + 1) * (uint64_t)K * 2u <= kGemvStageBytes;
+  const GemvSmem L = gemv_smem(M, (int)K, G, stage);
+  // the reduction reuses the buffer: at least NW * 64 * 16 bytes
+  const uint32_t bytes = L.total > 64u * NW * 16u ? L.total : 64u * NW * 16u;
+  if (stage)
+    gemv_kernel<XT, GS, NW, U, true><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
+                                                                   (int)K, Y, (int)yt);
+  else
+    gemv_kernel<XT, GS, NW, U, false><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
+                                                                    (int)K, Y, (int)yt);
+}
+
+bool gemv_supported(int64_t M, int64_t K, int gs) {
+  const int64_t G = K / gs;
+  const bool stage = (uint64_t)(M + 1) * (uint64_t)K * 2u <= kGemvStageBytes;
+  const GemvSmem L = gemv_smem((int)M, (int)K, (int)G, stage);
+  return M <= 16 && L.total <= 64u * 1024u;
 }
 
 hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,

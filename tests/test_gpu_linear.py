@@ -86,8 +86,11 @@ def test_ragged_shapes(M, N, K, g, dt):
         Y32 = out_to_f64(_run(X, dt, pd, g, kern, torch.float32))
         assert_close(Y32, ref, f"{M}x{N}x{K} fp32 out")
         Y16 = out_to_f64(_run(X, dt, pd, g, kern))          # same dtype as X
-        assert_close(Y16, ref, f"{M}x{N}x{K} 16-bit out")
-        # the 16-bit output is the fp32 result rounded once
+        if dt == "f16":
+            assert_close(Y16, ref, f"{M}x{N}x{K} 16-bit out")
+        # The 16-bit output is the fp32 result rounded once.  For bf16 that
+        # rounding alone (relative step 2^-8) exceeds the 1e-3 Frobenius bound,
+        # so bf16 activations are held to the bound through the fp32 output.
         want = torch.from_numpy(Y32).to(torch.float16 if dt == "f16" else torch.bfloat16)
         assert np.array_equal(Y16, want.float().numpy().astype(np.float64))
 
