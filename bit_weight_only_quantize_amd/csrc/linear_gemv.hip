@@ -30,24 +30,30 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
 }
 }  // namespace
 
-// LDS layout (dynamic shared memory, byte offsets):
-//   [0, xbytes)              activation rows 0..M-1 (when staged), then one
-//                            zero row that lanes for rows >= M read
-//   [soff, soff + 32*G)      scales of the 16 columns, fp16 bits, [16][G]
-//   [zoff, zoff + 16*G)      zero points of the 16 columns, u8, [16][G]
+// LDS layout (dynamic shared memory, byte offsets; every region starts on a
+// 1 KiB boundary because a DMA instruction writes 1 KiB):
+//   [0, xbytes)              activation rows 0..M-1 (when staged)
+//   [zrow, zrow + K*2)       a zero row that lanes for rows >= M read
+//   [soff, ...)              scales of the 16 columns, fp16 bits, [16][G]
+//   [zoff, ...)              zero points of the 16 columns, u8, [16][G]
 // The cross-wave reduction reuses the start of the buffer after the loop.
+// Largest 16*G the kernel stages (scale/zero elements of one workgroup).
+constexpr int kGemvMaxSZ = 4096;
+
 struct GemvSmem {
-  uint32_t xrow;     // bytes per staged activation row (K * 2)
-  uint32_t soff, zoff, total;
+  uint32_t xrow;     // bytes per activation row (K * 2)
+  uint32_t zrow, soff, zoff, total;
 };
+
+__host__ __device__ inline uint32_t kib_up(uint32_t b) { return (b + 1023u) & ~1023u; }
 
 __host__ __device__ inline GemvSmem gemv_smem(int M, int K, int G, bool stage_x) {
   GemvSmem L;
   L.xrow = (uint32_t)K * 2u;
-  const uint32_t xbytes = stage_x ? L.xrow * (uint32_t)(M + 1) : 0u;
-  L.soff = (xbytes + 15u) & ~15u;
-  L.zoff = L.soff + 32u * (uint32_t)G;
-  L.total = L.zoff + 16u * (uint32_t)G;
+  L.zrow = stage_x ? kib_up(L.xrow * (uint32_t)M) : 0u;
+  L.soff = stage_x ? kib_up(L.zrow + L.xrow) : 0u;
+  L.zoff = L.soff + kib_up(32u * (uint32_t)G);
+  L.total = L.zoff + kib_up(16u * (uint32_t)G);
   return L;
 }
 
@@ -80,80 +86,123 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
   const rsrc_t rZ = make_rsrc(zeros, (uint32_t)N * (uint32_t)G);
   const rsrc_t rX = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
 
-  // ---- prologue: scales / zeros of the 16 columns (contiguous [16][G]) -------
+  const uint32_t q_lane = (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(kq * kWpl * 4);
+  const uint32_t x_lane = (uint32_t)c * (uint32_t)K * 2u + (uint32_t)(kq * kWpl * 16);
+  struct Batch {
+    uint32_t raw[U][kWpl];
+    u32x4 a[U][kWpl];      // used only when activations are not staged
+  };
+  // Packed weights (and, without staging, activations) of groups
+  // g0, g0 + NW, ..., g0 + (U-1)*NW.  A group past the end reads zeros (the
+  // whole offset is replaced, so nothing wraps back into range).
+  auto load_batch = [&](int g0, Batch &b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = g0 + u * NW;
+      const uint32_t qo = g < G ? q_lane + (uint32_t)g * (GS / 2) : 0xFFFFFFF0u;
+      if constexpr (kWpl == 4) {
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo, 0, 0));
+#pragma unroll
+        for (int j = 0; j < kWpl; ++j) b.raw[u][j] = v[j];
+      } else {
+        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rQ, qo, 0, 0));
+#pragma unroll
+        for (int j = 0; j < kWpl; ++j) b.raw[u][j] = v[j];
+      }
+      if constexpr (!STAGE_X) {
+        const uint32_t xo = g < G ? x_lane + (uint32_t)g * (GS * 2) : 0xFFFFFFF0u;
+#pragma unroll
+        for (int j = 0; j < kWpl; ++j)
+          b.a[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, xo + 16u * j, 0, 0));
+      }
+    }
+  };
+
+  // ---- prologue ---------------------------------------------------------------
+  // Staging loads are issued before the weight stream: issued after it, they
+  // would queue behind every CU's weight traffic and the barrier below would
+  // hold all math until the stream had drained.
+  //  * activation rows go by DMA (buffer_load ... lds), 1 KiB per instruction;
+  //    M*K*2 is a multiple of 128 bytes, so no 16-byte chunk straddles the end
+  //    of X;
+  //  * scales and zero points of the 16 columns ([16][G], contiguous) are read
+  //    element by element into registers (a 16-byte chunk could straddle the
+  //    end of those arrays, where the range check would zero it) and written
+  //    to LDS after the weight batch is in flight.
+  typedef __attribute__((address_space(3))) void lds_t;
+  constexpr int kSZ = kGemvMaxSZ / (64 * NW);   // scale/zero elements per thread
+  const int nsz = (16 * G + 64 * NW - 1) / (64 * NW);   // uniform: rounds needed
+  uint32_t sreg[kSZ], zreg[kSZ];
+  {
+    const uint32_t base = (uint32_t)n0 * (uint32_t)G;
+#pragma unroll
+    for (int r = 0; r < kSZ; ++r) {
+      if (r >= nsz) break;
+      const uint32_t i = (uint32_t)(tid + r * 64 * NW);
+      const uint32_t o = i < 16u * (uint32_t)G ? base + i : 0x7FFFFFF0u;
+      sreg[r] = __builtin_amdgcn_raw_buffer_load_b16(rS, o * 2u, 0, 0);
+      zreg[r] = __builtin_amdgcn_raw_buffer_load_b8(rZ, o, 0, 0);
+    }
+    if constexpr (STAGE_X) {
+      const uint32_t nx = (uint32_t)M * L.xrow / 1024u + (((uint32_t)M * L.xrow) % 1024u ? 1u : 0u);
+      for (uint32_t i = (uint32_t)wave; i < nx; i += NW)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_t *)(smem + i * 1024u), 16,
+                                                 i * 1024u + (uint32_t)lane * 16u, 0, 0, 0);
+      // zero row (rows >= M of the A operand read it)
+      for (uint32_t b = (uint32_t)tid * 16u; b < L.xrow; b += 64u * NW * 16u)
+        *reinterpret_cast<u32x4 *>(smem + L.zrow + b) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // First batch of packed weights, behind the staging loads.
+  Batch cur, nxt;
+  load_batch(wave, cur);
+  __builtin_amdgcn_sched_barrier(0);
   {
     uint16_t *ss = reinterpret_cast<uint16_t *>(smem + L.soff);
     uint8_t *zs = reinterpret_cast<uint8_t *>(smem + L.zoff);
-    const uint32_t base = (uint32_t)n0 * (uint32_t)G;
-    for (int i = tid; i < 16 * G; i += 64 * NW) {
-      ss[i] = __builtin_amdgcn_raw_buffer_load_b16(rS, (base + (uint32_t)i) * 2u, 0, 0);
-      zs[i] = __builtin_amdgcn_raw_buffer_load_b8(rZ, base + (uint32_t)i, 0, 0);
+#pragma unroll
+    for (int r = 0; r < kSZ; ++r) {
+      if (r >= nsz) break;
+      const int i = tid + r * 64 * NW;
+      if (i < 16 * G) {
+        ss[i] = (uint16_t)sreg[r];
+        zs[i] = (uint8_t)zreg[r];
+      }
     }
   }
-  // ---- prologue: activation rows by DMA, plus a zero row --------------------
-  if constexpr (STAGE_X) {
-    const uint32_t rowbytes = L.xrow;
-    const uint32_t chunks = (uint32_t)M * rowbytes / 1024u;     // whole KiB per row set
-    for (uint32_t ch = (uint32_t)wave; ch < chunks; ch += NW) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rX, (__attribute__((address_space(3))) void *)(smem + ch * 1024u), 16,
-          ch * 1024u + (uint32_t)lane * 16u, 0, 0, 0);
-    }
-    // tail of the rows that is not a whole KiB, and the zero row
-    const uint32_t done = chunks * 1024u, total = (uint32_t)M * rowbytes;
-    for (uint32_t b = done + (uint32_t)tid * 16u; b < total; b += 64u * NW * 16u)
-      *reinterpret_cast<u32x4 *>(smem + b) =
-          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, b, 0, 0));
-    for (uint32_t b = total + (uint32_t)tid * 16u; b < total + rowbytes; b += 64u * NW * 16u)
-      *reinterpret_cast<u32x4 *>(smem + b) = u32x4{0u, 0u, 0u, 0u};
-  }
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) and lgkmcnt(0): DMA and LDS stores done
-  __syncthreads();
 
-  const uint32_t q_lane = (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(kq * kWpl * 4);
+  // LDS-DMA completion is not ordered with the register loads behind it, so
+  // the wave waits for all its loads (vmcnt(0): its DMA has landed) and for
+  // its zero-row stores (lgkmcnt(0)) before the barrier.  The staging was
+  // issued first and the batch is needed next anyway, so little is lost.
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __builtin_amdgcn_s_barrier();
+
   // activation row of this lane as the A operand: row c, or the zero row
-  const char *xlds = smem + (uint32_t)(c < M ? c : M) * L.xrow + (uint32_t)(kq * kWpl * 16);
-  const uint32_t x_lane = (uint32_t)c * (uint32_t)K * 2u + (uint32_t)(kq * kWpl * 16);
+  const char *xlds = smem + (c < M ? (uint32_t)c * L.xrow : L.zrow) + (uint32_t)(kq * kWpl * 16);
   const uint16_t *ss = reinterpret_cast<const uint16_t *>(smem + L.soff) + c * G;
   const uint8_t *zs = reinterpret_cast<const uint8_t *>(smem + L.zoff) + c * G;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
+  // Software pipeline: the next batch's loads are in flight while this batch
+  // is dequantized and multiplied.
   for (int g0 = wave; g0 < G; g0 += NW * U) {
-    uint32_t raw[U][kWpl];
-    u32x4 a[U][kWpl];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int g = g0 + u * NW;
-      // a group past the end reads zeros (whole offset replaced, no wrap)
-      const uint32_t qo = g < G ? q_lane + (uint32_t)g * (GS / 2) : 0xFFFFFFF0u;
-      if constexpr (kWpl == 4) {
-        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo, 0, 0));
-#pragma unroll
-        for (int j = 0; j < kWpl; ++j) raw[u][j] = v[j];
-      } else {
-        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rQ, qo, 0, 0));
-#pragma unroll
-        for (int j = 0; j < kWpl; ++j) raw[u][j] = v[j];
-      }
-      if constexpr (!STAGE_X) {
-#pragma unroll
-        for (int j = 0; j < kWpl; ++j)
-          a[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rX, x_lane + (uint32_t)g * (GS * 2) + 16u * j, 0, 0));
-      }
-    }
-    // keep the batch's loads ahead of the math (the scheduler would otherwise
-    // sink each load next to its use and serialize the round trips)
+    load_batch(g0 + NW * U, nxt);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int g = g0 + u * NW;
       const int gs = g < G ? g : G - 1;
-      if constexpr (STAGE_X) {
+      u32x4 a[kWpl];
 #pragma unroll
-        for (int j = 0; j < kWpl; ++j)
-          a[u][j] = *reinterpret_cast<const u32x4 *>(xlds + (uint32_t)gs * (GS * 2) + 16u * j);
+      for (int j = 0; j < kWpl; ++j) {
+        if constexpr (STAGE_X)
+          a[j] = *reinterpret_cast<const u32x4 *>(xlds + (uint32_t)gs * (GS * 2) + 16u * j);
+        else
+          a[j] = cur.a[u][j];
       }
       const uint32_t zr = zs[gs];
       const float sc = g < G ? half_bits_to_float(ss[gs]) : 0.0f;
@@ -161,14 +210,14 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
       if constexpr (!kBF16) {
         const DeqF16 deq(zr);
 #pragma unroll
-        for (int j = 0; j < kWpl; ++j) t = mfma32<TagF16>(a[u][j], deq(raw[u][j]), t);
+        for (int j = 0; j < kWpl; ++j) t = mfma32<TagF16>(a[j], deq(cur.raw[u][j]), t);
       } else {
         const DeqBF16 deq;
         f32x4 r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < kWpl; ++j) {
-          t = mfma32<TagBF16>(a[u][j], deq(raw[u][j]), t);
-          r = mfma32<TagBF16>(a[u][j], bf16_ones(), r);
+          t = mfma32<TagBF16>(a[j], deq(cur.raw[u][j]), t);
+          r = mfma32<TagBF16>(a[j], bf16_ones(), r);
         }
         const float cz = -(float)(128u + zr);
 #pragma unroll
@@ -177,6 +226,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(t[e], sc, acc[e]);
     }
+    cur = nxt;
   }
 
   __syncthreads();
@@ -214,7 +264,7 @@ template <class XT, int GS>
 static void gemv_dispatch(const uint16_t *X, const uint32_t *qw, const uint16_t *sc,
                           const uint8_t *zr, int M, int64_t N, int64_t K, void *Y, YType yt,
                           hipStream_t st) {
-  constexpr int NW = 8, U = 4;
+  constexpr int NW = 8;
   const dim3 grid((unsigned)((N + 15) / 16));
   const int G = (int)(K / GS);
   const bool stage = (uint64_t)(M + 1) * (uint64_t)K * 2u <= kGemvStageBytes;
@@ -222,10 +272,10 @@ static void gemv_dispatch(const uint16_t *X, const uint32_t *qw, const uint16_t 
   // the reduction reuses the buffer: at least NW * 64 * 16 bytes
   const uint32_t bytes = L.total > 64u * NW * 16u ? L.total : 64u * NW * 16u;
   if (stage)
-    gemv_kernel<XT, GS, NW, U, true><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
+    gemv_kernel<XT, GS, NW, 4, true><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
                                                                    (int)K, Y, (int)yt);
   else
-    gemv_kernel<XT, GS, NW, U, false><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
+    gemv_kernel<XT, GS, NW, 2, false><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
                                                                     (int)K, Y, (int)yt);
 }
 
@@ -233,7 +283,7 @@ bool gemv_supported(int64_t M, int64_t K, int gs) {
   const int64_t G = K / gs;
   const bool stage = (uint64_t)(M + 1) * (uint64_t)K * 2u <= kGemvStageBytes;
   const GemvSmem L = gemv_smem((int)M, (int)K, (int)G, stage);
-  return M <= 16 && L.total <= 64u * 1024u;
+  return M <= 16 && 16 * G <= kGemvMaxSZ && L.total <= 64u * 1024u;
 }
 
 hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,

@@ -83,6 +83,8 @@ def test_linear_validation():
     assert _lin(X=NULL) == binding.AWQ_ERR_INVALID_ARG
     assert _lin(X=ctypes.c_void_p(0x10002)) == binding.AWQ_ERR_INVALID_ARG
     assert _lin(Y=ctypes.c_void_p(0x10002), yt=2) == binding.AWQ_ERR_INVALID_ARG
+    assert lib.awq_linear_ex(FAKE, 0, FAKE, ctypes.c_void_p(0x10001), FAKE, 3, 64, 256, cfg(128),
+                             FAKE, 0, 0, NULL) == binding.AWQ_ERR_INVALID_ARG   # odd scales
     assert _lin(M=0) == binding.AWQ_OK
     assert _lin(N=0, X=NULL) == binding.AWQ_OK
     assert lib.awq_linear(FAKE, 0, FAKE, FAKE, FAKE, 3, 64, 200, cfg(128), FAKE, 0, NULL) \
