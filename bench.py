@@ -47,7 +47,55 @@ def parse():
     p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--rows", choices=("all", "none"), default="all")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 256 MiB device-to-device copy 10 times (the "
+                        "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+# Kernel sources whose hash keys the stored HBM-traffic measurement: once any
+# of them changes, the stored counters no longer describe the kernel.
+GEMV_SOURCES = ("bit_weight_only_quantize_amd/csrc/linear_gemv.hip",
+                "bit_weight_only_quantize_amd/csrc/device_common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_decode_m1_hbm_traffic.txt")
+
+
+def gemv_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMV_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per decode step from the committed counter summary, or None
+    when it is missing or was taken on other kernel sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for ln in f:
+                if ":" in ln and not ln.startswith("#"):
+                    k, v = ln.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_sha256_16") != gemv_source_hash():
+            return None
+        return float(kv["hbm_bytes_per_step"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    import torch
+    n = 128 << 20                       # fp16 elements: 256 MiB
+    src = torch.ones(n, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "launches": 10}))
 
 
 class Launcher:
@@ -146,6 +194,10 @@ def main():
               f"(this build has no multi-GPU path; run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
     import torch
     import bit_weight_only_quantize_amd as awq
     import workloads as wl
@@ -156,7 +208,7 @@ def main():
 
     # ---- headline workload: M=1 decode over three 7B-class layers --------------
     cases = wl.gemv_cases(Ms=(1,))
-    per_step_bytes = sum(c.weight_bytes for c in cases)
+    per_step_bytes = sum(c.io_bytes for c in cases)
     R = copies_for(per_step_bytes)
     log(f"decode GEMV: {len(cases)} layers, {per_step_bytes / 1e6:.2f} MB/step, {R} weight copies")
     layers = []
@@ -197,19 +249,31 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
     value = per_step_bytes * args.steps / wall / 1e9
-    achieved = per_step_bytes / gpu_step / 1e9
     log(f"decode step: wall {ms_per_step * 1e3:.2f} us, GPU {gpu_step * 1e6:.2f} us per step")
 
-    # per-layer kernel time (graph of R launches on rotating copies)
+    # per-layer kernel time: a graph of launches over >= 512 MB of copies of
+    # that layer alone, so no launch finds its weights in the Infinity Cache
     per_layer = []
     for (c, Xd, copies, Yd) in layers:
-        def f(c=c, Xd=Xd, copies=copies, Yd=Yd):
-            for r in range(R):
-                L.linear(Xd, copies[r], Yd, 128, awq.AWQ_KERNEL_AUTO)
+        Rl = copies_for(c.weight_bytes)
+        more = [tuple(t.clone() for t in copies[0]) for _ in range(max(0, Rl - R))]
+        lc = list(copies) + more
+
+        def f(c=c, Xd=Xd, lc=lc, Yd=Yd):
+            for cp in lc:
+                L.linear(Xd, cp, Yd, 128, awq.AWQ_KERNEL_AUTO)
         g = make_graph(torch, f)
-        t = time_graph(torch, g, 10, R)
+        t = time_graph(torch, g, 10, len(lc))
+        del g, more, lc
         per_layer.append({"layer": c.name, "us": round(t * 1e6, 3),
-                          "GB/s": round(c.weight_bytes / t / 1e9, 1)})
+                          "GB/s": round(c.io_bytes / t / 1e9, 1)})
+
+    # roofline of the GEMV kernel: algorithmic bytes of one launch of each
+    # layer over that launch's average duration, byte-weighted over the layers
+    launch_s = sum(r["us"] for r in per_layer) * 1e-6
+    achieved = per_step_bytes / launch_s / 1e9
+    traffic = stored_traffic()
+    log(f"GEMV launches: {launch_s * 1e6:.2f} us for the three layers, {achieved:.0f} GB/s")
 
     rows = {"decode_gemv_m1_layers": per_layer}
     if args.rows == "all":
@@ -237,7 +301,7 @@ def main():
             "workload": "decode GEMV, M=1, 7B-class layers (K,N)=(4096,4096),(4096,11008),"
                         "(11008,4096), int4 g128 zero-point, fp16 activations, fp16 out",
             "global_batch": 1,
-            "weight_bytes_per_step": per_step_bytes,
+            "bytes_per_step": per_step_bytes,
             "rotating_copies": R,
             "parallelism": "none (1 GPU)",
         },
@@ -247,7 +311,10 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else round(traffic / 3),
+            "kernel": "gemv_kernel (one launch per layer; achieved = layer bytes / average "
+                      "launch time, summed over the three layers; traffic = counter bytes "
+                      "per launch, averaged over the three layers)",
         },
         "cpu_baseline": cpu,
         "rows": rows,
@@ -266,11 +333,15 @@ def measure_rows(awq, torch, wl, L, decode_layers, R_dec):
         for (c, _, copies, _) in decode_layers:
             Xd = torch.from_numpy(c.activation(M=M)).cuda()
             Yd = torch.empty((M, c.N), dtype=torch.float16, device="cuda")
+            Rl = copies_for(c.weight_bytes)
+            lc = list(copies) + [tuple(t.clone() for t in copies[0])
+                                 for _ in range(max(0, Rl - R_dec))]
 
-            def f(Xd=Xd, Yd=Yd, copies=copies):
-                for r in range(R_dec):
-                    L.linear(Xd, copies[r], Yd, 128, kernel)
-            t = time_graph(torch, make_graph(torch, f), 10, R_dec)
+            def f(Xd=Xd, Yd=Yd, lc=lc):
+                for cp in lc:
+                    L.linear(Xd, cp, Yd, 128, kernel)
+            t = time_graph(torch, make_graph(torch, f), 10, len(lc))
+            del lc
             tot_b += c.weight_bytes
             tot_t += t
             per.append({"layer": c.name, "us": round(t * 1e6, 3)})

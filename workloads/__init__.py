@@ -125,6 +125,12 @@ class Case:
         return self.N * self.K // 2 + 3 * self.N * G
 
     @property
+    def io_bytes(self) -> int:
+        """Bytes a linear call must move to and from HBM at least: the packed
+        layer plus the fp16 activations read and the fp16 outputs written."""
+        return self.weight_bytes + 2 * self.M * self.K + 2 * self.M * self.N
+
+    @property
     def flops(self) -> int:
         return 2 * self.M * self.N * self.K
 
