@@ -41,47 +41,91 @@ __device__ __forceinline__ f32x4 mfma32<TagBF16>(u32x4 a, u32x4 b, f32x4 c) {
 // pair (2j, 2j+1) in the two 16-bit halves.
 __device__ __forceinline__ int nibble_of_channel(int i) { return (i >> 1) + 4 * (i & 1); }
 
-// fp16: the exact integers (q - z) for the 8 channels of word w, as 8 fp16 in
-// channel order.  OR-ing a code into the mantissa of 1024.0 (0x6400) gives
-// 1024 + q exactly; subtracting (1024 + z) leaves q - z exactly.  Codes that
-// sit 4 bits higher give 1024 + 16q, and (1024 + 16q) / 16 - (64 + z) is
-// q - z exactly as well, which saves two shifts per word.
-struct DeqF16 {
-  f16x2 nz1024;  // -(1024 + z) in both halves
-  f16x2 nz64;    // -(64 + z) in both halves
-  __device__ __forceinline__ explicit DeqF16(uint32_t z) {
-    const _Float16 a = (_Float16)(-(float)(1024 + z));
-    const _Float16 b = (_Float16)(-(float)(64 + z));
-    nz1024 = f16x2{a, a};
-    nz64 = f16x2{b, b};
+// Bit-pattern constants of the dequantization, held in registers.  gfx9-family
+// VOP3 encodings take no literal operand, so with literal masks every
+// (w & mask) | exponent would split into a v_and and a v_or; with the masks in
+// VGPRs and the exponent patterns in SGPRs it is one v_and_or_b32.  Build one
+// DeqRegs per kernel, outside the loops (the empty asm statements only hide
+// the constant values from the optimizer so that they stay in registers).
+struct DeqRegs {
+  uint32_t lo, hi;            // 0x000F000F, 0x00F000F0
+  uint32_t e1024, e64, e128;  // fp16 1024.0, fp16 64.0, bf16 128.0 in both halves
+  __device__ __forceinline__ DeqRegs()
+      : lo(0x000F000Fu), hi(0x00F000F0u), e1024(0x64006400u), e64(0x54005400u),
+        e128(0x43004300u) {
+    asm volatile("" : "+v"(lo));
+    asm volatile("" : "+v"(hi));
+    asm volatile("" : "+s"(e1024));
+    asm volatile("" : "+s"(e64));
+    asm volatile("" : "+s"(e128));
   }
-  __device__ __forceinline__ u32x4 operator()(uint32_t w) const {
-    const uint32_t kMagic = 0x64006400u;
-    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+};
+
+// fp16, biased codes of word w as the B operand of one 16x16x32 MFMA slot:
+// OR-ing a code held in bits 0..3 of a half into the mantissa of 1024.0
+// (0x6400) gives 1024 + q exactly; a code held in bits 4..7 OR-ed into 64.0
+// (0x5400) gives 64 + q exactly.  Channel pairs (0,1) and (4,5) come out as
+// 1024 + q, pairs (2,3) and (6,7) as 64 + q.  Five VALU instructions per
+// 8 weights.
+__device__ __forceinline__ u32x4 deq_f16_biased(uint32_t w, const DeqRegs &r) {
+  const uint32_t w8 = w >> 8;
+  return u32x4{(w & r.lo) | r.e1024, (w & r.hi) | r.e64, (w8 & r.lo) | r.e1024,
+               (w8 & r.hi) | r.e64};
+}
+
+// The B operand that removes the bias and the zero point from
+// deq_f16_biased: -(1024 + z) and -(64 + z) in the matching slots, built from
+// the fp16 bit patterns directly (0xE400 | z is -(1024 + z); 0xD400 + 16 z is
+// -(64 + z)).  mfma(a, deq_f16_biased(w)) + mfma(a, corr_f16(z)) is the
+// product of a with the exact integers q - z.
+__device__ __forceinline__ u32x4 corr_f16(uint32_t z) {
+  const uint32_t a = 0xE400u | z;
+  const uint32_t b = 0xD400u + (z << 4);
+  const uint32_t A = a | (a << 16), B = b | (b << 16);
+  return u32x4{A, B, A, B};
+}
+
+// fp16: the exact integers (q - z) for the 8 channels of word w, as 8 fp16 in
+// channel order (biased codes minus (1024 + z) or (64 + z) in packed half
+// arithmetic: exact, since every value is an integer of at most 11 bits).
+struct DeqF16 {
+  uint32_t nz1024, nz64;  // -(1024 + z), -(64 + z) in both halves (fp16 bits)
+  __device__ __forceinline__ explicit DeqF16(uint32_t z) {
+    const uint32_t a = 0xE400u | z;
+    const uint32_t b = 0xD400u + (z << 4);
+    nz1024 = a | (a << 16);
+    nz64 = b | (b << 16);
+  }
+  __device__ __forceinline__ u32x4 operator()(uint32_t w, const DeqRegs &r) const {
+    // (scalar copies first: bit-casting an element of a vector lvalue reads
+    // the vector's first element with this compiler)
     const uint32_t w8 = w >> 8;
-    const f16x2 p0 = __builtin_bit_cast(f16x2, (w & 0x000F000Fu) | kMagic);
-    const f16x2 p1 = __builtin_bit_cast(f16x2, (w & 0x00F000F0u) | kMagic);
-    const f16x2 p2 = __builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) | kMagic);
-    const f16x2 p3 = __builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) | kMagic);
-    const f16x2 h0 = p0 + nz1024;
-    const f16x2 h1 = __builtin_elementwise_fma(p1, sixteenth, nz64);
-    const f16x2 h2 = p2 + nz1024;
-    const f16x2 h3 = __builtin_elementwise_fma(p3, sixteenth, nz64);
+    const uint32_t p0 = (w & r.lo) | r.e1024, p1 = (w & r.hi) | r.e64;
+    const uint32_t p2 = (w8 & r.lo) | r.e1024, p3 = (w8 & r.hi) | r.e64;
+    const f16x2 h0 = __builtin_bit_cast(f16x2, p0) + __builtin_bit_cast(f16x2, nz1024);
+    const f16x2 h1 = __builtin_bit_cast(f16x2, p1) + __builtin_bit_cast(f16x2, nz64);
+    const f16x2 h2 = __builtin_bit_cast(f16x2, p2) + __builtin_bit_cast(f16x2, nz1024);
+    const f16x2 h3 = __builtin_bit_cast(f16x2, p3) + __builtin_bit_cast(f16x2, nz64);
     return u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
                  __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
   }
 };
 
 // bf16: 128 + q exactly (OR into the mantissa of 128.0 = 0x4300).  gfx950 has
-// no packed bf16 add, so the zero point is removed after the product:
+// no packed bf16 add, so the zero point is removed after the product, either
+// with an MFMA against corr_bf16(z) or with a row-sum MFMA:
 // sum_k a_k (q_k - z) = sum_k a_k (128 + q_k) - (128 + z) sum_k a_k.
-struct DeqBF16 {
-  __device__ __forceinline__ u32x4 operator()(uint32_t w) const {
-    const uint32_t kMagic = 0x43004300u;
-    return u32x4{(w & 0x000F000Fu) | kMagic, ((w >> 4) & 0x000F000Fu) | kMagic,
-                 ((w >> 8) & 0x000F000Fu) | kMagic, ((w >> 12) & 0x000F000Fu) | kMagic};
-  }
-};
+__device__ __forceinline__ u32x4 deq_bf16_biased(uint32_t w, const DeqRegs &r) {
+  return u32x4{(w & r.lo) | r.e128, ((w >> 4) & r.lo) | r.e128, ((w >> 8) & r.lo) | r.e128,
+               ((w >> 12) & r.lo) | r.e128};
+}
+
+// -(128 + z) in all 8 bf16 slots (0xC300 | z; exact, 128 + z < 256).
+__device__ __forceinline__ u32x4 corr_bf16(uint32_t z) {
+  const uint32_t a = 0xC300u | z;
+  const uint32_t A = a | (a << 16);
+  return u32x4{A, A, A, A};
+}
 
 // bf16 1.0 in all 8 slots: an MFMA against it yields the row sums of A.
 __device__ __forceinline__ u32x4 bf16_ones() {

@@ -79,6 +79,7 @@ void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qw
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const DeqRegs dq;
   const int wm = wave >> 1, wn = wave & 1;
   const int c = lane & 15, kq = lane >> 4;
 
@@ -214,11 +215,10 @@ void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qw
           if constexpr (!kBF16) {
             const DeqF16 deq(br.zr[j][gi]);
 #pragma unroll
-            for (int w = 0; w < kWpl; ++w) bq[w] = deq(br.raw[j][gi][w]);
+            for (int w = 0; w < kWpl; ++w) bq[w] = deq(br.raw[j][gi][w], dq);
           } else {
-            const DeqBF16 deq;
 #pragma unroll
-            for (int w = 0; w < kWpl; ++w) bq[w] = deq(br.raw[j][gi][w]);
+            for (int w = 0; w < kWpl; ++w) bq[w] = deq_bf16_biased(br.raw[j][gi][w], dq);
           }
           const float sc = half_bits_to_float((uint16_t)br.sc[j][gi]);
           f32x4 t[kMT];

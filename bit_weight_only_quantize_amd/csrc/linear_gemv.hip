@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15;
   const int kq = lane >> 4;
   const int n0 = blockIdx.x * 16;
@@ -93,13 +93,15 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     u32x4 a[U][kWpl];      // used only when activations are not staged
   };
   // Packed weights (and, without staging, activations) of groups
-  // g0, g0 + NW, ..., g0 + (U-1)*NW.  A group past the end reads zeros (the
-  // whole offset is replaced, so nothing wraps back into range).
+  // g0, g0 + NW, ..., g0 + (U-1)*NW.  No load is issued for a group past the
+  // end (g is uniform across the wave, so this is a scalar branch): its
+  // registers keep stale values, which the zero scale of such a group cancels.
   auto load_batch = [&](int g0, Batch &b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int g = g0 + u * NW;
-      const uint32_t qo = g < G ? q_lane + (uint32_t)g * (GS / 2) : 0xFFFFFFF0u;
+      if (g >= G) continue;
+      const uint32_t qo = q_lane + (uint32_t)g * (GS / 2);
       if constexpr (kWpl == 4) {
         const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo, 0, 0));
 #pragma unroll
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
         for (int j = 0; j < kWpl; ++j) b.raw[u][j] = v[j];
       }
       if constexpr (!STAGE_X) {
-        const uint32_t xo = g < G ? x_lane + (uint32_t)g * (GS * 2) : 0xFFFFFFF0u;
+        const uint32_t xo = x_lane + (uint32_t)g * (GS * 2);
 #pragma unroll
         for (int j = 0; j < kWpl; ++j)
           b.a[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, xo + 16u * j, 0, 0));
@@ -186,6 +188,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
   const uint8_t *zs = reinterpret_cast<const uint8_t *>(smem + L.zoff) + c * G;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const DeqRegs dq;
 
   // Software pipeline: the next batch's loads are in flight while this batch
   // is dequantized and multiplied.
@@ -201,30 +204,24 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
       for (int j = 0; j < kWpl; ++j) {
         if constexpr (STAGE_X)
           a[j] = *reinterpret_cast<const u32x4 *>(xlds + (uint32_t)gs * (GS * 2) + 16u * j);
-        else
-          a[j] = cur.a[u][j];
+        else  // a group past the end loaded nothing: its stale registers may hold any bits
+          a[j] = g < G ? cur.a[u][j] : u32x4{0u, 0u, 0u, 0u};
       }
       const uint32_t zr = zs[gs];
-      const float sc = g < G ? half_bits_to_float(ss[gs]) : 0.0f;
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (!kBF16) {
-        const DeqF16 deq(zr);
+      const uint16_t sb = ss[gs];
+      const float sc = g < G ? half_bits_to_float(sb) : 0.0f;
+      // Biased codes times a, plus a times the bias-and-zero correction: two
+      // independent MFMA chains, summed once per group.
+      const u32x4 corr = kBF16 ? corr_bf16(zr) : corr_f16(zr);
+      f32x4 t = {0.f, 0.f, 0.f, 0.f}, tc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < kWpl; ++j) t = mfma32<TagF16>(a[j], deq(cur.raw[u][j]), t);
-      } else {
-        const DeqBF16 deq;
-        f32x4 r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < kWpl; ++j) {
-          t = mfma32<TagBF16>(a[j], deq(cur.raw[u][j]), t);
-          r = mfma32<TagBF16>(a[j], bf16_ones(), r);
-        }
-        const float cz = -(float)(128u + zr);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = __builtin_fmaf(cz, r[e], t[e]);
+      for (int j = 0; j < kWpl; ++j) {
+        const u32x4 b = kBF16 ? deq_bf16_biased(cur.raw[u][j], dq) : deq_f16_biased(cur.raw[u][j], dq);
+        t = mfma32<XT>(a[j], b, t);
+        tc = mfma32<XT>(a[j], corr, tc);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(t[e], sc, acc[e]);
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(t[e] + tc[e], sc, acc[e]);
     }
     cur = nxt;
   }
@@ -260,11 +257,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 // 48 KiB; larger M*K streams them from global memory instead.
 constexpr uint32_t kGemvStageBytes = 48u * 1024u;
 
-template <class XT, int GS>
-static void gemv_dispatch(const uint16_t *X, const uint32_t *qw, const uint16_t *sc,
-                          const uint8_t *zr, int M, int64_t N, int64_t K, void *Y, YType yt,
-                          hipStream_t st) {
-  constexpr int NW = 8;
+template <class XT, int GS, int NW>
+static void gemv_launch(const uint16_t *X, const uint32_t *qw, const uint16_t *sc,
+                        const uint8_t *zr, int M, int64_t N, int64_t K, void *Y, YType yt,
+                        hipStream_t st) {
   const dim3 grid((unsigned)((N + 15) / 16));
   const int G = (int)(K / GS);
   const bool stage = (uint64_t)(M + 1) * (uint64_t)K * 2u <= kGemvStageBytes;
@@ -272,11 +268,27 @@ static void gemv_dispatch(const uint16_t *X, const uint32_t *qw, const uint16_t 
   // the reduction reuses the buffer: at least NW * 64 * 16 bytes
   const uint32_t bytes = L.total > 64u * NW * 16u ? L.total : 64u * NW * 16u;
   if (stage)
-    gemv_kernel<XT, GS, NW, 4, true><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
+    gemv_kernel<XT, GS, NW, 1, true><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
                                                                    (int)K, Y, (int)yt);
   else
     gemv_kernel<XT, GS, NW, 2, false><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
                                                                     (int)K, Y, (int)yt);
+}
+
+// Waves per workgroup.  Every workgroup of a launch should be resident at
+// once (a second partial round of workgroups costs a whole extra memory
+// latency): with at most one workgroup per CU (N <= 16 * 256) the workgroup
+// takes 16 waves, otherwise 8.  One group per wave is in flight ahead of the
+// one being computed: deeper windows were measured slower on MI355X (every
+// wave's staging loads then queue behind more weight traffic).
+template <class XT, int GS>
+static void gemv_dispatch(const uint16_t *X, const uint32_t *qw, const uint16_t *sc,
+                          const uint8_t *zr, int M, int64_t N, int64_t K, void *Y, YType yt,
+                          hipStream_t st) {
+  if ((N + 15) / 16 <= 256)
+    gemv_launch<XT, GS, 16>(X, qw, sc, zr, M, N, K, Y, yt, st);
+  else
+    gemv_launch<XT, GS, 8>(X, qw, sc, zr, M, N, K, Y, yt, st);
 }
 
 bool gemv_supported(int64_t M, int64_t K, int gs) {
