@@ -7,7 +7,8 @@ loads the library and raises ImportError if it is not built.
 """
 
 _API = (
-    "awq_quantize_pack", "awq_linear", "awq_linear_ex", "awq_scale_search",
+    "awq_quantize_pack", "awq_linear", "awq_linear_ex", "awq_linear_ws",
+    "awq_linear_workspace_size", "awq_scale_search",
     "awq_scale_search_workspace_size", "AwqError", "config", "empty_packed", "lib",
     "AWQ_F16", "AWQ_BF16", "AWQ_F32", "AWQ_KERNEL_AUTO", "AWQ_KERNEL_GEMV",
     "AWQ_KERNEL_GEMM", "AWQ_GEMV_MAX_M", "EXPORTS", "LIB_PATH",

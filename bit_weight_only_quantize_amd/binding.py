@@ -33,6 +33,8 @@ EXPORTS = (
     "awq_quantize_pack",
     "awq_linear",
     "awq_linear_ex",
+    "awq_linear_workspace_size",
+    "awq_linear_ws",
     "awq_scale_search_workspace_size",
     "awq_scale_search",
     "awq_status_string",
@@ -71,6 +73,11 @@ def _load():
     lib.awq_linear.restype = ctypes.c_int
     lib.awq_linear_ex.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32, i32, vp]
     lib.awq_linear_ex.restype = ctypes.c_int
+    lib.awq_linear_workspace_size.argtypes = [i64, i64, i64, awq_config]
+    lib.awq_linear_workspace_size.restype = ctypes.c_size_t
+    lib.awq_linear_ws.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32, vp,
+                                  ctypes.c_size_t, vp]
+    lib.awq_linear_ws.restype = ctypes.c_int
     lib.awq_scale_search_workspace_size.argtypes = [i64, i64, i64, awq_config, i32]
     lib.awq_scale_search_workspace_size.restype = ctypes.c_size_t
     lib.awq_scale_search.argtypes = [vp, vp, i64, i64, i64, awq_config,
@@ -191,8 +198,36 @@ def awq_linear_ex(X, qweight, scales, zeros, kernel: int = AWQ_KERNEL_AUTO, grou
 
 
 def awq_linear(X, qweight, scales, zeros, group_size: int = 128, out_dtype=None, out=None):
-    """Y = X * deq(W)^T; M <= AWQ_GEMV_MAX_M runs the GEMV kernel, larger M the GEMM."""
+    """Y = X * deq(W)^T; small M runs the GEMV kernel, larger M the GEMM."""
     return awq_linear_ex(X, qweight, scales, zeros, AWQ_KERNEL_AUTO, group_size, out_dtype, out)
+
+
+def awq_linear_workspace_size(M: int, N: int, K: int, group_size: int = 128) -> int:
+    return int(lib.awq_linear_workspace_size(M, N, K, config(group_size)))
+
+
+def awq_linear_ws(X, qweight, scales, zeros, workspace, group_size: int = 128, out_dtype=None,
+                  out=None):
+    """awq_linear with a caller workspace (uint8 tensor, zero-filled before first use,
+    at least awq_linear_workspace_size bytes); the call allocates nothing."""
+    torch = _torch()
+    if X.dim() != 2:
+        raise TypeError("X must be 2-D")
+    M, K = X.shape
+    N = qweight.shape[0]
+    if qweight.shape != (N, K // 8) or scales.shape != (N, K // group_size) or zeros.shape != scales.shape:
+        raise ValueError("packed weight shapes do not match X and group_size")
+    if out is None:
+        odt = X.dtype if out_dtype is None else out_dtype
+        out = torch.empty((M, N), dtype=odt, device=X.device)
+    wp = ctypes.c_void_p(0) if workspace is None else _dev_ptr(workspace, "workspace")
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.awq_linear_ws(_dev_ptr(X, "X"), _dtype_code(X.dtype), _dev_ptr(qweight, "qweight"),
+                           _dev_ptr(scales, "scales"), _dev_ptr(zeros, "zeros"), M, N, K,
+                           config(group_size), _dev_ptr(out, "Y"), _dtype_code(out.dtype), wp, wb,
+                           _stream(X.device))
+    check(st, "awq_linear_ws")
+    return out
 
 
 def awq_scale_search_workspace_size(M: int, N: int, K: int, group_size: int = 128,

@@ -8,6 +8,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <vector>
 
 #include "../../include/awq355.h"
@@ -36,6 +39,38 @@ awq_status hip_status(hipError_t e, const char *where) {
 }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Split-K scratch of awq_linear / awq_linear_ex, one per device, allocated the
+// first time a call needs it (or needs more).  A buffer is never freed: a
+// larger one replaces it for later calls, and HIP graphs captured with the
+// old one stay valid.  Split counters start at zero and every launch leaves
+// them at zero.
+struct Scratch {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_scratch_mu;
+std::map<int, Scratch> g_scratch;
+
+hipError_t linear_scratch(size_t bytes, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  Scratch &s = g_scratch[dev];
+  if (s.bytes < bytes) {
+    const size_t want = bytes > 2 * s.bytes ? bytes : 2 * s.bytes;
+    void *p = nullptr;
+    e = hipMalloc(&p, want);
+    if (e != hipSuccess) return e;
+    e = hipMemset(p, 0, want);
+    if (e != hipSuccess) return e;
+    s.ptr = p;
+    s.bytes = want;
+  }
+  *out = s.ptr;
+  return hipSuccess;
+}
 
 awq_status check_config(awq_config cfg, int64_t K) {
   if (cfg.w_bit != 4) return fail(AWQ_ERR_UNSUPPORTED, "w_bit=%d: only 4 is supported", cfg.w_bit);
@@ -180,28 +215,74 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
                     "awq_quantize_pack");
 }
 
-awq_status awq_linear_ex(const void *X, int32_t x_dtype, const uint32_t *qweight,
-                         const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
-                         int64_t K, awq_config cfg, void *Y, int32_t y_dtype, int32_t kernel,
-                         awq_stream_t stream) {
+namespace {
+
+// awq_linear_ex with an optional caller workspace (NULL: the library scratch).
+awq_status linear_impl(const void *X, int32_t x_dtype, const uint32_t *qweight,
+                       const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
+                       int64_t K, awq_config cfg, void *Y, int32_t y_dtype, int32_t kernel,
+                       void *workspace, size_t workspace_bytes, bool caller_ws,
+                       awq_stream_t stream) {
   awq_status st =
       check_linear(X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype, kernel);
   if (st != AWQ_OK) return st;
+  const awq::GemmPlan plan = awq::gemm_plan(M > 0 ? M : 1, N > 0 ? N : 1, K);
+  const bool gemv_ok = awq::gemv_supported(M, K, cfg.group_size);
+  if (kernel == AWQ_KERNEL_GEMV && !gemv_ok)
+    return fail(AWQ_ERR_UNSUPPORTED, "GEMV kernel cannot serve K=%lld", (long long)K);
+  // Automatic choice: the GEMV for M <= AWQ_GEMV_MAX_M, the GEMM above.
+  const bool gemv = kernel == AWQ_KERNEL_GEMV ||
+                    (kernel == AWQ_KERNEL_AUTO && M <= AWQ_GEMV_MAX_M && gemv_ok);
+  if (caller_ws && !gemv && plan.workspace_bytes > 0) {
+    if (!workspace) return fail(AWQ_ERR_INVALID_ARG, "this shape needs a workspace");
+    if (!aligned(workspace, 256)) return fail(AWQ_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    if (workspace_bytes < plan.workspace_bytes)
+      return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                  plan.workspace_bytes);
+  }
   if (M == 0 || N == 0) return ok();
   const awq::XType xt = x_dtype == AWQ_F16 ? awq::XType::F16 : awq::XType::BF16;
   const awq::YType yt = y_dtype == AWQ_F16    ? awq::YType::F16
                         : y_dtype == AWQ_BF16 ? awq::YType::BF16
                                               : awq::YType::F32;
-  const bool gemv_ok = awq::gemv_supported(M, K, cfg.group_size);
-  if (kernel == AWQ_KERNEL_GEMV && !gemv_ok)
-    return fail(AWQ_ERR_UNSUPPORTED, "GEMV kernel cannot serve K=%lld", (long long)K);
-  const bool gemv = kernel == AWQ_KERNEL_GEMV ||
-                    (kernel == AWQ_KERNEL_AUTO && M <= AWQ_GEMV_MAX_M && gemv_ok);
-  hipError_t e = gemv ? awq::launch_gemv(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size,
-                                         Y, yt, as_stream(stream))
-                      : awq::launch_gemm(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size,
-                                         Y, yt, as_stream(stream));
-  return hip_status(e, gemv ? "awq_linear (gemv)" : "awq_linear (gemm)");
+  const hipStream_t hs = as_stream(stream);
+  if (gemv)
+    return hip_status(awq::launch_gemv(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size, Y,
+                                       yt, hs),
+                      "awq_linear (gemv)");
+  void *scratch = caller_ws ? workspace : nullptr;
+  if (!caller_ws && plan.workspace_bytes > 0) {
+    const hipError_t e = linear_scratch(plan.workspace_bytes, &scratch);
+    if (e != hipSuccess) return hip_status(e, "awq_linear (split-K scratch)");
+  }
+  return hip_status(awq::launch_gemm(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size, Y,
+                                     yt, scratch, hs),
+                    "awq_linear (gemm)");
+}
+
+}  // namespace
+
+awq_status awq_linear_ex(const void *X, int32_t x_dtype, const uint32_t *qweight,
+                         const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
+                         int64_t K, awq_config cfg, void *Y, int32_t y_dtype, int32_t kernel,
+                         awq_stream_t stream) {
+  return linear_impl(X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype, kernel,
+                     nullptr, 0, false, stream);
+}
+
+size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg) {
+  if (check_config(cfg, K) != AWQ_OK || M < 0 || N < 0) return 0;
+  if (M == 0 || N == 0) return 0;
+  if (M <= AWQ_GEMV_MAX_M && awq::gemv_supported(M, K, cfg.group_size)) return 0;
+  return awq::gemm_plan(M, N, K).workspace_bytes;
+}
+
+awq_status awq_linear_ws(const void *X, int32_t x_dtype, const uint32_t *qweight,
+                         const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
+                         int64_t K, awq_config cfg, void *Y, int32_t y_dtype, void *workspace,
+                         size_t workspace_bytes, awq_stream_t stream) {
+  return linear_impl(X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype,
+                     AWQ_KERNEL_AUTO, workspace, workspace_bytes, true, stream);
 }
 
 awq_status awq_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,

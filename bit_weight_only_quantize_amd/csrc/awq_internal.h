@@ -20,16 +20,28 @@ hipError_t launch_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int gs,
 // ---- linear_gemv.hip (M <= 16) -------------------------------------------------
 // Whether the GEMV kernel can serve this shape (M <= 16, LDS staging fits).
 bool gemv_supported(int64_t M, int64_t K, int gs);
+// Whether the GEMV stages the M activation rows in LDS (its fast path).
+bool gemv_stages_activations(int64_t M, int64_t K);
 hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M,
                        int64_t N, int64_t K, int gs, void *Y, YType yt,
                        hipStream_t st);
 
 // ---- linear_gemm.hip (any M) ---------------------------------------------------
+// Row tile (32 * mt rows), K split and split-K workspace of a quantized GEMM.
+struct GemmPlan {
+  int mt, splits;
+  int64_t tiles;
+  size_t counter_bytes;    // fixed-size u32 counter region (zero between launches)
+  size_t workspace_bytes;  // 0 when splits == 1
+};
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K);
+// `workspace` (gemm_plan(...).workspace_bytes, 256-byte aligned, counters
+// zeroed once) is needed only when the plan splits K.
 hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M,
                        int64_t N, int64_t K, int gs, void *Y, YType yt,
-                       hipStream_t st);
+                       void *workspace, hipStream_t st);
 
 // Dense fp16 B (X * W^T with W fp16 [N][K]), fp32 output.
 hipError_t launch_gemm_dense_f32(const uint16_t *X, const uint16_t *W, int64_t M,

@@ -9,12 +9,20 @@
 // in fp32, and the group's scale multiplies that fp32 partial.  No dequantized
 // weight is ever rounded to 16 bits.
 //
-// Tiling for the MI355X: a 256-thread workgroup (one wave per SIMD) computes a
-// 256 x 128 tile of Y; each wave owns 128 x 64 (8 x 4 MFMA tiles of 16 x 16).
-// K advances in blocks of 128 channels (one g128 group or two g64 groups).
-//  * Activations: each 256 x 128 fp16 block (64 KiB) goes from global memory
+// Tiling for the MI355X: a 256-thread workgroup computes a BM x 128 tile of Y,
+// BM = 32 * MT (MT = 1, 2, 4 or 8 MFMA row tiles per wave); each wave owns
+// BM/2 x 64 (MT x 4 MFMA tiles of 16 x 16).  Small M takes a small BM so the
+// matrix core does not multiply padding rows.  K advances in blocks of 128
+// channels (one g128 group or two g64 groups).
+//  * Split K: when the M x N tiles alone cannot fill the 256 CUs (batched
+//    decode), the K blocks of each tile are divided among S workgroups.  Each
+//    writes its fp32 partial tile to a workspace; the last of the S to finish
+//    (a per-tile counter, reset by that workgroup) adds the S partials in
+//    split order -- the same order whichever finishes last -- and runs the
+//    epilogue.
+//  * Activations: each BM x 128 fp16 block goes from global memory
 //    straight to LDS (buffer_load_dwordx4 ... lds, no VGPR staging),
-//    double-buffered in two 64 KiB arrays.  16-byte chunk c of row r is stored
+//    double-buffered in two arrays.  16-byte chunk c of row r is stored
 //    at chunk c ^ (r mod 16): the 16 rows read by one 128-bit LDS access land
 //    in 16 distinct bank groups.
 //  * Per group, a wave reads all its A fragments (8 tiles x 32 channels) from
@@ -43,8 +51,8 @@ namespace awq {
 
 namespace {
 
-constexpr int kBM = 256, kBN = 128, kBK = 128;
-constexpr int kMT = 8, kNT = 4;        // 16x16 tiles per wave along M and N
+constexpr int kBN = 128, kBK = 128;
+constexpr int kNT = 4;                 // 16x16 tiles per wave along N
 constexpr int kThreads = 256;
 constexpr uint32_t kNone = 0xFFFFFFFFu; // an offset every range check rejects
 
@@ -62,19 +70,34 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 
 }  // namespace
 
-template <class XT, int GS, int EPI, bool DENSE, int YT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
-                 const uint16_t *__restrict__ Wdense, const uint16_t *__restrict__ scales,
-                 const uint8_t *__restrict__ zeros, int M, int N, int K, void *__restrict__ Y,
-                 const float *__restrict__ Yref, double *__restrict__ partials) {
+// Split-K bookkeeping of one launch: `splits` workgroups per output tile, a
+// u32 counter per tile (zero between launches) and the fp32 partial tiles.
+struct SplitK {
+  int splits;
+  uint32_t *counters;
+  float *partials;
+};
+
+template <class XT, int GS, int EPI, bool DENSE, int YT, int MT>
+__device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
+                                          const uint32_t *__restrict__ qweight,
+                                          const uint16_t *__restrict__ Wdense,
+                                          const uint16_t *__restrict__ scales,
+                                          const uint8_t *__restrict__ zeros, int M, int N, int K,
+                                          void *__restrict__ Y, const float *__restrict__ Yref,
+                                          double *__restrict__ partials, SplitK sk) {
   constexpr bool kBF16 = __is_same(XT, TagBF16);
   constexpr int kGS = DENSE ? 128 : GS;
   constexpr int kWpl = kGS / 32;        // 8-channel words per lane per group
   constexpr int kGPB = kBK / kGS;       // groups per K block
+  constexpr int kMT = MT;               // 16x16 tiles per wave along M
+  constexpr int kBM = 32 * MT;
+  constexpr int kRowsPerWave = kBM / 4; // rows of the A block each wave fetches
+  constexpr int kDma = kRowsPerWave / 4;
 
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kBM * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBM * kBK];
+  __shared__ uint32_t s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,34 +107,41 @@ void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qw
   const int c = lane & 15, kq = lane >> 4;
 
   const int tiles_n = (N + kBN - 1) / kBN;
+  const int tiles = ((M + kBM - 1) / kBM) * tiles_n;
   const int bid = (int)xcd_remap(blockIdx.x, (int64_t)gridDim.x);
-  const int tm = bid / tiles_n, tn = bid - (bid / tiles_n) * tiles_n;
+  const int tile = bid % tiles, split = bid / tiles;
+  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
   const int row0 = tm * kBM, col0 = tn * kBN;
 
   const int G = K / kGS;
   const int nkb = (K + kBK - 1) / kBK;
+  const int kb_begin = (int)((int64_t)split * nkb / sk.splits);
+  const int kb_end = (int)((int64_t)(split + 1) * nkb / sk.splits);
 
   const rsrc_t rX = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
 
-  // ---- activation block -> LDS: 16 DMA instructions per wave, 1 KiB each ------
-  // Instruction r of wave w fills rows 4*(16w + r) .. +3; lane l writes row
-  // +l/16 at physical chunk l%16 and so fetches logical chunk (l%16) ^ (row%16).
-  // row%16 = 4*(r%4) + l/16, so four lane offsets cover all sixteen r.
+  // ---- activation block -> LDS: kDma DMA instructions per wave, 1 KiB each ---
+  // Instruction r of wave w fills rows kRowsPerWave*w + 4r .. +3; lane l writes
+  // row +l/16 at physical chunk l%16 and so fetches logical chunk
+  // (l%16) ^ (row%16).  row%16 = 4*((r + b) % 4) + l/16 with b the wave's first
+  // row / 4, so four lane offsets cover every r.
   uint32_t a_voff[4];
   {
     const int lrow = lane >> 4;
-    const uint32_t base = (uint32_t)(row0 + 64 * wave + lrow) * (uint32_t)K * 2u;
+    const int wrow = kRowsPerWave * wave;
+    const uint32_t base = (uint32_t)(row0 + wrow + lrow) * (uint32_t)K * 2u;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a_voff[q] = base + ((uint32_t)((lane & 15) ^ (4 * q + lrow)) << 4);
+    for (int q = 0; q < 4; ++q)
+      a_voff[q] = base + ((uint32_t)((lane & 15) ^ (4 * ((q + wrow / 4) & 3) + lrow)) << 4);
   }
   const uint32_t a_rstep = 8u * (uint32_t)K;   // bytes between rows 4 apart
   auto issue_a = [&](int kb, uint16_t *buf) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < kDma; ++r) {
       const uint32_t off = a_voff[r & 3] + (uint32_t)r * a_rstep + (uint32_t)kb * (kBK * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rX, (lds_void *)(reinterpret_cast<char *>(buf) + (16 * wave + r) * 1024), 16, off, 0, 0,
-          0);
+          rX, (lds_void *)(reinterpret_cast<char *>(buf) + (kDma * wave + r) * 1024), 16, off, 0,
+          0, 0);
     }
   };
 
@@ -160,7 +190,7 @@ void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qw
 
   // A fragment: M tile i, logical 16-byte chunk ch of the block row.
   auto a_frag = [&](const uint16_t *buf, int i, int ch) {
-    const int row = wm * 128 + i * 16 + c;
+    const int row = wm * (16 * kMT) + i * 16 + c;
     return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(buf) + row * (kBK * 2) +
                                             ((ch ^ c) << 4));
   };
@@ -248,17 +278,17 @@ void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qw
   // no load sits under a branch; the surplus prefetch of the last iteration
   // lands in a buffer nobody reads again.
   BRegs r0, r1;
-  const int last = nkb - 1;
-  issue_a(0, sA0);
-  if constexpr (!DENSE) load_b(0, r0);
-  for (int kb = 0; kb < nkb; kb += 2) {
+  const int last = kb_end - 1;
+  issue_a(kb_begin, sA0);
+  if constexpr (!DENSE) load_b(kb_begin, r0);
+  for (int kb = kb_begin; kb < kb_end; kb += 2) {
     wait_vmem_all();
     __builtin_amdgcn_s_barrier();
     issue_a(kb + 1 < last ? kb + 1 : last, sA1);
     if constexpr (!DENSE) load_b(kb + 1 < last ? kb + 1 : last, r1);
     __builtin_amdgcn_sched_barrier(0);   // issue the prefetch before the math
     compute(kb, sA0, r0);
-    if (kb + 1 >= nkb) break;
+    if (kb + 1 >= kb_end) break;
 
     wait_vmem_all();
     __builtin_amdgcn_s_barrier();
@@ -268,6 +298,44 @@ void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qw
     compute(kb + 1, sA1, r1);
   }
   wait_vmem_all();
+
+  // ---- split K: publish the partial tile; the last workgroup sums them ------
+  if (sk.splits > 1) {
+    constexpr int kRegs = kMT * kNT * 4;
+    const size_t wave_stride = (size_t)kRegs * 64;
+    float *mine = sk.partials + ((size_t)tile * sk.splits + split) * 4 * wave_stride +
+                  (size_t)wave * wave_stride + lane;
+#pragma unroll
+    for (int i = 0; i < kMT; ++i)
+#pragma unroll
+      for (int j = 0; j < kNT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mine[((i * kNT + j) * 4 + e) * 64] = acc[i][j][e];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&sk.counters[tile], 1u) == (uint32_t)(sk.splits - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const float *base = sk.partials + (size_t)tile * sk.splits * 4 * wave_stride +
+                        (size_t)wave * wave_stride + lane;
+#pragma unroll
+    for (int i = 0; i < kMT; ++i)
+#pragma unroll
+      for (int j = 0; j < kNT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = base[((i * kNT + j) * 4 + e) * 64];
+    for (int sp = 1; sp < sk.splits; ++sp) {
+      const float *p = base + (size_t)sp * 4 * wave_stride;
+#pragma unroll
+      for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] += p[((i * kNT + j) * 4 + e) * 64];
+    }
+    if (tid == 0) sk.counters[tile] = 0u;   // ready for the next launch
+  }
 
   // ---- epilogue -------------------------------------------------------------
   // Lane (c, kq) holds rows 4*kq + e of column c of every 16x16 tile.
@@ -281,7 +349,7 @@ void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qw
       for (int i = 0; i < kMT; ++i) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = row0 + wm * 128 + i * 16 + 4 * kq + e;
+          const int m = row0 + wm * (16 * kMT) + i * 16 + 4 * kq + e;
           const uint32_t o = n < N ? (uint32_t)m * (uint32_t)N + (uint32_t)n : kNone / 4u;
           const float v = acc[i][j][e];
           if constexpr (YT == (int)YType::F16)
@@ -304,7 +372,7 @@ void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qw
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // rows >= M and columns >= N read 0 and have acc = 0: they add nothing
-          const int m = row0 + wm * 128 + i * 16 + 4 * kq + e;
+          const int m = row0 + wm * (16 * kMT) + i * 16 + 4 * kq + e;
           const uint32_t o = n < N ? (uint32_t)m * (uint32_t)N + (uint32_t)n : kNone / 4u;
           const float ref = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, o * 4u, 0, 0));
           const double d = (double)ref - (double)acc[i][j][e];
@@ -322,92 +390,191 @@ void gemm_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qw
   }
 }
 
+// The 128- and 256-row tiles keep one wave per SIMD and the whole register
+// file; smaller tiles leave room for two workgroups per CU.
+template <class XT, int GS, int EPI, bool DENSE, int YT, int MT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_kernel_big(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
+                     const uint16_t *__restrict__ Wdense, const uint16_t *__restrict__ scales,
+                     const uint8_t *__restrict__ zeros, int M, int N, int K, void *__restrict__ Y,
+                     const float *__restrict__ Yref, double *__restrict__ partials, SplitK sk) {
+  gemm_body<XT, GS, EPI, DENSE, YT, MT>(X, qweight, Wdense, scales, zeros, M, N, K, Y, Yref,
+                                        partials, sk);
+}
+
+template <class XT, int GS, int EPI, bool DENSE, int YT, int MT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_kernel_small(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
+                       const uint16_t *__restrict__ Wdense, const uint16_t *__restrict__ scales,
+                       const uint8_t *__restrict__ zeros, int M, int N, int K,
+                       void *__restrict__ Y, const float *__restrict__ Yref,
+                       double *__restrict__ partials, SplitK sk) {
+  gemm_body<XT, GS, EPI, DENSE, YT, MT>(X, qweight, Wdense, scales, zeros, M, N, K, Y, Yref,
+                                        partials, sk);
+}
+
+// The search's dense and loss GEMMs use the 256-row tile and no K split.
 int64_t gemm_tile_count(int64_t M, int64_t N) {
-  return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  return ((M + 255) / 256) * ((N + kBN - 1) / kBN);
 }
 
 // Largest row count per launch that keeps every per-launch buffer below 2 GiB
-// (a multiple of the 256-row tile).
-static int64_t rows_per_launch(int64_t N, int64_t K) {
+// (a multiple of the row tile bm).
+static int64_t rows_per_launch(int64_t N, int64_t K, int64_t bm) {
   const int64_t lim = ((int64_t)1 << 31) - 1;
   int64_t r = lim / (K * 2);
   const int64_t ry = lim / (N * 4);
   r = r < ry ? r : ry;
-  return (r / kBM) * kBM;
+  return (r / bm) * bm;
 }
 
 bool gemm_supported(int64_t N, int64_t K, bool dense) {
   const int64_t lim = ((int64_t)1 << 31) - 1;
-  return (dense ? N * K * 2 : N * K / 2) <= lim && rows_per_launch(N, K) > 0;
+  return (dense ? N * K * 2 : N * K / 2) <= lim && rows_per_launch(N, K, 256) > 0;
 }
 
-template <class XT, int GS, int EPI, bool DENSE, int YT>
-static hipError_t gemm_go1(const uint16_t *X, const uint32_t *qw, const uint16_t *Wd,
-                          const uint16_t *sc, const uint8_t *zr, int64_t M, int64_t N, int64_t K,
-                          void *Y, int yt, const float *Yref, double *partials, hipStream_t st) {
-  const int ysize = yt == (int)YType::F32 ? 4 : 2;
-  const int64_t rows = rows_per_launch(N, K);
+constexpr size_t kSplitCounterBytes = 512 * 4;
+
+// Row tile and K split of a quantized GEMM launch.  M <= 32, 64, 256 take
+// 32-, 64- and 128-row tiles, larger M the 256-row tile.  When the tiles
+// cannot give every CU two workgroups, K is split (at most 8 ways, at least
+// two K blocks per split).
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K) {
+  GemmPlan p{};
+  p.mt = M <= 32 ? 1 : M <= 64 ? 2 : M <= 256 ? 4 : 8;
+  const int64_t bm = 32 * p.mt;
+  p.tiles = ((M + bm - 1) / bm) * ((N + kBN - 1) / kBN);
+  const int64_t nkb = (K + kBK - 1) / kBK;
+  p.splits = 1;
+  if (p.mt < 8 && p.tiles < 512) {
+    int64_t sp = (512 + p.tiles - 1) / p.tiles;
+    const int64_t cap = nkb / 2 < 8 ? nkb / 2 : 8;
+    sp = sp < cap ? sp : cap;
+    p.splits = sp > 1 ? (int)sp : 1;
+  }
+  if (p.splits > 1) {
+    // A fixed counter region: K is split only when there are fewer than 512
+    // tiles, and every plan must find its counters at the same place (the
+    // partials of one shape must never overlap the counters of another).
+    p.counter_bytes = kSplitCounterBytes;
+    p.workspace_bytes = p.counter_bytes + (size_t)p.tiles * p.splits * bm * kBN * 4;
+  }
+  return p;
+}
+
+template <class XT, int GS, int EPI, bool DENSE, int YT, int MT>
+static hipError_t gemm_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *Wd,
+                                 const uint16_t *sc, const uint8_t *zr, int64_t M, int64_t N,
+                                 int64_t K, void *Y, const float *Yref, double *partials,
+                                 SplitK sk, hipStream_t st) {
+  constexpr int64_t bm = 32 * MT;
+  const int ysize = YT == (int)YType::F32 ? 4 : 2;
+  const int64_t rows = sk.splits > 1 ? M : rows_per_launch(N, K, bm);
   if (rows <= 0) return hipErrorInvalidValue;
   int64_t tile_base = 0;
   for (int64_t m0 = 0; m0 < M; m0 += rows) {
     const int64_t mm = M - m0 < rows ? M - m0 : rows;
-    const dim3 grid((unsigned)gemm_tile_count(mm, N));
-    gemm_kernel<XT, GS, EPI, DENSE, YT><<<grid, kThreads, 0, st>>>(
-        X + m0 * K, qw, Wd, sc, zr, (int)mm, (int)N, (int)K,
-        Y ? reinterpret_cast<char *>(Y) + m0 * N * ysize : nullptr,
-        Yref ? Yref + m0 * N : nullptr, partials ? partials + tile_base : nullptr);
-    tile_base += gemm_tile_count(mm, N);
+    const int64_t tiles = ((mm + bm - 1) / bm) * ((N + kBN - 1) / kBN);
+    const dim3 grid((unsigned)(tiles * sk.splits));
+    void *y = Y ? reinterpret_cast<char *>(Y) + m0 * N * ysize : nullptr;
+    const float *yr = Yref ? Yref + m0 * N : nullptr;
+    double *pp = partials ? partials + tile_base : nullptr;
+    if constexpr (MT >= 4)
+      gemm_kernel_big<XT, GS, EPI, DENSE, YT, MT><<<grid, kThreads, 0, st>>>(
+          X + m0 * K, qw, Wd, sc, zr, (int)mm, (int)N, (int)K, y, yr, pp, sk);
+    else
+      gemm_kernel_small<XT, GS, EPI, DENSE, YT, MT><<<grid, kThreads, 0, st>>>(
+          X + m0 * K, qw, Wd, sc, zr, (int)mm, (int)N, (int)K, y, yr, pp, sk);
+    tile_base += tiles;
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+template <class XT, int GS, int EPI, bool DENSE, int YT>
+static hipError_t gemm_go1(const uint16_t *X, const uint32_t *qw, const uint16_t *Wd,
+                           const uint16_t *sc, const uint8_t *zr, int64_t M, int64_t N, int64_t K,
+                           void *Y, const float *Yref, double *partials, int mt, SplitK sk,
+                           hipStream_t st) {
+  if constexpr (EPI == kEpiStore && !DENSE) {
+    if (mt == 1)
+      return gemm_launch_mt<XT, GS, EPI, DENSE, YT, 1>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
+                                                       partials, sk, st);
+    if (mt == 2)
+      return gemm_launch_mt<XT, GS, EPI, DENSE, YT, 2>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
+                                                       partials, sk, st);
+    if (mt == 4)
+      return gemm_launch_mt<XT, GS, EPI, DENSE, YT, 4>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
+                                                       partials, sk, st);
+  }
+  return gemm_launch_mt<XT, GS, EPI, DENSE, YT, 8>(X, qw, Wd, sc, zr, M, N, K, Y, Yref, partials,
+                                                   sk, st);
+}
+
 template <class XT, int GS, int EPI, bool DENSE>
 static hipError_t gemm_go(const uint16_t *X, const uint32_t *qw, const uint16_t *Wd,
                           const uint16_t *sc, const uint8_t *zr, int64_t M, int64_t N, int64_t K,
-                          void *Y, int yt, const float *Yref, double *partials, hipStream_t st) {
+                          void *Y, int yt, const float *Yref, double *partials, int mt,
+                          SplitK sk, hipStream_t st) {
   if (EPI == kEpiLoss || yt == (int)YType::F32)
-    return gemm_go1<XT, GS, EPI, DENSE, (int)YType::F32>(X, qw, Wd, sc, zr, M, N, K, Y, yt, Yref,
-                                                         partials, st);
+    return gemm_go1<XT, GS, EPI, DENSE, (int)YType::F32>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
+                                                         partials, mt, sk, st);
   if (yt == (int)YType::BF16)
-    return gemm_go1<XT, GS, EPI, DENSE, (int)YType::BF16>(X, qw, Wd, sc, zr, M, N, K, Y, yt, Yref,
-                                                          partials, st);
-  return gemm_go1<XT, GS, EPI, DENSE, (int)YType::F16>(X, qw, Wd, sc, zr, M, N, K, Y, yt, Yref,
-                                                       partials, st);
+    return gemm_go1<XT, GS, EPI, DENSE, (int)YType::BF16>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
+                                                          partials, mt, sk, st);
+  return gemm_go1<XT, GS, EPI, DENSE, (int)YType::F16>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
+                                                       partials, mt, sk, st);
 }
 
 hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
-                       int64_t K, int gs, void *Y, YType yt, hipStream_t st) {
+                       int64_t K, int gs, void *Y, YType yt, void *workspace,
+                       hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
+  const GemmPlan p = gemm_plan(M, N, K);
+  SplitK sk{1, nullptr, nullptr};
+  if (p.splits > 1) {
+    if (!workspace) return hipErrorInvalidValue;
+    sk.splits = p.splits;
+    sk.counters = reinterpret_cast<uint32_t *>(workspace);
+    sk.partials = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + p.counter_bytes);
+  }
   const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
   const int y = (int)yt;
   if (xt == XType::F16)
     return gs == 128 ? gemm_go<TagF16, 128, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
-                                                              M, N, K, Y, y, nullptr, nullptr, st)
+                                                              M, N, K, Y, y, nullptr, nullptr,
+                                                              p.mt, sk, st)
                      : gemm_go<TagF16, 64, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
-                                                             M, N, K, Y, y, nullptr, nullptr, st);
+                                                             M, N, K, Y, y, nullptr, nullptr,
+                                                             p.mt, sk, st);
   return gs == 128 ? gemm_go<TagBF16, 128, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
-                                                             M, N, K, Y, y, nullptr, nullptr, st)
+                                                             M, N, K, Y, y, nullptr, nullptr,
+                                                             p.mt, sk, st)
                    : gemm_go<TagBF16, 64, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
-                                                            M, N, K, Y, y, nullptr, nullptr, st);
+                                                            M, N, K, Y, y, nullptr, nullptr,
+                                                            p.mt, sk, st);
 }
 
 hipError_t launch_gemm_dense_f32(const uint16_t *X, const uint16_t *W, int64_t M, int64_t N,
                                  int64_t K, float *Y, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   return gemm_go<TagF16, 128, kEpiStore, true>(X, nullptr, W, nullptr, nullptr, M, N, K, Y,
-                                               (int)YType::F32, nullptr, nullptr, st);
+                                               (int)YType::F32, nullptr, nullptr, 8,
+                                               SplitK{1, nullptr, nullptr}, st);
 }
 
 hipError_t launch_gemm_loss(const uint16_t *A, const uint32_t *qweight, const uint16_t *scales,
                             const uint8_t *zeros, int64_t M, int64_t N, int64_t K, int gs,
                             const float *Yref, double *partials, hipStream_t st) {
+  const SplitK one{1, nullptr, nullptr};
   return gs == 128 ? gemm_go<TagF16, 128, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M,
-                                                           N, K, nullptr, 0, Yref, partials, st)
+                                                           N, K, nullptr, 0, Yref, partials, 8,
+                                                           one, st)
                    : gemm_go<TagF16, 64, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M,
-                                                          N, K, nullptr, 0, Yref, partials, st);
+                                                          N, K, nullptr, 0, Yref, partials, 8,
+                                                          one, st);
 }
 
 }  // namespace awq

@@ -291,6 +291,10 @@ static void gemv_dispatch(const uint16_t *X, const uint32_t *qw, const uint16_t 
     gemv_launch<XT, GS, 8>(X, qw, sc, zr, M, N, K, Y, yt, st);
 }
 
+bool gemv_stages_activations(int64_t M, int64_t K) {
+  return (uint64_t)(M + 1) * (uint64_t)K * 2u <= kGemvStageBytes;
+}
+
 bool gemv_supported(int64_t M, int64_t K, int gs) {
   const int64_t G = K / gs;
   const bool stage = (uint64_t)(M + 1) * (uint64_t)K * 2u <= kGemvStageBytes;

@@ -116,7 +116,15 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
  * Products are formed from the exact integer (code - zero) and the 16-bit
  * activation, accumulated in fp32 within a group, multiplied by the group's
  * scale and accumulated in fp32 across groups; Y is rounded once to y_dtype.
- * Dispatch: M <= AWQ_GEMV_MAX_M uses the GEMV kernel, larger M the MFMA GEMM.
+ * Dispatch: M <= AWQ_GEMV_MAX_M uses the GEMV kernel, larger M the MFMA
+ * GEMM.  When its tiles alone cannot fill the GPU, the GEMM splits K
+ * across workgroups and needs a scratch buffer (see awq_linear_ws): awq_linear
+ * and awq_linear_ex take it from a per-device buffer the library allocates the
+ * first time a shape needs it (or needs more) and keeps until the process
+ * ends.  Consequently (a) inside a HIP-graph capture, first call the same
+ * shape once outside the capture; (b) split-K calls on one device that may
+ * overlap in time (different streams) share that buffer and must instead use
+ * awq_linear_ws with a workspace each.
  * Requirements: M, N >= 0, K > 0, K % g == 0.  M == 0 or N == 0 is a no-op.
  */
 awq_status awq_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,
@@ -134,6 +142,30 @@ awq_status awq_linear_ex(const void *X, int32_t x_dtype, const uint32_t *qweight
                          const uint16_t *scales, const uint8_t *zeros, int64_t M,
                          int64_t N, int64_t K, awq_config cfg, void *Y,
                          int32_t y_dtype, int32_t kernel, awq_stream_t stream);
+
+/*
+ * awq_linear_workspace_size - bytes of device workspace awq_linear_ws needs
+ * for this shape (0: none; also 0 on invalid arguments).
+ */
+size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg);
+
+/*
+ * awq_linear_ws - awq_linear (automatic kernel choice) with a caller-owned
+ * workspace instead of the library's scratch; allocates nothing.
+ * Cites: as awq_linear.
+ *
+ *   workspace  device, at least awq_linear_workspace_size() bytes, 256-byte
+ *            aligned, zero-filled before its first use.  Every call leaves it
+ *            zero-filled again, so it can be reused by later calls (of any
+ *            shape) without clearing.  May be NULL when the size is 0.
+ *   Calls that share a workspace must not overlap in time.
+ * Errors: AWQ_ERR_WORKSPACE when workspace_bytes is too small; otherwise as
+ * awq_linear.
+ */
+awq_status awq_linear_ws(const void *X, int32_t x_dtype, const uint32_t *qweight,
+                         const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
+                         int64_t K, awq_config cfg, void *Y, int32_t y_dtype, void *workspace,
+                         size_t workspace_bytes, awq_stream_t stream);
 
 /*
  * awq_scale_search_workspace_size - bytes of device workspace that

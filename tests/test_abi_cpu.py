@@ -91,6 +91,24 @@ def test_linear_validation():
         == binding.AWQ_ERR_INVALID_ARG
 
 
+def test_linear_workspace_size_and_validation():
+    # one row of a 4096-wide layer runs the GEMV: no workspace
+    assert lib.awq_linear_workspace_size(1, 4096, 4096, cfg(128)) == 0
+    # a batch of 64 splits K across workgroups: fp32 partial tiles
+    ws = lib.awq_linear_workspace_size(64, 13824, 5120, cfg(128))
+    assert ws >= 64 * 13824 * 4
+    assert lib.awq_linear_workspace_size(64, 13824, 100, cfg(128)) == 0     # invalid K
+    assert lib.awq_linear_workspace_size(0, 13824, 5120, cfg(128)) == 0
+
+    def call(ws_ptr=FAKE, ws_bytes=ws, M=64, N=13824, K=5120):
+        return lib.awq_linear_ws(FAKE, 0, FAKE, FAKE, FAKE, M, N, K, cfg(128), FAKE, 0, ws_ptr,
+                                 ws_bytes, NULL)
+    assert call(ws_bytes=ws - 1) == binding.AWQ_ERR_WORKSPACE
+    assert call(ws_ptr=NULL) == binding.AWQ_ERR_INVALID_ARG
+    assert call(ws_ptr=ctypes.c_void_p(0x10010)) == binding.AWQ_ERR_INVALID_ARG
+    assert call(M=0, ws_ptr=NULL, ws_bytes=0) == binding.AWQ_OK
+
+
 def test_search_workspace_and_validation():
     ws = lib.awq_scale_search_workspace_size(4096, 4096, 4096, cfg(128), 20)
     # dominated by the fp32 reference output and the scaled activation copy

@@ -95,6 +95,55 @@ def test_ragged_shapes(M, N, K, g, dt):
         assert np.array_equal(Y16, want.float().numpy().astype(np.float64))
 
 
+def test_split_k_repeatable_and_workspace_regrowth():
+    """Small-M GEMMs split K across workgroups through a per-stream scratch
+    buffer whose counters each launch must leave at zero.  Repeated calls give
+    bit-identical results (the partials are summed in split order whichever
+    workgroup finishes last), and growing the scratch for a larger shape does
+    not disturb a later call of the first shape."""
+    torch = torch_mod()
+    # the second shape has more tiles than the first: its counters must not be
+    # overwritten by the first shape's partials on the way back
+    shapes = [(64, 640, 4096, 128), (32, 4096, 8192, 64), (256, 1280, 2048, 128)]
+    outs = {}
+    for rep in range(2):
+        for (M, N, K, g) in shapes:
+            W = wl.gen_weight(N, K, 60 + N)
+            X = wl.gen_activation(M, K, 61 + M, 62, "f16")
+            qw, sc, zr, pd = _packed(W, g)
+            say("split-K", rep, M, N, K, g)
+            Y = [out_to_f64(_run(X, "f16", pd, g, GEMM, torch.float32)) for _ in range(3)]
+            assert np.array_equal(Y[0], Y[1]) and np.array_equal(Y[0], Y[2])
+            if rep == 0:
+                assert_close(Y[0], linear64(X.astype(np.float64), qw, sc, zr, g), f"{M}x{N}x{K}")
+                outs[(M, N, K)] = Y[0]
+            else:
+                assert np.array_equal(Y[0], outs[(M, N, K)])
+
+
+def test_caller_workspace_matches_library_scratch():
+    """awq_linear_ws with a caller workspace (zero-filled once, reused) gives the
+    same bits as awq_linear with the library's scratch."""
+    awq = _awq()
+    torch = torch_mod()
+    M, N, K, g = 64, 1536, 5120, 128
+    W = wl.gen_weight(N, K, 70)
+    X = wl.gen_activation(M, K, 71, 72, "f16")
+    qw, sc, zr, pd = _packed(W, g)
+    need = awq.awq_linear_workspace_size(M, N, K, g)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    Xd = to_dev(X)
+    say("workspace", M, N, K, need)
+    a = awq.awq_linear(Xd, *pd, group_size=g, out_dtype=torch.float32)
+    b1 = awq.awq_linear_ws(Xd, *pd, ws, group_size=g, out_dtype=torch.float32)
+    b2 = awq.awq_linear_ws(Xd, *pd, ws, group_size=g, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b1) and torch.equal(a, b2)
+    assert int(ws[:2048].count_nonzero()) == 0        # split counters left at zero
+    assert_close(out_to_f64(b1), linear64(X.astype(np.float64), qw, sc, zr, g), "workspace")
+
+
 def test_tiny_layer_config():
     """Tiny single layer: W 512x512, g128, X at M=1 and M=8 with 5 outlier channels."""
     torch = torch_mod()
