@@ -94,6 +94,10 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
   constexpr int kBM = 32 * MT;
   constexpr int kRowsPerWave = kBM / 4; // rows of the A block each wave fetches
   constexpr int kDma = kRowsPerWave / 4;
+  // Tiles up to 128 rows stage activations through registers and keep a window
+  // of kWin weight blocks in flight; the 256-row tile (search GEMMs) uses DMA.
+  constexpr bool kRegA = MT <= 4 && !DENSE;
+  constexpr int kWin = kGPB > 1 ? 3 : 4;
 
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kBM * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBM * kBK];
@@ -153,10 +157,12 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
   const uint32_t q_lane = lane_col * (uint32_t)(K / 2) + (uint32_t)(kq * kWpl * 4);
   const uint32_t s_lane = lane_col * (uint32_t)G;
 
+  // Scales and zero points keep the width they are loaded with: widening them
+  // here would make the compiler wait for those loads right after issuing them.
   struct BRegs {
     uint32_t raw[kNT][kGPB][kWpl];
-    uint32_t sc[kNT][kGPB];
-    uint32_t zr[kNT][kGPB];
+    uint16_t sc[kNT][kGPB];
+    uint8_t zr[kNT][kGPB];
   };
   auto load_b = [&](int kb, BRegs &r) {
 #pragma unroll
@@ -243,14 +249,14 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
         for (int j = 0; j < kNT; ++j) {
           u32x4 bq[kWpl];
           if constexpr (!kBF16) {
-            const DeqF16 deq(br.zr[j][gi]);
+            const DeqF16 deq((uint32_t)br.zr[j][gi]);
 #pragma unroll
             for (int w = 0; w < kWpl; ++w) bq[w] = deq(br.raw[j][gi][w], dq);
           } else {
 #pragma unroll
             for (int w = 0; w < kWpl; ++w) bq[w] = deq_bf16_biased(br.raw[j][gi][w], dq);
           }
-          const float sc = half_bits_to_float((uint16_t)br.sc[j][gi]);
+          const float sc = half_bits_to_float(br.sc[j][gi]);
           f32x4 t[kMT];
 #pragma unroll
           for (int i = 0; i < kMT; ++i) t[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -261,7 +267,7 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
 #pragma unroll
           for (int i = 0; i < kMT; ++i) {
             if constexpr (kBF16) {
-              const float cz = -(float)(128u + br.zr[j][gi]);
+              const float cz = -(float)(128u + (uint32_t)br.zr[j][gi]);
 #pragma unroll
               for (int e = 0; e < 4; ++e) t[i][e] = __builtin_fmaf(cz, rs[i][e], t[i][e]);
             }
@@ -273,6 +279,69 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
     }
   };
 
+  if constexpr (kRegA) {
+    // ---- main loop, register-staged activations --------------------------------
+    // Every wait here is a counted vmcnt on ordinary loads, so the weight window
+    // of kWin blocks stays in flight while the math runs.  Activations: block
+    // k+1 is written to LDS during step k (its loads were issued in step k-1)
+    // and block k+2 is requested; one barrier per step orders LDS writes and
+    // reads.  Weights, scales and zeros: slot u holds block k, refilled with
+    // block k+kWin as soon as block k has been used.
+    constexpr int kARounds = kBM / 16;            // 16-byte chunks per thread per block
+    u32x4 areg[kARounds];
+    const rsrc_t rXa = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+    auto load_a = [&](int kb) {
+#pragma unroll
+      for (int r = 0; r < kARounds; ++r) {
+        const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
+        const uint32_t off = (uint32_t)(row0 + row) * (uint32_t)K * 2u + (uint32_t)kb * (kBK * 2) +
+                             (uint32_t)ch * 16u;
+        areg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rXa, off, 0, 0));
+      }
+    };
+    auto store_a = [&](uint16_t *buf) {
+#pragma unroll
+      for (int r = 0; r < kARounds; ++r) {
+        const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(buf) + row * (kBK * 2) +
+                                   ((ch ^ (row & 15)) << 4)) = areg[r];
+      }
+    };
+    // Loads are never under a branch (prefetch indices are clamped to the last
+    // block; the surplus loads of the last steps are never consumed), so every
+    // step issues the same sequence and the compiler's counted waits stay exact.
+    BRegs rw[kWin];
+    const int last = kb_end - 1;
+    auto clampk = [&](int k) { return k < last ? k : last; };
+    // The prologue ends with the same issue order as every step (activations,
+    // then one weight block) so that the wait counts the compiler derives at
+    // the loop header equal the steady-state ones.
+    load_a(kb_begin);
+#pragma unroll
+    for (int u = 0; u < kWin - 1; ++u) load_b(clampk(kb_begin + u), rw[u]);
+    store_a(sA0);
+    load_a(clampk(kb_begin + 1));
+    load_b(clampk(kb_begin + kWin - 1), rw[kWin - 1]);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes landed
+    __builtin_amdgcn_s_barrier();
+    for (int kb = kb_begin; kb < kb_end; kb += kWin) {
+#pragma unroll
+      for (int u = 0; u < kWin; ++u) {
+        const int k = kb + u;
+        if (k >= kb_end) break;
+        const bool odd = ((k - kb_begin) & 1) != 0;
+        uint16_t *buf = odd ? sA1 : sA0;
+        uint16_t *nbuf = odd ? sA0 : sA1;
+        store_a(nbuf);                      // block k+1 (a copy of the last block at the end)
+        load_a(clampk(k + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(k, buf, rw[u]);
+        load_b(clampk(k + kWin), rw[u]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+      }
+    }
+  } else {
   // ---- main loop: two static buffers, one barrier per block -------------------
   // Prefetch indices are clamped to the last block instead of branched on, so
   // no load sits under a branch; the surplus prefetch of the last iteration
@@ -298,43 +367,58 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
     compute(kb + 1, sA1, r1);
   }
   wait_vmem_all();
+  }
 
   // ---- split K: publish the partial tile; the last workgroup sums them ------
-  if (sk.splits > 1) {
+  // The partials cross workgroups that may sit on different XCDs, whose L2s
+  // are not coherent with each other.  A device-scope fence would write back
+  // and invalidate a whole L2 per workgroup; instead the partials are stored
+  // write-through and read back bypassing both cache levels (the sc0 sc1
+  // cache-policy bits), and the per-tile counter is an atomic, which is
+  // coherent across XCDs.  vmcnt(0) orders the stores before the atomic.
+  // (compiled only for the tiles the plan may split: the 256-row tile's
+  // registers are all taken by its main loop)
+  if constexpr (MT < 8) if (sk.splits > 1) {
     constexpr int kRegs = kMT * kNT * 4;
-    const size_t wave_stride = (size_t)kRegs * 64;
-    float *mine = sk.partials + ((size_t)tile * sk.splits + split) * 4 * wave_stride +
-                  (size_t)wave * wave_stride + lane;
+    constexpr int kSys = 1 | 16;          // sc0 | sc1: system-coherent access
+    const uint32_t wave_stride = (uint32_t)kRegs * 64u;
+    const uint32_t tile_stride = 4u * wave_stride;
+    const rsrc_t rP = make_rsrc(sk.partials, 0x7FFFFFF0u);
+    const uint32_t mine = (((uint32_t)tile * (uint32_t)sk.splits + (uint32_t)split) * tile_stride +
+                           (uint32_t)wave * wave_stride + (uint32_t)lane) * 4u;
 #pragma unroll
     for (int i = 0; i < kMT; ++i)
 #pragma unroll
       for (int j = 0; j < kNT; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mine[((i * kNT + j) * 4 + e) * 64] = acc[i][j][e];
-    __threadfence();
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[i][j][e];   // scalar first: see DeqF16
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rP,
+                                                mine + (uint32_t)((i * kNT + j) * 4 + e) * 256u, 0,
+                                                kSys);
+        }
+    wait_vmem_all();
     __syncthreads();
     if (tid == 0) s_last = atomicAdd(&sk.counters[tile], 1u) == (uint32_t)(sk.splits - 1);
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    const float *base = sk.partials + (size_t)tile * sk.splits * 4 * wave_stride +
-                        (size_t)wave * wave_stride + lane;
-#pragma unroll
-    for (int i = 0; i < kMT; ++i)
-#pragma unroll
-      for (int j = 0; j < kNT; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] = base[((i * kNT + j) * 4 + e) * 64];
-    for (int sp = 1; sp < sk.splits; ++sp) {
-      const float *p = base + (size_t)sp * 4 * wave_stride;
+    const uint32_t base = ((uint32_t)tile * (uint32_t)sk.splits * tile_stride +
+                           (uint32_t)wave * wave_stride + (uint32_t)lane) * 4u;
+    for (int sp = 0; sp < sk.splits; ++sp) {
+      const uint32_t p = base + (uint32_t)sp * tile_stride * 4u;
 #pragma unroll
       for (int i = 0; i < kMT; ++i)
 #pragma unroll
         for (int j = 0; j < kNT; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] += p[((i * kNT + j) * 4 + e) * 64];
+          for (int e = 0; e < 4; ++e) {
+            const float v = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(
+                           rP, p + (uint32_t)((i * kNT + j) * 4 + e) * 256u, 0, kSys));
+            acc[i][j][e] = sp == 0 ? v : acc[i][j][e] + v;
+          }
     }
-    if (tid == 0) sk.counters[tile] = 0u;   // ready for the next launch
+    if (tid == 0) atomicExch(&sk.counters[tile], 0u);   // ready for the next launch
   }
 
   // ---- epilogue -------------------------------------------------------------
@@ -390,8 +474,9 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
   }
 }
 
-// The 128- and 256-row tiles keep one wave per SIMD and the whole register
-// file; smaller tiles leave room for two workgroups per CU.
+// The 128- and 256-row tiles keep one wave per SIMD and the whole register file
+// (accumulators plus the weight window); smaller tiles run two workgroups per
+// CU.
 template <class XT, int GS, int EPI, bool DENSE, int YT, int MT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel_big(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
@@ -435,13 +520,15 @@ bool gemm_supported(int64_t N, int64_t K, bool dense) {
 
 constexpr size_t kSplitCounterBytes = 512 * 4;
 
-// Row tile and K split of a quantized GEMM launch.  M <= 32, 64, 256 take
-// 32-, 64- and 128-row tiles, larger M the 256-row tile.  When the tiles
+// Row tile and K split of a quantized GEMM launch.  M <= 32 and M <= 64 take
+// 32- and 64-row tiles, larger M the 128-row tile (the 256-row tile needs more
+// registers than one wave of two per SIMD has and spends its VALU time moving
+// accumulators through AGPRs).  When the tiles
 // cannot give every CU two workgroups, K is split (at most 8 ways, at least
 // two K blocks per split).
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan p{};
-  p.mt = M <= 32 ? 1 : M <= 64 ? 2 : M <= 256 ? 4 : 8;
+  p.mt = M <= 32 ? 1 : M <= 64 ? 2 : 4;
   const int64_t bm = 32 * p.mt;
   p.tiles = ((M + bm - 1) / bm) * ((N + kBN - 1) / kBN);
   const int64_t nkb = (K + kBK - 1) / kBK;
