@@ -14,7 +14,8 @@
 // Mapping: one lane per output word (8 input channels, 16 bytes of W);
 // g/8 consecutive lanes form a group and exchange min/max with lane shuffles.
 // The kernel is bound by HBM traffic (2 bytes in, 0.5 + 3/g bytes out per
-// weight) plus the division chain.
+// weight); the per-weight division is replaced by a reciprocal multiply whose
+// rounding provably agrees except next to half-integers (checked per lane).
 
 #include "awq_internal.h"
 #include "device_common.h"
@@ -75,10 +76,30 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
   const float sf = (float)sh;
   const float zf = fminf(fmaxf(__builtin_rintf(-lo / sf), 0.0f), 15.0f);
 
+  // rint(v / sf) with the correctly rounded quotient, without eight divisions:
+  // |v / sf| < 16 (|v| <= hi - lo <= 15 sf (1 + 2^-10)), so both the quotient
+  // rounded once and y = fl(v * fl(1 / sf)) lie within 2^-19 of the exact
+  // v / sf and hence within 2^-18 of each other.  Unless y is that close to a
+  // half-integer, both round to the same integer (ties included, since a
+  // rounded quotient exactly at k + 1/2 puts y within 2^-18 of it); the rare
+  // lanes that are that close divide.
+  const float rs = 1.0f / sf;
+  float qv[8];
+  bool near_half = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float y = v[i] * rs;
+    qv[i] = __builtin_rintf(y);
+    near_half |= __builtin_fabsf((y - __builtin_floorf(y)) - 0.5f) < 0x1p-18f;
+  }
+  if (near_half) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = __builtin_rintf(v[i] / sf);
+  }
   uint32_t word = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float qf = fminf(fmaxf(__builtin_rintf(v[i] / sf) + zf, 0.0f), 15.0f);
+    const float qf = fminf(fmaxf(qv[i] + zf, 0.0f), 15.0f);
     word |= ((uint32_t)qf) << (4 * nibble_of_channel(i));
   }
 
