@@ -52,7 +52,6 @@ namespace awq {
 namespace {
 
 constexpr int kBN = 128, kBK = 128;
-constexpr int kNT = 4;                 // 16x16 tiles per wave along N
 constexpr int kThreads = 256;
 constexpr uint32_t kNone = 0xFFFFFFFFu; // an offset every range check rejects
 
@@ -90,8 +89,13 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
   constexpr int kGS = DENSE ? 128 : GS;
   constexpr int kWpl = kGS / 32;        // 8-channel words per lane per group
   constexpr int kGPB = kBK / kGS;       // groups per K block
-  constexpr int kMT = MT;               // 16x16 tiles per wave along M
   constexpr int kBM = 32 * MT;
+  // Wave layout: 2 x 2 waves of (BM/2) x 64, or (kTall) 1 x 4 waves of
+  // BM x 32, where every dequantized weight fragment feeds twice as many MFMAs.
+  constexpr bool kTall = false;
+  constexpr int kMT = kTall ? 2 * MT : MT;  // 16x16 tiles per wave along M
+  constexpr int kNT = kTall ? 2 : 4;        // 16x16 tiles per wave along N
+  constexpr int kWaveCols = 16 * kNT;
   constexpr int kRowsPerWave = kBM / 4; // rows of the A block each wave fetches
   constexpr int kDma = kRowsPerWave / 4;
   // Tiles up to 128 rows stage activations through registers and keep a window
@@ -107,7 +111,7 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const DeqRegs dq;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = kTall ? 0 : wave >> 1, wn = kTall ? wave : wave & 1;
   const int c = lane & 15, kq = lane >> 4;
 
   const int tiles_n = (N + kBN - 1) / kBN;
@@ -150,7 +154,7 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
   };
 
   // ---- packed weights, scales and zeros of one K block (registers) -------------
-  const uint32_t lane_col = (uint32_t)(wn * 64 + c);
+  const uint32_t lane_col = (uint32_t)(wn * kWaveCols + c);
   const rsrc_t rQ = make_rsrc(qweight, DENSE ? 0u : (uint32_t)N * (uint32_t)K / 2u);
   const rsrc_t rS = make_rsrc(scales, DENSE ? 0u : (uint32_t)N * (uint32_t)G * 2u);
   const rsrc_t rZ = make_rsrc(zeros, DENSE ? 0u : (uint32_t)N * (uint32_t)G);
@@ -379,44 +383,40 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
   // (compiled only for the tiles the plan may split: the 256-row tile's
   // registers are all taken by its main loop)
   if constexpr (MT < 8) if (sk.splits > 1) {
-    constexpr int kRegs = kMT * kNT * 4;
+    constexpr int kTiles = kMT * kNT;     // f32x4 accumulators per lane
     constexpr int kSys = 1 | 16;          // sc0 | sc1: system-coherent access
-    const uint32_t wave_stride = (uint32_t)kRegs * 64u;
-    const uint32_t tile_stride = 4u * wave_stride;
+    // partial layout: [tile][split][wave][16x16 tile][lane] of 16 bytes
+    const uint32_t wave_bytes = (uint32_t)kTiles * 64u * 16u;
+    const uint32_t tile_bytes = 4u * wave_bytes;
     const rsrc_t rP = make_rsrc(sk.partials, 0x7FFFFFF0u);
-    const uint32_t mine = (((uint32_t)tile * (uint32_t)sk.splits + (uint32_t)split) * tile_stride +
-                           (uint32_t)wave * wave_stride + (uint32_t)lane) * 4u;
+    const uint32_t lane_off = (uint32_t)wave * wave_bytes + (uint32_t)lane * 16u;
+    const uint32_t mine = ((uint32_t)tile * (uint32_t)sk.splits + (uint32_t)split) * tile_bytes +
+                          lane_off;
 #pragma unroll
     for (int i = 0; i < kMT; ++i)
 #pragma unroll
-      for (int j = 0; j < kNT; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = acc[i][j][e];   // scalar first: see DeqF16
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rP,
-                                                mine + (uint32_t)((i * kNT + j) * 4 + e) * 256u, 0,
-                                                kSys);
-        }
+      for (int j = 0; j < kNT; ++j) {
+        const f32x4 v = acc[i][j];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rP,
+                                               mine + (uint32_t)(i * kNT + j) * 1024u, 0, kSys);
+      }
     wait_vmem_all();
     __syncthreads();
     if (tid == 0) s_last = atomicAdd(&sk.counters[tile], 1u) == (uint32_t)(sk.splits - 1);
     __syncthreads();
     if (!s_last) return;
-    const uint32_t base = ((uint32_t)tile * (uint32_t)sk.splits * tile_stride +
-                           (uint32_t)wave * wave_stride + (uint32_t)lane) * 4u;
+    const uint32_t base = (uint32_t)tile * (uint32_t)sk.splits * tile_bytes + lane_off;
     for (int sp = 0; sp < sk.splits; ++sp) {
-      const uint32_t p = base + (uint32_t)sp * tile_stride * 4u;
+      const uint32_t p = base + (uint32_t)sp * tile_bytes;
 #pragma unroll
       for (int i = 0; i < kMT; ++i)
 #pragma unroll
-        for (int j = 0; j < kNT; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(
-                           rP, p + (uint32_t)((i * kNT + j) * 4 + e) * 256u, 0, kSys));
-            acc[i][j][e] = sp == 0 ? v : acc[i][j][e] + v;
-          }
+        for (int j = 0; j < kNT; ++j) {
+          const f32x4 v = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rP, p + (uint32_t)(i * kNT + j) * 1024u,
+                                                           0, kSys));
+          acc[i][j] = sp == 0 ? v : acc[i][j] + v;
+        }
     }
     if (tid == 0) atomicExch(&sk.counters[tile], 0u);   // ready for the next launch
   }
@@ -428,7 +428,7 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
     const rsrc_t rY = make_rsrc(Y, (uint32_t)M * (uint32_t)N * (uint32_t)ysz);
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
-      const int n = col0 + wn * 64 + j * 16 + c;
+      const int n = col0 + wn * kWaveCols + j * 16 + c;
 #pragma unroll
       for (int i = 0; i < kMT; ++i) {
 #pragma unroll
@@ -450,7 +450,7 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
     double sum = 0.0;
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
-      const int n = col0 + wn * 64 + j * 16 + c;
+      const int n = col0 + wn * kWaveCols + j * 16 + c;
 #pragma unroll
       for (int i = 0; i < kMT; ++i) {
 #pragma unroll
