@@ -28,6 +28,7 @@ SOURCES = [
     "quantize_pack.hip",
     "linear_gemv.hip",
     "linear_gemm.hip",
+    "gemm_f16.hip",
     "search.hip",
     "api.cpp",
 ]

@@ -226,7 +226,8 @@ awq_status linear_impl(const void *X, int32_t x_dtype, const uint32_t *qweight,
   awq_status st =
       check_linear(X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype, kernel);
   if (st != AWQ_OK) return st;
-  const awq::GemmPlan plan = awq::gemm_plan(M > 0 ? M : 1, N > 0 ? N : 1, K);
+  const awq::XType xt = x_dtype == AWQ_F16 ? awq::XType::F16 : awq::XType::BF16;
+  const awq::GemmPlan plan = awq::gemm_plan(M > 0 ? M : 1, N > 0 ? N : 1, K, xt);
   const bool gemv_ok = awq::gemv_supported(M, K, cfg.group_size);
   if (kernel == AWQ_KERNEL_GEMV && !gemv_ok)
     return fail(AWQ_ERR_UNSUPPORTED, "GEMV kernel cannot serve K=%lld", (long long)K);
@@ -236,12 +237,13 @@ awq_status linear_impl(const void *X, int32_t x_dtype, const uint32_t *qweight,
   if (caller_ws && !gemv && plan.workspace_bytes > 0) {
     if (!workspace) return fail(AWQ_ERR_INVALID_ARG, "this shape needs a workspace");
     if (!aligned(workspace, 256)) return fail(AWQ_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-    if (workspace_bytes < plan.workspace_bytes)
-      return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
-                  plan.workspace_bytes);
+    // The documented minimum (awq_linear_workspace_size) covers both
+    // activation types.
+    const size_t need = awq::gemm_workspace_bytes(M, N, K);
+    if (workspace_bytes < need)
+      return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   }
   if (M == 0 || N == 0) return ok();
-  const awq::XType xt = x_dtype == AWQ_F16 ? awq::XType::F16 : awq::XType::BF16;
   const awq::YType yt = y_dtype == AWQ_F16    ? awq::YType::F16
                         : y_dtype == AWQ_BF16 ? awq::YType::BF16
                                               : awq::YType::F32;
@@ -274,7 +276,7 @@ size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg
   if (check_config(cfg, K) != AWQ_OK || M < 0 || N < 0) return 0;
   if (M == 0 || N == 0) return 0;
   if (M <= AWQ_GEMV_MAX_M && awq::gemv_supported(M, K, cfg.group_size)) return 0;
-  return awq::gemm_plan(M, N, K).workspace_bytes;
+  return awq::gemm_workspace_bytes(M, N, K);
 }
 
 awq_status awq_linear_ws(const void *X, int32_t x_dtype, const uint32_t *qweight,

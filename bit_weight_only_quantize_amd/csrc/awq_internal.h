@@ -27,6 +27,18 @@ hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,
                        int64_t N, int64_t K, int gs, void *Y, YType yt,
                        hipStream_t st);
 
+// ---- split K (both GEMM kernels) ---------------------------------------------------
+// Split-K bookkeeping of one launch: `splits` workgroups per output tile, a
+// u32 counter per tile (zero between launches) and the fp32 partial tiles.
+struct SplitK {
+  int splits;
+  uint32_t *counters;
+  float *partials;
+};
+// The counters sit in a fixed region at the start of the workspace (the
+// partials of one shape never overlap the counters of another).
+constexpr size_t kSplitCounterBytes = 512 * 4;
+
 // ---- linear_gemm.hip (any M) ---------------------------------------------------
 // Row tile (32 * mt rows), K split and split-K workspace of a quantized GEMM.
 struct GemmPlan {
@@ -35,13 +47,24 @@ struct GemmPlan {
   size_t counter_bytes;    // fixed-size u32 counter region (zero between launches)
   size_t workspace_bytes;  // 0 when splits == 1
 };
-GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K);
+// The plan of the kernel that serves activations of type xt (fp16: the
+// kernel of gemm_f16.hip).
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, XType xt);
+// Workspace that serves either activation type.
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // `workspace` (gemm_plan(...).workspace_bytes, 256-byte aligned, counters
 // zeroed once) is needed only when the plan splits K.
 hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M,
                        int64_t N, int64_t K, int gs, void *Y, YType yt,
                        void *workspace, hipStream_t st);
+
+// ---- gemm_f16.hip (fp16 activations, any M) ------------------------------------------
+// Row tile (16 * mt rows) and K split of the fp16 GEMM.
+GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_f16(const uint16_t *X, const uint32_t *qweight, const uint16_t *scales,
+                           const uint8_t *zeros, int64_t M, int64_t N, int64_t K, int gs,
+                           void *Y, YType yt, void *workspace, hipStream_t st);
 
 // Dense fp16 B (X * W^T with W fp16 [N][K]), fp32 output.
 hipError_t launch_gemm_dense_f32(const uint16_t *X, const uint16_t *W, int64_t M,

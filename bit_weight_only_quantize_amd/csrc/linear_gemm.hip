@@ -69,13 +69,6 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 
 }  // namespace
 
-// Split-K bookkeeping of one launch: `splits` workgroups per output tile, a
-// u32 counter per tile (zero between launches) and the fp32 partial tiles.
-struct SplitK {
-  int splits;
-  uint32_t *counters;
-  float *partials;
-};
 
 template <class XT, int GS, int EPI, bool DENSE, int YT, int MT>
 __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
@@ -518,7 +511,6 @@ bool gemm_supported(int64_t N, int64_t K, bool dense) {
   return (dense ? N * K * 2 : N * K / 2) <= lim && rows_per_launch(N, K, 256) > 0;
 }
 
-constexpr size_t kSplitCounterBytes = 512 * 4;
 
 // Row tile and K split of a quantized GEMM launch.  M <= 32 and M <= 64 take
 // 32- and 64-row tiles, larger M the 128-row tile (the 256-row tile needs more
@@ -526,7 +518,7 @@ constexpr size_t kSplitCounterBytes = 512 * 4;
 // accumulators through AGPRs).  When the tiles
 // cannot give every CU two workgroups, K is split (at most 8 ways, at least
 // two K blocks per split).
-GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K) {
+static GemmPlan gemm_bf16_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan p{};
   p.mt = M <= 32 ? 1 : M <= 64 ? 2 : 4;
   const int64_t bm = 32 * p.mt;
@@ -547,6 +539,16 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K) {
     p.workspace_bytes = p.counter_bytes + (size_t)p.tiles * p.splits * bm * kBN * 4;
   }
   return p;
+}
+
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, XType xt) {
+  return xt == XType::F16 ? gemm_f16_plan(M, N, K) : gemm_bf16_plan(M, N, K);
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const size_t a = gemm_f16_plan(M, N, K).workspace_bytes;
+  const size_t b = gemm_bf16_plan(M, N, K).workspace_bytes;
+  return a > b ? a : b;
 }
 
 template <class XT, int GS, int EPI, bool DENSE, int YT, int MT>
@@ -619,7 +621,10 @@ hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
                        int64_t K, int gs, void *Y, YType yt, void *workspace,
                        hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  const GemmPlan p = gemm_plan(M, N, K);
+  if (xt == XType::F16)
+    return launch_gemm_f16(reinterpret_cast<const uint16_t *>(X), qweight, scales, zeros, M, N, K,
+                           gs, Y, yt, workspace, st);
+  const GemmPlan p = gemm_bf16_plan(M, N, K);
   SplitK sk{1, nullptr, nullptr};
   if (p.splits > 1) {
     if (!workspace) return hipErrorInvalidValue;

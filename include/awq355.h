@@ -145,7 +145,8 @@ awq_status awq_linear_ex(const void *X, int32_t x_dtype, const uint32_t *qweight
 
 /*
  * awq_linear_workspace_size - bytes of device workspace awq_linear_ws needs
- * for this shape (0: none; also 0 on invalid arguments).
+ * for this shape, for either activation type (0: none; also 0 on invalid
+ * arguments).
  */
 size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg);
 
@@ -155,9 +156,10 @@ size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg
  * Cites: as awq_linear.
  *
  *   workspace  device, at least awq_linear_workspace_size() bytes, 256-byte
- *            aligned, zero-filled before its first use.  Every call leaves it
- *            zero-filled again, so it can be reused by later calls (of any
- *            shape) without clearing.  May be NULL when the size is 0.
+ *            aligned, zero-filled before its first use.  Its first 2 KiB hold
+ *            counters that every call leaves at zero again (the rest is
+ *            scratch), so it can be reused by later calls (of any shape)
+ *            without clearing.  May be NULL when the size is 0.
  *   Calls that share a workspace must not overlap in time.
  * Errors: AWQ_ERR_WORKSPACE when workspace_bytes is too small; otherwise as
  * awq_linear.
