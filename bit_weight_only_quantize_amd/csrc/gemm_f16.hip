@@ -3,34 +3,32 @@
 // The GEMM variant of the quantized linear layer ("AWQ Advanced Usage Guide",
 // "WQLinear Kernel Variants": batch sizes above one), Y = X * deq(W)^T with
 // deq = (q - z) * s per group of g input channels (the pages' zero-point,
-// group-wise int4 configuration).
+// group-wise int4 configuration).  Like the GEMM kernels the pages describe,
+// it dequantizes each weight to fp16 and runs an fp16 matrix product with
+// fp32 accumulation: the B operand is fp16((q - z) * s), the exact integer
+// q - z times the group's fp16 scale rounded once (relative error at most
+// 2^-11 per weight).
 //
-// Exactness: the B operand is the exact integer q - z in fp16, MFMA sums one
-// group in fp32 and the group's scale multiplies that fp32 partial; no
-// dequantized weight is rounded to 16 bits.
-//
-// Work split, chosen for the MI355X's balance of MFMA, VALU and LDS rates:
-//  * A 256-thread workgroup owns a BM x 128 tile of Y (BM = 16 * MT rows).
-//    Wave v owns columns 32v .. 32v+31 over all BM rows, so every weight word
-//    is loaded and dequantized by exactly one lane of the workgroup, and each
-//    dequantized B fragment feeds MT MFMAs (8 for the 128-row tile).
-//  * The price is that every wave reads the whole activation block from LDS
-//    (4x replication); gfx950's 64-bank LDS carries that at well under its
-//    rate.  A 16-byte chunk c of block row r is stored at chunk c ^ (r % 16),
-//    so the 16 rows one 128-bit LDS read touches fall in 16 distinct bank
-//    groups.
-//  * Per group, a lane dequantizes its 2 x (g/32) words up front; then per
-//    16-row tile it reads g/32 activation fragments and runs two short MFMA
-//    chains (one per 16-column tile) whose fp32 sums are scaled into the
-//    accumulators.  Registers stay under half the file, so two workgroups
-//    share each CU and one's VALU work overlaps the other's MFMAs.
-//  * Compute-bound tiles (128 rows) stream activations straight into LDS with
-//    buffer_load ... lds, double-buffered, one block ahead.  Memory-bound
-//    tiles (32 and 64 rows, batched decode) stage activations through
-//    registers instead, so that only ordinary loads are in flight and counted
-//    waits can keep a window of several weight blocks streaming from HBM.
+// Work split, chosen from measured MI355X rates (one wave keeps the MFMA unit
+// busy when it issues about two VALU operations or fewer per 16x16x32 MFMA;
+// a CU's LDS delivers about 160 bytes per clock to ds_read_b128):
+//  * A 256-thread workgroup owns a BM x 256 tile of Y (BM = 16 * MT rows);
+//    wave v owns columns 64v .. 64v+63 over all BM rows.  Each packed weight
+//    word is loaded and dequantized by exactly one lane and feeds MT MFMAs;
+//    each activation fragment read from LDS feeds four.
+//  * Dequantizing costs 13 VALU operations per word (8 weights): 4 and-or
+//    into the mantissa of 1024.0 or 64.0, 4 packed subtractions of the biased
+//    zero point (exact), 4 packed multiplies by the scale (rounded once).  A
+//    block's 16 words per lane are dequantized while the previous block's
+//    MFMAs run, so the VALU work overlaps the matrix core.
+//  * Activations are staged through registers into LDS, double-buffered.
+//    16-byte chunk c of block row r lives at chunk c ^ (r % 16) ^ f(c), where
+//    f flips bit 3 for the odd lane quarters of an MFMA fragment read: that
+//    layout measured free of bank conflicts for the fragment reads.
+//  * Only ordinary loads are in flight, so counted vmcnt waits keep a window
+//    of kWin weight blocks streaming from HBM while the math runs.
 //  * Split K (when the M x N tiles cannot fill the CUs) and its fence-free
-//    fixup follow the same scheme as the other GEMM kernels of this library.
+//    fixup follow the scheme of the other GEMM kernels of this library.
 //  * Tiles are visited in groups of four row tiles, row index fastest, so the
 //    workgroups resident on one XCD share activation rows and weight columns
 //    in that XCD's L2.
@@ -46,13 +44,14 @@ namespace awq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBN = 128;        // columns per workgroup (4 waves x 32)
-constexpr int kBK = 128;        // input channels per K block
-constexpr int kGroupRows = 4;   // row tiles per tile group
+constexpr int kNT = 4;            // 16-column MFMA tiles per wave
+constexpr int kBN = 64 * 4;       // columns per workgroup
+constexpr int kBK = 128;          // input channels per K block
+constexpr int kSteps = kBK / 32;  // MFMA K steps per block
+constexpr int kGroupRows = 4;     // row tiles per tile group
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
@@ -63,9 +62,16 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 // s_waitcnt lgkmcnt(0).
 __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Physical 16-byte chunk of logical chunk ch in block row `row`.  KQ_BIT is
+// the bit of ch that holds the lowest bit of the reading lane's quarter.
+template <int KQ_BIT>
+__device__ __forceinline__ int a_chunk(int row, int ch) {
+  return ch ^ (row & 15) ^ (((ch >> KQ_BIT) & 1) << 3);
+}
+
 }  // namespace
 
-template <int GS, int YT, int MT, bool DMA, bool KTAIL>
+template <int GS, int YT, int MT, bool KTAIL>
 __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
                                               const uint32_t *__restrict__ qweight,
                                               const uint16_t *__restrict__ scales,
@@ -74,12 +80,15 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   constexpr int kBM = 16 * MT;
   constexpr int kWpl = GS / 32;      // packed words per lane per group and column
   constexpr int kGPB = kBK / GS;     // groups per K block
-  // Weight blocks in flight on the register-staged path (as many as the
-  // register budget of two workgroups per CU allows).
-  constexpr int kWin = (MT <= 2 ? 4 : 3) - (kGPB > 1 ? 1 : 0);
+  constexpr int kKqBit = GS == 128 ? 2 : 1;
+  constexpr int kWin = MT >= 8 ? 2 : 4;   // weight blocks in flight (even: bq buffers alternate)
+  constexpr int kWords = kNT * kSteps;          // packed words per lane per block
+  constexpr int kWordsPerTile = kWords / MT;    // dequantized alongside each row tile
 
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kBM * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint32_t sSZ0[256 * kGPB];
+  __shared__ __attribute__((aligned(16))) uint32_t sSZ1[256 * kGPB];
   __shared__ uint32_t s_last;
 
   const int tid = threadIdx.x;
@@ -110,227 +119,253 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   const int kb_begin = (int)((int64_t)split * nkb / sk.splits);
   const int kb_end = (int)((int64_t)(split + 1) * nkb / sk.splits);
 
-  // ---- packed weights, scales and zeros of one K block (registers) -------------
+  // ---- packed weights of one K block (registers) ------------------------------
   // Lane (c, kq) holds, for column tile j, words kq*kWpl .. kq*kWpl+kWpl-1 of
-  // each group of column col0 + 32*wave + 16*j + c: channels
-  // 8*(kq*kWpl + w) .. +7 of the group for MFMA step w.
-  const uint32_t lane_col = (uint32_t)(col0 + wave * 32 + c);
+  // each group of column col0 + 64*wave + 16*j + c: channels
+  // 8*(kq*kWpl + w) .. +7 of the group, for MFMA step gi*kWpl + w.
+  const uint32_t lane_col = (uint32_t)(col0 + wave * 64 + c);
   const rsrc_t rQ = make_rsrc(qweight, (uint32_t)N * (uint32_t)K / 2u);
-  const rsrc_t rS = make_rsrc(scales, (uint32_t)N * (uint32_t)G * 2u);
-  const rsrc_t rZ = make_rsrc(zeros, (uint32_t)N * (uint32_t)G);
   const uint32_t q_lane = lane_col * (uint32_t)(K / 2) + (uint32_t)(kq * kWpl * 4);
-  const uint32_t s_lane = lane_col * (uint32_t)G;
-
-  // Scales and zero points keep their load width: widening them right after
-  // the load would make the compiler wait for it there.
-  struct BRegs {
-    uint32_t raw[2][kGPB][kWpl];
-    uint16_t sc[2][kGPB];
-    uint8_t zr[2][kGPB];
+  struct Raw {
+    uint32_t w[kNT][kGPB][kWpl];
   };
-  auto load_b = [&](int kb, BRegs &r) {
+  // Column tile j of block kb (one load).  With KTAIL (K % 128 == 64, g = 64)
+  // a group past the end of K reads zero weights and, below, zero scale and
+  // activations: it adds nothing.
+  auto load_w = [&](int kb, int j, Raw &r) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int gi = 0; gi < kGPB; ++gi) {
+      const uint32_t g = (uint32_t)(kb * kGPB + gi);
+      const bool in_k = !KTAIL || g < (uint32_t)G;
+      const uint32_t qo =
+          in_k ? q_lane + (uint32_t)(16 * j) * (uint32_t)(K / 2) + g * (GS / 2) : kNone;
+      if constexpr (kWpl == 4) {
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo, 0, 0));
 #pragma unroll
-      for (int gi = 0; gi < kGPB; ++gi) {
-        const uint32_t g = (uint32_t)(kb * kGPB + gi);
-        // With KTAIL, a group past the end of K reads zero weights, scale and
-        // zero point (and zero activations), so it adds exactly nothing.
-        const bool in_k = !KTAIL || g < (uint32_t)G;
-        const uint32_t qo =
-            in_k ? q_lane + (uint32_t)(16 * j) * (uint32_t)(K / 2) + g * (GS / 2) : kNone;
-        if constexpr (kWpl == 4) {
-          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo, 0, 0));
+        for (int w = 0; w < kWpl; ++w) r.w[j][gi][w] = v[w];
+      } else {
+        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rQ, qo, 0, 0));
 #pragma unroll
-          for (int w = 0; w < kWpl; ++w) r.raw[j][gi][w] = v[w];
-        } else {
-          const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rQ, qo, 0, 0));
-#pragma unroll
-          for (int w = 0; w < kWpl; ++w) r.raw[j][gi][w] = v[w];
-        }
-        const uint32_t so = in_k ? s_lane + (uint32_t)(16 * j) * (uint32_t)G + g : kNone / 2u;
-        r.sc[j][gi] = __builtin_amdgcn_raw_buffer_load_b16(rS, so * 2u, 0, 0);
-        r.zr[j][gi] = __builtin_amdgcn_raw_buffer_load_b8(rZ, so, 0, 0);
+        for (int w = 0; w < kWpl; ++w) r.w[j][gi][w] = v[w];
       }
     }
   };
 
-  f32x4 acc[MT][2];
+  // ---- scales and zero points: one column per thread, handed over in LDS ------
+  // Thread t loads column col0 + t's scale(s) and zero point(s) of a block
+  // (one or two loads instead of one per lane and column tile) and stores
+  // them as u32 (zero << 16 | scale) at [group][wave][c][j] with
+  // t = 64 * wave + 16 * j + c, so that lane (c, kq) reads its four column
+  // tiles' values with one 16-byte LDS read per group.
+  const rsrc_t rS = make_rsrc(scales, (uint32_t)N * (uint32_t)G * 2u);
+  const rsrc_t rZ = make_rsrc(zeros, (uint32_t)N * (uint32_t)G);
+  const uint32_t sz_col = (uint32_t)(col0 + tid) * (uint32_t)G;
+  struct SZ {
+    uint32_t sc;     // kGPB scales: u16, or two u16 in one u32 (g = 64)
+    uint32_t zr;     // kGPB zero points: u8, or two u8 in one u16 (g = 64)
+    uint16_t sc1;    // second group (KTAIL only: loaded separately)
+    uint8_t zr1;
+  };
+  auto load_sz = [&](int kb, SZ &r) {
+    const uint32_t g = (uint32_t)(kb * kGPB);
+    if constexpr (kGPB == 1) {
+      r.sc = __builtin_amdgcn_raw_buffer_load_b16(rS, (sz_col + g) * 2u, 0, 0);
+      r.zr = __builtin_amdgcn_raw_buffer_load_b8(rZ, sz_col + g, 0, 0);
+    } else if constexpr (!KTAIL) {
+      // G even and g even: both groups' scales (4 bytes) and zeros (2 bytes)
+      // are naturally aligned.
+      r.sc = __builtin_amdgcn_raw_buffer_load_b32(rS, (sz_col + g) * 2u, 0, 0);
+      r.zr = __builtin_amdgcn_raw_buffer_load_b16(rZ, sz_col + g, 0, 0);
+    } else {
+      const uint32_t o1 = g + 1 < (uint32_t)G ? sz_col + g + 1 : kNone / 2u;
+      r.sc = __builtin_amdgcn_raw_buffer_load_b16(rS, (sz_col + g) * 2u, 0, 0);
+      r.zr = __builtin_amdgcn_raw_buffer_load_b8(rZ, sz_col + g, 0, 0);
+      r.sc1 = __builtin_amdgcn_raw_buffer_load_b16(rS, o1 * 2u, 0, 0);
+      r.zr1 = __builtin_amdgcn_raw_buffer_load_b8(rZ, o1, 0, 0);
+    }
+  };
+  const int sz_slot = ((wave * 16 + c) * 4 + kq) * 4;   // this thread's column: j = kq
+  auto store_sz = [&](uint32_t *buf, const SZ &r) {
+    if constexpr (kGPB == 1) {
+      buf[sz_slot / 4] = ((uint32_t)(uint8_t)r.zr << 16) | (uint16_t)r.sc;
+    } else if constexpr (!KTAIL) {
+      buf[sz_slot / 4] = ((r.zr & 0xFFu) << 16) | (r.sc & 0xFFFFu);
+      buf[256 + sz_slot / 4] = ((r.zr & 0xFF00u) << 8) | (r.sc >> 16);
+    } else {
+      buf[sz_slot / 4] = ((uint32_t)(uint8_t)r.zr << 16) | (uint16_t)r.sc;
+      buf[256 + sz_slot / 4] = ((uint32_t)r.zr1 << 16) | (uint32_t)r.sc1;
+    }
+  };
+
+  // ---- dequantized B fragments of one block: bq[j][step] ------------------------
+  typedef u32x4 BQ[kNT][kSteps];
+  // Words (j, gi, *) of a block: fp16((q - z) * s) of 8 channels each, in the
+  // MFMA B-operand order; sz is the column's (zero << 16 | scale).
+  auto deq_word = [&](const Raw &r, uint32_t sz, int j, int gi, int w, BQ &out) {
+    const DeqF16 deq(sz >> 16);
+    const u32x4 e = deq(r.w[j][gi][w], dq);
+    const uint32_t s1 = sz & 0xFFFFu;
+    const f16x2 s2 = __builtin_bit_cast(f16x2, s1 | (s1 << 16));
+    // (scalar copies first: bit-casting an element of a vector lvalue reads
+    // the vector's first element with this compiler)
+    const uint32_t e0 = e[0], e1 = e[1], e2 = e[2], e3 = e[3];
+    out[j][gi * kWpl + w] =
+        u32x4{__builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, e0) * s2),
+              __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, e1) * s2),
+              __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, e2) * s2),
+              __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, e3) * s2)};
+  };
+  auto read_sz = [&](const uint32_t *buf, int gi) {
+    return *reinterpret_cast<const u32x4 *>(buf + gi * 256 + (wave * 16 + c) * 4);
+  };
+
+  f32x4 acc[MT][kNT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    acc[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // A fragment: 16-row tile i, logical 16-byte chunk ch of the block row.
   auto a_frag = [&](const uint16_t *buf, int i, int ch) {
     return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(buf) +
-                                            (i * 16 + c) * (kBK * 2) + ((ch ^ c) << 4));
+                                            (i * 16 + c) * (kBK * 2) +
+                                            (a_chunk<kKqBit>(c, ch) << 4));
   };
-
-  // One K block.  Per group: dequantize this lane's 2 x kWpl words, then walk
-  // the 16-row tiles in a software pipeline: iteration i requests tile i+1's
-  // activation fragments, runs tile i's two MFMA chains and scales tile i-1's
-  // finished chains into the accumulators, so neither the LDS reads nor the
-  // MFMA results are waited for right after they were issued.  The scheduling
-  // barriers keep the compiler from hoisting every fragment read of the group
-  // to the top (which would need 4 x MT x kWpl live registers).
-  auto compute = [&](const uint16_t *buf, const BRegs &br) {
-#pragma unroll
-    for (int gi = 0; gi < kGPB; ++gi) {
-      u32x4 bq[2][kWpl];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const DeqF16 deq((uint32_t)br.zr[j][gi]);
-#pragma unroll
-        for (int w = 0; w < kWpl; ++w) bq[j][w] = deq(br.raw[j][gi][w], dq);
-      }
-      const float s0 = half_bits_to_float(br.sc[0][gi]);
-      const float s1 = half_bits_to_float(br.sc[1][gi]);
-      u32x4 a[2][kWpl];
-      f32x4 t[2][2];
-#pragma unroll
-      for (int w = 0; w < kWpl; ++w) a[0][w] = a_frag(buf, 0, gi * (GS / 8) + kq * kWpl + w);
-#pragma unroll
-      for (int i = 0; i <= MT; ++i) {
-        const int cur = i & 1;
-        if (i + 1 < MT) {
-#pragma unroll
-          for (int w = 0; w < kWpl; ++w)
-            a[cur ^ 1][w] = a_frag(buf, i + 1, gi * (GS / 8) + kq * kWpl + w);
-        }
-        if (i < MT) {
-          f32x4 t0 = f32x4{0.f, 0.f, 0.f, 0.f}, t1 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int w = 0; w < kWpl; ++w) {
-            t0 = mfma32<TagF16>(a[cur][w], bq[0][w], t0);
-            t1 = mfma32<TagF16>(a[cur][w], bq[1][w], t1);
-          }
-          t[cur][0] = t0;
-          t[cur][1] = t1;
-        }
-        if (i > 0) {
-          const int p = cur ^ 1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[i - 1][0][e] = __builtin_fmaf(t[p][0][e], s0, acc[i - 1][0][e]);
-            acc[i - 1][1][e] = __builtin_fmaf(t[p][1][e], s1, acc[i - 1][1][e]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
+  auto a_ch = [&](int st) { return (st / kWpl) * (GS / 8) + kq * kWpl + (st % kWpl); };
 
   const rsrc_t rX = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
   const int last = kb_end - 1;
   auto clampk = [&](int k) { return k < last ? k : last; };
-  // Byte offset of 16-byte activation chunk ch of block kb in row `row` of the
-  // tile; with KTAIL (K % 128 == 64, g = 64) chunks past the end of K read as
-  // zeros.
-  auto a_off = [&](int row, int kb, int ch) {
-    const uint32_t o = (uint32_t)(row0 + row) * (uint32_t)K * 2u + (uint32_t)kb * (kBK * 2) +
-                       (uint32_t)ch * 16u;
-    if constexpr (KTAIL) return kb * kBK + ch * 8 < K ? o : kNone;
-    return o;
+
+  // ---- activations staged through registers ----------------------------------
+  constexpr int kARounds = kBM / 16;     // 16-byte chunks per thread per block
+  u32x4 areg[kARounds];
+  auto load_a1 = [&](int kb, int r) {
+    const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
+    uint32_t off = (uint32_t)(row0 + row) * (uint32_t)K * 2u + (uint32_t)kb * (kBK * 2) +
+                   (uint32_t)ch * 16u;
+    if constexpr (KTAIL) off = kb * kBK + ch * 8 < K ? off : kNone;   // zeros past K
+    areg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
+  };
+  auto store_a = [&](uint16_t *buf) {
+#pragma unroll
+    for (int r = 0; r < kARounds; ++r) {
+      const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(buf) + row * (kBK * 2) +
+                                 (a_chunk<kKqBit>(row, ch) << 4)) = areg[r];
+    }
   };
 
-  // Both main loops have no branch between a prefetch and the step that
-  // consumes it; given one (a loop exit, a skipped tail group) the compiler
-  // sinks the prefetch loads past the math down to that branch, right before
-  // the wait that then drains them.
-  if constexpr (DMA) {
-    // ---- activations straight to LDS, two buffers, one barrier per block ------
-    // DMA instruction d (wave*kDma + r) fills block rows 4d .. 4d+3; lane l
-    // writes row 4d + l/16 at physical chunk l%16, i.e. logical chunk
-    // (l%16) ^ (row%16).  The DMA's LDS writes are known complete only after
-    // vmcnt(0), so block k+1's weights are requested together with its
-    // activations at the top of step k and both are waited for at the top of
-    // step k+1; the weight registers rotate by one copy per step.
-    constexpr int kDma = kBM / 16;
-    auto issue_a = [&](int kb, uint16_t *buf) {
+  // ---- main loop ------------------------------------------------------------------
+  // Block b's data moves in stages: its activations and its weights' scales
+  // are loaded during step b-2 (activations) / b-3 (scales) and written to
+  // LDS at the start of step b-1 / b-2; its packed weights are loaded during
+  // step b-kWin; its words are dequantized during step b-1; its MFMAs run in
+  // step b.  One barrier per step (at its end) orders every LDS write before
+  // the reads of the next step.  Each step issues its 16-byte and smaller
+  // prefetch loads spread over the row tiles, between MFMAs: a load takes
+  // tens of clocks to issue, and one wave per SIMD stalls on each.  Every wait
+  // is a counted vmcnt on ordinary loads.  The main loop runs whole windows
+  // of kWin steps so that no branch separates a prefetch from the step that
+  // consumes it (given one, the compiler sinks the prefetch loads down to it,
+  // right before the wait that then drains them); the last steps follow
+  // unrolled.
+  constexpr int kLoads = kARounds + kNT + 1;      // prefetch loads per step
+  Raw rw[kWin];
+  BQ bq[2];
+  SZ szr;
+  // Load n of a step: scales first and activations next (both are needed at
+  // the start of the next step), then the weight window's refill.
+  auto issue = [&](int n, int k, int u) {
+    if (n == 0) load_sz(clampk(k + 3), szr);
+    else if (n <= kARounds) load_a1(clampk(k + 2), n - 1);
+    else load_w(clampk(k + kWin), n - 1 - kARounds, rw[u]);
+  };
+  auto step = [&](int k, int u) {
+    const int p = u & 1;
+    const bool odd = ((k - kb_begin) & 1) != 0;
+    uint16_t *abuf = odd ? sA1 : sA0;
+    store_a(odd ? sA0 : sA1);                 // block k+1 (a copy of the last block at the end)
+    store_sz(((k - kb_begin) & 1) ? sSZ1 : sSZ0, szr);    // block k+2
+    const uint32_t *zbuf = ((k - kb_begin) & 1) ? sSZ0 : sSZ1;   // block k+1
+    u32x4 szv[kGPB];
 #pragma unroll
-      for (int r = 0; r < kDma; ++r) {
-        const int d = wave * kDma + r;
-        const int row = 4 * d + (lane >> 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rX, (lds_void *)(reinterpret_cast<char *>(buf) + d * 1024), 16,
-            a_off(row, kb, (lane & 15) ^ (row & 15)), 0, 0, 0);
+    for (int gi = 0; gi < kGPB; ++gi) szv[gi] = read_sz(zbuf, gi);
+    const Raw &nx = rw[(u + 1) % kWin];
+    u32x4 a[2][kSteps];
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) a[0][st] = a_frag(abuf, 0, a_ch(st));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int cur = i & 1;
+      if (i + 1 < MT) {
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) a[cur ^ 1][st] = a_frag(abuf, i + 1, a_ch(st));
       }
-    };
-    BRegs cur, nxt;
-    issue_a(kb_begin, sA0);
-    load_b(kb_begin, nxt);
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
-      wait_vmem_all();
-      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st)
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+          acc[i][j] = mfma32<TagF16>(a[cur][st], bq[p][j][st], acc[i][j]);
+      // dequantize words [i*kWordsPerTile, (i+1)*kWordsPerTile) of block k+1
+#pragma unroll
+      for (int q = i * kWordsPerTile; q < (i + 1) * kWordsPerTile; ++q) {
+        const int j = q / kSteps, st = q % kSteps, gi = st / kWpl, w = st % kWpl;
+        const u32x4 zz = szv[gi];
+        const uint32_t sz = zz[j];
+        deq_word(nx, sz, j, gi, w, bq[p ^ 1]);
+      }
+#pragma unroll
+      for (int n = i * kLoads / MT; n < (i + 1) * kLoads / MT; ++n) issue(n, k, u);
       __builtin_amdgcn_sched_barrier(0);
-      cur = nxt;
-      const bool odd = ((kb - kb_begin) & 1) != 0;
-      issue_a(clampk(kb + 1), odd ? sA0 : sA1);
-      load_b(clampk(kb + 1), nxt);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(odd ? sA1 : sA0, cur);
     }
-    wait_vmem_all();
-  } else {
-    // ---- activations staged through registers, kWin weight blocks in flight ---
-    // Every wait is a counted vmcnt on ordinary loads.  Step k writes block
-    // k+1's activations (loaded during step k-1) to LDS, requests block k+2's,
-    // computes block k and refills its weight slot with block k+kWin.  The
-    // main loop runs whole windows of kWin steps so that every slot's refill
-    // is consumed in the next iteration; the last steps follow unrolled.
-    constexpr int kARounds = kBM / 16;     // 16-byte chunks per thread per block
-    u32x4 areg[kARounds];
-    auto load_a = [&](int kb) {
-#pragma unroll
-      for (int r = 0; r < kARounds; ++r) {
-        const int q = tid + kThreads * r;
-        areg[r] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, a_off(q >> 4, kb, q & 15), 0, 0));
-      }
-    };
-    auto store_a = [&](uint16_t *buf) {
-#pragma unroll
-      for (int r = 0; r < kARounds; ++r) {
-        const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(buf) + row * (kBK * 2) +
-                                   ((ch ^ (row & 15)) << 4)) = areg[r];
-      }
-    };
-    BRegs rw[kWin];
-    auto step = [&](int k, BRegs &slot) {
-      const bool odd = ((k - kb_begin) & 1) != 0;
-      store_a(odd ? sA0 : sA1);           // block k+1 (a copy of the last block at the end)
-      load_a(clampk(k + 2));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(odd ? sA1 : sA0, slot);
-      load_b(clampk(k + kWin), slot);
-      __builtin_amdgcn_sched_barrier(0);
-      wait_lds_all();
-      __builtin_amdgcn_s_barrier();
-    };
-    // The prologue ends with the issue order of a steady-state step
-    // (activations, then one weight block) so the counted waits the compiler
-    // derives at the loop header equal the steady-state ones.
-    load_a(kb_begin);
-#pragma unroll
-    for (int u = 0; u < kWin - 1; ++u) load_b(clampk(kb_begin + u), rw[u]);
-    store_a(sA0);
-    load_a(clampk(kb_begin + 1));
-    load_b(clampk(kb_begin + kWin - 1), rw[kWin - 1]);
     wait_lds_all();
     __builtin_amdgcn_s_barrier();
-    int k = kb_begin;
-    for (; k + kWin <= kb_end; k += kWin) {
+  };
+
+  // Prologue: blocks kb0 .. kb0+kWin-1's weights, kb0's and kb0+1's scales in
+  // LDS, kb0+2's in registers, kb0's activations in LDS and kb0+1's in
+  // registers, kb0 dequantized.
+  {
+    const int kb0 = kb_begin;
 #pragma unroll
-      for (int u = 0; u < kWin; ++u) step(k + u, rw[u]);
+    for (int r = 0; r < kARounds; ++r) load_a1(kb0, r);
+#pragma unroll
+    for (int u = 0; u < kWin; ++u)
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) load_w(clampk(kb0 + u), j, rw[u]);
+    SZ s0, s1;
+    load_sz(kb0, s0);
+    load_sz(clampk(kb0 + 1), s1);
+    load_sz(clampk(kb0 + 2), szr);
+    store_a(sA0);
+#pragma unroll
+    for (int r = 0; r < kARounds; ++r) load_a1(clampk(kb0 + 1), r);
+    store_sz(sSZ0, s0);
+    store_sz(sSZ1, s1);
+    wait_lds_all();
+    __builtin_amdgcn_s_barrier();
+    u32x4 szv[kGPB];
+#pragma unroll
+    for (int gi = 0; gi < kGPB; ++gi) szv[gi] = read_sz(sSZ0, gi);
+#pragma unroll
+    for (int q = 0; q < kWords; ++q) {
+      const int j = q / kSteps, st = q % kSteps, gi = st / kWpl, w = st % kWpl;
+      const u32x4 zz = szv[gi];
+      const uint32_t sz = zz[j];
+      deq_word(rw[0], sz, j, gi, w, bq[0]);
     }
-#pragma unroll
-    for (int u = 0; u < kWin - 1; ++u)
-      if (k + u < kb_end) step(k + u, rw[u]);
-    wait_vmem_all();
   }
+  int k = kb_begin;
+  for (; k + kWin <= kb_end; k += kWin) {
+#pragma unroll
+    for (int u = 0; u < kWin; ++u) step(k + u, u);
+  }
+#pragma unroll
+  for (int u = 0; u < kWin - 1; ++u)
+    if (k + u < kb_end) step(k + u, u);
+  wait_vmem_all();
 
   // ---- split K: publish the partial tile; the last workgroup sums them --------
   // Partials are stored write-through and read back bypassing both cache
@@ -338,7 +373,7 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // fence (a whole-L2 write-back and invalidate) is needed across XCDs.
   // vmcnt(0) orders the stores before the atomic.
   if (sk.splits > 1) {
-    constexpr int kTiles = MT * 2;       // f32x4 accumulators per lane
+    constexpr int kTiles = MT * kNT;     // f32x4 accumulators per lane
     constexpr int kSys = 1 | 16;         // sc0 | sc1
     // layout: [tile][split][wave][16x16 tile][lane] of 16 bytes
     const uint32_t wave_bytes = (uint32_t)kTiles * 64u * 16u;
@@ -350,10 +385,10 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kNT; ++j) {
         const f32x4 v = acc[i][j];
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rP,
-                                               mine + (uint32_t)(i * 2 + j) * 1024u, 0, kSys);
+                                               mine + (uint32_t)(i * kNT + j) * 1024u, 0, kSys);
       }
     wait_vmem_all();
     __syncthreads();
@@ -366,9 +401,9 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < kNT; ++j) {
           const f32x4 v = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rP, p + (uint32_t)(i * 2 + j) * 1024u,
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rP, p + (uint32_t)(i * kNT + j) * 1024u,
                                                            0, kSys));
           acc[i][j] = sp == 0 ? v : acc[i][j] + v;
         }
@@ -380,8 +415,8 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   constexpr int ysz = YT == (int)YType::F32 ? 4 : 2;
   const rsrc_t rY = make_rsrc(Y, (uint32_t)M * (uint32_t)N * (uint32_t)ysz);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = col0 + wave * 32 + j * 16 + c;
+  for (int j = 0; j < kNT; ++j) {
+    const int n = col0 + wave * 64 + j * 16 + c;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -400,18 +435,20 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   }
 }
 
-template <int GS, int YT, int MT, bool DMA, bool KTAIL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// One wave per SIMD: accumulators, two dequantized blocks and a four-block
+// weight window live in registers.
+template <int GS, int YT, int MT, bool KTAIL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_f16_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
                      const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
                      int M, int N, int K, void *__restrict__ Y, SplitK sk) {
-  gemm_f16_body<GS, YT, MT, DMA, KTAIL>(X, qweight, scales, zeros, M, N, K, Y, sk);
+  gemm_f16_body<GS, YT, MT, KTAIL>(X, qweight, scales, zeros, M, N, K, Y, sk);
 }
 
 namespace {
 
-// Two workgroups per CU.
-constexpr int64_t kSlots = 512;
+// One workgroup per CU.
+constexpr int64_t kSlots = 256;
 
 int64_t f16_rows_per_launch(int64_t N, int64_t K, int64_t bm) {
   const int64_t lim = ((int64_t)1 << 31) - 1;
@@ -421,7 +458,7 @@ int64_t f16_rows_per_launch(int64_t N, int64_t K, int64_t bm) {
   return (r / bm) * bm;
 }
 
-template <int GS, int YT, int MT, bool DMA, bool KTAIL>
+template <int GS, int YT, int MT, bool KTAIL>
 hipError_t f16_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *sc,
                          const uint8_t *zr, int64_t M, int64_t N, int64_t K, void *Y, SplitK sk,
                          hipStream_t st) {
@@ -434,8 +471,8 @@ hipError_t f16_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *
     const int64_t tiles = ((mm + bm - 1) / bm) * ((N + kBN - 1) / kBN);
     const dim3 grid((unsigned)(tiles * sk.splits));
     void *y = reinterpret_cast<char *>(Y) + m0 * N * ysize;
-    gemm_f16_kernel<GS, YT, MT, DMA, KTAIL><<<grid, kThreads, 0, st>>>(X + m0 * K, qw, sc, zr, (int)mm,
-                                                                (int)N, (int)K, y, sk);
+    gemm_f16_kernel<GS, YT, MT, KTAIL><<<grid, kThreads, 0, st>>>(X + m0 * K, qw, sc, zr, (int)mm,
+                                                                  (int)N, (int)K, y, sk);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -445,9 +482,9 @@ hipError_t f16_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *
 template <int GS, int YT, bool KTAIL>
 hipError_t f16_go2(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, const uint8_t *zr,
                    int64_t M, int64_t N, int64_t K, void *Y, int mt, SplitK sk, hipStream_t st) {
-  if (mt == 2) return f16_launch_mt<GS, YT, 2, false, KTAIL>(X, qw, sc, zr, M, N, K, Y, sk, st);
-  if (mt == 4) return f16_launch_mt<GS, YT, 4, false, KTAIL>(X, qw, sc, zr, M, N, K, Y, sk, st);
-  return f16_launch_mt<GS, YT, 8, true, KTAIL>(X, qw, sc, zr, M, N, K, Y, sk, st);
+  if (mt == 2) return f16_launch_mt<GS, YT, 2, KTAIL>(X, qw, sc, zr, M, N, K, Y, sk, st);
+  if (mt == 4) return f16_launch_mt<GS, YT, 4, KTAIL>(X, qw, sc, zr, M, N, K, Y, sk, st);
+  return f16_launch_mt<GS, YT, 8, KTAIL>(X, qw, sc, zr, M, N, K, Y, sk, st);
 }
 
 // K is a multiple of the group size; only g = 64 can leave half a K block.
@@ -464,8 +501,8 @@ hipError_t f16_go(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, con
 
 // Row tile and K split.  M <= 32 and M <= 64 take 32- and 64-row tiles (the
 // weight stream dominates there), larger M the 128-row tile.  When the tiles
-// cannot fill every CU's two workgroup slots, K is split into as many parts
-// as still fit in one round of slots (at most 8, at least two K blocks each).
+// cannot give every CU a workgroup, K is split into as many parts as still
+// fit in one round (at most 8, at least two K blocks each).
 GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan p{};
   p.mt = M <= 32 ? 2 : M <= 64 ? 4 : 8;
