@@ -69,6 +69,18 @@ __device__ __forceinline__ int a_chunk(int row, int ch) {
   return ch ^ (row & 15) ^ (((ch >> KQ_BIT) & 1) << 3);
 }
 
+// Instruction order of one row tile (for the scheduler): each MFMA followed
+// by up to V VALU operations.  One wave issues in order, so VALU work
+// clustered after the MFMAs would leave the matrix core idle.
+template <int M, int V>
+__device__ __forceinline__ void tile_order() {
+  if constexpr (M > 0) {
+    tile_order<M - 1, V>();
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);          // V VALU
+  }
+}
+
 }  // namespace
 
 template <int GS, int YT, int MT, bool KTAIL>
@@ -247,19 +259,20 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     if constexpr (KTAIL) off = kb * kBK + ch * 8 < K ? off : kNone;   // zeros past K
     areg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
   };
+  auto store_a1 = [&](uint16_t *buf, int r) {
+    const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
+    *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(buf) + row * (kBK * 2) +
+                               (a_chunk<kKqBit>(row, ch) << 4)) = areg[r];
+  };
   auto store_a = [&](uint16_t *buf) {
 #pragma unroll
-    for (int r = 0; r < kARounds; ++r) {
-      const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
-      *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(buf) + row * (kBK * 2) +
-                                 (a_chunk<kKqBit>(row, ch) << 4)) = areg[r];
-    }
+    for (int r = 0; r < kARounds; ++r) store_a1(buf, r);
   };
 
   // ---- main loop ------------------------------------------------------------------
-  // Block b's data moves in stages: its activations and its weights' scales
-  // are loaded during step b-2 (activations) / b-3 (scales) and written to
-  // LDS at the start of step b-1 / b-2; its packed weights are loaded during
+  // Block b's data moves in stages: its activations are loaded during step
+  // b-2 and written to LDS during step b-1; its weights' scales are loaded
+  // during step b-3 and written to LDS at the start of step b-2; its packed weights are loaded during
   // step b-kWin; its words are dequantized during step b-1; its MFMAs run in
   // step b.  One barrier per step (at its end) orders every LDS write before
   // the reads of the next step.  Each step issues its 16-byte and smaller
@@ -275,17 +288,23 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   BQ bq[2];
   SZ szr;
   // Load n of a step: scales first and activations next (both are needed at
-  // the start of the next step), then the weight window's refill.
-  auto issue = [&](int n, int k, int u) {
-    if (n == 0) load_sz(clampk(k + 3), szr);
-    else if (n <= kARounds) load_a1(clampk(k + 2), n - 1);
-    else load_w(clampk(k + kWin), n - 1 - kARounds, rw[u]);
+  // the start of the next step), then the weight window's refill.  Each
+  // activation chunk's register first goes to LDS (block k+1, into the
+  // buffer this step does not read), then is refilled with block k+2's chunk.
+  auto issue = [&](int n, int k, int u, uint16_t *nbuf) {
+    if (n == 0) {
+      load_sz(clampk(k + 3), szr);
+    } else if (n <= kARounds) {
+      store_a1(nbuf, n - 1);
+      load_a1(clampk(k + 2), n - 1);
+    } else {
+      load_w(clampk(k + kWin), n - 1 - kARounds, rw[u]);
+    }
   };
   auto step = [&](int k, int u) {
     const int p = u & 1;
     const bool odd = ((k - kb_begin) & 1) != 0;
     uint16_t *abuf = odd ? sA1 : sA0;
-    store_a(odd ? sA0 : sA1);                 // block k+1 (a copy of the last block at the end)
     store_sz(((k - kb_begin) & 1) ? sSZ1 : sSZ0, szr);    // block k+2
     const uint32_t *zbuf = ((k - kb_begin) & 1) ? sSZ0 : sSZ1;   // block k+1
     u32x4 szv[kGPB];
@@ -317,7 +336,8 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
         deq_word(nx, sz, j, gi, w, bq[p ^ 1]);
       }
 #pragma unroll
-      for (int n = i * kLoads / MT; n < (i + 1) * kLoads / MT; ++n) issue(n, k, u);
+      for (int n = i * kLoads / MT; n < (i + 1) * kLoads / MT; ++n) issue(n, k, u, odd ? sA0 : sA1);
+      tile_order<kNT * kSteps, (kWordsPerTile * 13 + kNT * kSteps - 1) / (kNT * kSteps) + 1>();
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_lds_all();
