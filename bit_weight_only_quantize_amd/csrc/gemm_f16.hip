@@ -49,6 +49,10 @@ constexpr int kBN = 64 * 4;       // columns per workgroup
 constexpr int kBK = 128;          // input channels per K block
 constexpr int kSteps = kBK / 32;  // MFMA K steps per block
 constexpr int kGroupRows = 4;     // row tiles per tile group
+// One workgroup per CU; K is split only when there are fewer tiles than
+// slots, and the split-K counters of tile t sit at t and kSlots + t.
+constexpr int kSlots = 256;
+static_assert(2 * kSlots * 4 <= (int)kSplitCounterBytes, "split-K counters");
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -387,11 +391,19 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     if (k + u < kb_end) step(k + u, u);
   wait_vmem_all();
 
-  // ---- split K: publish the partial tile; the last workgroup sums them --------
-  // Partials are stored write-through and read back bypassing both cache
-  // levels (sc0 sc1), and the per-tile counter is an atomic, so no device-scope
-  // fence (a whole-L2 write-back and invalidate) is needed across XCDs.
-  // vmcnt(0) orders the stores before the atomic.
+  // ---- split K: the last workgroup of a tile sums the partial tiles -----------
+  // Each workgroup first takes an arrival ticket (an atomic on the tile's
+  // counter).  All but the last store their fp32 partial tile and then count
+  // themselves done on a second counter; the last keeps its own partial in
+  // registers, waits until the others are done, reads theirs and adds all of
+  // them in split order (the same sum whichever workgroup arrives last), then
+  // resets both counters for the next launch.  The partials cross workgroups
+  // that may sit on different XCDs, whose L2s are not coherent with each
+  // other: they are stored write-through and read back bypassing both cache
+  // levels (sc0 sc1), the counters are atomics (coherent across XCDs), and
+  // vmcnt(0) orders a workgroup's stores before its done count.  The wait
+  // ends: every other workgroup of the tile already holds a ticket, so it is
+  // resident and finishes its stores.
   if (sk.splits > 1) {
     constexpr int kTiles = MT * kNT;     // f32x4 accumulators per lane
     constexpr int kSys = 1 | 16;         // sc0 | sc1
@@ -400,35 +412,53 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     const uint32_t tile_bytes = 4u * wave_bytes;
     const rsrc_t rP = make_rsrc(sk.partials, 0x7FFFFFF0u);
     const uint32_t lane_off = (uint32_t)wave * wave_bytes + (uint32_t)lane * 16u;
-    const uint32_t mine =
-        ((uint32_t)tile * (uint32_t)sk.splits + (uint32_t)split) * tile_bytes + lane_off;
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) {
-        const f32x4 v = acc[i][j];
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rP,
-                                               mine + (uint32_t)(i * kNT + j) * 1024u, 0, kSys);
-      }
-    wait_vmem_all();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&sk.counters[tile], 1u) == (uint32_t)(sk.splits - 1);
-    __syncthreads();
-    if (!s_last) return;
     const uint32_t base = (uint32_t)tile * (uint32_t)sk.splits * tile_bytes + lane_off;
-    for (int sp = 0; sp < sk.splits; ++sp) {
-      const uint32_t p = base + (uint32_t)sp * tile_bytes;
+    uint32_t *arrive = sk.counters + tile;
+    uint32_t *done = sk.counters + kSlots + tile;
+    if (tid == 0) s_last = atomicAdd(arrive, 1u) == (uint32_t)(sk.splits - 1);
+    __syncthreads();
+    if (!s_last) {
+      const uint32_t mine = base + (uint32_t)split * tile_bytes;
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
-          const f32x4 v = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rP, p + (uint32_t)(i * kNT + j) * 1024u,
-                                                           0, kSys));
+          const f32x4 v = acc[i][j];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rP,
+                                                 mine + (uint32_t)(i * kNT + j) * 1024u, 0, kSys);
+        }
+      wait_vmem_all();
+      __syncthreads();
+      if (tid == 0) atomicAdd(done, 1u);
+      return;
+    }
+    if (tid == 0) {
+      while (atomicAdd(done, 0u) != (uint32_t)(sk.splits - 1)) __builtin_amdgcn_s_sleep(2);
+    }
+    __syncthreads();
+    f32x4 own[MT][kNT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) own[i][j] = acc[i][j];
+    for (int sp = 0; sp < sk.splits; ++sp) {
+      const uint32_t p = base + (uint32_t)sp * tile_bytes;
+      const bool self = sp == split;
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) {
+          const f32x4 v =
+              self ? own[i][j]
+                   : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rP, p + (uint32_t)(i * kNT + j) * 1024u, 0, kSys));
           acc[i][j] = sp == 0 ? v : acc[i][j] + v;
         }
     }
-    if (tid == 0) atomicExch(&sk.counters[tile], 0u);   // ready for the next launch
+    if (tid == 0) {
+      atomicExch(arrive, 0u);                 // ready for the next launch
+      atomicExch(done, 0u);
+    }
   }
 
   // ---- epilogue: lane (c, kq) holds rows 4*kq + e of column c of each tile ------
@@ -467,8 +497,6 @@ void gemm_f16_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict_
 
 namespace {
 
-// One workgroup per CU.
-constexpr int64_t kSlots = 256;
 
 int64_t f16_rows_per_launch(int64_t N, int64_t K, int64_t bm) {
   const int64_t lim = ((int64_t)1 << 31) - 1;
