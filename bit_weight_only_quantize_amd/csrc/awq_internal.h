@@ -45,7 +45,8 @@ struct GemmPlan {
   int mt, splits;
   int64_t tiles;
   size_t counter_bytes;    // fixed-size u32 counter region (zero between launches)
-  size_t workspace_bytes;  // 0 when splits == 1
+  size_t rowf_offset;      // bf16 input: per-row activation factors (fp32 [M])
+  size_t workspace_bytes;  // 0 when splits == 1 and the input is fp16
 };
 // The plan of the kernel that serves activations of type xt (fp16: the
 // kernel of gemm_f16.hip).
@@ -59,12 +60,12 @@ hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
                        int64_t N, int64_t K, int gs, void *Y, YType yt,
                        void *workspace, hipStream_t st);
 
-// ---- gemm_f16.hip (fp16 activations, any M) ------------------------------------------
-// Row tile (16 * mt rows) and K split of the fp16 GEMM.
-GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_f16(const uint16_t *X, const uint32_t *qweight, const uint16_t *scales,
-                           const uint8_t *zeros, int64_t M, int64_t N, int64_t K, int gs,
-                           void *Y, YType yt, void *workspace, hipStream_t st);
+// ---- gemm_f16.hip (the quantized GEMM: fp16, or bf16 converted to fp16) ---------------
+// Row tile (16 * mt rows), K split and workspace of the GEMM.
+GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16);
+hipError_t launch_gemm_f16(const uint16_t *X, bool bf16, const uint32_t *qweight,
+                           const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
+                           int64_t K, int gs, void *Y, YType yt, void *workspace, hipStream_t st);
 
 // Dense fp16 B (X * W^T with W fp16 [N][K]), fp32 output.
 hipError_t launch_gemm_dense_f32(const uint16_t *X, const uint16_t *W, int64_t M,

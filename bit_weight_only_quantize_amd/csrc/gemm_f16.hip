@@ -87,12 +87,13 @@ __device__ __forceinline__ void tile_order() {
 
 }  // namespace
 
-template <int GS, int YT, int MT, bool KTAIL>
+template <int GS, int YT, int MT, bool KTAIL, bool BF16X>
 __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
                                               const uint32_t *__restrict__ qweight,
                                               const uint16_t *__restrict__ scales,
                                               const uint8_t *__restrict__ zeros, int M, int N,
-                                              int K, void *__restrict__ Y, SplitK sk) {
+                                              int K, void *__restrict__ Y, SplitK sk,
+                                              const float *__restrict__ rowf) {
   constexpr int kBM = 16 * MT;
   constexpr int kWpl = GS / 32;      // packed words per lane per group and column
   constexpr int kGPB = kBK / GS;     // groups per K block
@@ -263,10 +264,33 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     if constexpr (KTAIL) off = kb * kBK + ch * 8 < K ? off : kNone;   // zeros past K
     areg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
   };
+  // bf16 activations: chunk r's 8 values times its row's power-of-two factor
+  // (exact), converted to fp16: exact for every value in fp16's normal range,
+  // which the factor guarantees for the row's largest value; smaller values
+  // below that range are truncated to fp16 subnormals.
+  float rf[kARounds];
+  if constexpr (BF16X) {
+    const rsrc_t rR = make_rsrc(rowf, (uint32_t)M * 4u);
+#pragma unroll
+    for (int r = 0; r < kARounds; ++r) {
+      const uint32_t row = (uint32_t)(row0 + ((tid + kThreads * r) >> 4));
+      rf[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, row * 4u, 0, 0));
+    }
+  }
   auto store_a1 = [&](uint16_t *buf, int r) {
     const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
+    u32x4 v = areg[r];
+    if constexpr (BF16X) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t u = v[x];
+        const float lo = __builtin_bit_cast(float, u << 16) * rf[r];
+        const float hi = __builtin_bit_cast(float, u & 0xFFFF0000u) * rf[r];
+        v[x] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+      }
+    }
     *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(buf) + row * (kBK * 2) +
-                               (a_chunk<kKqBit>(row, ch) << 4)) = areg[r];
+                               (a_chunk<kKqBit>(row, ch) << 4)) = v;
   };
   auto store_a = [&](uint16_t *buf) {
 #pragma unroll
@@ -462,6 +486,23 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   }
 
   // ---- epilogue: lane (c, kq) holds rows 4*kq + e of column c of each tile ------
+  if constexpr (BF16X) {
+    // undo the rows' activation factors (exact powers of two; rows past M
+    // read 0 and keep their unused values)
+    const rsrc_t rR = make_rsrc(rowf, (uint32_t)M * 4u);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const f32x4 f = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, (uint32_t)(row0 + i * 16 + 4 * kq) * 4u, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float fe = f[e];
+        const float inv = fe > 0.0f ? 1.0f / fe : 1.0f;
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) acc[i][j][e] *= inv;
+      }
+    }
+  }
   constexpr int ysz = YT == (int)YType::F32 ? 4 : 2;
   const rsrc_t rY = make_rsrc(Y, (uint32_t)M * (uint32_t)N * (uint32_t)ysz);
 #pragma unroll
@@ -487,12 +528,53 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 
 // One wave per SIMD: accumulators, two dequantized blocks and a four-block
 // weight window live in registers.
-template <int GS, int YT, int MT, bool KTAIL>
+template <int GS, int YT, int MT, bool KTAIL, bool BF16X>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_f16_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
                      const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-                     int M, int N, int K, void *__restrict__ Y, SplitK sk) {
-  gemm_f16_body<GS, YT, MT, KTAIL>(X, qweight, scales, zeros, M, N, K, Y, sk);
+                     int M, int N, int K, void *__restrict__ Y, SplitK sk,
+                     const float *__restrict__ rowf) {
+  gemm_f16_body<GS, YT, MT, KTAIL, BF16X>(X, qweight, scales, zeros, M, N, K, Y, sk, rowf);
+}
+
+// Per-row activation factor for bf16 input: the power of two that brings the
+// row's largest magnitude into [2^14, 2^15), so every value of the row is
+// within fp16's range and those within 2^38 of the largest keep their full
+// precision (exponent capped to stay a normal fp32); 1 for rows that are all
+// zero or hold inf or NaN.  One workgroup per row.
+__global__ __launch_bounds__(256) void bf16_row_factor_kernel(const uint16_t *__restrict__ X,
+                                                              int K, float *__restrict__ rowf) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const rsrc_t rX = make_rsrc(X + row * K, (uint32_t)K * 2u);
+  float mx = 0.0f;
+  for (int c = threadIdx.x; c * 8 < K; c += 256) {
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, (uint32_t)c * 16u, 0, 0));
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const uint32_t u = v[x];
+      mx = __builtin_fmaxf(mx, __builtin_fabsf(__builtin_bit_cast(float, u << 16)));
+      mx = __builtin_fmaxf(mx, __builtin_fabsf(__builtin_bit_cast(float, u & 0xFFFF0000u)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float m = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    float f = 1.0f;
+    if (m > 0.0f && __builtin_isfinite(m)) {
+      // floor(log2 m) from the fp32 bits (bf16 subnormals widen to fp32
+      // subnormals: biased exponent 0, read here as -127, so they scale up by
+      // at most the cap)
+      const int ex = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFF) - 127;
+      int e = 14 - ex;                                  // m * 2^e in [2^14, 2^15)
+      e = e > 126 ? 126 : e;
+      f = __builtin_bit_cast(float, (uint32_t)(127 + e) << 23);
+    }
+    rowf[row] = f;
+  }
 }
 
 namespace {
@@ -506,10 +588,10 @@ int64_t f16_rows_per_launch(int64_t N, int64_t K, int64_t bm) {
   return (r / bm) * bm;
 }
 
-template <int GS, int YT, int MT, bool KTAIL>
+template <int GS, int YT, int MT, bool KTAIL, bool BF16X>
 hipError_t f16_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *sc,
                          const uint8_t *zr, int64_t M, int64_t N, int64_t K, void *Y, SplitK sk,
-                         hipStream_t st) {
+                         const float *rowf, hipStream_t st) {
   constexpr int64_t bm = 16 * MT;
   const int ysize = YT == (int)YType::F32 ? 4 : 2;
   const int64_t rows = sk.splits > 1 ? M : f16_rows_per_launch(N, K, bm);
@@ -519,30 +601,40 @@ hipError_t f16_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *
     const int64_t tiles = ((mm + bm - 1) / bm) * ((N + kBN - 1) / kBN);
     const dim3 grid((unsigned)(tiles * sk.splits));
     void *y = reinterpret_cast<char *>(Y) + m0 * N * ysize;
-    gemm_f16_kernel<GS, YT, MT, KTAIL><<<grid, kThreads, 0, st>>>(X + m0 * K, qw, sc, zr, (int)mm,
-                                                                  (int)N, (int)K, y, sk);
+    gemm_f16_kernel<GS, YT, MT, KTAIL, BF16X><<<grid, kThreads, 0, st>>>(
+        X + m0 * K, qw, sc, zr, (int)mm, (int)N, (int)K, y, sk, rowf ? rowf + m0 : nullptr);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+template <int GS, int YT, bool KTAIL, bool BF16X>
+hipError_t f16_go3(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, const uint8_t *zr,
+                   int64_t M, int64_t N, int64_t K, void *Y, int mt, SplitK sk, const float *rowf,
+                   hipStream_t st) {
+  if (mt == 2) return f16_launch_mt<GS, YT, 2, KTAIL, BF16X>(X, qw, sc, zr, M, N, K, Y, sk, rowf, st);
+  if (mt == 4) return f16_launch_mt<GS, YT, 4, KTAIL, BF16X>(X, qw, sc, zr, M, N, K, Y, sk, rowf, st);
+  return f16_launch_mt<GS, YT, 8, KTAIL, BF16X>(X, qw, sc, zr, M, N, K, Y, sk, rowf, st);
+}
+
 template <int GS, int YT, bool KTAIL>
 hipError_t f16_go2(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, const uint8_t *zr,
-                   int64_t M, int64_t N, int64_t K, void *Y, int mt, SplitK sk, hipStream_t st) {
-  if (mt == 2) return f16_launch_mt<GS, YT, 2, KTAIL>(X, qw, sc, zr, M, N, K, Y, sk, st);
-  if (mt == 4) return f16_launch_mt<GS, YT, 4, KTAIL>(X, qw, sc, zr, M, N, K, Y, sk, st);
-  return f16_launch_mt<GS, YT, 8, KTAIL>(X, qw, sc, zr, M, N, K, Y, sk, st);
+                   int64_t M, int64_t N, int64_t K, void *Y, int mt, SplitK sk, const float *rowf,
+                   hipStream_t st) {
+  if (rowf) return f16_go3<GS, YT, KTAIL, true>(X, qw, sc, zr, M, N, K, Y, mt, sk, rowf, st);
+  return f16_go3<GS, YT, KTAIL, false>(X, qw, sc, zr, M, N, K, Y, mt, sk, nullptr, st);
 }
 
 // K is a multiple of the group size; only g = 64 can leave half a K block.
 template <int GS, int YT>
 hipError_t f16_go(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, const uint8_t *zr,
-                  int64_t M, int64_t N, int64_t K, void *Y, int mt, SplitK sk, hipStream_t st) {
+                  int64_t M, int64_t N, int64_t K, void *Y, int mt, SplitK sk, const float *rowf,
+                  hipStream_t st) {
   if constexpr (GS < kBK) {
-    if (K % kBK != 0) return f16_go2<GS, YT, true>(X, qw, sc, zr, M, N, K, Y, mt, sk, st);
+    if (K % kBK != 0) return f16_go2<GS, YT, true>(X, qw, sc, zr, M, N, K, Y, mt, sk, rowf, st);
   }
-  return f16_go2<GS, YT, false>(X, qw, sc, zr, M, N, K, Y, mt, sk, st);
+  return f16_go2<GS, YT, false>(X, qw, sc, zr, M, N, K, Y, mt, sk, rowf, st);
 }
 
 }  // namespace
@@ -550,8 +642,9 @@ hipError_t f16_go(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, con
 // Row tile and K split.  M <= 32 and M <= 64 take 32- and 64-row tiles (the
 // weight stream dominates there), larger M the 128-row tile.  When the tiles
 // cannot give every CU a workgroup, K is split into as many parts as still
-// fit in one round (at most 8, at least two K blocks each).
-GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K) {
+// fit in one round (at most 8, at least two K blocks each).  bf16 input adds
+// one fp32 activation factor per row to the workspace.
+GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16) {
   GemmPlan p{};
   p.mt = M <= 32 ? 2 : M <= 64 ? 4 : 8;
   const int64_t bm = 16 * p.mt;
@@ -564,33 +657,49 @@ GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K) {
     sp = sp < cap ? sp : cap;
     p.splits = sp > 1 ? (int)sp : 1;
   }
+  size_t bytes = 0;
   if (p.splits > 1) {
     p.counter_bytes = kSplitCounterBytes;
-    p.workspace_bytes = p.counter_bytes + (size_t)p.tiles * p.splits * bm * kBN * 4;
+    bytes = p.counter_bytes + (size_t)p.tiles * p.splits * bm * kBN * 4;
   }
+  if (bf16) {
+    // never inside the counter region, which other calls sharing the
+    // workspace expect to find zeroed
+    const size_t after = bytes > kSplitCounterBytes ? bytes : kSplitCounterBytes;
+    p.rowf_offset = (after + 255) / 256 * 256;
+    bytes = p.rowf_offset + (size_t)M * 4;
+  }
+  p.workspace_bytes = bytes;
   return p;
 }
 
-hipError_t launch_gemm_f16(const uint16_t *X, const uint32_t *qweight, const uint16_t *scales,
-                           const uint8_t *zeros, int64_t M, int64_t N, int64_t K, int gs, void *Y,
-                           YType yt, void *workspace, hipStream_t st) {
+hipError_t launch_gemm_f16(const uint16_t *X, bool bf16, const uint32_t *qweight,
+                           const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
+                           int64_t K, int gs, void *Y, YType yt, void *workspace, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  const GemmPlan p = gemm_f16_plan(M, N, K);
+  const GemmPlan p = gemm_f16_plan(M, N, K, bf16);
+  if (p.workspace_bytes > 0 && !workspace) return hipErrorInvalidValue;
   SplitK sk{1, nullptr, nullptr};
   if (p.splits > 1) {
-    if (!workspace) return hipErrorInvalidValue;
     sk.splits = p.splits;
     sk.counters = reinterpret_cast<uint32_t *>(workspace);
     sk.partials = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + p.counter_bytes);
   }
-  if (gs == 128) {
-    if (yt == YType::F32) return f16_go<128, (int)YType::F32>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, st);
-    if (yt == YType::BF16) return f16_go<128, (int)YType::BF16>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, st);
-    return f16_go<128, (int)YType::F16>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, st);
+  float *rowf = nullptr;
+  if (bf16) {
+    rowf = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + p.rowf_offset);
+    bf16_row_factor_kernel<<<dim3((unsigned)M), 256, 0, st>>>(X, (int)K, rowf);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  if (yt == YType::F32) return f16_go<64, (int)YType::F32>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, st);
-  if (yt == YType::BF16) return f16_go<64, (int)YType::BF16>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, st);
-  return f16_go<64, (int)YType::F16>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, st);
+  if (gs == 128) {
+    if (yt == YType::F32) return f16_go<128, (int)YType::F32>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, rowf, st);
+    if (yt == YType::BF16) return f16_go<128, (int)YType::BF16>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, rowf, st);
+    return f16_go<128, (int)YType::F16>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, rowf, st);
+  }
+  if (yt == YType::F32) return f16_go<64, (int)YType::F32>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, rowf, st);
+  if (yt == YType::BF16) return f16_go<64, (int)YType::BF16>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, rowf, st);
+  return f16_go<64, (int)YType::F16>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, rowf, st);
 }
 
 }  // namespace awq

@@ -1,46 +1,34 @@
-// Batched / prefill W4A16 GEMM on gfx950 MFMA.
+// The scale search's GEMMs on gfx950 MFMA ("AWQ Advanced Usage Guide", "How
+// AWQ Works": the per-alpha reconstruction loss of the scaled, quantized
+// layer; ai.lansai.wang explainer, section "AWQ 的四步链路", the scale search).
+//  * Dense B: Y_ref = X * W^T with fp16 W, fp32 output.
+//  * Loss: A * deq(Q(sW))^T against Y_ref; the epilogue reduces the squared
+//    error of its tile to one fp64 partial instead of storing Y.
 //
-// The GEMM variant of the quantized linear layer ("AWQ Advanced Usage Guide",
-// "WQLinear Kernel Variants": batch sizes > 1).  Y = X * deq(W)^T with
-// deq = (q - z) * s per group of g input channels.
+// Exactness (the losses are compared to an fp64 oracle at 1e-5): the B
+// operand is the exact integer q - z, MFMA accumulates one group in fp32 and
+// the group's scale multiplies that fp32 partial; no dequantized weight is
+// rounded to 16 bits.  (The linear layer's GEMM, gemm_f16.hip, rounds it to
+// fp16 instead.)
 //
-// Exactness: the B operand is the exact integer q - z (fp16) or 128 + q
-// (bf16, zero removed through the row sums of A), MFMA accumulates one group
-// in fp32, and the group's scale multiplies that fp32 partial.  No dequantized
-// weight is ever rounded to 16 bits.
-//
-// Tiling for the MI355X: a 256-thread workgroup computes a BM x 128 tile of Y,
-// BM = 32 * MT (MT = 1, 2, 4 or 8 MFMA row tiles per wave); each wave owns
-// BM/2 x 64 (MT x 4 MFMA tiles of 16 x 16).  Small M takes a small BM so the
-// matrix core does not multiply padding rows.  K advances in blocks of 128
+// Tiling: a 256-thread workgroup computes a 256 x 128 tile of Y; each wave
+// owns 128 x 64 (8 x 4 MFMA tiles of 16 x 16).  K advances in blocks of 128
 // channels (one g128 group or two g64 groups).
-//  * Split K: when the M x N tiles alone cannot fill the 256 CUs (batched
-//    decode), the K blocks of each tile are divided among S workgroups.  Each
-//    writes its fp32 partial tile to a workspace; the last of the S to finish
-//    (a per-tile counter, reset by that workgroup) adds the S partials in
-//    split order -- the same order whichever finishes last -- and runs the
-//    epilogue.
-//  * Activations: each BM x 128 fp16 block goes from global memory
-//    straight to LDS (buffer_load_dwordx4 ... lds, no VGPR staging),
-//    double-buffered in two arrays.  16-byte chunk c of row r is stored
-//    at chunk c ^ (r mod 16): the 16 rows read by one 128-bit LDS access land
-//    in 16 distinct bank groups.
-//  * Per group, a wave reads all its A fragments (8 tiles x 32 channels) from
-//    LDS once; they are MFMA-only operands, so the register allocator may keep
-//    them in AGPRs.  Columns are then walked one 16-wide tile at a time: the
-//    lane dequantizes its 32 codes of that column (16 VGPRs live) and runs 8
-//    MFMA chains (one per M tile) whose fp32 sums are scaled into the
-//    accumulator.  Each dequantized fragment feeds 8 MFMAs.
+//  * Activations: each 256 x 128 fp16 block goes from global memory straight
+//    to LDS (buffer_load_dwordx4 ... lds), double-buffered.  16-byte chunk c
+//    of row r is stored at chunk c ^ (r mod 16).
+//  * Per group, a wave reads its A fragments from LDS once; columns are then
+//    walked one 16-wide tile at a time: the lane dequantizes its codes of that
+//    column and runs 8 MFMA chains (one per M tile) whose fp32 sums are
+//    scaled into the accumulator.
 //  * Packed weights, scales and zeros bypass LDS and are prefetched one block
 //    ahead into registers.
-//  * All global accesses go through buffer resources: out-of-range reads return
-//    zero and out-of-range writes are dropped by the hardware, so edge tiles
-//    need no clamping or branches around loads.
-//  * One s_barrier per block, after an explicit vmcnt(0): the data waited for
-//    was issued a whole block earlier.  __syncthreads() is avoided in the loop
-//    because its release fence would also drain the prefetches in flight.
-//  * Block ids are remapped so each XCD works on a contiguous run of tiles
-//    along N that share one activation block in that XCD's L2.
+//  * All global accesses go through buffer resources: out-of-range reads
+//    return zero and out-of-range writes are dropped, so edge tiles need no
+//    branches around loads.
+//  * One s_barrier per block, after an explicit vmcnt(0): the LDS DMA's
+//    writes are known complete only then.
+//  * Block ids are remapped so each XCD works on a contiguous run of tiles.
 // 32-bit buffer offsets: the launcher slices M so that X, Y and the reference
 // output of one launch stay below 2 GiB.
 
@@ -83,28 +71,21 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
   constexpr int kWpl = kGS / 32;        // 8-channel words per lane per group
   constexpr int kGPB = kBK / kGS;       // groups per K block
   constexpr int kBM = 32 * MT;
-  // Wave layout: 2 x 2 waves of (BM/2) x 64, or (kTall) 1 x 4 waves of
-  // BM x 32, where every dequantized weight fragment feeds twice as many MFMAs.
-  constexpr bool kTall = false;
-  constexpr int kMT = kTall ? 2 * MT : MT;  // 16x16 tiles per wave along M
-  constexpr int kNT = kTall ? 2 : 4;        // 16x16 tiles per wave along N
+  // Wave layout: 2 x 2 waves of (BM/2) x 64.
+  constexpr int kMT = MT;                   // 16x16 tiles per wave along M
+  constexpr int kNT = 4;                    // 16x16 tiles per wave along N
   constexpr int kWaveCols = 16 * kNT;
   constexpr int kRowsPerWave = kBM / 4; // rows of the A block each wave fetches
   constexpr int kDma = kRowsPerWave / 4;
-  // Tiles up to 128 rows stage activations through registers and keep a window
-  // of kWin weight blocks in flight; the 256-row tile (search GEMMs) uses DMA.
-  constexpr bool kRegA = MT <= 4 && !DENSE;
-  constexpr int kWin = kGPB > 1 ? 3 : 4;
 
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kBM * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBM * kBK];
-  __shared__ uint32_t s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const DeqRegs dq;
-  const int wm = kTall ? 0 : wave >> 1, wn = kTall ? wave : wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;
   const int c = lane & 15, kq = lane >> 4;
 
   const int tiles_n = (N + kBN - 1) / kBN;
@@ -276,69 +257,6 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
     }
   };
 
-  if constexpr (kRegA) {
-    // ---- main loop, register-staged activations --------------------------------
-    // Every wait here is a counted vmcnt on ordinary loads, so the weight window
-    // of kWin blocks stays in flight while the math runs.  Activations: block
-    // k+1 is written to LDS during step k (its loads were issued in step k-1)
-    // and block k+2 is requested; one barrier per step orders LDS writes and
-    // reads.  Weights, scales and zeros: slot u holds block k, refilled with
-    // block k+kWin as soon as block k has been used.
-    constexpr int kARounds = kBM / 16;            // 16-byte chunks per thread per block
-    u32x4 areg[kARounds];
-    const rsrc_t rXa = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
-    auto load_a = [&](int kb) {
-#pragma unroll
-      for (int r = 0; r < kARounds; ++r) {
-        const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
-        const uint32_t off = (uint32_t)(row0 + row) * (uint32_t)K * 2u + (uint32_t)kb * (kBK * 2) +
-                             (uint32_t)ch * 16u;
-        areg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rXa, off, 0, 0));
-      }
-    };
-    auto store_a = [&](uint16_t *buf) {
-#pragma unroll
-      for (int r = 0; r < kARounds; ++r) {
-        const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(buf) + row * (kBK * 2) +
-                                   ((ch ^ (row & 15)) << 4)) = areg[r];
-      }
-    };
-    // Loads are never under a branch (prefetch indices are clamped to the last
-    // block; the surplus loads of the last steps are never consumed), so every
-    // step issues the same sequence and the compiler's counted waits stay exact.
-    BRegs rw[kWin];
-    const int last = kb_end - 1;
-    auto clampk = [&](int k) { return k < last ? k : last; };
-    // The prologue ends with the same issue order as every step (activations,
-    // then one weight block) so that the wait counts the compiler derives at
-    // the loop header equal the steady-state ones.
-    load_a(kb_begin);
-#pragma unroll
-    for (int u = 0; u < kWin - 1; ++u) load_b(clampk(kb_begin + u), rw[u]);
-    store_a(sA0);
-    load_a(clampk(kb_begin + 1));
-    load_b(clampk(kb_begin + kWin - 1), rw[kWin - 1]);
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes landed
-    __builtin_amdgcn_s_barrier();
-    for (int kb = kb_begin; kb < kb_end; kb += kWin) {
-#pragma unroll
-      for (int u = 0; u < kWin; ++u) {
-        const int k = kb + u;
-        if (k >= kb_end) break;
-        const bool odd = ((k - kb_begin) & 1) != 0;
-        uint16_t *buf = odd ? sA1 : sA0;
-        uint16_t *nbuf = odd ? sA0 : sA1;
-        store_a(nbuf);                      // block k+1 (a copy of the last block at the end)
-        load_a(clampk(k + 2));
-        __builtin_amdgcn_sched_barrier(0);
-        compute(k, buf, rw[u]);
-        load_b(clampk(k + kWin), rw[u]);
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_s_barrier();
-      }
-    }
-  } else {
   // ---- main loop: two static buffers, one barrier per block -------------------
   // Prefetch indices are clamped to the last block instead of branched on, so
   // no load sits under a branch; the surplus prefetch of the last iteration
@@ -364,55 +282,6 @@ __device__ __forceinline__ void gemm_body(const uint16_t *__restrict__ X,
     compute(kb + 1, sA1, r1);
   }
   wait_vmem_all();
-  }
-
-  // ---- split K: publish the partial tile; the last workgroup sums them ------
-  // The partials cross workgroups that may sit on different XCDs, whose L2s
-  // are not coherent with each other.  A device-scope fence would write back
-  // and invalidate a whole L2 per workgroup; instead the partials are stored
-  // write-through and read back bypassing both cache levels (the sc0 sc1
-  // cache-policy bits), and the per-tile counter is an atomic, which is
-  // coherent across XCDs.  vmcnt(0) orders the stores before the atomic.
-  // (compiled only for the tiles the plan may split: the 256-row tile's
-  // registers are all taken by its main loop)
-  if constexpr (MT < 8) if (sk.splits > 1) {
-    constexpr int kTiles = kMT * kNT;     // f32x4 accumulators per lane
-    constexpr int kSys = 1 | 16;          // sc0 | sc1: system-coherent access
-    // partial layout: [tile][split][wave][16x16 tile][lane] of 16 bytes
-    const uint32_t wave_bytes = (uint32_t)kTiles * 64u * 16u;
-    const uint32_t tile_bytes = 4u * wave_bytes;
-    const rsrc_t rP = make_rsrc(sk.partials, 0x7FFFFFF0u);
-    const uint32_t lane_off = (uint32_t)wave * wave_bytes + (uint32_t)lane * 16u;
-    const uint32_t mine = ((uint32_t)tile * (uint32_t)sk.splits + (uint32_t)split) * tile_bytes +
-                          lane_off;
-#pragma unroll
-    for (int i = 0; i < kMT; ++i)
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) {
-        const f32x4 v = acc[i][j];
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rP,
-                                               mine + (uint32_t)(i * kNT + j) * 1024u, 0, kSys);
-      }
-    wait_vmem_all();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&sk.counters[tile], 1u) == (uint32_t)(sk.splits - 1);
-    __syncthreads();
-    if (!s_last) return;
-    const uint32_t base = (uint32_t)tile * (uint32_t)sk.splits * tile_bytes + lane_off;
-    for (int sp = 0; sp < sk.splits; ++sp) {
-      const uint32_t p = base + (uint32_t)sp * tile_bytes;
-#pragma unroll
-      for (int i = 0; i < kMT; ++i)
-#pragma unroll
-        for (int j = 0; j < kNT; ++j) {
-          const f32x4 v = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rP, p + (uint32_t)(i * kNT + j) * 1024u,
-                                                           0, kSys));
-          acc[i][j] = sp == 0 ? v : acc[i][j] + v;
-        }
-    }
-    if (tid == 0) atomicExch(&sk.counters[tile], 0u);   // ready for the next launch
-  }
 
   // ---- epilogue -------------------------------------------------------------
   // Lane (c, kq) holds rows 4*kq + e of column c of every 16x16 tile.
@@ -480,17 +349,6 @@ void gemm_kernel_big(const uint16_t *__restrict__ X, const uint32_t *__restrict_
                                         partials, sk);
 }
 
-template <class XT, int GS, int EPI, bool DENSE, int YT, int MT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_kernel_small(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
-                       const uint16_t *__restrict__ Wdense, const uint16_t *__restrict__ scales,
-                       const uint8_t *__restrict__ zeros, int M, int N, int K,
-                       void *__restrict__ Y, const float *__restrict__ Yref,
-                       double *__restrict__ partials, SplitK sk) {
-  gemm_body<XT, GS, EPI, DENSE, YT, MT>(X, qweight, Wdense, scales, zeros, M, N, K, Y, Yref,
-                                        partials, sk);
-}
-
 // The search's dense and loss GEMMs use the 256-row tile and no K split.
 int64_t gemm_tile_count(int64_t M, int64_t N) {
   return ((M + 255) / 256) * ((N + kBN - 1) / kBN);
@@ -512,68 +370,34 @@ bool gemm_supported(int64_t N, int64_t K, bool dense) {
 }
 
 
-// Row tile and K split of a quantized GEMM launch.  M <= 32 and M <= 64 take
-// 32- and 64-row tiles, larger M the 128-row tile (the 256-row tile needs more
-// registers than one wave of two per SIMD has and spends its VALU time moving
-// accumulators through AGPRs).  When the tiles
-// cannot give every CU two workgroups, K is split (at most 8 ways, at least
-// two K blocks per split).
-static GemmPlan gemm_bf16_plan(int64_t M, int64_t N, int64_t K) {
-  GemmPlan p{};
-  p.mt = M <= 32 ? 1 : M <= 64 ? 2 : 4;
-  const int64_t bm = 32 * p.mt;
-  p.tiles = ((M + bm - 1) / bm) * ((N + kBN - 1) / kBN);
-  const int64_t nkb = (K + kBK - 1) / kBK;
-  p.splits = 1;
-  if (p.mt < 8 && p.tiles < 512) {
-    int64_t sp = (512 + p.tiles - 1) / p.tiles;
-    const int64_t cap = nkb / 2 < 8 ? nkb / 2 : 8;
-    sp = sp < cap ? sp : cap;
-    p.splits = sp > 1 ? (int)sp : 1;
-  }
-  if (p.splits > 1) {
-    // A fixed counter region: K is split only when there are fewer than 512
-    // tiles, and every plan must find its counters at the same place (the
-    // partials of one shape must never overlap the counters of another).
-    p.counter_bytes = kSplitCounterBytes;
-    p.workspace_bytes = p.counter_bytes + (size_t)p.tiles * p.splits * bm * kBN * 4;
-  }
-  return p;
-}
-
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, XType xt) {
-  return xt == XType::F16 ? gemm_f16_plan(M, N, K) : gemm_bf16_plan(M, N, K);
+  return gemm_f16_plan(M, N, K, xt == XType::BF16);
 }
 
+// The bf16 plan adds the row factors to the fp16 plan's workspace.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const size_t a = gemm_f16_plan(M, N, K).workspace_bytes;
-  const size_t b = gemm_bf16_plan(M, N, K).workspace_bytes;
-  return a > b ? a : b;
+  return gemm_f16_plan(M, N, K, true).workspace_bytes;
 }
 
-template <class XT, int GS, int EPI, bool DENSE, int YT, int MT>
-static hipError_t gemm_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *Wd,
-                                 const uint16_t *sc, const uint8_t *zr, int64_t M, int64_t N,
-                                 int64_t K, void *Y, const float *Yref, double *partials,
-                                 SplitK sk, hipStream_t st) {
+// The search's GEMMs: the 256-row tile, fp32 output or the loss epilogue.
+template <int GS, int EPI, bool DENSE>
+static hipError_t gemm_go(const uint16_t *X, const uint32_t *qw, const uint16_t *Wd,
+                          const uint16_t *sc, const uint8_t *zr, int64_t M, int64_t N, int64_t K,
+                          void *Y, const float *Yref, double *partials, hipStream_t st) {
+  constexpr int MT = 8;
   constexpr int64_t bm = 32 * MT;
-  const int ysize = YT == (int)YType::F32 ? 4 : 2;
-  const int64_t rows = sk.splits > 1 ? M : rows_per_launch(N, K, bm);
+  const SplitK sk{1, nullptr, nullptr};
+  const int64_t rows = rows_per_launch(N, K, bm);
   if (rows <= 0) return hipErrorInvalidValue;
   int64_t tile_base = 0;
   for (int64_t m0 = 0; m0 < M; m0 += rows) {
     const int64_t mm = M - m0 < rows ? M - m0 : rows;
     const int64_t tiles = ((mm + bm - 1) / bm) * ((N + kBN - 1) / kBN);
-    const dim3 grid((unsigned)(tiles * sk.splits));
-    void *y = Y ? reinterpret_cast<char *>(Y) + m0 * N * ysize : nullptr;
+    void *y = Y ? reinterpret_cast<char *>(Y) + m0 * N * 4 : nullptr;
     const float *yr = Yref ? Yref + m0 * N : nullptr;
     double *pp = partials ? partials + tile_base : nullptr;
-    if constexpr (MT >= 4)
-      gemm_kernel_big<XT, GS, EPI, DENSE, YT, MT><<<grid, kThreads, 0, st>>>(
-          X + m0 * K, qw, Wd, sc, zr, (int)mm, (int)N, (int)K, y, yr, pp, sk);
-    else
-      gemm_kernel_small<XT, GS, EPI, DENSE, YT, MT><<<grid, kThreads, 0, st>>>(
-          X + m0 * K, qw, Wd, sc, zr, (int)mm, (int)N, (int)K, y, yr, pp, sk);
+    gemm_kernel_big<TagF16, GS, EPI, DENSE, (int)YType::F32, MT><<<dim3((unsigned)tiles), kThreads, 0, st>>>(
+        X + m0 * K, qw, Wd, sc, zr, (int)mm, (int)N, (int)K, y, yr, pp, sk);
     tile_base += tiles;
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -581,92 +405,28 @@ static hipError_t gemm_launch_mt(const uint16_t *X, const uint32_t *qw, const ui
   return hipSuccess;
 }
 
-template <class XT, int GS, int EPI, bool DENSE, int YT>
-static hipError_t gemm_go1(const uint16_t *X, const uint32_t *qw, const uint16_t *Wd,
-                           const uint16_t *sc, const uint8_t *zr, int64_t M, int64_t N, int64_t K,
-                           void *Y, const float *Yref, double *partials, int mt, SplitK sk,
-                           hipStream_t st) {
-  if constexpr (EPI == kEpiStore && !DENSE) {
-    if (mt == 1)
-      return gemm_launch_mt<XT, GS, EPI, DENSE, YT, 1>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
-                                                       partials, sk, st);
-    if (mt == 2)
-      return gemm_launch_mt<XT, GS, EPI, DENSE, YT, 2>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
-                                                       partials, sk, st);
-    if (mt == 4)
-      return gemm_launch_mt<XT, GS, EPI, DENSE, YT, 4>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
-                                                       partials, sk, st);
-  }
-  return gemm_launch_mt<XT, GS, EPI, DENSE, YT, 8>(X, qw, Wd, sc, zr, M, N, K, Y, Yref, partials,
-                                                   sk, st);
-}
-
-template <class XT, int GS, int EPI, bool DENSE>
-static hipError_t gemm_go(const uint16_t *X, const uint32_t *qw, const uint16_t *Wd,
-                          const uint16_t *sc, const uint8_t *zr, int64_t M, int64_t N, int64_t K,
-                          void *Y, int yt, const float *Yref, double *partials, int mt,
-                          SplitK sk, hipStream_t st) {
-  if (EPI == kEpiLoss || yt == (int)YType::F32)
-    return gemm_go1<XT, GS, EPI, DENSE, (int)YType::F32>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
-                                                         partials, mt, sk, st);
-  if (yt == (int)YType::BF16)
-    return gemm_go1<XT, GS, EPI, DENSE, (int)YType::BF16>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
-                                                          partials, mt, sk, st);
-  return gemm_go1<XT, GS, EPI, DENSE, (int)YType::F16>(X, qw, Wd, sc, zr, M, N, K, Y, Yref,
-                                                       partials, mt, sk, st);
-}
-
 hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
                        int64_t K, int gs, void *Y, YType yt, void *workspace,
                        hipStream_t st) {
-  if (M == 0 || N == 0) return hipSuccess;
-  if (xt == XType::F16)
-    return launch_gemm_f16(reinterpret_cast<const uint16_t *>(X), qweight, scales, zeros, M, N, K,
-                           gs, Y, yt, workspace, st);
-  const GemmPlan p = gemm_bf16_plan(M, N, K);
-  SplitK sk{1, nullptr, nullptr};
-  if (p.splits > 1) {
-    if (!workspace) return hipErrorInvalidValue;
-    sk.splits = p.splits;
-    sk.counters = reinterpret_cast<uint32_t *>(workspace);
-    sk.partials = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + p.counter_bytes);
-  }
-  const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
-  const int y = (int)yt;
-  if (xt == XType::F16)
-    return gs == 128 ? gemm_go<TagF16, 128, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
-                                                              M, N, K, Y, y, nullptr, nullptr,
-                                                              p.mt, sk, st)
-                     : gemm_go<TagF16, 64, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
-                                                             M, N, K, Y, y, nullptr, nullptr,
-                                                             p.mt, sk, st);
-  return gs == 128 ? gemm_go<TagBF16, 128, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
-                                                             M, N, K, Y, y, nullptr, nullptr,
-                                                             p.mt, sk, st)
-                   : gemm_go<TagBF16, 64, kEpiStore, false>(x, qweight, nullptr, scales, zeros,
-                                                            M, N, K, Y, y, nullptr, nullptr,
-                                                            p.mt, sk, st);
+  return launch_gemm_f16(reinterpret_cast<const uint16_t *>(X), xt == XType::BF16, qweight,
+                         scales, zeros, M, N, K, gs, Y, yt, workspace, st);
 }
 
 hipError_t launch_gemm_dense_f32(const uint16_t *X, const uint16_t *W, int64_t M, int64_t N,
                                  int64_t K, float *Y, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  return gemm_go<TagF16, 128, kEpiStore, true>(X, nullptr, W, nullptr, nullptr, M, N, K, Y,
-                                               (int)YType::F32, nullptr, nullptr, 8,
-                                               SplitK{1, nullptr, nullptr}, st);
+  return gemm_go<128, kEpiStore, true>(X, nullptr, W, nullptr, nullptr, M, N, K, Y, nullptr,
+                                       nullptr, st);
 }
 
 hipError_t launch_gemm_loss(const uint16_t *A, const uint32_t *qweight, const uint16_t *scales,
                             const uint8_t *zeros, int64_t M, int64_t N, int64_t K, int gs,
                             const float *Yref, double *partials, hipStream_t st) {
-  const SplitK one{1, nullptr, nullptr};
-  return gs == 128 ? gemm_go<TagF16, 128, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M,
-                                                           N, K, nullptr, 0, Yref, partials, 8,
-                                                           one, st)
-                   : gemm_go<TagF16, 64, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M,
-                                                          N, K, nullptr, 0, Yref, partials, 8,
-                                                          one, st);
+  return gs == 128 ? gemm_go<128, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M, N, K,
+                                                   nullptr, Yref, partials, st)
+                   : gemm_go<64, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M, N, K,
+                                                  nullptr, Yref, partials, st);
 }
 
 }  // namespace awq

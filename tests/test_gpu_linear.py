@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from gpu_common import (assert_close, dev, out_to_f64, say, to_dev, to_np, torch_mod)
+from gpu_common import (REL_FRO, assert_close, dev, out_to_f64, say, to_dev, to_np, torch_mod)
 from oracle import (QuantConfig, bf16_bits_to_f32, dequantize, linear64, quantize_pack,
                     unpack_codes)
 
@@ -97,6 +97,62 @@ def test_ragged_shapes(M, N, K, g, dt):
         # so bf16 activations are held to the bound through the fp32 output.
         want = torch.from_numpy(Y32).to(torch.float16 if dt == "f16" else torch.bfloat16)
         assert np.array_equal(Y16, want.float().numpy().astype(np.float64))
+
+
+def test_bf16_rows_beyond_fp16_range():
+    """The GEMM runs bf16 activations in fp16 after multiplying each row by
+    the power of two that brings its largest magnitude to [2^14, 2^15).  Rows
+    far beyond 65504, rows of tiny values and ordinary rows all stay within
+    the relative tolerance of the fp64 oracle, row by row (the max-abs bound
+    is taken relative to the row's magnitude, since these rows' outputs reach
+    1e7 and 1e-6)."""
+    torch = torch_mod()
+    M, N, K, g = 40, 300, 640, 128
+    W = wl.gen_weight(N, K, 61)
+    qw, sc, zr, pd = _packed(W, g)
+    x = wl.gen_activation(M, K, 62, 63, "f16").astype(np.float32)
+    x[3] *= 3.0e6                    # largest |x| ~ 1e8
+    x[7] *= 1.0e-6                   # fp16 subnormal territory
+    x[11, 5] = 2.0e9                 # one huge value in an ordinary row
+    x[20] *= 7.0e4
+    X = wl.f32_to_bf16_bits(x)
+    ref = linear64(_x_f64(X, "bf16"), qw, sc, zr, g)
+    say("bf16 wide range", M, N, K)
+    Y = out_to_f64(_run(X, "bf16", pd, g, GEMM, torch.float32))
+    assert np.isfinite(Y).all()
+    for r in range(M):
+        err = Y[r] - ref[r]
+        rel = np.linalg.norm(err) / np.linalg.norm(ref[r])
+        assert rel <= REL_FRO, f"row {r}: rel_fro={rel:.3e}"
+        assert np.max(np.abs(err)) <= REL_FRO * np.max(np.abs(ref[r])), f"row {r}"
+
+
+def test_bf16_row_factors_leave_split_counters_alone():
+    """A bf16 GEMM without a K split keeps its per-row activation factors in
+    the workspace too; they must not land in the split-K counter region, or
+    the next split-K call on the same workspace finds its counters dirty."""
+    torch = torch_mod()
+    awq = _awq()
+    # the first call sizes the library scratch so that the later ones reuse it
+    shapes = [(40, 300, 640, 128), (16, 48, 256, 128), (5, 130, 1024, 64), (16, 48, 256, 128),
+              (40, 300, 640, 128)]
+    ws = torch.zeros(max(awq.awq_linear_workspace_size(64, 640, 4096, g) for g in (64, 128)),
+                     dtype=torch.uint8, device=dev())
+    for (M, N, K, g) in shapes:
+        W = wl.gen_weight(N, K, 70 + N)
+        X = wl.gen_activation(M, K, 71 + M, 72, "bf16")
+        qw, sc, zr, pd = _packed(W, g)
+        ref = linear64(_x_f64(X, "bf16"), qw, sc, zr, g)
+        say("bf16 shared workspace", M, N, K, g)
+        Xd = to_dev(X, bf16=True)
+        a = out_to_f64(awq.awq_linear_ex(Xd, *pd, kernel=GEMM, group_size=g,
+                                         out_dtype=torch.float32))
+        if M > 16:
+            b = out_to_f64(awq.awq_linear_ws(Xd, *pd, ws, group_size=g, out_dtype=torch.float32))
+            assert_close(b, ref, f"{M}x{N}x{K} caller workspace")
+        torch.cuda.synchronize()
+        assert_close(a, ref, f"{M}x{N}x{K} library scratch")
+    assert int(ws[:2048].count_nonzero()) == 0
 
 
 def test_split_k_repeatable_and_workspace_regrowth():
