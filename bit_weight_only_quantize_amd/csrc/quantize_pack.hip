@@ -12,106 +12,141 @@
 // are reproducible bit for bit on any IEEE machine.
 //
 // Mapping: one lane per output word (8 input channels, 16 bytes of W);
-// g/8 consecutive lanes form a group and exchange min/max with lane shuffles.
+// g/8 consecutive lanes form a group and exchange min/max with DPP moves.
 // The kernel is bound by HBM traffic (2 bytes in, 0.5 + 3/g bytes out per
 // weight); the per-weight division is replaced by a reciprocal multiply whose
 // rounding provably agrees except next to half-integers (checked per lane).
+
+#include <type_traits>
 
 #include "awq_internal.h"
 #include "device_common.h"
 
 namespace awq {
 
+// Min and max over the g/8 lanes of a group (aligned runs of 8 or 16 lanes)
+// with DPP lane exchanges: swap neighbours, swap pairs, mirror within 8, then
+// (g = 128) mirror within 16.  Each step pairs every lane with one of the other
+// half of its current run, so after log2(g/8) steps every lane of a group
+// holds the group's extremes.
+template <int LANES>
+__device__ __forceinline__ float group_min(float v) {
+  auto step = [](float x, auto ctrl_tag) {
+    constexpr int kCtrl = decltype(ctrl_tag)::value;
+    const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true);
+    return __builtin_fminf(x, __builtin_bit_cast(float, y));
+  };
+  v = step(v, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+  v = step(v, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+  v = step(v, std::integral_constant<int, 0x141>{});   // row_half_mirror
+  if constexpr (LANES == 16) v = step(v, std::integral_constant<int, 0x140>{});   // row_mirror
+  return v;
+}
+template <int LANES>
+__device__ __forceinline__ float group_max(float v) {
+  auto step = [](float x, auto ctrl_tag) {
+    constexpr int kCtrl = decltype(ctrl_tag)::value;
+    const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true);
+    return __builtin_fmaxf(x, __builtin_bit_cast(float, y));
+  };
+  v = step(v, std::integral_constant<int, 0xB1>{});
+  v = step(v, std::integral_constant<int, 0x4E>{});
+  v = step(v, std::integral_constant<int, 0x141>{});
+  if constexpr (LANES == 16) v = step(v, std::integral_constant<int, 0x140>{});
+  return v;
+}
+
+// Grid: x covers the words of one row in chunks of 256 (a multiple of the
+// group's word count, so no group straddles workgroups), y the rows (looped
+// when N exceeds the grid's y limit).  No per-lane 64-bit division.
 template <int GS>
 __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const uint16_t *__restrict__ W, int64_t N, int64_t K, const float *__restrict__ s,
     uint32_t *__restrict__ qweight, uint16_t *__restrict__ scales,
     uint8_t *__restrict__ zeros, int32_t *__restrict__ nonfinite) {
   constexpr int kLanesPerGroup = GS / 8;
-  const int64_t words_per_row = K / 8;
-  const int64_t total = N * words_per_row;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  // total is a multiple of kLanesPerGroup and groups start at multiples of
-  // it, so a group is either entirely active or entirely idle.
-  const bool active = t < total;
-
-  float v[8];
+  const int wpr = (int)(K / 8);                       // words per row
+  const int c = blockIdx.x * 256 + threadIdx.x;       // word within the row
+  // words_per_row is a multiple of kLanesPerGroup and groups start at
+  // multiples of it, so a group is either entirely active or entirely idle.
+  const bool active = c < wpr;
+  float sv[8];
+  if (s != nullptr && active) {
+    const float4 s0 = *reinterpret_cast<const float4 *>(s + (int64_t)c * 8);
+    const float4 s1 = *reinterpret_cast<const float4 *>(s + (int64_t)c * 8 + 4);
+    sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w;
+    sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+  }
   int bad = 0;
-  if (active) {
-    const int64_t n = t / words_per_row;
-    const int64_t c = t - n * words_per_row;
-    const u32x4 raw = *reinterpret_cast<const u32x4 *>(W + n * K + c * 8);
+  for (int64_t n = blockIdx.y; n < N; n += gridDim.y) {
+    float v[8];
+    if (active) {
+      const u32x4 raw = *reinterpret_cast<const u32x4 *>(W + n * K + (int64_t)c * 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = half_bits_to_float((uint16_t)(raw[i] & 0xFFFFu));
-      v[2 * i + 1] = half_bits_to_float((uint16_t)(raw[i] >> 16));
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t r = raw[i];
+        v[2 * i] = half_bits_to_float((uint16_t)(r & 0xFFFFu));
+        v[2 * i + 1] = half_bits_to_float((uint16_t)(r >> 16));
+      }
+      if (s != nullptr) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = sv[i] * v[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bad += !__builtin_isfinite(v[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
-    if (s != nullptr) {
-      const float4 s0 = *reinterpret_cast<const float4 *>(s + c * 8);
-      const float4 s1 = *reinterpret_cast<const float4 *>(s + c * 8 + 4);
-      v[0] = s0.x * v[0]; v[1] = s0.y * v[1]; v[2] = s0.z * v[2]; v[3] = s0.w * v[3];
-      v[4] = s1.x * v[4]; v[5] = s1.y * v[5]; v[6] = s1.z * v[6]; v[7] = s1.w * v[7];
+
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo = fminf(lo, v[i]);
+      hi = fmaxf(hi, v[i]);
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) bad += !__builtin_isfinite(v[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-  }
+    lo = group_min<kLanesPerGroup>(lo);
+    hi = group_max<kLanesPerGroup>(hi);
 
-  float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    lo = fminf(lo, v[i]);
-    hi = fmaxf(hi, v[i]);
-  }
-#pragma unroll
-  for (int off = 1; off < kLanesPerGroup; off <<= 1) {
-    lo = fminf(lo, __shfl_xor(lo, off, 64));
-    hi = fmaxf(hi, __shfl_xor(hi, off, 64));
-  }
+    const float step = (hi - lo) / 15.0f;
+    const _Float16 sh = (_Float16)fmaxf(step, 0x1p-14f);
+    const float sf = (float)sh;
+    const float zf = fminf(fmaxf(__builtin_rintf(-lo / sf), 0.0f), 15.0f);
 
-  const float step = (hi - lo) / 15.0f;
-  const _Float16 sh = (_Float16)fmaxf(step, 0x1p-14f);
-  const float sf = (float)sh;
-  const float zf = fminf(fmaxf(__builtin_rintf(-lo / sf), 0.0f), 15.0f);
+    // rint(v / sf) with the correctly rounded quotient, without eight
+    // divisions: |v / sf| < 16 (|v| <= hi - lo <= 15 sf (1 + 2^-10)), so both
+    // the quotient rounded once and y = fl(v * fl(1 / sf)) lie within 2^-19 of
+    // the exact v / sf and hence within 2^-18 of each other.  Unless y is that
+    // close to a half-integer, both round to the same integer (ties included,
+    // since a rounded quotient exactly at k + 1/2 puts y within 2^-18 of it);
+    // the rare lanes that are that close divide.
+    const float rs = 1.0f / sf;
+    float qv[8];
+    bool near_half = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float y = v[i] * rs;
+      qv[i] = __builtin_rintf(y);
+      near_half |= __builtin_fabsf((y - __builtin_floorf(y)) - 0.5f) < 0x1p-18f;
+    }
+    if (near_half) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[i] = __builtin_rintf(v[i] / sf);
+    }
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float qf = fminf(fmaxf(qv[i] + zf, 0.0f), 15.0f);
+      word |= ((uint32_t)qf) << (4 * nibble_of_channel(i));
+    }
 
-  // rint(v / sf) with the correctly rounded quotient, without eight divisions:
-  // |v / sf| < 16 (|v| <= hi - lo <= 15 sf (1 + 2^-10)), so both the quotient
-  // rounded once and y = fl(v * fl(1 / sf)) lie within 2^-19 of the exact
-  // v / sf and hence within 2^-18 of each other.  Unless y is that close to a
-  // half-integer, both round to the same integer (ties included, since a
-  // rounded quotient exactly at k + 1/2 puts y within 2^-18 of it); the rare
-  // lanes that are that close divide.
-  const float rs = 1.0f / sf;
-  float qv[8];
-  bool near_half = false;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float y = v[i] * rs;
-    qv[i] = __builtin_rintf(y);
-    near_half |= __builtin_fabsf((y - __builtin_floorf(y)) - 0.5f) < 0x1p-18f;
-  }
-  if (near_half) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qv[i] = __builtin_rintf(v[i] / sf);
-  }
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float qf = fminf(fmaxf(qv[i] + zf, 0.0f), 15.0f);
-    word |= ((uint32_t)qf) << (4 * nibble_of_channel(i));
-  }
-
-  if (active) {
-    qweight[t] = word;
-    const int64_t n = t / words_per_row;
-    const int64_t c = t - n * words_per_row;
-    if ((c % kLanesPerGroup) == 0) {
-      const int64_t G = K / GS;
-      const int64_t gi = n * G + c / kLanesPerGroup;
-      scales[gi] = __builtin_bit_cast(uint16_t, sh);
-      zeros[gi] = (uint8_t)zf;
+    if (active) {
+      qweight[n * wpr + c] = word;
+      if ((c % kLanesPerGroup) == 0) {
+        const int64_t gi = n * (K / GS) + c / kLanesPerGroup;
+        scales[gi] = __builtin_bit_cast(uint16_t, sh);
+        zeros[gi] = (uint8_t)zf;
+      }
     }
   }
 
@@ -125,9 +160,9 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
 hipError_t launch_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int gs,
                                 const float *s, uint32_t *qweight, uint16_t *scales,
                                 uint8_t *zeros, int32_t *nonfinite, hipStream_t st) {
-  const int64_t total = N * (K / 8);
-  if (total == 0) return hipSuccess;
-  const dim3 grid((unsigned)((total + 255) / 256));
+  if (N == 0) return hipSuccess;
+  const int64_t wpr = K / 8;
+  const dim3 grid((unsigned)((wpr + 255) / 256), (unsigned)(N < 65535 ? N : 65535));
   if (gs == 128)
     quantize_pack_kernel<128><<<grid, 256, 0, st>>>(W, N, K, s, qweight, scales, zeros, nonfinite);
   else
