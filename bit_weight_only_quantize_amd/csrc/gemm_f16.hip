@@ -87,13 +87,19 @@ __device__ __forceinline__ void tile_order() {
 
 }  // namespace
 
-template <int GS, int YT, int MT, bool KTAIL, bool BF16X>
+// EPI: 0 stores Y with fp16-dequantized weights; 1 (the search's loss) uses
+// the exact integer q - z with the group scale on fp32 group sums and reduces
+// (Yref - Y)^2 of the tile to one fp64 partial instead of storing Y.
+template <int GS, int YT, int MT, bool KTAIL, bool BF16X, int EPI>
 __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
                                               const uint32_t *__restrict__ qweight,
                                               const uint16_t *__restrict__ scales,
                                               const uint8_t *__restrict__ zeros, int M, int N,
                                               int K, void *__restrict__ Y, SplitK sk,
-                                              const float *__restrict__ rowf) {
+                                              const float *__restrict__ rowf,
+                                              const float *__restrict__ Yref,
+                                              double *__restrict__ partials) {
+  constexpr bool kExact = EPI == 1;
   constexpr int kBM = 16 * MT;
   constexpr int kWpl = GS / 32;      // packed words per lane per group and column
   constexpr int kGPB = kBK / GS;     // groups per K block
@@ -221,6 +227,10 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   auto deq_word = [&](const Raw &r, uint32_t sz, int j, int gi, int w, BQ &out) {
     const DeqF16 deq(sz >> 16);
     const u32x4 e = deq(r.w[j][gi][w], dq);
+    if constexpr (kExact) {
+      out[j][gi * kWpl + w] = e;        // q - z exactly; the scale comes later
+      return;
+    }
     const uint32_t s1 = sz & 0xFFFFu;
     const f16x2 s2 = __builtin_bit_cast(f16x2, s1 | (s1 << 16));
     // (scalar copies first: bit-casting an element of a vector lvalue reads
@@ -315,6 +325,7 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   Raw rw[kWin];
   BQ bq[2];
   SZ szr;
+  u32x4 szc[2][kGPB];                    // exact path: blocks' scales, by step parity
   // Load n of a step: scales first and activations next (both are needed at
   // the start of the next step), then the weight window's refill.  Each
   // activation chunk's register first goes to LDS (block k+1, into the
@@ -338,6 +349,19 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     u32x4 szv[kGPB];
 #pragma unroll
     for (int gi = 0; gi < kGPB; ++gi) szv[gi] = read_sz(zbuf, gi);
+    float sk[kGPB][kNT];                 // block k's scales (exact path)
+    if constexpr (kExact) {
+#pragma unroll
+      for (int gi = 0; gi < kGPB; ++gi) {
+        const u32x4 zz = szc[p][gi];
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) {
+          const uint32_t z1 = zz[j];
+          sk[gi][j] = half_bits_to_float((uint16_t)(z1 & 0xFFFFu));
+        }
+        szc[p ^ 1][gi] = szv[gi];
+      }
+    }
     const Raw &nx = rw[(u + 1) % kWin];
     u32x4 a[2][kSteps];
 #pragma unroll
@@ -350,11 +374,30 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) a[cur ^ 1][st] = a_frag(abuf, i + 1, a_ch(st));
       }
+      if constexpr (kExact) {
 #pragma unroll
-      for (int st = 0; st < kSteps; ++st)
+        for (int gi = 0; gi < kGPB; ++gi) {
+          f32x4 t[kNT];
 #pragma unroll
-        for (int j = 0; j < kNT; ++j)
-          acc[i][j] = mfma32<TagF16>(a[cur][st], bq[p][j][st], acc[i][j]);
+          for (int j = 0; j < kNT; ++j) t[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int w = 0; w < kWpl; ++w)
+#pragma unroll
+            for (int j = 0; j < kNT; ++j)
+              t[j] = mfma32<TagF16>(a[cur][gi * kWpl + w], bq[p][j][gi * kWpl + w], t[j]);
+#pragma unroll
+          for (int j = 0; j < kNT; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[i][j][e] = __builtin_fmaf(t[j][e], sk[gi][j], acc[i][j][e]);
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st)
+#pragma unroll
+          for (int j = 0; j < kNT; ++j)
+            acc[i][j] = mfma32<TagF16>(a[cur][st], bq[p][j][st], acc[i][j]);
+      }
       // dequantize words [i*kWordsPerTile, (i+1)*kWordsPerTile) of block k+1
 #pragma unroll
       for (int q = i * kWordsPerTile; q < (i + 1) * kWordsPerTile; ++q) {
@@ -365,7 +408,8 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
       }
 #pragma unroll
       for (int n = i * kLoads / MT; n < (i + 1) * kLoads / MT; ++n) issue(n, k, u, odd ? sA0 : sA1);
-      tile_order<kNT * kSteps, (kWordsPerTile * 13 + kNT * kSteps - 1) / (kNT * kSteps) + 1>();
+      tile_order<kNT * kSteps, (kWordsPerTile * (kExact ? 9 : 13) + (kExact ? 4 * kNT * kGPB : 0) +
+                                kNT * kSteps - 1) / (kNT * kSteps) + 1>();
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_lds_all();
@@ -397,6 +441,8 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     u32x4 szv[kGPB];
 #pragma unroll
     for (int gi = 0; gi < kGPB; ++gi) szv[gi] = read_sz(sSZ0, gi);
+#pragma unroll
+    for (int gi = 0; gi < kGPB; ++gi) szc[0][gi] = szv[gi];
 #pragma unroll
     for (int q = 0; q < kWords; ++q) {
       const int j = q / kSteps, st = q % kSteps, gi = st / kWpl, w = st % kWpl;
@@ -486,6 +532,35 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   }
 
   // ---- epilogue: lane (c, kq) holds rows 4*kq + e of column c of each tile ------
+  if constexpr (EPI == 1) {
+    // sum of (Yref - Y)^2 over the tile, fp64, in a fixed order (lanes, then
+    // waves); rows >= M and columns >= N read 0 and have Y = 0
+    const rsrc_t rR = make_rsrc(Yref, (uint32_t)M * (uint32_t)N * 4u);
+    double sum = 0.0;
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) {
+      const int n = col0 + wave * 64 + j * 16 + c;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = row0 + i * 16 + 4 * kq + e;
+          const uint32_t o = n < N ? (uint32_t)m * (uint32_t)N + (uint32_t)n : kNone / 4u;
+          const float ref = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, o * 4u, 0, 0));
+          const double d = (double)ref - (double)acc[i][j][e];
+          sum = __builtin_fma(d, d, sum);
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    __syncthreads();
+    double *wsum = reinterpret_cast<double *>(sA0);
+    if (lane == 0) wsum[wave] = sum;
+    __syncthreads();
+    if (tid == 0) partials[tile] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    return;
+  }
   if constexpr (BF16X) {
     // undo the rows' activation factors (exact powers of two; rows past M
     // read 0 and keep their unused values)
@@ -528,13 +603,15 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 
 // One wave per SIMD: accumulators, two dequantized blocks and a four-block
 // weight window live in registers.
-template <int GS, int YT, int MT, bool KTAIL, bool BF16X>
+template <int GS, int YT, int MT, bool KTAIL, bool BF16X, int EPI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_f16_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
                      const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
                      int M, int N, int K, void *__restrict__ Y, SplitK sk,
-                     const float *__restrict__ rowf) {
-  gemm_f16_body<GS, YT, MT, KTAIL, BF16X>(X, qweight, scales, zeros, M, N, K, Y, sk, rowf);
+                     const float *__restrict__ rowf, const float *__restrict__ Yref,
+                     double *__restrict__ partials) {
+  gemm_f16_body<GS, YT, MT, KTAIL, BF16X, EPI>(X, qweight, scales, zeros, M, N, K, Y, sk, rowf,
+                                               Yref, partials);
 }
 
 // Per-row activation factor for bf16 input: the power of two that brings the
@@ -601,8 +678,9 @@ hipError_t f16_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *
     const int64_t tiles = ((mm + bm - 1) / bm) * ((N + kBN - 1) / kBN);
     const dim3 grid((unsigned)(tiles * sk.splits));
     void *y = reinterpret_cast<char *>(Y) + m0 * N * ysize;
-    gemm_f16_kernel<GS, YT, MT, KTAIL, BF16X><<<grid, kThreads, 0, st>>>(
-        X + m0 * K, qw, sc, zr, (int)mm, (int)N, (int)K, y, sk, rowf ? rowf + m0 : nullptr);
+    gemm_f16_kernel<GS, YT, MT, KTAIL, BF16X, 0><<<grid, kThreads, 0, st>>>(
+        X + m0 * K, qw, sc, zr, (int)mm, (int)N, (int)K, y, sk, rowf ? rowf + m0 : nullptr,
+        nullptr, nullptr);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -700,6 +778,41 @@ hipError_t launch_gemm_f16(const uint16_t *X, bool bf16, const uint32_t *qweight
   if (yt == YType::F32) return f16_go<64, (int)YType::F32>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, rowf, st);
   if (yt == YType::BF16) return f16_go<64, (int)YType::BF16>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, rowf, st);
   return f16_go<64, (int)YType::F16>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, rowf, st);
+}
+
+// ---- the search's loss GEMM ------------------------------------------------------
+int64_t gemm_tile_count(int64_t M, int64_t N) {
+  return ((M + 127) / 128) * ((N + kBN - 1) / kBN);
+}
+
+template <int GS, bool KTAIL>
+static hipError_t loss_go(const uint16_t *A, const uint32_t *qw, const uint16_t *sc,
+                          const uint8_t *zr, int64_t M, int64_t N, int64_t K, const float *Yref,
+                          double *partials, hipStream_t st) {
+  constexpr int64_t bm = 128;
+  const int64_t rows = f16_rows_per_launch(N, K, bm);
+  if (rows <= 0) return hipErrorInvalidValue;
+  int64_t tile_base = 0;
+  for (int64_t m0 = 0; m0 < M; m0 += rows) {
+    const int64_t mm = M - m0 < rows ? M - m0 : rows;
+    const int64_t tiles = ((mm + bm - 1) / bm) * ((N + kBN - 1) / kBN);
+    gemm_f16_kernel<GS, (int)YType::F32, 8, KTAIL, false, 1><<<dim3((unsigned)tiles), kThreads, 0, st>>>(
+        A + m0 * K, qw, sc, zr, (int)mm, (int)N, (int)K, nullptr, SplitK{1, nullptr, nullptr},
+        nullptr, Yref + m0 * N, partials + tile_base);
+    tile_base += tiles;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_gemm_loss(const uint16_t *A, const uint32_t *qweight, const uint16_t *scales,
+                            const uint8_t *zeros, int64_t M, int64_t N, int64_t K, int gs,
+                            const float *Yref, double *partials, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (gs == 128) return loss_go<128, false>(A, qweight, scales, zeros, M, N, K, Yref, partials, st);
+  if (K % kBK != 0) return loss_go<64, true>(A, qweight, scales, zeros, M, N, K, Yref, partials, st);
+  return loss_go<64, false>(A, qweight, scales, zeros, M, N, K, Yref, partials, st);
 }
 
 }  // namespace awq

@@ -349,11 +349,6 @@ void gemm_kernel_big(const uint16_t *__restrict__ X, const uint32_t *__restrict_
                                         partials, sk);
 }
 
-// The search's dense and loss GEMMs use the 256-row tile and no K split.
-int64_t gemm_tile_count(int64_t M, int64_t N) {
-  return ((M + 255) / 256) * ((N + kBN - 1) / kBN);
-}
-
 // Largest row count per launch that keeps every per-launch buffer below 2 GiB
 // (a multiple of the row tile bm).
 static int64_t rows_per_launch(int64_t N, int64_t K, int64_t bm) {
@@ -418,15 +413,6 @@ hipError_t launch_gemm_dense_f32(const uint16_t *X, const uint16_t *W, int64_t M
   if (M == 0 || N == 0) return hipSuccess;
   return gemm_go<128, kEpiStore, true>(X, nullptr, W, nullptr, nullptr, M, N, K, Y, nullptr,
                                        nullptr, st);
-}
-
-hipError_t launch_gemm_loss(const uint16_t *A, const uint32_t *qweight, const uint16_t *scales,
-                            const uint8_t *zeros, int64_t M, int64_t N, int64_t K, int gs,
-                            const float *Yref, double *partials, hipStream_t st) {
-  return gs == 128 ? gemm_go<128, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M, N, K,
-                                                   nullptr, Yref, partials, st)
-                   : gemm_go<64, kEpiLoss, false>(A, qweight, nullptr, scales, zeros, M, N, K,
-                                                  nullptr, Yref, partials, st);
 }
 
 }  // namespace awq
