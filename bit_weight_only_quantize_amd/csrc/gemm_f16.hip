@@ -73,6 +73,14 @@ __device__ __forceinline__ int a_chunk(int row, int ch) {
   return ch ^ (row & 15) ^ (((ch >> KQ_BIT) & 1) << 3);
 }
 
+// Logical chunk held by physical chunk p of block row `row` (inverse of
+// a_chunk: bit KQ_BIT is left alone by the bit-3 flip).
+template <int KQ_BIT>
+__device__ __forceinline__ int a_chunk_inv(int row, int p) {
+  const int t = p ^ (row & 15);
+  return t ^ (((t >> KQ_BIT) & 1) << 3);
+}
+
 // Instruction order of one row tile (for the scheduler): each MFMA followed
 // by up to V VALU operations.  One wave issues in order, so VALU work
 // clustered after the MFMAs would leave the matrix core idle.
@@ -107,6 +115,10 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   constexpr int kWin = MT >= 8 ? 2 : 4;   // weight blocks in flight (even: bq buffers alternate)
   constexpr int kWords = kNT * kSteps;          // packed words per lane per block
   constexpr int kWordsPerTile = kWords / MT;    // dequantized alongside each row tile
+  // The 256-row tile's 256 accumulators fill the AGPRs: its activations go to
+  // LDS by DMA (buffer_load ... lds), without staging registers.
+  constexpr bool kDMA = MT == 16;
+  static_assert(!(kDMA && (BF16X || kExact)), "the 256-row tile takes fp16 X and stores Y");
 
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kBM * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBM * kBK];
@@ -306,6 +318,19 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 #pragma unroll
     for (int r = 0; r < kARounds; ++r) store_a1(buf, r);
   };
+  // DMA r of this wave (kDMA): block rows 4d .. 4d+3, d = wave + 4r, 1 KiB.
+  // Lane l writes physical chunk l & 15 of row 4d + (l >> 4), so it loads the
+  // logical chunk that a_chunk maps there.
+  typedef __attribute__((address_space(3))) void lds_t;
+  auto dma_a1 = [&](uint16_t *buf, int kb, int r) {
+    const int d = wave + 4 * r, row = 4 * d + (lane >> 4);
+    const int ch = a_chunk_inv<kKqBit>(row, lane & 15);
+    uint32_t off = (uint32_t)(row0 + row) * (uint32_t)K * 2u + (uint32_t)kb * (kBK * 2) +
+                   (uint32_t)ch * 16u;
+    if constexpr (KTAIL) off = kb * kBK + ch * 8 < K ? off : kNone;   // zeros past K
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_t *)(reinterpret_cast<char *>(buf) + d * 1024),
+                                             16, off, 0, 0, 0);
+  };
 
   // ---- main loop ------------------------------------------------------------------
   // Block b's data moves in stages: its activations are loaded during step
@@ -322,6 +347,9 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // right before the wait that then drains them); the last steps follow
   // unrolled.
   constexpr int kLoads = kARounds + kNT + 1;      // prefetch loads per step
+  // row tiles that issue them: all, or with the DMA the first half, so the
+  // last ones still have half a step to land before the step's vmcnt(0)
+  constexpr int kIssueTiles = kDMA ? MT / 2 : MT;
   Raw rw[kWin];
   BQ bq[2];
   SZ szr;
@@ -331,6 +359,15 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // activation chunk's register first goes to LDS (block k+1, into the
   // buffer this step does not read), then is refilled with block k+2's chunk.
   auto issue = [&](int n, int k, int u, uint16_t *nbuf) {
+    if constexpr (kDMA) {
+      // weights first: every load of a step must land by its end (the DMA
+      // is waited for with vmcnt(0)); then scales, then block k+1's
+      // activations straight into the buffer this step does not read
+      if (n < kNT) load_w(clampk(k + kWin), n, rw[u]);
+      else if (n == kNT) load_sz(clampk(k + 3), szr);
+      else dma_a1(nbuf, clampk(k + 1), n - kNT - 1);
+      return;
+    }
     if (n == 0) {
       load_sz(clampk(k + 3), szr);
     } else if (n <= kARounds) {
@@ -406,13 +443,19 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
         const uint32_t sz = zz[j];
         deq_word(nx, sz, j, gi, w, bq[p ^ 1]);
       }
+      if (i < kIssueTiles) {
 #pragma unroll
-      for (int n = i * kLoads / MT; n < (i + 1) * kLoads / MT; ++n) issue(n, k, u, odd ? sA0 : sA1);
+        for (int n = i * kLoads / kIssueTiles; n < (i + 1) * kLoads / kIssueTiles; ++n)
+          issue(n, k, u, odd ? sA0 : sA1);
+      }
       tile_order<kNT * kSteps, (kWordsPerTile * (kExact ? 9 : 13) + (kExact ? 4 * kNT * kGPB : 0) +
                                 kNT * kSteps - 1) / (kNT * kSteps) + 1>();
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_lds_all();
+    if constexpr (kDMA)
+      __builtin_amdgcn_s_waitcnt(0x0070);     // vmcnt(0) lgkmcnt(0): the DMA has landed
+    else
+      wait_lds_all();
     __builtin_amdgcn_s_barrier();
   };
 
@@ -421,8 +464,13 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // registers, kb0 dequantized.
   {
     const int kb0 = kb_begin;
+    if constexpr (kDMA) {
 #pragma unroll
-    for (int r = 0; r < kARounds; ++r) load_a1(kb0, r);
+      for (int r = 0; r < kARounds; ++r) dma_a1(sA0, kb0, r);
+    } else {
+#pragma unroll
+      for (int r = 0; r < kARounds; ++r) load_a1(kb0, r);
+    }
 #pragma unroll
     for (int u = 0; u < kWin; ++u)
 #pragma unroll
@@ -431,12 +479,17 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     load_sz(kb0, s0);
     load_sz(clampk(kb0 + 1), s1);
     load_sz(clampk(kb0 + 2), szr);
-    store_a(sA0);
+    if constexpr (!kDMA) {
+      store_a(sA0);
 #pragma unroll
-    for (int r = 0; r < kARounds; ++r) load_a1(clampk(kb0 + 1), r);
+      for (int r = 0; r < kARounds; ++r) load_a1(clampk(kb0 + 1), r);
+    }
     store_sz(sSZ0, s0);
     store_sz(sSZ1, s1);
-    wait_lds_all();
+    if constexpr (kDMA)
+      __builtin_amdgcn_s_waitcnt(0x0070);
+    else
+      wait_lds_all();
     __builtin_amdgcn_s_barrier();
     u32x4 szv[kGPB];
 #pragma unroll
@@ -474,7 +527,9 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // vmcnt(0) orders a workgroup's stores before its done count.  The wait
   // ends: every other workgroup of the tile already holds a ticket, so it is
   // resident and finishes its stores.
-  if (sk.splits > 1) {
+  // (not compiled for the 256-row tile, which the plan never splits: its
+  // partial-sum registers would not fit beside the accumulators)
+  if (!kDMA && sk.splits > 1) {
     constexpr int kTiles = MT * kNT;     // f32x4 accumulators per lane
     constexpr int kSys = 1 | 16;         // sc0 | sc1
     // layout: [tile][split][wave][16x16 tile][lane] of 16 bytes
@@ -691,6 +746,12 @@ template <int GS, int YT, bool KTAIL, bool BF16X>
 hipError_t f16_go3(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, const uint8_t *zr,
                    int64_t M, int64_t N, int64_t K, void *Y, int mt, SplitK sk, const float *rowf,
                    hipStream_t st) {
+  if constexpr (!BF16X && !KTAIL) {
+    if (mt == 16) {
+      if (sk.splits > 1) return hipErrorInvalidValue;
+      return f16_launch_mt<GS, YT, 16, KTAIL, false>(X, qw, sc, zr, M, N, K, Y, sk, rowf, st);
+    }
+  }
   if (mt == 2) return f16_launch_mt<GS, YT, 2, KTAIL, BF16X>(X, qw, sc, zr, M, N, K, Y, sk, rowf, st);
   if (mt == 4) return f16_launch_mt<GS, YT, 4, KTAIL, BF16X>(X, qw, sc, zr, M, N, K, Y, sk, rowf, st);
   return f16_launch_mt<GS, YT, 8, KTAIL, BF16X>(X, qw, sc, zr, M, N, K, Y, sk, rowf, st);
@@ -718,13 +779,17 @@ hipError_t f16_go(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, con
 }  // namespace
 
 // Row tile and K split.  M <= 32 and M <= 64 take 32- and 64-row tiles (the
-// weight stream dominates there), larger M the 128-row tile.  When the tiles
+// weight stream dominates there), larger M the 128-row tile, and fp16 input
+// whose 256-row tiles fill every CU without a K split the 256-row tile.  When the tiles
 // cannot give every CU a workgroup, K is split into as many parts as still
 // fit in one round (at most 8, at least two K blocks each).  bf16 input adds
 // one fp32 activation factor per row to the workspace.
 GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16) {
   GemmPlan p{};
   p.mt = M <= 32 ? 2 : M <= 64 ? 4 : 8;
+  // fp16 X whose 256-row tiles alone fill every CU: the 256-row tile (each
+  // dequantized weight then feeds 16 MFMAs instead of 8)
+  if (!bf16 && K % kBK == 0 && ((M + 255) / 256) * ((N + kBN - 1) / kBN) >= kSlots) p.mt = 16;
   const int64_t bm = 16 * p.mt;
   p.tiles = ((M + bm - 1) / bm) * ((N + kBN - 1) / kBN);
   const int64_t nkb = (K + kBK - 1) / kBK;

@@ -99,6 +99,51 @@ def test_ragged_shapes(M, N, K, g, dt):
         assert np.array_equal(Y16, want.float().numpy().astype(np.float64))
 
 
+# --- the 256-row tile (fp16 X, activations staged by LDS DMA) --------------------
+
+def _takes_256_row_tile(M, N, K):
+    """The plan's rule: fp16 X, K a multiple of 128, and at least 256 tiles of
+    256 x 256 (so no K split)."""
+    return K % 128 == 0 and ((M + 255) // 256) * ((N + 255) // 256) >= 256
+
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_256_row_tile_one_hot_exact(g):
+    """One-hot rows through the 256-row tile: Y[r][n] = fp16(deq[n][r]) exactly,
+    for every row of a full 256-row tile and a ragged last column tile.  Any
+    misplaced 16-byte activation chunk in the DMA-staged LDS tile breaks it."""
+    torch = torch_mod()
+    M = K = 256
+    N = 65536 - 77
+    assert _takes_256_row_tile(M, N, K)
+    W = wl.gen_weight(N, K, 81)
+    qw, sc, zr, pd = _packed(W, g)
+    deq = dequantize(unpack_codes(qw, K), sc, zr, g).astype(np.float16).astype(np.float64)
+    X = np.eye(K, dtype=np.float16)
+    say("256-row tile one-hot", g, N)
+    Y = out_to_f64(_run(X, "f16", pd, g, GEMM, torch.float32))
+    assert np.array_equal(Y, deq.T)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(300, 32600, 384, 128), (1000, 16300, 256, 64)])
+def test_256_row_tile_ragged(M, N, K, g):
+    """Ragged M and N through the 256-row tile, fp32 and fp16 output, against
+    the oracle element by element."""
+    torch = torch_mod()
+    assert _takes_256_row_tile(M, N, K)
+    W = wl.gen_weight(N, K, 90 + M)
+    X = wl.gen_activation(M, K, 91 + M, 92, "f16")
+    qw, sc, zr, pd = _packed(W, g)
+    ref = linear64(X.astype(np.float64), qw, sc, zr, g)
+    say("256-row tile ragged", M, N, K, g)
+    Y32 = out_to_f64(_run(X, "f16", pd, g, GEMM, torch.float32))
+    assert_close(Y32, ref, f"{M}x{N}x{K} fp32 out")
+    Y16 = out_to_f64(_run(X, "f16", pd, g, GEMM))
+    assert_close(Y16, ref, f"{M}x{N}x{K} fp16 out")
+    want = torch.from_numpy(Y32).to(torch.float16)
+    assert np.array_equal(Y16, want.float().numpy().astype(np.float64))
+
+
 def test_bf16_rows_beyond_fp16_range():
     """The GEMM runs bf16 activations in fp16 after multiplying each row by
     the power of two that brings its largest magnitude to [2^14, 2^15).  Rows
