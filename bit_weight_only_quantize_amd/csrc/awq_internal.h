@@ -46,6 +46,7 @@ struct GemmPlan {
   int64_t tiles;
   size_t counter_bytes;    // fixed-size u32 counter region (zero between launches)
   size_t rowf_offset;      // bf16 input: per-row activation factors (fp32 [M])
+  size_t xh_offset;        // bf16 input, 256-row tile: X scaled to fp16 ([M][K]), else 0
   size_t workspace_bytes;  // 0 when splits == 1 and the input is fp16
 };
 // The plan of the kernel that serves activations of type xt (fp16: the

@@ -118,7 +118,9 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // The 256-row tile's 256 accumulators fill the AGPRs: its activations go to
   // LDS by DMA (buffer_load ... lds), without staging registers.
   constexpr bool kDMA = MT == 16;
-  static_assert(!(kDMA && (BF16X || kExact)), "the 256-row tile takes fp16 X and stores Y");
+  // (bf16 input reaches it already scaled and converted to fp16 by the row
+  // prescan; only the epilogue's row factors remain)
+  static_assert(!(kDMA && kExact), "the 256-row tile stores Y");
 
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kBM * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBM * kBK];
@@ -291,7 +293,7 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // which the factor guarantees for the row's largest value; smaller values
   // below that range are truncated to fp16 subnormals.
   float rf[kARounds];
-  if constexpr (BF16X) {
+  if constexpr (BF16X && !kDMA) {
     const rsrc_t rR = make_rsrc(rowf, (uint32_t)M * 4u);
 #pragma unroll
     for (int r = 0; r < kARounds; ++r) {
@@ -673,10 +675,14 @@ void gemm_f16_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict_
 // row's largest magnitude into [2^14, 2^15), so every value of the row is
 // within fp16's range and those within 2^38 of the largest keep their full
 // precision (exponent capped to stay a normal fp32); 1 for rows that are all
-// zero or hold inf or NaN.  One workgroup per row.
+// zero or hold inf or NaN.  One workgroup per row.  With Xh, the row is also
+// written there multiplied by its factor and converted to fp16 (round toward
+// zero, as the GEMM's own staging does), for the 256-row tile.
 __global__ __launch_bounds__(256) void bf16_row_factor_kernel(const uint16_t *__restrict__ X,
-                                                              int K, float *__restrict__ rowf) {
+                                                              int K, float *__restrict__ rowf,
+                                                              uint16_t *__restrict__ Xh) {
   __shared__ float red[4];
+  __shared__ float fsh;
   const int64_t row = blockIdx.x;
   const rsrc_t rX = make_rsrc(X + row * K, (uint32_t)K * 2u);
   float mx = 0.0f;
@@ -706,6 +712,22 @@ __global__ __launch_bounds__(256) void bf16_row_factor_kernel(const uint16_t *__
       f = __builtin_bit_cast(float, (uint32_t)(127 + e) << 23);
     }
     rowf[row] = f;
+    fsh = f;
+  }
+  if (!Xh) return;
+  __syncthreads();
+  const float f = fsh;
+  const rsrc_t rH = make_rsrc(Xh + row * K, (uint32_t)K * 2u);
+  for (int c = threadIdx.x; c * 8 < K; c += 256) {
+    u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, (uint32_t)c * 16u, 0, 0));
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const uint32_t u = v[x];
+      const float lo = __builtin_bit_cast(float, u << 16) * f;
+      const float hi = __builtin_bit_cast(float, u & 0xFFFF0000u) * f;
+      v[x] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(v, rH, (uint32_t)c * 16u, 0, 0);
   }
 }
 
@@ -746,10 +768,10 @@ template <int GS, int YT, bool KTAIL, bool BF16X>
 hipError_t f16_go3(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, const uint8_t *zr,
                    int64_t M, int64_t N, int64_t K, void *Y, int mt, SplitK sk, const float *rowf,
                    hipStream_t st) {
-  if constexpr (!BF16X && !KTAIL) {
+  if constexpr (!KTAIL) {
     if (mt == 16) {
       if (sk.splits > 1) return hipErrorInvalidValue;
-      return f16_launch_mt<GS, YT, 16, KTAIL, false>(X, qw, sc, zr, M, N, K, Y, sk, rowf, st);
+      return f16_launch_mt<GS, YT, 16, KTAIL, BF16X>(X, qw, sc, zr, M, N, K, Y, sk, rowf, st);
     }
   }
   if (mt == 2) return f16_launch_mt<GS, YT, 2, KTAIL, BF16X>(X, qw, sc, zr, M, N, K, Y, sk, rowf, st);
@@ -780,16 +802,17 @@ hipError_t f16_go(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, con
 
 // Row tile and K split.  M <= 32 and M <= 64 take 32- and 64-row tiles (the
 // weight stream dominates there), larger M the 128-row tile, and fp16 input
-// whose 256-row tiles fill every CU without a K split the 256-row tile.  When the tiles
+// whose 256-row tiles fill every CU without a K split the 256-row tile (bf16
+// input then takes its fp16 copy, scaled by the row factors, in the workspace).  When the tiles
 // cannot give every CU a workgroup, K is split into as many parts as still
 // fit in one round (at most 8, at least two K blocks each).  bf16 input adds
 // one fp32 activation factor per row to the workspace.
 GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16) {
   GemmPlan p{};
   p.mt = M <= 32 ? 2 : M <= 64 ? 4 : 8;
-  // fp16 X whose 256-row tiles alone fill every CU: the 256-row tile (each
+  // 256-row tiles that alone fill every CU: the 256-row tile (each
   // dequantized weight then feeds 16 MFMAs instead of 8)
-  if (!bf16 && K % kBK == 0 && ((M + 255) / 256) * ((N + kBN - 1) / kBN) >= kSlots) p.mt = 16;
+  if (K % kBK == 0 && ((M + 255) / 256) * ((N + kBN - 1) / kBN) >= kSlots) p.mt = 16;
   const int64_t bm = 16 * p.mt;
   p.tiles = ((M + bm - 1) / bm) * ((N + kBN - 1) / kBN);
   const int64_t nkb = (K + kBK - 1) / kBK;
@@ -811,6 +834,10 @@ GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16) {
     const size_t after = bytes > kSplitCounterBytes ? bytes : kSplitCounterBytes;
     p.rowf_offset = (after + 255) / 256 * 256;
     bytes = p.rowf_offset + (size_t)M * 4;
+    if (p.mt == 16) {
+      p.xh_offset = (bytes + 255) / 256 * 256;
+      bytes = p.xh_offset + (size_t)M * (size_t)K * 2;
+    }
   }
   p.workspace_bytes = bytes;
   return p;
@@ -831,9 +858,12 @@ hipError_t launch_gemm_f16(const uint16_t *X, bool bf16, const uint32_t *qweight
   float *rowf = nullptr;
   if (bf16) {
     rowf = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + p.rowf_offset);
-    bf16_row_factor_kernel<<<dim3((unsigned)M), 256, 0, st>>>(X, (int)K, rowf);
+    uint16_t *xh = p.xh_offset ? reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(workspace) + p.xh_offset)
+                               : nullptr;
+    bf16_row_factor_kernel<<<dim3((unsigned)M), 256, 0, st>>>(X, (int)K, rowf, xh);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (xh) X = xh;
   }
   if (gs == 128) {
     if (yt == YType::F32) return f16_go<128, (int)YType::F32>(X, qweight, scales, zeros, M, N, K, Y, p.mt, sk, rowf, st);

@@ -118,7 +118,9 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
  * scale and accumulated in fp32 across groups; Y is rounded once to y_dtype.
  * Dispatch: M <= AWQ_GEMV_MAX_M uses the GEMV kernel, larger M the MFMA
  * GEMM.  When its tiles alone cannot fill the GPU, the GEMM splits K
- * across workgroups and needs a scratch buffer (see awq_linear_ws): awq_linear
+ * across workgroups and needs a scratch buffer (see awq_linear_ws); bf16
+ * activations need one too (a factor per row, and for shapes large enough
+ * for the 256-row tile an fp16 copy of X, M * K * 2 bytes): awq_linear
  * and awq_linear_ex take it from a per-device buffer the library allocates the
  * first time a shape needs it (or needs more) and keeps until the process
  * ends.  Consequently (a) inside a HIP-graph capture, first call the same

@@ -125,22 +125,41 @@ def test_256_row_tile_one_hot_exact(g):
     assert np.array_equal(Y, deq.T)
 
 
-@pytest.mark.parametrize("M,N,K,g", [(300, 32600, 384, 128), (1000, 16300, 256, 64)])
-def test_256_row_tile_ragged(M, N, K, g):
-    """Ragged M and N through the 256-row tile, fp32 and fp16 output, against
-    the oracle element by element."""
+@pytest.mark.parametrize("M,N,K,g,dt", [(300, 32600, 384, 128, "f16"), (1000, 16300, 256, 64, "f16"),
+                                        (300, 32600, 384, 128, "bf16")])
+def test_256_row_tile_ragged(M, N, K, g, dt):
+    """Ragged M and N through the 256-row tile, fp32 and 16-bit output, against
+    the oracle element by element.  bf16 X goes through the row prescan's
+    scaled fp16 copy; some of its rows lie far outside fp16's range (up to
+    ~1e8) or deep in its subnormals, and are held to the tolerance row by row
+    relative to their own magnitude."""
     torch = torch_mod()
     assert _takes_256_row_tile(M, N, K)
     W = wl.gen_weight(N, K, 90 + M)
     X = wl.gen_activation(M, K, 91 + M, 92, "f16")
+    if dt == "bf16":
+        x = X.astype(np.float32)
+        x[3] *= 3.0e6
+        x[7] *= 1.0e-6
+        x[260, 5] = 2.0e9            # second row tile
+        x[299] *= 7.0e4              # last row
+        X = wl.f32_to_bf16_bits(x)
     qw, sc, zr, pd = _packed(W, g)
-    ref = linear64(X.astype(np.float64), qw, sc, zr, g)
-    say("256-row tile ragged", M, N, K, g)
-    Y32 = out_to_f64(_run(X, "f16", pd, g, GEMM, torch.float32))
-    assert_close(Y32, ref, f"{M}x{N}x{K} fp32 out")
-    Y16 = out_to_f64(_run(X, "f16", pd, g, GEMM))
-    assert_close(Y16, ref, f"{M}x{N}x{K} fp16 out")
-    want = torch.from_numpy(Y32).to(torch.float16)
+    ref = linear64(_x_f64(X, dt), qw, sc, zr, g)
+    say("256-row tile ragged", M, N, K, g, dt)
+    Y32 = out_to_f64(_run(X, dt, pd, g, GEMM, torch.float32))
+    if dt == "f16":
+        assert_close(Y32, ref, f"{M}x{N}x{K} fp32 out")
+    else:
+        assert np.isfinite(Y32).all()
+        for r in range(M):
+            err = Y32[r] - ref[r]
+            assert np.linalg.norm(err) <= REL_FRO * np.linalg.norm(ref[r]), f"row {r}"
+            assert np.max(np.abs(err)) <= REL_FRO * np.max(np.abs(ref[r])), f"row {r}"
+    Y16 = out_to_f64(_run(X, dt, pd, g, GEMM))
+    if dt == "f16":
+        assert_close(Y16, ref, f"{M}x{N}x{K} fp16 out")
+    want = torch.from_numpy(Y32).to(torch.float16 if dt == "f16" else torch.bfloat16)
     assert np.array_equal(Y16, want.float().numpy().astype(np.float64))
 
 
