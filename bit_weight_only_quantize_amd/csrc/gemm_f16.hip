@@ -27,8 +27,11 @@
 //    layout measured free of bank conflicts for the fragment reads.
 //  * Only ordinary loads are in flight, so counted vmcnt waits keep a window
 //    of kWin weight blocks streaming from HBM while the math runs.
-//  * Split K (when the M x N tiles cannot fill the CUs) and its fence-free
-//    fixup follow the scheme of the other GEMM kernels of this library.
+//  * Split K (when the M x N tiles cannot fill the CUs): the workgroups of a
+//    tile exchange fp32 partial tiles without fences, through arrival and
+//    completion counters; the last to arrive sums them in split order.
+//  * The 256-row tile (large M) stages activations by LDS DMA and never
+//    splits K.
 //  * Tiles are visited in groups of four row tiles, row index fastest, so the
 //    workgroups resident on one XCD share activation rows and weight columns
 //    in that XCD's L2.
