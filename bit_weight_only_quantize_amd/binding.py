@@ -208,8 +208,8 @@ def awq_linear_workspace_size(M: int, N: int, K: int, group_size: int = 128) -> 
 
 def awq_linear_ws(X, qweight, scales, zeros, workspace, group_size: int = 128, out_dtype=None,
                   out=None):
-    """awq_linear with a caller workspace (uint8 tensor, zero-filled before first use,
-    at least awq_linear_workspace_size bytes); the call allocates nothing."""
+    """awq_linear with a caller workspace (uint8 tensor of at least
+    awq_linear_workspace_size bytes, any contents); the call allocates nothing."""
     torch = _torch()
     if X.dim() != 2:
         raise TypeError("X must be 2-D")

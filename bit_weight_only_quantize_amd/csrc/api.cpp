@@ -40,11 +40,11 @@ awq_status hip_status(hipError_t e, const char *where) {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Split-K scratch of awq_linear / awq_linear_ex, one per device, allocated the
-// first time a call needs it (or needs more).  A buffer is never freed: a
-// larger one replaces it for later calls, and HIP graphs captured with the
-// old one stay valid.  Split counters start at zero and every launch leaves
-// them at zero.
+// GEMM scratch of awq_linear / awq_linear_ex (split-K partials, bf16 row
+// factors and converted rows), one per device, allocated the first time a
+// call needs it (or needs more).  A buffer is never freed: a larger one
+// replaces it for later calls, and HIP graphs captured with the old one stay
+// valid.  Its contents between calls do not matter.
 struct Scratch {
   void *ptr = nullptr;
   size_t bytes = 0;
@@ -62,8 +62,6 @@ hipError_t linear_scratch(size_t bytes, void **out) {
     const size_t want = bytes > 2 * s.bytes ? bytes : 2 * s.bytes;
     void *p = nullptr;
     e = hipMalloc(&p, want);
-    if (e != hipSuccess) return e;
-    e = hipMemset(p, 0, want);
     if (e != hipSuccess) return e;
     s.ptr = p;
     s.bytes = want;

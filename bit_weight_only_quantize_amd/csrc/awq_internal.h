@@ -32,30 +32,25 @@ hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,
 // u32 counter per tile (zero between launches) and the fp32 partial tiles.
 struct SplitK {
   int splits;
-  uint32_t *counters;
-  float *partials;
+  float *partials;   // [tile][split] fp32 partial tiles, summed by a second kernel
 };
-// The counters sit in a fixed region at the start of the workspace (the
-// partials of one shape never overlap the counters of another).
-constexpr size_t kSplitCounterBytes = 512 * 4;
 
-// ---- linear_gemm.hip (any M) ---------------------------------------------------
-// Row tile (32 * mt rows), K split and split-K workspace of a quantized GEMM.
+// ---- the quantized GEMM (any M) -------------------------------------------------
+// Row tile (16 * mt rows), K split and workspace of a quantized GEMM.
 struct GemmPlan {
   int mt, splits;
   int64_t tiles;
-  size_t counter_bytes;    // fixed-size u32 counter region (zero between launches)
   size_t rowf_offset;      // bf16 input: per-row activation factors (fp32 [M])
   size_t xh_offset;        // bf16 input, 256-row tile: X scaled to fp16 ([M][K]), else 0
-  size_t workspace_bytes;  // 0 when splits == 1 and the input is fp16
+  size_t workspace_bytes;  // 0 when splits == 1 and the input is fp16; partials first
 };
 // The plan of the kernel that serves activations of type xt (fp16: the
 // kernel of gemm_f16.hip).
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, XType xt);
 // Workspace that serves either activation type.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
-// `workspace` (gemm_plan(...).workspace_bytes, 256-byte aligned, counters
-// zeroed once) is needed only when the plan splits K.
+// `workspace` (gemm_plan(...).workspace_bytes, 256-byte aligned; its contents
+// on entry are ignored) is needed only when the plan's workspace_bytes > 0.
 hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M,
                        int64_t N, int64_t K, int gs, void *Y, YType yt,

@@ -27,9 +27,9 @@
 //    layout measured free of bank conflicts for the fragment reads.
 //  * Only ordinary loads are in flight, so counted vmcnt waits keep a window
 //    of kWin weight blocks streaming from HBM while the math runs.
-//  * Split K (when the M x N tiles cannot fill the CUs): the workgroups of a
-//    tile exchange fp32 partial tiles without fences, through arrival and
-//    completion counters; the last to arrive sums them in split order.
+//  * Split K (when the M x N tiles cannot fill the CUs): every split stores
+//    its fp32 partial tile and a second kernel, spread over all CUs, sums
+//    them in split order (deterministic) and stores Y.
 //  * The 256-row tile (large M) stages activations by LDS DMA and never
 //    splits K.
 //  * Tiles are visited in groups of four row tiles, row index fastest, so the
@@ -53,9 +53,8 @@ constexpr int kBK = 128;          // input channels per K block
 constexpr int kSteps = kBK / 32;  // MFMA K steps per block
 constexpr int kGroupRows = 4;     // row tiles per tile group
 // One workgroup per CU; K is split only when there are fewer tiles than
-// slots, and the split-K counters of tile t sit at t and kSlots + t.
+// slots (CUs).
 constexpr int kSlots = 256;
-static_assert(2 * kSlots * 4 <= (int)kSplitCounterBytes, "split-K counters");
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -96,6 +95,17 @@ __device__ __forceinline__ void tile_order() {
   }
 }
 
+// Row and column tile of tile index t: groups of kGroupRows row tiles, row
+// index fastest within a group.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int per = kGroupRows * tiles_n;
+  const int grp = t / per, first = grp * kGroupRows;
+  const int rows = tiles_m - first < kGroupRows ? tiles_m - first : kGroupRows;
+  const int r = t - grp * per;
+  tm = first + r % rows;
+  tn = r / rows;
+}
+
 }  // namespace
 
 // EPI: 0 stores Y with fp16-dequantized weights; 1 (the search's loss) uses
@@ -129,7 +139,6 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBM * kBK];
   __shared__ __attribute__((aligned(16))) uint32_t sSZ0[256 * kGPB];
   __shared__ __attribute__((aligned(16))) uint32_t sSZ1[256 * kGPB];
-  __shared__ uint32_t s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -144,14 +153,7 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   const int bid = (int)xcd_remap(blockIdx.x, (int64_t)gridDim.x);
   const int tile = bid % tiles, split = bid / tiles;
   int tm, tn;
-  {
-    const int per = kGroupRows * tiles_n;
-    const int grp = tile / per, first = grp * kGroupRows;
-    const int rows = tiles_m - first < kGroupRows ? tiles_m - first : kGroupRows;
-    const int r = tile - grp * per;
-    tm = first + r % rows;
-    tn = r / rows;
-  }
+  tile_coords(tile, tiles_m, tiles_n, tm, tn);
   const int row0 = tm * kBM, col0 = tn * kBN;
 
   const int G = K / GS;
@@ -519,76 +521,25 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     if (k + u < kb_end) step(k + u, u);
   wait_vmem_all();
 
-  // ---- split K: the last workgroup of a tile sums the partial tiles -----------
-  // Each workgroup first takes an arrival ticket (an atomic on the tile's
-  // counter).  All but the last store their fp32 partial tile and then count
-  // themselves done on a second counter; the last keeps its own partial in
-  // registers, waits until the others are done, reads theirs and adds all of
-  // them in split order (the same sum whichever workgroup arrives last), then
-  // resets both counters for the next launch.  The partials cross workgroups
-  // that may sit on different XCDs, whose L2s are not coherent with each
-  // other: they are stored write-through and read back bypassing both cache
-  // levels (sc0 sc1), the counters are atomics (coherent across XCDs), and
-  // vmcnt(0) orders a workgroup's stores before its done count.  The wait
-  // ends: every other workgroup of the tile already holds a ticket, so it is
-  // resident and finishes its stores.
-  // (not compiled for the 256-row tile, which the plan never splits: its
-  // partial-sum registers would not fit beside the accumulators)
+  // ---- split K: store this split's partial tile --------------------------------
+  // Layout [tile][split][wave][16x16 tile][lane] of 16 bytes.  Plain stores:
+  // the kernel boundary makes them visible to the reduction kernel, which
+  // sums the splits in order and stores Y.  (Not compiled for the 256-row
+  // tile, which the plan never splits.)
   if (!kDMA && sk.splits > 1) {
     constexpr int kTiles = MT * kNT;     // f32x4 accumulators per lane
-    constexpr int kSys = 1 | 16;         // sc0 | sc1
-    // layout: [tile][split][wave][16x16 tile][lane] of 16 bytes
     const uint32_t wave_bytes = (uint32_t)kTiles * 64u * 16u;
     const uint32_t tile_bytes = 4u * wave_bytes;
     const rsrc_t rP = make_rsrc(sk.partials, 0x7FFFFFF0u);
-    const uint32_t lane_off = (uint32_t)wave * wave_bytes + (uint32_t)lane * 16u;
-    const uint32_t base = (uint32_t)tile * (uint32_t)sk.splits * tile_bytes + lane_off;
-    uint32_t *arrive = sk.counters + tile;
-    uint32_t *done = sk.counters + kSlots + tile;
-    if (tid == 0) s_last = atomicAdd(arrive, 1u) == (uint32_t)(sk.splits - 1);
-    __syncthreads();
-    if (!s_last) {
-      const uint32_t mine = base + (uint32_t)split * tile_bytes;
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < kNT; ++j) {
-          const f32x4 v = acc[i][j];
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rP,
-                                                 mine + (uint32_t)(i * kNT + j) * 1024u, 0, kSys);
-        }
-      wait_vmem_all();
-      __syncthreads();
-      if (tid == 0) atomicAdd(done, 1u);
-      return;
-    }
-    if (tid == 0) {
-      while (atomicAdd(done, 0u) != (uint32_t)(sk.splits - 1)) __builtin_amdgcn_s_sleep(2);
-    }
-    __syncthreads();
-    f32x4 own[MT][kNT];
+    const uint32_t mine = ((uint32_t)tile * (uint32_t)sk.splits + (uint32_t)split) * tile_bytes +
+                          (uint32_t)wave * wave_bytes + (uint32_t)lane * 16u;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) own[i][j] = acc[i][j];
-    for (int sp = 0; sp < sk.splits; ++sp) {
-      const uint32_t p = base + (uint32_t)sp * tile_bytes;
-      const bool self = sp == split;
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < kNT; ++j) {
-          const f32x4 v =
-              self ? own[i][j]
-                   : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rP, p + (uint32_t)(i * kNT + j) * 1024u, 0, kSys));
-          acc[i][j] = sp == 0 ? v : acc[i][j] + v;
-        }
-    }
-    if (tid == 0) {
-      atomicExch(arrive, 0u);                 // ready for the next launch
-      atomicExch(done, 0u);
-    }
+      for (int j = 0; j < kNT; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rP,
+                                               mine + (uint32_t)(i * kNT + j) * 1024u, 0, 0);
+    return;
   }
 
   // ---- epilogue: lane (c, kq) holds rows 4*kq + e of column c of each tile ------
@@ -672,6 +623,59 @@ void gemm_f16_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict_
                      double *__restrict__ partials) {
   gemm_f16_body<GS, YT, MT, KTAIL, BF16X, EPI>(X, qweight, scales, zeros, M, N, K, Y, sk, rowf,
                                                Yref, partials);
+}
+
+// Second pass of a split-K GEMM: one thread per 16-byte partial fragment
+// (lane l of 16x16 tile t of wave w of a tile) sums the splits' fragments in
+// split order and stores its four outputs (rows 4*(l >> 4) + e of column
+// l & 15).  Every CU takes a share of the partials: summing them in the GEMM
+// kernel's last workgroup of each tile was bound by that one CU's load
+// bandwidth (measured 25% slower at 6 splits, 3% at 2).
+template <int YT, int MT, bool BF16X>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ partials,
+                                                            int splits, int M, int N,
+                                                            void *__restrict__ Y,
+                                                            const float *__restrict__ rowf) {
+  constexpr int kTiles = MT * kNT;
+  constexpr int kBM = 16 * MT;
+  const int tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM;
+  const int64_t total = (int64_t)tiles_m * tiles_n * 4 * kTiles * 64;
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= total) return;
+  const int lane = (int)(q & 63);
+  int64_t r = q >> 6;
+  const int t = (int)(r % kTiles);
+  r /= kTiles;
+  const int wave = (int)(r & 3);
+  const int tile = (int)(r >> 2);
+  int tm, tn;
+  tile_coords(tile, tiles_m, tiles_n, tm, tn);
+  // [tile][split][wave][t][lane] of f32x4
+  const int64_t split_stride = (int64_t)4 * kTiles * 64;
+  const f32x4 *p = reinterpret_cast<const f32x4 *>(partials) +
+                   (int64_t)tile * splits * split_stride + ((int64_t)wave * kTiles + t) * 64 + lane;
+  f32x4 sum = p[0];
+  for (int sp = 1; sp < splits; ++sp) sum += p[sp * split_stride];
+  const int c = lane & 15, kq = lane >> 4, i = t / kNT, j = t % kNT;
+  const int n = tn * kBN + wave * 64 + j * 16 + c;
+  if (n >= N) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int m = tm * kBM + i * 16 + 4 * kq + e;
+    if (m >= M) break;
+    float v = sum[e];
+    if constexpr (BF16X) {
+      const float f = rowf[m];
+      v *= f > 0.0f ? 1.0f / f : 1.0f;
+    }
+    const int64_t o = (int64_t)m * N + n;
+    if constexpr (YT == (int)YType::F16)
+      reinterpret_cast<uint16_t *>(Y)[o] = float_to_half_bits(v);
+    else if constexpr (YT == (int)YType::BF16)
+      reinterpret_cast<uint16_t *>(Y)[o] = float_to_bf16_bits(v);
+    else
+      reinterpret_cast<float *>(Y)[o] = v;
+  }
 }
 
 // Per-row activation factor for bf16 input: the power of two that brings the
@@ -761,8 +765,17 @@ hipError_t f16_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *
     gemm_f16_kernel<GS, YT, MT, KTAIL, BF16X, 0><<<grid, kThreads, 0, st>>>(
         X + m0 * K, qw, sc, zr, (int)mm, (int)N, (int)K, y, sk, rowf ? rowf + m0 : nullptr,
         nullptr, nullptr);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if constexpr (MT < 16) {
+      if (sk.splits > 1) {
+        const int64_t frags = tiles * 4 * (MT * kNT) * 64;
+        splitk_reduce_kernel<YT, MT, BF16X><<<dim3((unsigned)((frags + 255) / 256)), 256, 0, st>>>(
+            sk.partials, sk.splits, (int)mm, (int)N, y, rowf ? rowf + m0 : nullptr);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+    }
   }
   return hipSuccess;
 }
@@ -827,15 +840,9 @@ GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16) {
     p.splits = sp > 1 ? (int)sp : 1;
   }
   size_t bytes = 0;
-  if (p.splits > 1) {
-    p.counter_bytes = kSplitCounterBytes;
-    bytes = p.counter_bytes + (size_t)p.tiles * p.splits * bm * kBN * 4;
-  }
+  if (p.splits > 1) bytes = (size_t)p.tiles * p.splits * bm * kBN * 4;   // partials
   if (bf16) {
-    // never inside the counter region, which other calls sharing the
-    // workspace expect to find zeroed
-    const size_t after = bytes > kSplitCounterBytes ? bytes : kSplitCounterBytes;
-    p.rowf_offset = (after + 255) / 256 * 256;
+    p.rowf_offset = (bytes + 255) / 256 * 256;
     bytes = p.rowf_offset + (size_t)M * 4;
     if (p.mt == 16) {
       p.xh_offset = (bytes + 255) / 256 * 256;
@@ -852,11 +859,10 @@ hipError_t launch_gemm_f16(const uint16_t *X, bool bf16, const uint32_t *qweight
   if (M == 0 || N == 0) return hipSuccess;
   const GemmPlan p = gemm_f16_plan(M, N, K, bf16);
   if (p.workspace_bytes > 0 && !workspace) return hipErrorInvalidValue;
-  SplitK sk{1, nullptr, nullptr};
+  SplitK sk{1, nullptr};
   if (p.splits > 1) {
     sk.splits = p.splits;
-    sk.counters = reinterpret_cast<uint32_t *>(workspace);
-    sk.partials = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + p.counter_bytes);
+    sk.partials = reinterpret_cast<float *>(workspace);
   }
   float *rowf = nullptr;
   if (bf16) {
@@ -895,7 +901,7 @@ static hipError_t loss_go(const uint16_t *A, const uint32_t *qw, const uint16_t 
     const int64_t mm = M - m0 < rows ? M - m0 : rows;
     const int64_t tiles = ((mm + bm - 1) / bm) * ((N + kBN - 1) / kBN);
     gemm_f16_kernel<GS, (int)YType::F32, 8, KTAIL, false, 1><<<dim3((unsigned)tiles), kThreads, 0, st>>>(
-        A + m0 * K, qw, sc, zr, (int)mm, (int)N, (int)K, nullptr, SplitK{1, nullptr, nullptr},
+        A + m0 * K, qw, sc, zr, (int)mm, (int)N, (int)K, nullptr, SplitK{1, nullptr},
         nullptr, Yref + m0 * N, partials + tile_base);
     tile_base += tiles;
     const hipError_t e = hipGetLastError();

@@ -381,7 +381,7 @@ static hipError_t gemm_go(const uint16_t *X, const uint32_t *qw, const uint16_t 
                           void *Y, const float *Yref, double *partials, hipStream_t st) {
   constexpr int MT = 8;
   constexpr int64_t bm = 32 * MT;
-  const SplitK sk{1, nullptr, nullptr};
+  const SplitK sk{1, nullptr};
   const int64_t rows = rows_per_launch(N, K, bm);
   if (rows <= 0) return hipErrorInvalidValue;
   int64_t tile_base = 0;

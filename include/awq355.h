@@ -158,10 +158,10 @@ size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg
  * Cites: as awq_linear.
  *
  *   workspace  device, at least awq_linear_workspace_size() bytes, 256-byte
- *            aligned, zero-filled before its first use.  Its first 2 KiB hold
- *            counters that every call leaves at zero again (the rest is
- *            scratch), so it can be reused by later calls (of any shape)
- *            without clearing.  May be NULL when the size is 0.
+ *            aligned.  Scratch only: its contents on entry are ignored and
+ *            on return are unspecified, so it needs no clearing and can be
+ *            reused by later calls of any shape.  May be NULL when the size
+ *            is 0.
  *   Calls that share a workspace must not overlap in time.
  * Errors: AWQ_ERR_WORKSPACE when workspace_bytes is too small; otherwise as
  * awq_linear.
