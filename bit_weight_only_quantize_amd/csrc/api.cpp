@@ -70,6 +70,17 @@ hipError_t linear_scratch(size_t bytes, void **out) {
   return hipSuccess;
 }
 
+// Automatic kernel choice (measured on MI355X, fp16, graph replays): the GEMV
+// up to M = 8; from 9 to AWQ_GEMV_MAX_M rows only for layers of at most 5e7
+// weights.  Above that the GEMV, whose activation reads grow with M once the
+// rows no longer fit its LDS staging, is slower than the split-K GEMM (at
+// M = 16: 28.7 vs 22.0 us for 13824 x 5120; the GEMV stays ahead on the
+// 4096 x 4096 and 4096 x 11008 layers).
+bool auto_gemv(int64_t M, int64_t N, int64_t K, int g) {
+  if (M > AWQ_GEMV_MAX_M || !awq::gemv_supported(M, K, g)) return false;
+  return M <= 8 || N * K <= 50000000;
+}
+
 awq_status check_config(awq_config cfg, int64_t K) {
   if (cfg.w_bit != 4) return fail(AWQ_ERR_UNSUPPORTED, "w_bit=%d: only 4 is supported", cfg.w_bit);
   if (cfg.zero_point != 1)
@@ -229,9 +240,8 @@ awq_status linear_impl(const void *X, int32_t x_dtype, const uint32_t *qweight,
   const bool gemv_ok = awq::gemv_supported(M, K, cfg.group_size);
   if (kernel == AWQ_KERNEL_GEMV && !gemv_ok)
     return fail(AWQ_ERR_UNSUPPORTED, "GEMV kernel cannot serve K=%lld", (long long)K);
-  // Automatic choice: the GEMV for M <= AWQ_GEMV_MAX_M, the GEMM above.
   const bool gemv = kernel == AWQ_KERNEL_GEMV ||
-                    (kernel == AWQ_KERNEL_AUTO && M <= AWQ_GEMV_MAX_M && gemv_ok);
+                    (kernel == AWQ_KERNEL_AUTO && auto_gemv(M, N, K, cfg.group_size));
   if (caller_ws && !gemv && plan.workspace_bytes > 0) {
     if (!workspace) return fail(AWQ_ERR_INVALID_ARG, "this shape needs a workspace");
     if (!aligned(workspace, 256)) return fail(AWQ_ERR_INVALID_ARG, "workspace not 256-byte aligned");
@@ -273,7 +283,7 @@ awq_status awq_linear_ex(const void *X, int32_t x_dtype, const uint32_t *qweight
 size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg) {
   if (check_config(cfg, K) != AWQ_OK || M < 0 || N < 0) return 0;
   if (M == 0 || N == 0) return 0;
-  if (M <= AWQ_GEMV_MAX_M && awq::gemv_supported(M, K, cfg.group_size)) return 0;
+  if (auto_gemv(M, N, K, cfg.group_size)) return 0;
   return awq::gemm_workspace_bytes(M, N, K);
 }
 

@@ -113,20 +113,25 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
  *   qweight, scales, zeros: as produced by awq_quantize_pack for [N][K].
  *   Y        device, [M][N] of y_dtype (AWQ_F16, AWQ_BF16 or AWQ_F32).
  *
- * Products are formed from the exact integer (code - zero) and the 16-bit
+ * Dispatch: the GEMV kernel for M <= 8, and for M <= AWQ_GEMV_MAX_M when
+ * N * K <= 5e7 (where it measured faster); otherwise the MFMA GEMM.
+ * GEMV: products of the exact integer (code - zero) and the 16-bit
  * activation, accumulated in fp32 within a group, multiplied by the group's
- * scale and accumulated in fp32 across groups; Y is rounded once to y_dtype.
- * Dispatch: M <= AWQ_GEMV_MAX_M uses the GEMV kernel, larger M the MFMA
- * GEMM.  When its tiles alone cannot fill the GPU, the GEMM splits K
+ * scale and accumulated in fp32 across groups.  GEMM: the dequantized weight
+ * (code - zero) * scale is rounded once to fp16 (relative error <= 2^-11),
+ * as the pages' GEMM kernels dequantize to fp16, and the products are
+ * accumulated in fp32; bf16 activations are scaled per row by a power of two
+ * into fp16's range (exact) and the row's output divided by it.  Y is rounded
+ * once to y_dtype.  When its tiles alone cannot fill the GPU, the GEMM splits K
  * across workgroups and needs a scratch buffer (see awq_linear_ws); bf16
  * activations need one too (a factor per row, and for shapes large enough
  * for the 256-row tile an fp16 copy of X, M * K * 2 bytes): awq_linear
  * and awq_linear_ex take it from a per-device buffer the library allocates the
  * first time a shape needs it (or needs more) and keeps until the process
  * ends.  Consequently (a) inside a HIP-graph capture, first call the same
- * shape once outside the capture; (b) split-K calls on one device that may
- * overlap in time (different streams) share that buffer and must instead use
- * awq_linear_ws with a workspace each.
+ * shape once outside the capture; (b) calls on one device that need the
+ * scratch and may overlap in time (different streams) share that buffer and
+ * must instead use awq_linear_ws with a workspace each.
  * Requirements: M, N >= 0, K > 0, K % g == 0.  M == 0 or N == 0 is a no-op.
  */
 awq_status awq_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,
