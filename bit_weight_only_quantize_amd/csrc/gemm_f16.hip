@@ -1,4 +1,5 @@
-// Batched / prefill W4A16 GEMM for fp16 activations on gfx950 MFMA.
+// Batched / prefill W4A16 GEMM on gfx950 MFMA: fp16 activations, bf16 ones
+// scaled into fp16 per row, and the scale search's loss GEMM.
 //
 // The GEMM variant of the quantized linear layer ("AWQ Advanced Usage Guide",
 // "WQLinear Kernel Variants": batch sizes above one), Y = X * deq(W)^T with
@@ -7,7 +8,9 @@
 // it dequantizes each weight to fp16 and runs an fp16 matrix product with
 // fp32 accumulation: the B operand is fp16((q - z) * s), the exact integer
 // q - z times the group's fp16 scale rounded once (relative error at most
-// 2^-11 per weight).
+// 2^-11 per weight).  The search's loss variant (EPI = 1) keeps B the exact
+// integer q - z, scales each group's fp32 sum, and reduces (Yref - Y)^2 of
+// its tile instead of storing Y.
 //
 // Work split, chosen from measured MI355X rates (one wave keeps the MFMA unit
 // busy when it issues about two VALU operations or fewer per 16x16x32 MFMA;
@@ -21,12 +24,12 @@
 //    zero point (exact), 4 packed multiplies by the scale (rounded once).  A
 //    block's 16 words per lane are dequantized while the previous block's
 //    MFMAs run, so the VALU work overlaps the matrix core.
-//  * Activations are staged through registers into LDS, double-buffered.
-//    16-byte chunk c of block row r lives at chunk c ^ (r % 16) ^ f(c), where
-//    f flips bit 3 for the odd lane quarters of an MFMA fragment read: that
-//    layout measured free of bank conflicts for the fragment reads.
-//  * Only ordinary loads are in flight, so counted vmcnt waits keep a window
-//    of kWin weight blocks streaming from HBM while the math runs.
+//  * Activations are double-buffered in LDS: 16-byte chunk c of block row r
+//    lives at chunk c ^ (r % 16) ^ f(c), where f flips bit 3 for the odd lane
+//    quarters of an MFMA fragment read (measured free of bank conflicts).
+//    Tiles of up to 128 rows stage them through registers, so only ordinary
+//    loads are in flight and counted vmcnt waits keep a window of kWin
+//    weight blocks streaming from HBM while the math runs.
 //  * Split K (when the M x N tiles cannot fill the CUs): every split stores
 //    its fp32 partial tile and a second kernel, spread over all CUs, sums
 //    them in split order (deterministic) and stores Y.
@@ -612,8 +615,8 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   }
 }
 
-// One wave per SIMD: accumulators, two dequantized blocks and a four-block
-// weight window live in registers.
+// One wave per SIMD: accumulators, two dequantized blocks and the weight
+// window (two or four blocks) live in registers.
 template <int GS, int YT, int MT, bool KTAIL, bool BF16X, int EPI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_f16_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
@@ -817,12 +820,12 @@ hipError_t f16_go(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, con
 }  // namespace
 
 // Row tile and K split.  M <= 32 and M <= 64 take 32- and 64-row tiles (the
-// weight stream dominates there), larger M the 128-row tile, and fp16 input
-// whose 256-row tiles fill every CU without a K split the 256-row tile (bf16
-// input then takes its fp16 copy, scaled by the row factors, in the workspace).  When the tiles
-// cannot give every CU a workgroup, K is split into as many parts as still
-// fit in one round (at most 8, at least two K blocks each).  bf16 input adds
-// one fp32 activation factor per row to the workspace.
+// weight stream dominates there), larger M the 128-row tile, and shapes whose
+// 256-row tiles fill every CU without a K split the 256-row tile.  When the
+// tiles cannot give every CU a workgroup, K is split into as many parts as
+// still fit in one round (at most 8, at least two K blocks each), with the
+// fp32 partial tiles in the workspace.  bf16 input adds one fp32 activation
+// factor per row, and with the 256-row tile its fp16 copy scaled by them.
 GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16) {
   GemmPlan p{};
   p.mt = M <= 32 ? 2 : M <= 64 ? 4 : 8;
