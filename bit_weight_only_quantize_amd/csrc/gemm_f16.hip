@@ -71,8 +71,8 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 // s_waitcnt lgkmcnt(0).
 __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Physical 16-byte chunk of logical chunk ch in block row `row`.  KQ_BIT is
-// the bit of ch that holds the lowest bit of the reading lane's quarter.
+// Physical 16-byte chunk of logical chunk ch in block row `row`: an XOR with
+// the row, and bit 3 flipped by bit KQ_BIT of ch.
 template <int KQ_BIT>
 __device__ __forceinline__ int a_chunk(int row, int ch) {
   return ch ^ (row & 15) ^ (((ch >> KQ_BIT) & 1) << 3);
@@ -127,7 +127,11 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   constexpr int kBM = 16 * MT;
   constexpr int kWpl = GS / 32;      // packed words per lane per group and column
   constexpr int kGPB = kBK / GS;     // groups per K block
-  constexpr int kKqBit = GS == 128 ? 2 : 1;
+  // Chunk bit whose value flips bit 3 of the physical chunk: 2 for both group
+  // sizes.  (With g = 64 the lane quarter's lowest bit sits at chunk bit 1,
+  // but flipping on it measured 39% of LDS cycles with bank conflicts, bit 2
+  // 2%: rocprofv3 SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE.)
+  constexpr int kKqBit = 2;
   constexpr int kWin = MT >= 8 ? 2 : 4;   // weight blocks in flight (even: bq buffers alternate)
   constexpr int kWords = kNT * kSteps;          // packed words per lane per block
   constexpr int kWordsPerTile = kWords / MT;    // dequantized alongside each row tile
