@@ -590,7 +590,9 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float fe = f[e];
-        const float inv = fe > 0.0f ? 1.0f / fe : 1.0f;
+        // 1 / 2^k exactly: the exponent field mirrored around the bias
+        const float inv = fe > 0.0f ? __builtin_bit_cast(float, 0x7F000000u - __builtin_bit_cast(uint32_t, fe))
+                                    : 1.0f;
 #pragma unroll
         for (int j = 0; j < kNT; ++j) acc[i][j][e] *= inv;
       }
@@ -672,8 +674,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     if (m >= M) break;
     float v = sum[e];
     if constexpr (BF16X) {
-      const float f = rowf[m];
-      v *= f > 0.0f ? 1.0f / f : 1.0f;
+      const float f = rowf[m];     // a power of two: its inverse is exact
+      v *= f > 0.0f ? __builtin_bit_cast(float, 0x7F000000u - __builtin_bit_cast(uint32_t, f)) : 1.0f;
     }
     const int64_t o = (int64_t)m * N + n;
     if constexpr (YT == (int)YType::F16)
