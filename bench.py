@@ -46,7 +46,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=300)
     p.add_argument("--warmup", type=int, default=30)
-    p.add_argument("--rows", choices=("all", "none"), default="all")
+    p.add_argument("--rows", choices=("all", "gemm", "none"), default="all",
+                   help="extra rows after the headline: all, only the batched and prefill GEMM "
+                        "rows (short counter runs), or none")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy 10 times (the "
@@ -291,8 +293,8 @@ def main():
     log(f"GEMV launches: {launch_s * 1e6:.2f} us for the three layers, {achieved:.0f} GB/s")
 
     rows = {"decode_gemv_m1_layers": per_layer}
-    if args.rows == "all":
-        rows.update(measure_rows(awq, torch, wl, L, layers, R))
+    if args.rows != "none":
+        rows.update(measure_rows(awq, torch, wl, L, layers, R, only_gemm=args.rows == "gemm"))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -337,9 +339,18 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure_rows(awq, torch, wl, L, decode_layers, R_dec):
+def measure_rows(awq, torch, wl, L, decode_layers, R_dec, only_gemm=False):
     rows = {}
+    if not only_gemm:
+        rows.update(measure_decode_extra_rows(awq, torch, wl, L, decode_layers, R_dec))
+    rows.update(measure_gemm_rows(awq, torch, wl, L))
+    if not only_gemm:
+        rows.update(measure_search_row(awq, torch, wl))
+    return rows
 
+
+def measure_decode_extra_rows(awq, torch, wl, L, decode_layers, R_dec):
+    rows = {}
     # GEMV at M=4 and GEMM at M=1 on the decode layers
     for M, kernel, key in ((4, awq.AWQ_KERNEL_AUTO, "decode_gemv_m4"),
                            (1, awq.AWQ_KERNEL_GEMM, "decode_gemm_kernel_m1")):
@@ -380,7 +391,11 @@ def measure_rows(awq, torch, wl, L, decode_layers, R_dec):
                                         "frac_hbm": round(qbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
     log("quantize", rows["quantize_pack_4096x11008"])
     del Wd, outs
+    return rows
 
+
+def measure_gemm_rows(awq, torch, wl, L):
+    rows = {}
     # batched GEMM (13B-class MLP) at M = 16, 64, 256, g64 and g128
     gemm = []
     for case in wl.gemm_cases():
@@ -435,7 +450,11 @@ def measure_rows(awq, torch, wl, L, decode_layers, R_dec):
         log(case.name, res[-1])
         del packed, Xd, Yd
     rows["prefill_gemm"] = res
+    return rows
 
+
+def measure_search_row(awq, torch, wl):
+    rows = {}
     # full alpha search, 4096 tokens x 4096 x 4096, 20 alphas
     case = wl.search_case()
     Xd = torch.from_numpy(case.activation()).cuda()
