@@ -111,7 +111,6 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const float step = (hi - lo) / 15.0f;
     const _Float16 sh = (_Float16)fmaxf(step, 0x1p-14f);
     const float sf = (float)sh;
-    const float zf = fminf(fmaxf(__builtin_rintf(-lo / sf), 0.0f), 15.0f);
 
     // rint(v / sf) with the correctly rounded quotient, without eight
     // divisions: |v / sf| < 16 (|v| <= hi - lo <= 15 sf (1 + 2^-10)), so both
@@ -119,20 +118,27 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     // the exact v / sf and hence within 2^-18 of each other.  Unless y is that
     // close to a half-integer, both round to the same integer (ties included,
     // since a rounded quotient exactly at k + 1/2 puts y within 2^-18 of it);
-    // the rare lanes that are that close divide.
+    // the rare lanes that are that close divide.  The zero point's -lo / sf
+    // (also below 16) takes the same path.
     const float rs = 1.0f / sf;
+    const float zy = -lo * rs;
+    float zq = __builtin_rintf(zy);
+    bool near_half = __builtin_fabsf(zy - zq) > 0.5f - 0x1p-18f;
     float qv[8];
-    bool near_half = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float y = v[i] * rs;
       qv[i] = __builtin_rintf(y);
-      near_half |= __builtin_fabsf((y - __builtin_floorf(y)) - 0.5f) < 0x1p-18f;
+      // within 2^-18 of a half-integer: y - rint(y) (exact) is that close to
+      // +-1/2
+      near_half |= __builtin_fabsf(y - qv[i]) > 0.5f - 0x1p-18f;
     }
     if (near_half) {
+      zq = __builtin_rintf(-lo / sf);
 #pragma unroll
       for (int i = 0; i < 8; ++i) qv[i] = __builtin_rintf(v[i] / sf);
     }
+    const float zf = fminf(fmaxf(zq, 0.0f), 15.0f);
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
