@@ -18,7 +18,7 @@ hipError_t launch_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int gs,
                                 int32_t *nonfinite, hipStream_t st);
 
 // ---- linear_gemv.hip (M <= 16) -------------------------------------------------
-// Whether the GEMV kernel can serve this shape (M <= 16, LDS staging fits).
+// Whether the GEMV kernel can serve this shape (M <= 16, its LDS fits).
 bool gemv_supported(int64_t M, int64_t K, int gs);
 // Whether the GEMV stages the M activation rows in LDS (its fast path).
 bool gemv_stages_activations(int64_t M, int64_t K);
@@ -27,16 +27,17 @@ hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,
                        int64_t N, int64_t K, int gs, void *Y, YType yt,
                        hipStream_t st);
 
-// ---- split K (both GEMM kernels) ---------------------------------------------------
-// Split-K bookkeeping of one launch: `splits` workgroups per output tile, a
-// u32 counter per tile (zero between launches) and the fp32 partial tiles.
+// ---- split K (gemm_f16.hip) ---------------------------------------------------------
+// Split-K bookkeeping of one launch: `splits` workgroups per output tile, each
+// storing its fp32 partial tile for the reduction kernel that follows.
 struct SplitK {
   int splits;
   float *partials;   // [tile][split] fp32 partial tiles, summed by a second kernel
 };
 
 // ---- the quantized GEMM (any M) -------------------------------------------------
-// Row tile (16 * mt rows), K split and workspace of a quantized GEMM.
+// Row tile (16 * mt rows), K split and workspace of a quantized GEMM
+// (gemm_f16.hip; gemm_plan and the wrappers below are in linear_gemm.hip).
 struct GemmPlan {
   int mt, splits;
   int64_t tiles;
@@ -63,12 +64,14 @@ hipError_t launch_gemm_f16(const uint16_t *X, bool bf16, const uint32_t *qweight
                            const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
                            int64_t K, int gs, void *Y, YType yt, void *workspace, hipStream_t st);
 
-// Dense fp16 B (X * W^T with W fp16 [N][K]), fp32 output.
+// linear_gemm.hip: the search's reference GEMM, X * W^T with W fp16 [N][K],
+// fp32 output.
 hipError_t launch_gemm_dense_f32(const uint16_t *X, const uint16_t *W, int64_t M,
                                  int64_t N, int64_t K, float *Y, hipStream_t st);
 
-// Quantized GEMM whose epilogue accumulates sum (Yref - Y)^2: one fp64
-// partial per workgroup tile into `partials` (gemm_tile_count entries).
+// gemm_f16.hip: the search's loss GEMM, exact q - z operand and fp32 group
+// scaling, whose epilogue accumulates sum (Yref - Y)^2: one fp64 partial per
+// workgroup tile into `partials` (gemm_tile_count entries).
 hipError_t launch_gemm_loss(const uint16_t *A, const uint32_t *qweight,
                             const uint16_t *scales, const uint8_t *zeros,
                             int64_t M, int64_t N, int64_t K, int gs,
