@@ -30,15 +30,19 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
 }
 }  // namespace
 
+// Largest 16*G the kernel stages (scale/zero elements of one workgroup).
+constexpr int kGemvMaxSZ = 4096;
+// Activations are staged in LDS when M rows (plus the zero row) fit in
+// 48 KiB; larger M*K streams them from global memory instead.
+constexpr uint32_t kGemvStageBytes = 48u * 1024u;
+
 // LDS layout (dynamic shared memory, byte offsets; every region starts on a
-// 1 KiB boundary because a DMA instruction writes 1 KiB):
+// 1 KiB boundary):
 //   [0, xbytes)              activation rows 0..M-1 (when staged)
 //   [zrow, zrow + K*2)       a zero row that lanes for rows >= M read
 //   [soff, ...)              scales of the 16 columns, fp16 bits, [16][G]
 //   [zoff, ...)              zero points of the 16 columns, u8, [16][G]
 // The cross-wave reduction reuses the start of the buffer after the loop.
-// Largest 16*G the kernel stages (scale/zero elements of one workgroup).
-constexpr int kGemvMaxSZ = 4096;
 
 struct GemvSmem {
   uint32_t xrow;     // bytes per activation row (K * 2)
@@ -60,8 +64,8 @@ __host__ __device__ inline GemvSmem gemv_smem(int M, int K, int G, bool stage_x)
 // Memory instructions are the scarce resource here (each one occupies the
 // CU's address unit for tens of cycles), so per group a wave issues exactly
 // one: the 16-byte packed-weight load of each lane.  Activations (staged by
-// the workgroup once, by DMA, when M*K*2 fits the LDS budget), scales and
-// zero points come from LDS.  All global reads use buffer resources, so rows
+// the workgroup once when M*K*2 fits the LDS budget), scales and zero points
+// come from LDS.  All global reads use buffer resources, so rows
 // >= M, columns >= N and groups >= G read zero without branches.
 template <class XT, int GS, int NW, int U, bool STAGE_X>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(
@@ -123,18 +127,22 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
   // ---- prologue ---------------------------------------------------------------
   // Staging loads are issued before the weight stream: issued after it, they
   // would queue behind every CU's weight traffic and the barrier below would
-  // hold all math until the stream had drained.
-  //  * activation rows go by DMA (buffer_load ... lds), 1 KiB per instruction;
-  //    M*K*2 is a multiple of 128 bytes, so no 16-byte chunk straddles the end
-  //    of X;
-  //  * scales and zero points of the 16 columns ([16][G], contiguous) are read
-  //    element by element into registers (a 16-byte chunk could straddle the
-  //    end of those arrays, where the range check would zero it) and written
-  //    to LDS after the weight batch is in flight.
-  typedef __attribute__((address_space(3))) void lds_t;
+  // hold all math until the stream had drained.  They go to registers and
+  // are written to LDS once the first weight batch is in flight, so the
+  // barrier waits for the staging loads only (counted vmcnt), not for that
+  // batch (an LDS DMA could only be waited for with vmcnt(0)):
+  //  * activation rows, 16 bytes per thread and round (M*K*2 is a multiple
+  //    of 128 bytes, so no chunk straddles the end of X);
+  //  * scales and zero points of the 16 columns ([16][G], contiguous),
+  //    element by element (a 16-byte chunk could straddle the end of those
+  //    arrays, where the range check would zero it).
   constexpr int kSZ = kGemvMaxSZ / (64 * NW);   // scale/zero elements per thread
+  constexpr int kXR = STAGE_X ? kGemvStageBytes / (64 * NW * 16) : 1;   // X chunks per thread
   const int nsz = (16 * G + 64 * NW - 1) / (64 * NW);   // uniform: rounds needed
+  const uint32_t xbytes = STAGE_X ? (uint32_t)M * L.xrow : 0u;
+  const int nxr = (int)((xbytes + 64u * NW * 16u - 1u) / (64u * NW * 16u));
   uint32_t sreg[kSZ], zreg[kSZ];
+  u32x4 xreg[kXR];
   {
     const uint32_t base = (uint32_t)n0 * (uint32_t)G;
 #pragma unroll
@@ -146,10 +154,13 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
       zreg[r] = __builtin_amdgcn_raw_buffer_load_b8(rZ, o, 0, 0);
     }
     if constexpr (STAGE_X) {
-      const uint32_t nx = (uint32_t)M * L.xrow / 1024u + (((uint32_t)M * L.xrow) % 1024u ? 1u : 0u);
-      for (uint32_t i = (uint32_t)wave; i < nx; i += NW)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_t *)(smem + i * 1024u), 16,
-                                                 i * 1024u + (uint32_t)lane * 16u, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < kXR; ++r) {
+        if (r >= nxr) break;
+        const uint32_t o = (uint32_t)(tid + r * 64 * NW) * 16u;
+        xreg[r] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, o < xbytes ? o : 0x7FFFFFF0u, 0, 0));
+      }
       // zero row (rows >= M of the A operand read it)
       for (uint32_t b = (uint32_t)tid * 16u; b < L.xrow; b += 64u * NW * 16u)
         *reinterpret_cast<u32x4 *>(smem + L.zrow + b) = u32x4{0u, 0u, 0u, 0u};
@@ -173,14 +184,16 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
         zs[i] = (uint8_t)zreg[r];
       }
     }
+    if constexpr (STAGE_X) {
+#pragma unroll
+      for (int r = 0; r < kXR; ++r) {
+        if (r >= nxr) break;
+        const uint32_t o = (uint32_t)(tid + r * 64 * NW) * 16u;
+        if (o < xbytes) *reinterpret_cast<u32x4 *>(smem + o) = xreg[r];
+      }
+    }
   }
-
-  // LDS-DMA completion is not ordered with the register loads behind it, so
-  // the wave waits for all its loads (vmcnt(0): its DMA has landed) and for
-  // its zero-row stores (lgkmcnt(0)) before the barrier.  The staging was
-  // issued first and the batch is needed next anyway, so little is lost.
-  __builtin_amdgcn_s_waitcnt(0x0070);
-  __builtin_amdgcn_s_barrier();
+  __syncthreads();
 
   // activation row of this lane as the A operand: row c, or the zero row
   const char *xlds = smem + (c < M ? (uint32_t)c * L.xrow : L.zrow) + (uint32_t)(kq * kWpl * 16);
@@ -253,9 +266,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
   }
 }
 
-// Activations are staged in LDS when M rows (plus the zero row) fit in
-// 48 KiB; larger M*K streams them from global memory instead.
-constexpr uint32_t kGemvStageBytes = 48u * 1024u;
 
 template <class XT, int GS, int NW>
 static void gemv_launch(const uint16_t *X, const uint32_t *qw, const uint16_t *sc,
