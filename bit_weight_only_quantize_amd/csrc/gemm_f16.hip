@@ -58,6 +58,7 @@ constexpr int kGroupRows = 4;     // row tiles per tile group
 // One workgroup per CU; K is split only when there are fewer tiles than
 // slots (CUs).
 constexpr int kSlots = 256;
+constexpr int kMaxSplits = 8;     // K splits per tile (the reduction loads them all at once)
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -531,8 +532,9 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // ---- split K: store this split's partial tile --------------------------------
   // Layout [tile][split][wave][16x16 tile][lane] of 16 bytes.  Plain stores:
   // the kernel boundary makes them visible to the reduction kernel, which
-  // sums the splits in order and stores Y.  (Not compiled for the 256-row
-  // tile, which the plan never splits.)
+  // sums the splits in order and stores Y (and reads no row tile that starts
+  // at or past row M).  (Not compiled for the 256-row tile, which the plan
+  // never splits.)
   if (!kDMA && sk.splits > 1) {
     constexpr int kTiles = MT * kNT;     // f32x4 accumulators per lane
     const uint32_t wave_bytes = (uint32_t)kTiles * 64u * 16u;
@@ -541,11 +543,19 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     const uint32_t mine = ((uint32_t)tile * (uint32_t)sk.splits + (uint32_t)split) * tile_bytes +
                           (uint32_t)wave * wave_bytes + (uint32_t)lane * 16u;
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i) {
+      // For the 32-row tile (M <= 32: decode batches, where rows 16..31 are
+      // often all past M) a row tile that starts at or past M stores out of
+      // range, where the stores are dropped.  A branch here, or the test in
+      // larger tiles, changed the code of their main loop or epilogue and
+      // cost more than it saved.
+      const bool live = MT > 2 || row0 + i * 16 < M;   // uniform
 #pragma unroll
       for (int j = 0; j < kNT; ++j)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rP,
-                                               mine + (uint32_t)(i * kNT + j) * 1024u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, acc[i][j]), rP,
+            live ? mine + (uint32_t)(i * kNT + j) * 1024u : 0x7FFFFFF0u, 0, 0);
+    }
     return;
   }
 
@@ -640,7 +650,7 @@ void gemm_f16_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict_
 // l & 15).  Every CU takes a share of the partials: summing them in the GEMM
 // kernel's last workgroup of each tile was bound by that one CU's load
 // bandwidth (measured 25% slower at 6 splits, 3% at 2).
-template <int YT, int MT, bool BF16X>
+template <int YT, int MT, bool BF16X, int NS>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ partials,
                                                             int splits, int M, int N,
                                                             void *__restrict__ Y,
@@ -648,24 +658,46 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
   constexpr int kTiles = MT * kNT;
   constexpr int kBM = 16 * MT;
   const int tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM;
-  const int64_t total = (int64_t)tiles_m * tiles_n * 4 * kTiles * 64;
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (q >= total) return;
-  const int lane = (int)(q & 63);
-  int64_t r = q >> 6;
-  const int t = (int)(r % kTiles);
-  r /= kTiles;
-  const int wave = (int)(r & 3);
-  const int tile = (int)(r >> 2);
-  int tm, tn;
-  tile_coords(tile, tiles_m, tiles_n, tm, tn);
-  // [tile][split][wave][t][lane] of f32x4
-  const int64_t split_stride = (int64_t)4 * kTiles * 64;
-  const f32x4 *p = reinterpret_cast<const f32x4 *>(partials) +
-                   (int64_t)tile * splits * split_stride + ((int64_t)wave * kTiles + t) * 64 + lane;
-  f32x4 sum = p[0];
-  for (int sp = 1; sp < splits; ++sp) sum += p[sp * split_stride];
-  const int c = lane & 15, kq = lane >> 4, i = t / kNT, j = t % kNT;
+  // kTiles workgroups per output tile (4 GEMM waves x kTiles fragments x 64
+  // lanes): workgroup b < kTiles of a tile takes the fragments of GEMM wave
+  // b / MT in row tile i = b % MT, its own wave j those of 16x16 tile (i, j).
+  // Everything but j and the lane is uniform per workgroup, so the tile's
+  // coordinates and the dead-row test are scalar work.
+  const int tile = (int)(blockIdx.x / kTiles);
+  if (tile >= tiles_m * tiles_n) return;
+  const int bt = (int)(blockIdx.x % kTiles);
+  const int wave = bt / MT, i = bt % MT;
+  const int j = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = i * kNT + j;
+  // one row of tiles (M within one tile: the common split-K case) needs no
+  // division before the loads can start
+  int tm = 0, tn = tile;
+  if (tiles_m > 1) tile_coords(tile, tiles_m, tiles_n, tm, tn);
+  // a row tile that starts at or past row M holds nothing to sum (and was
+  // not stored by the 32-row tile)
+  if (tm * kBM + i * 16 >= M) return;
+  const int c = lane & 15, kq = lane >> 4;
+  // [tile][split][wave][t][lane] of 16 bytes (below 32 MiB: K is split only
+  // for fewer than kSlots tiles of at most 128 x 256)
+  constexpr uint32_t kSplitBytes = 4u * kTiles * 64u * 16u;
+  const rsrc_t rP = make_rsrc(partials, (uint32_t)(tiles_m * tiles_n) * (uint32_t)splits * kSplitBytes);
+  const uint32_t base = ((uint32_t)tile * (uint32_t)splits * 4u * kTiles +
+                         (uint32_t)(wave * kTiles + t)) * 1024u + (uint32_t)lane * 16u;
+  // Every split's load is issued before the first is used (a loop adding
+  // each as it arrived waited for them one by one).  NS >= splits is the
+  // launch's bucket (2, 4 or 8) so few loads are wasted; splits past the last
+  // read out of range (zero) and are skipped, so the sum runs in split order.
+  f32x4 part[NS];
+#pragma unroll
+  for (int sp = 0; sp < NS; ++sp) {
+    const uint32_t o = sp < splits ? base + (uint32_t)sp * kSplitBytes : 0x7FFFFFF0u;
+    part[sp] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rP, o, 0, 0));
+  }
+  f32x4 sum = part[0];
+#pragma unroll
+  for (int sp = 1; sp < NS; ++sp)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum[e] = sp < splits ? sum[e] + part[sp][e] : sum[e];
   const int n = tn * kBN + wave * 64 + j * 16 + c;
   if (n >= N) return;
 #pragma unroll
@@ -765,7 +797,7 @@ hipError_t f16_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *
   constexpr int64_t bm = 16 * MT;
   const int ysize = YT == (int)YType::F32 ? 4 : 2;
   const int64_t rows = sk.splits > 1 ? M : f16_rows_per_launch(N, K, bm);
-  if (rows <= 0) return hipErrorInvalidValue;
+  if (rows <= 0 || sk.splits > kMaxSplits) return hipErrorInvalidValue;
   for (int64_t m0 = 0; m0 < M; m0 += rows) {
     const int64_t mm = M - m0 < rows ? M - m0 : rows;
     const int64_t tiles = ((mm + bm - 1) / bm) * ((N + kBN - 1) / kBN);
@@ -778,9 +810,15 @@ hipError_t f16_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *
     if (e != hipSuccess) return e;
     if constexpr (MT < 16) {
       if (sk.splits > 1) {
-        const int64_t frags = tiles * 4 * (MT * kNT) * 64;
-        splitk_reduce_kernel<YT, MT, BF16X><<<dim3((unsigned)((frags + 255) / 256)), 256, 0, st>>>(
-            sk.partials, sk.splits, (int)mm, (int)N, y, rowf ? rowf + m0 : nullptr);
+        // kTiles = MT * kNT reduction workgroups per output tile
+        const dim3 rgrid((unsigned)(tiles * MT * kNT));
+        const float *rf = rowf ? rowf + m0 : nullptr;
+        if (sk.splits <= 2)
+          splitk_reduce_kernel<YT, MT, BF16X, 2><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
+        else if (sk.splits <= 4)
+          splitk_reduce_kernel<YT, MT, BF16X, 4><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
+        else
+          splitk_reduce_kernel<YT, MT, BF16X, kMaxSplits><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
       }
@@ -844,7 +882,7 @@ GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16) {
   p.splits = 1;
   if (p.tiles < kSlots) {
     int64_t sp = kSlots / p.tiles;
-    const int64_t cap = nkb / 2 < 8 ? nkb / 2 : 8;
+    const int64_t cap = nkb / 2 < kMaxSplits ? nkb / 2 : kMaxSplits;
     sp = sp < cap ? sp : cap;
     p.splits = sp > 1 ? (int)sp : 1;
   }

@@ -74,6 +74,9 @@ RAGGED = [
     (5, 130, 1024, 64, "bf16"), (33, 77, 320, 64, "f16"), (77, 200, 384, 128, "f16"),
     (130, 260, 640, 64, "bf16"), (257, 129, 1152, 128, "f16"), (1, 512, 512, 128, "f16"),
     (8, 512, 512, 128, "f16"),
+    # K split 8 ways with row tiles wholly or partly past M: 32-row tile at
+    # M = 16 and 17, 64-row tile at M = 33
+    (16, 300, 2048, 64, "f16"), (17, 300, 2048, 128, "f16"), (33, 300, 2048, 128, "bf16"),
 ]
 
 
