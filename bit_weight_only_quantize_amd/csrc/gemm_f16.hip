@@ -58,7 +58,7 @@ constexpr int kGroupRows = 4;     // row tiles per tile group
 // One workgroup per CU; K is split only when there are fewer tiles than
 // slots (CUs).
 constexpr int kSlots = 256;
-constexpr int kMaxSplits = 8;     // K splits per tile (the reduction loads them all at once)
+constexpr int kMaxSplits = 16;    // K splits per tile (the reduction loads them all at once)
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -685,8 +685,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
                          (uint32_t)(wave * kTiles + t)) * 1024u + (uint32_t)lane * 16u;
   // Every split's load is issued before the first is used (a loop adding
   // each as it arrived waited for them one by one).  NS >= splits is the
-  // launch's bucket (2, 4 or 8) so few loads are wasted; splits past the last
-  // read out of range (zero) and are skipped, so the sum runs in split order.
+  // launch's bucket (2, 4, 8 or 16) so few loads are wasted; splits past the
+  // last read out of range (zero) and are skipped, so the sum runs in split
+  // order.
   f32x4 part[NS];
 #pragma unroll
   for (int sp = 0; sp < NS; ++sp) {
@@ -817,6 +818,8 @@ hipError_t f16_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *
           splitk_reduce_kernel<YT, MT, BF16X, 2><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
         else if (sk.splits <= 4)
           splitk_reduce_kernel<YT, MT, BF16X, 4><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
+        else if (sk.splits <= 8)
+          splitk_reduce_kernel<YT, MT, BF16X, 8><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
         else
           splitk_reduce_kernel<YT, MT, BF16X, kMaxSplits><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
         e = hipGetLastError();
@@ -882,7 +885,11 @@ GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16) {
   p.splits = 1;
   if (p.tiles < kSlots) {
     int64_t sp = kSlots / p.tiles;
-    const int64_t cap = nkb / 2 < kMaxSplits ? nkb / 2 : kMaxSplits;
+    // at least 2 K blocks per split up to 8 splits, at least 4 beyond (up to
+    // 16): a split of few blocks is mostly pipeline fill and drain
+    const int64_t c2 = nkb / 2 < 8 ? nkb / 2 : 8;
+    const int64_t c4 = nkb / 4 < kMaxSplits ? nkb / 4 : kMaxSplits;
+    const int64_t cap = c2 > c4 ? c2 : c4;
     sp = sp < cap ? sp : cap;
     p.splits = sp > 1 ? (int)sp : 1;
   }

@@ -229,10 +229,11 @@ def test_split_k_repeatable_and_workspace_regrowth():
     scratch for a larger shape does not disturb a later call of the first
     shape."""
     torch = torch_mod()
-    # 8 splits for the first three shapes; the last has 102 tiles of
-    # 128 x 256, so two.
+    # 8 splits for the first three shapes; the fourth has 102 tiles of
+    # 128 x 256, so two; the last two split 16 and 12 ways (at least 4 K
+    # blocks per split beyond 8).
     shapes = [(64, 640, 4096, 128), (32, 4096, 8192, 64), (256, 1280, 2048, 128),
-              (200, 13000, 512, 128)]
+              (200, 13000, 512, 128), (16, 1000, 8192, 128), (40, 4000, 6144, 64)]
     outs = {}
     for rep in range(2):
         for (M, N, K, g) in shapes:
