@@ -76,8 +76,15 @@ hipError_t linear_scratch(size_t bytes, void **out) {
 // rows no longer fit its LDS staging, is slower than the split-K GEMM (at
 // M = 16: 28.7 vs 22.0 us for 13824 x 5120; the GEMV stays ahead on the
 // 4096 x 4096 and 4096 x 11008 layers).
+// GEMV or GEMM, from measured times on 7B- and 13B-class layers: the GEMV
+// wins wherever it stages the activation rows in LDS; unstaged, its
+// activation reads grow with M, and it loses where each wave walks a long
+// chain of groups (> 8), beyond M = 8, or beyond M = 16 on layers of at most
+// 5e7 weights.
 bool auto_gemv(int64_t M, int64_t N, int64_t K, int g) {
   if (M > AWQ_GEMV_MAX_M || !awq::gemv_supported(M, K, g)) return false;
+  if (awq::gemv_stages_activations(M, K)) return true;
+  if (awq::gemv_groups_per_wave(N, K, g) > 8) return false;
   return M <= 8 || N * K <= 50000000;
 }
 

@@ -113,8 +113,11 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
  *   qweight, scales, zeros: as produced by awq_quantize_pack for [N][K].
  *   Y        device, [M][N] of y_dtype (AWQ_F16, AWQ_BF16 or AWQ_F32).
  *
- * Dispatch: the GEMV kernel for M <= 8, and for M <= AWQ_GEMV_MAX_M when
- * N * K <= 5e7 (where it measured faster); otherwise the MFMA GEMM.
+ * Dispatch (where each measured faster): the GEMV kernel for M <=
+ * AWQ_GEMV_MAX_M when M * K * 2 <= 48 KiB (its activation rows fit in LDS);
+ * otherwise, unless K / group_size exceeds 8 times its waves per workgroup
+ * (16 when N <= 4096, else 8), for M <= 8, and for M <= AWQ_GEMV_MAX_M when
+ * N * K <= 5e7; else the MFMA GEMM.
  * GEMV: products of the exact integer (code - zero) and the 16-bit
  * activation, accumulated in fp32 within a group, multiplied by the group's
  * scale and accumulated in fp32 across groups.  GEMM: the dequantized weight

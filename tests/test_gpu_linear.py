@@ -77,6 +77,9 @@ RAGGED = [
     # K split 8 ways with row tiles wholly or partly past M: 32-row tile at
     # M = 16 and 17, 64-row tile at M = 33
     (16, 300, 2048, 64, "f16"), (17, 300, 2048, 128, "f16"), (33, 300, 2048, 128, "bf16"),
+    # GEMV with staged rows and more than 8 groups per wave (two batches in
+    # flight): 8 waves per workgroup (N > 4096), K / g > 64
+    (1, 5000, 8448, 128, "f16"), (2, 4200, 5120, 64, "bf16"),
 ]
 
 
