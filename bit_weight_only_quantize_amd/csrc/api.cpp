@@ -82,8 +82,8 @@ hipError_t linear_scratch(size_t bytes, void **out) {
 // chain of groups (> 8), beyond M = 8, or beyond M = 16 on layers of at most
 // 5e7 weights.
 bool auto_gemv(int64_t M, int64_t N, int64_t K, int g) {
-  if (M > AWQ_GEMV_MAX_M || !awq::gemv_supported(M, K, g)) return false;
-  if (awq::gemv_stages_activations(M, K)) return true;
+  if (M > AWQ_GEMV_MAX_M || !awq::gemv_supported(M, N, K, g)) return false;
+  if (awq::gemv_stages_activations(M, N, K)) return true;
   if (awq::gemv_groups_per_wave(N, K, g) > 8) return false;
   return M <= 8 || N * K <= 50000000;
 }
@@ -244,7 +244,7 @@ awq_status linear_impl(const void *X, int32_t x_dtype, const uint32_t *qweight,
   if (st != AWQ_OK) return st;
   const awq::XType xt = x_dtype == AWQ_F16 ? awq::XType::F16 : awq::XType::BF16;
   const awq::GemmPlan plan = awq::gemm_plan(M > 0 ? M : 1, N > 0 ? N : 1, K, xt);
-  const bool gemv_ok = awq::gemv_supported(M, K, cfg.group_size);
+  const bool gemv_ok = awq::gemv_supported(M, N > 0 ? N : 1, K, cfg.group_size);
   if (kernel == AWQ_KERNEL_GEMV && !gemv_ok)
     return fail(AWQ_ERR_UNSUPPORTED, "GEMV kernel cannot serve K=%lld", (long long)K);
   const bool gemv = kernel == AWQ_KERNEL_GEMV ||

@@ -19,9 +19,9 @@ hipError_t launch_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int gs,
 
 // ---- linear_gemv.hip (M <= 16) -------------------------------------------------
 // Whether the GEMV kernel can serve this shape (M <= 16, its LDS fits).
-bool gemv_supported(int64_t M, int64_t K, int gs);
+bool gemv_supported(int64_t M, int64_t N, int64_t K, int gs);
 // Whether the GEMV stages the M activation rows in LDS (its fast path).
-bool gemv_stages_activations(int64_t M, int64_t K);
+bool gemv_stages_activations(int64_t M, int64_t N, int64_t K);
 // Groups of K each GEMV wave walks in sequence.
 int64_t gemv_groups_per_wave(int64_t N, int64_t K, int gs);
 hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,

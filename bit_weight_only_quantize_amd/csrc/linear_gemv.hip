@@ -32,9 +32,17 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
 
 // Largest 16*G the kernel stages (scale/zero elements of one workgroup).
 constexpr int kGemvMaxSZ = 4096;
-// Activations are staged in LDS when their M rows fit in 48 KiB; larger M*K
-// streams them from global memory instead.
+// Activations are staged in LDS when their M rows fit the budget: 48 KiB, or
+// 128 KiB for 16-wave workgroups (grids of at most 256 workgroups, one per
+// CU, which then owns the CU's 160 KiB of LDS).  Larger M*K streams them
+// from global memory instead.
 constexpr uint32_t kGemvStageBytes = 48u * 1024u;
+constexpr uint32_t kGemvStageBytesSolo = 128u * 1024u;
+// Waves per workgroup for N output columns (see gemv_dispatch).
+__host__ __device__ constexpr int gemv_waves(int64_t N) { return (N + 15) / 16 <= 256 ? 16 : 8; }
+__host__ __device__ constexpr uint32_t gemv_stage_budget(int nw) {
+  return nw == 16 ? kGemvStageBytesSolo : kGemvStageBytes;
+}
 
 // LDS layout (dynamic shared memory, byte offsets; every region starts on a
 // 1 KiB boundary):
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
   //    element by element (a 16-byte chunk could straddle the end of those
   //    arrays, where the range check would zero it).
   constexpr int kSZ = kGemvMaxSZ / (64 * NW);   // scale/zero elements per thread
-  constexpr int kXR = STAGE_X ? kGemvStageBytes / (64 * NW * 16) : 1;   // X chunks per thread
+  constexpr int kXR = STAGE_X ? gemv_stage_budget(NW) / (64 * NW * 16) : 1;   // X chunks per thread
   const int nsz = (16 * G + 64 * NW - 1) / (64 * NW);   // uniform: rounds needed
   const uint32_t xbytes = STAGE_X ? (uint32_t)M * L.xrow : 0u;
   const int nxr = (int)((xbytes + 64u * NW * 16u - 1u) / (64u * NW * 16u));
@@ -271,7 +279,7 @@ static void gemv_launch(const uint16_t *X, const uint32_t *qw, const uint16_t *s
                         hipStream_t st) {
   const dim3 grid((unsigned)((N + 15) / 16));
   const int G = (int)(K / GS);
-  const bool stage = (uint64_t)M * (uint64_t)K * 2u <= kGemvStageBytes;
+  const bool stage = (uint64_t)M * (uint64_t)K * 2u <= gemv_stage_budget(NW);
   const GemvSmem L = gemv_smem(M, (int)K, G, stage);
   // the reduction reuses the buffer: at least NW * 64 * 16 bytes
   const uint32_t bytes = L.total > 64u * NW * 16u ? L.total : 64u * NW * 16u;
@@ -298,25 +306,26 @@ template <class XT, int GS>
 static void gemv_dispatch(const uint16_t *X, const uint32_t *qw, const uint16_t *sc,
                           const uint8_t *zr, int M, int64_t N, int64_t K, void *Y, YType yt,
                           hipStream_t st) {
-  if ((N + 15) / 16 <= 256)
+  if (gemv_waves(N) == 16)
     gemv_launch<XT, GS, 16>(X, qw, sc, zr, M, N, K, Y, yt, st);
   else
     gemv_launch<XT, GS, 8>(X, qw, sc, zr, M, N, K, Y, yt, st);
 }
 
 int64_t gemv_groups_per_wave(int64_t N, int64_t K, int gs) {
-  return (K / gs) / ((N + 15) / 16 <= 256 ? 16 : 8);
+  return (K / gs) / gemv_waves(N);
 }
 
-bool gemv_stages_activations(int64_t M, int64_t K) {
-  return (uint64_t)M * (uint64_t)K * 2u <= kGemvStageBytes;
+bool gemv_stages_activations(int64_t M, int64_t N, int64_t K) {
+  return (uint64_t)M * (uint64_t)K * 2u <= gemv_stage_budget(gemv_waves(N));
 }
 
-bool gemv_supported(int64_t M, int64_t K, int gs) {
+bool gemv_supported(int64_t M, int64_t N, int64_t K, int gs) {
   const int64_t G = K / gs;
-  const bool stage = (uint64_t)M * (uint64_t)K * 2u <= kGemvStageBytes;
+  const bool stage = gemv_stages_activations(M, N, K);
   const GemvSmem L = gemv_smem((int)M, (int)K, (int)G, stage);
-  return M <= 16 && 16 * G <= kGemvMaxSZ && L.total <= 64u * 1024u;
+  const uint32_t lds = gemv_waves(N) == 16 ? 160u * 1024u : 64u * 1024u;
+  return M <= 16 && 16 * G <= kGemvMaxSZ && L.total <= lds;
 }
 
 hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,
