@@ -13,9 +13,11 @@
 //
 // Mapping: one lane per output word (8 input channels, 16 bytes of W);
 // g/8 consecutive lanes form a group and exchange min/max with DPP moves.
-// The kernel is bound by HBM traffic (2 bytes in, 0.5 + 3/g bytes out per
-// weight); the per-weight division is replaced by a reciprocal multiply whose
-// rounding provably agrees except next to half-integers (checked per lane).
+// The kernel moves 2 bytes in and 0.5 + 3/g bytes out per weight and is
+// close to bound by its VALU work: the per-weight division is replaced by a
+// reciprocal multiply whose rounding provably agrees except next to
+// half-integers (checked per lane), and that same check catches non-finite
+// values, so the common path carries no separate test for them.
 
 #include <type_traits>
 
@@ -92,8 +94,6 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = sv[i] * v[i];
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) bad += !__builtin_isfinite(v[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = 0.0f;
@@ -112,31 +112,37 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const _Float16 sh = (_Float16)fmaxf(step, 0x1p-14f);
     const float sf = (float)sh;
 
-    // rint(v / sf) with the correctly rounded quotient, without eight
-    // divisions: |v / sf| < 16 (|v| <= hi - lo <= 15 sf (1 + 2^-10)), so both
-    // the quotient rounded once and y = fl(v * fl(1 / sf)) lie within 2^-19 of
-    // the exact v / sf and hence within 2^-18 of each other.  Unless y is that
-    // close to a half-integer, both round to the same integer (ties included,
-    // since a rounded quotient exactly at k + 1/2 puts y within 2^-18 of it);
-    // the rare lanes that are that close divide.  The zero point's -lo / sf
-    // (also below 16) takes the same path.
-    const float rs = 1.0f / sf;
+    // rint(v / sf) with the correctly rounded quotient q, without eight
+    // divisions: |v / sf| < 16 (|v| <= hi - lo <= 15 sf (1 + 2^-10)), so q
+    // lies within 2^-20 of the exact v / sf, and y = fl(v * rcp(sf)), with
+    // the hardware reciprocal (specified to 1 ulp; up to 7 ulp would do),
+    // within 2^-16 - 2^-20.  Unless y is within 2^-16 of a half-integer, both
+    // round to the same integer (ties included: a q exactly at k + 1/2 puts
+    // y that close to it); the rare lanes that are that close divide.  The
+    // zero point's -lo / sf (also below 16) takes the same path.  The test is
+    // written so that a NaN y also fails it: every non-finite v makes its own
+    // lane's y NaN (v * rcp(sf) is NaN or +-inf, and inf - rint(inf) is NaN;
+    // an inf in the group makes sf inf and rcp(sf) 0), so those lanes take
+    // the slow path too, where they are counted.
+    const float rs = __builtin_amdgcn_rcpf(sf);
     const float zy = -lo * rs;
     float zq = __builtin_rintf(zy);
-    bool near_half = __builtin_fabsf(zy - zq) > 0.5f - 0x1p-18f;
+    bool near_half = !(__builtin_fabsf(zy - zq) <= 0.5f - 0x1p-16f);
     float qv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float y = v[i] * rs;
       qv[i] = __builtin_rintf(y);
-      // within 2^-18 of a half-integer: y - rint(y) (exact) is that close to
-      // +-1/2
-      near_half |= __builtin_fabsf(y - qv[i]) > 0.5f - 0x1p-18f;
+      // y - rint(y) is exact
+      near_half |= !(__builtin_fabsf(y - qv[i]) <= 0.5f - 0x1p-16f);
     }
     if (near_half) {
       zq = __builtin_rintf(-lo / sf);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qv[i] = __builtin_rintf(v[i] / sf);
+      for (int i = 0; i < 8; ++i) {
+        qv[i] = __builtin_rintf(v[i] / sf);
+        bad += !__builtin_isfinite(v[i]);
+      }
     }
     const float zf = fminf(fmaxf(zq, 0.0f), 15.0f);
     uint32_t word = 0;
