@@ -32,11 +32,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
 
 // Largest 16*G the kernel stages (scale/zero elements of one workgroup).
 constexpr int kGemvMaxSZ = 4096;
-// Activations are staged in LDS when their M rows fit the budget: 48 KiB, or
-// 128 KiB for 16-wave workgroups (grids of at most 256 workgroups, one per
-// CU, which then owns the CU's 160 KiB of LDS).  Larger M*K streams them
-// from global memory instead.
-constexpr uint32_t kGemvStageBytes = 48u * 1024u;
+// Activations are staged in LDS when their M rows fit the budget: 64 KiB for
+// 8-wave workgroups (at most 80 KiB of LDS each, two per CU), 128 KiB for
+// 16-wave workgroups (grids of at most 256 workgroups, one per CU, which
+// then owns the CU's 160 KiB of LDS).  Larger M*K streams them from global
+// memory instead.
+constexpr uint32_t kGemvStageBytes = 64u * 1024u;
 constexpr uint32_t kGemvStageBytesSolo = 128u * 1024u;
 // Waves per workgroup for N output columns (see gemv_dispatch).
 __host__ __device__ constexpr int gemv_waves(int64_t N) { return (N + 15) / 16 <= 256 ? 16 : 8; }
@@ -324,7 +325,7 @@ bool gemv_supported(int64_t M, int64_t N, int64_t K, int gs) {
   const int64_t G = K / gs;
   const bool stage = gemv_stages_activations(M, N, K);
   const GemvSmem L = gemv_smem((int)M, (int)K, (int)G, stage);
-  const uint32_t lds = gemv_waves(N) == 16 ? 160u * 1024u : 64u * 1024u;
+  const uint32_t lds = gemv_waves(N) == 16 ? 160u * 1024u : 80u * 1024u;
   return M <= 16 && 16 * G <= kGemvMaxSZ && L.total <= lds;
 }
 

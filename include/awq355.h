@@ -115,7 +115,7 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
  *
  * Dispatch (where each measured faster): the GEMV kernel for M <=
  * AWQ_GEMV_MAX_M when its activation rows fit in LDS (M * K * 2 <= 128 KiB
- * for N <= 4096, else 48 KiB);
+ * for N <= 4096, else 64 KiB);
  * otherwise, unless K / group_size exceeds 8 times its waves per workgroup
  * (16 when N <= 4096, else 8), for M <= 8, and for M <= AWQ_GEMV_MAX_M when
  * N * K <= 5e7; else the MFMA GEMM.

@@ -80,8 +80,10 @@ RAGGED = [
     # GEMV with staged rows and more than 8 groups per wave (two batches in
     # flight): 8 waves per workgroup (N > 4096), K / g > 64
     (1, 5000, 8448, 128, "f16"), (2, 4200, 5120, 64, "bf16"),
-    # GEMV staging beyond 48 KiB (16-wave workgroups, N <= 4096): 86 and 128 KiB
+    # GEMV staging of 86 and 128 KiB (16-wave workgroups, N <= 4096), and of
+    # 50 and 64 KiB with 8-wave workgroups (N > 4096)
     (4, 4096, 11008, 128, "f16"), (16, 4000, 4096, 64, "bf16"),
+    (5, 6000, 5120, 64, "bf16"), (8, 5000, 4096, 128, "f16"),
 ]
 
 
