@@ -109,6 +109,24 @@ def test_linear_workspace_size_and_validation():
     assert call(M=0, ws_ptr=NULL, ws_bytes=0) == binding.AWQ_OK
 
 
+def test_linear_dispatch_rule():
+    """awq_linear's GEMV/GEMM choice (host logic, no GPU): the GEMV, which
+    needs no workspace, wherever its activation rows fit in LDS (64 KiB, or
+    128 KiB when N <= 4096); unstaged, the GEMM (split K, so a workspace)
+    where a GEMV wave would walk more than 8 groups, else the GEMV up to
+    M = 8, or 16 for layers of at most 5e7 weights."""
+    ws = lambda M, N, K: lib.awq_linear_workspace_size(M, N, K, cfg(128))
+    assert ws(2, 5120, 13824) == 0          # 55 KiB of rows: staged
+    assert ws(4, 5120, 13824) > 0           # unstaged, 108 groups over 8 waves
+    assert ws(8, 11008, 4096) == 0          # 64 KiB: staged
+    assert ws(12, 11008, 4096) == 0         # unstaged, 4.5e7 weights, M <= 16
+    assert ws(12, 13824, 5120) > 0          # unstaged, 7.1e7 weights, M > 8
+    assert ws(8, 13824, 5120) == 0          # unstaged, M <= 8, 5 groups per wave
+    assert ws(16, 4096, 4096) == 0          # 128 KiB: staged (16-wave workgroups)
+    assert ws(6, 4096, 11008) == 0          # unstaged, 4.5e7 weights
+    assert ws(17, 4096, 4096) > 0           # beyond the GEMV's 16 rows
+
+
 def test_search_workspace_and_validation():
     ws = lib.awq_scale_search_workspace_size(4096, 4096, 4096, cfg(128), 20)
     # dominated by the fp32 reference output and the scaled activation copy
