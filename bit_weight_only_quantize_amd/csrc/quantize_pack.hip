@@ -108,7 +108,15 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     lo = group_min<kLanesPerGroup>(lo);
     hi = group_max<kLanesPerGroup>(hi);
 
-    const float step = (hi - lo) / 15.0f;
+    // (hi - lo) / 15, correctly rounded, from the product with RN(1/15) and
+    // one exact-remainder correction (Markstein): checked against IEEE
+    // division for every non-negative finite fp32 dividend; an infinite
+    // dividend (the only other value hi - lo takes) passes through as the
+    // division would give it.
+    const float d = hi - lo;
+    const float q0 = d * 0x1.111112p-4f;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-15.0f, q0, d), 0x1.111112p-4f, q0);
+    const float step = d == __builtin_inff() ? d : q1;
     const _Float16 sh = (_Float16)fmaxf(step, 0x1p-14f);
     const float sf = (float)sh;
 
