@@ -18,7 +18,15 @@ namespace awq {
 // column sums are accumulated as 64-bit integers: exact for any M < 2^24 and
 // independent of the order in which the atomics land.  The mean is then the
 // correctly rounded quotient of the exact sum by M.
-constexpr int kAbsRows = 64;
+// A workgroup of 16 waves sums a block of 512 columns by 128 rows: each wave
+// takes every 16th row of the block (8 rows, all loads in flight at once),
+// the waves' sums meet in LDS, and one 64-bit atomic per column and block
+// adds the block's sum.  (Per-thread atomics over 16- or 64-row strips were
+// atomic- or latency-bound at a tenth of HBM bandwidth.)
+constexpr int kAbsWaves = 16;
+constexpr int kAbsRowsPerWave = 8;
+constexpr int kAbsRows = kAbsWaves * kAbsRowsPerWave;
+constexpr int kAbsCols = 64 * 8;
 
 __device__ __forceinline__ uint64_t half_magnitude_units(uint32_t h) {
   const uint32_t e = (h >> 10) & 0x1Fu;
@@ -31,24 +39,48 @@ __global__ __launch_bounds__(256) void zero_u64_kernel(uint64_t *p, int64_t n) {
   if (i < n) p[i] = 0;
 }
 
-__global__ __launch_bounds__(256) void abs_colsum_kernel(const uint16_t *__restrict__ X,
-                                                         int64_t M, int64_t K,
-                                                         unsigned long long *__restrict__ sums) {
-  const int64_t k0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-  if (k0 >= K) return;
-  const int64_t m0 = (int64_t)blockIdx.y * kAbsRows;
-  const int64_t m1 = m0 + kAbsRows < M ? m0 + kAbsRows : M;
+__global__ __launch_bounds__(64 * kAbsWaves) void abs_colsum_kernel(
+    const uint16_t *__restrict__ X, int64_t M, int64_t K, unsigned long long *__restrict__ sums) {
+  __shared__ uint64_t part[kAbsWaves][kAbsCols];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t k0 = (int64_t)blockIdx.x * kAbsCols + lane * 8;   // this lane's 8 columns
   uint64_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t m = m0; m < m1; ++m) {
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(X + m * K + k0);
+  // row blocks blockIdx.y, + gridDim.y, ... (the grid's y extent is capped)
+  for (int64_t b = blockIdx.y; k0 < K && b * kAbsRows < M; b += gridDim.y) {
+    const int64_t m0 = b * kAbsRows + wave;                       // rows m0 + 16 r
+    u32x4 v[kAbsRowsPerWave];
+    if ((b + 1) * kAbsRows <= M) {                      // uniform: a full block
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += half_magnitude_units(v[i] & 0xFFFFu);
-      acc[2 * i + 1] += half_magnitude_units(v[i] >> 16);
+      for (int r = 0; r < kAbsRowsPerWave; ++r)
+        v[r] = *reinterpret_cast<const u32x4 *>(X + (m0 + kAbsWaves * r) * K + k0);
+    } else {                                            // rows past M count as zero
+#pragma unroll
+      for (int r = 0; r < kAbsRowsPerWave; ++r) {
+        const int64_t m = m0 + kAbsWaves * r;
+        v[r] = m < M ? *reinterpret_cast<const u32x4 *>(X + m * K + k0) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kAbsRowsPerWave; ++r) {
+      const u32x4 w = v[r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t x = w[i];
+        acc[2 * i] += half_magnitude_units(x & 0xFFFFu);
+        acc[2 * i + 1] += half_magnitude_units(x >> 16);
+      }
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) atomicAdd(&sums[k0 + i], (unsigned long long)acc[i]);
+  for (int i = 0; i < 8; ++i) part[wave][lane * 8 + i] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < kAbsCols) {
+    uint64_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kAbsWaves; ++w) t += part[w][threadIdx.x];
+    const int64_t k = (int64_t)blockIdx.x * kAbsCols + threadIdx.x;
+    if (k < K) atomicAdd(&sums[k], (unsigned long long)t);
+  }
 }
 
 __global__ __launch_bounds__(256) void mean_from_units_kernel(const uint64_t *__restrict__ units,
@@ -62,8 +94,10 @@ hipError_t launch_mean_abs(const uint16_t *X, int64_t M, int64_t K, uint64_t *un
                            double *xbar, hipStream_t st) {
   const unsigned gk = (unsigned)((K + 255) / 256);
   zero_u64_kernel<<<gk, 256, 0, st>>>(units, K);
-  const dim3 grid((unsigned)((K / 8 + 255) / 256), (unsigned)((M + kAbsRows - 1) / kAbsRows));
-  abs_colsum_kernel<<<grid, 256, 0, st>>>(X, M, K, reinterpret_cast<unsigned long long *>(units));
+  const int64_t blocks = (M + kAbsRows - 1) / kAbsRows;
+  const dim3 grid((unsigned)((K + kAbsCols - 1) / kAbsCols), (unsigned)(blocks < 4096 ? blocks : 4096));
+  abs_colsum_kernel<<<grid, 64 * kAbsWaves, 0, st>>>(X, M, K,
+                                                     reinterpret_cast<unsigned long long *>(units));
   mean_from_units_kernel<<<gk, 256, 0, st>>>(units, K, (double)M, xbar);
   return hipGetLastError();
 }
@@ -156,22 +190,39 @@ hipError_t launch_scale_activation(const uint16_t *X, const float *s, int64_t M,
 }
 
 // ---- losses and argmin --------------------------------------------------------------
-// One thread per alpha sums that alpha's tile partials in index order, so the
-// result does not depend on scheduling; thread 0 then takes the first minimum.
-__global__ __launch_bounds__(64) void reduce_losses_kernel(const double *__restrict__ partials,
-                                                           int64_t n, int n_alpha,
-                                                           double *__restrict__ losses,
-                                                           int32_t *__restrict__ best) {
+// Each alpha's tile partials are summed sequentially in index order, so the
+// result does not depend on scheduling.  The workgroup streams the partials
+// through LDS in chunks of kLossChunk per alpha (cooperative, coalesced
+// loads), and thread j continues alpha j's running sum over each chunk: the
+// order of additions is the plain sequential one.  Thread 0 then takes the
+// first minimum.
+constexpr int kLossChunk = 128;
+
+__global__ __launch_bounds__(1024) void reduce_losses_kernel(const double *__restrict__ partials,
+                                                             int64_t n, int n_alpha,
+                                                             double *__restrict__ losses,
+                                                             int32_t *__restrict__ best) {
+  __shared__ double chunk[64 * kLossChunk];
   __shared__ double sl[64];
-  const int j = threadIdx.x;
-  if (j < n_alpha) {
-    double s = 0.0;
-    for (int64_t i = 0; i < n; ++i) s += partials[(int64_t)j * n + i];
-    sl[j] = s;
-    losses[j] = s;
+  const int tid = threadIdx.x;
+  double s = 0.0;
+  for (int64_t c0 = 0; c0 < n; c0 += kLossChunk) {
+    const int len = n - c0 < kLossChunk ? (int)(n - c0) : kLossChunk;
+    for (int i = tid; i < n_alpha * len; i += 1024) {
+      const int j = i / len, t = i - j * len;
+      chunk[j * kLossChunk + t] = partials[(int64_t)j * n + c0 + t];
+    }
+    __syncthreads();
+    if (tid < n_alpha)
+      for (int t = 0; t < len; ++t) s += chunk[tid * kLossChunk + t];
+    __syncthreads();
+  }
+  if (tid < n_alpha) {
+    sl[tid] = s;
+    losses[tid] = s;
   }
   __syncthreads();
-  if (j == 0) {
+  if (tid == 0) {
     int b = 0;
     for (int i = 1; i < n_alpha; ++i)
       if (sl[i] < sl[b]) b = i;
@@ -181,7 +232,7 @@ __global__ __launch_bounds__(64) void reduce_losses_kernel(const double *__restr
 
 hipError_t launch_reduce_losses(const double *partials, int64_t n_per_alpha, int n_alpha,
                                 double *losses, int32_t *best, hipStream_t st) {
-  reduce_losses_kernel<<<1, 64, 0, st>>>(partials, n_per_alpha, n_alpha, losses, best);
+  reduce_losses_kernel<<<1, 1024, 0, st>>>(partials, n_per_alpha, n_alpha, losses, best);
   return hipGetLastError();
 }
 
