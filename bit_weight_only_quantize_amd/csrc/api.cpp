@@ -79,13 +79,13 @@ hipError_t linear_scratch(size_t bytes, void **out) {
 // GEMV or GEMM, from measured times on 7B- and 13B-class layers: the GEMV
 // wins wherever it stages the activation rows in LDS; unstaged, its
 // activation reads grow with M, and it loses where each wave walks a long
-// chain of groups (> 8), beyond M = 8, or beyond M = 16 on layers of at most
+// chain of groups (> 8), beyond M = 8, or beyond M = 12 on layers of at most
 // 5e7 weights.
 bool auto_gemv(int64_t M, int64_t N, int64_t K, int g) {
   if (M > AWQ_GEMV_MAX_M || !awq::gemv_supported(M, N, K, g)) return false;
   if (awq::gemv_stages_activations(M, N, K)) return true;
   if (awq::gemv_groups_per_wave(N, K, g) > 8) return false;
-  return M <= 8 || N * K <= 50000000;
+  return M <= 8 || (M <= 12 && N * K <= 50000000);
 }
 
 awq_status check_config(awq_config cfg, int64_t K) {

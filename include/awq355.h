@@ -117,7 +117,7 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
  * AWQ_GEMV_MAX_M when its activation rows fit in LDS (M * K * 2 <= 128 KiB
  * for N <= 4096, else 64 KiB);
  * otherwise, unless K / group_size exceeds 8 times its waves per workgroup
- * (16 when N <= 4096, else 8), for M <= 8, and for M <= AWQ_GEMV_MAX_M when
+ * (16 when N <= 4096, else 8), for M <= 8, and for M <= 12 when
  * N * K <= 5e7; else the MFMA GEMM.
  * GEMV: products of the exact integer (code - zero) and the 16-bit
  * activation, accumulated in fp32 within a group, multiplied by the group's

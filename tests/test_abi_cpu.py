@@ -114,12 +114,13 @@ def test_linear_dispatch_rule():
     needs no workspace, wherever its activation rows fit in LDS (64 KiB, or
     128 KiB when N <= 4096); unstaged, the GEMM (split K, so a workspace)
     where a GEMV wave would walk more than 8 groups, else the GEMV up to
-    M = 8, or 16 for layers of at most 5e7 weights."""
+    M = 8, or 12 for layers of at most 5e7 weights."""
     ws = lambda M, N, K: lib.awq_linear_workspace_size(M, N, K, cfg(128))
     assert ws(2, 5120, 13824) == 0          # 55 KiB of rows: staged
     assert ws(4, 5120, 13824) > 0           # unstaged, 108 groups over 8 waves
     assert ws(8, 11008, 4096) == 0          # 64 KiB: staged
-    assert ws(12, 11008, 4096) == 0         # unstaged, 4.5e7 weights, M <= 16
+    assert ws(12, 11008, 4096) == 0         # unstaged, 4.5e7 weights, M <= 12
+    assert ws(16, 11008, 4096) > 0          # unstaged, 4.5e7 weights, M > 12
     assert ws(12, 13824, 5120) > 0          # unstaged, 7.1e7 weights, M > 8
     assert ws(8, 13824, 5120) == 0          # unstaged, M <= 8, 5 groups per wave
     assert ws(16, 4096, 4096) == 0          # 128 KiB: staged (16-wave workgroups)
