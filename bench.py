@@ -102,24 +102,34 @@ def calibrate_copy():
 
 
 class Launcher:
-    """Direct ctypes calls with pre-marshalled arguments (no per-call tensor checks)."""
+    """Direct ctypes calls of awq_linear_ex with pre-marshalled arguments (no
+    per-call tensor checks).  One workspace, grown when a shape needs more; the
+    first call of a shape happens outside graph capture (make_graph warms up),
+    so no allocation is ever captured."""
 
     def __init__(self, awq, torch):
         self.awq = awq
         self.torch = torch
         self.lib = awq.lib
+        self.ws = None
 
     def linear(self, X, packed, Y, g, kernel):
         qw, sc, zr = packed
         M, K = X.shape
         N = qw.shape[0]
+        xd = 0 if X.dtype == self.torch.float16 else 1
+        cfg = self.awq.config(g)
+        need = self.lib.awq_linear_workspace_size(M, N, K, cfg, xd, kernel)
+        if need and (self.ws is None or self.ws.numel() < need):
+            self.ws = self.torch.empty(need, dtype=self.torch.uint8, device=X.device)
+        wp = ctypes.c_void_p(self.ws.data_ptr() if need else 0)
         st = self.lib.awq_linear_ex(
-            ctypes.c_void_p(X.data_ptr()), 0 if X.dtype == self.torch.float16 else 1,
+            ctypes.c_void_p(X.data_ptr()), xd,
             ctypes.c_void_p(qw.data_ptr()), ctypes.c_void_p(sc.data_ptr()),
-            ctypes.c_void_p(zr.data_ptr()), M, N, K, self.awq.config(g),
+            ctypes.c_void_p(zr.data_ptr()), M, N, K, cfg,
             ctypes.c_void_p(Y.data_ptr()),
             {self.torch.float16: 0, self.torch.bfloat16: 1, self.torch.float32: 2}[Y.dtype],
-            kernel, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+            kernel, wp, need, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
         if st != 0:
             raise RuntimeError(self.lib.awq_last_error().decode())
 

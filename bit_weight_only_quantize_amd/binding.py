@@ -1,8 +1,9 @@
 """ctypes binding of libawq355.so (argument marshalling only).
 
-Every function here validates tensor placement, allocates outputs with torch
-when the caller does not pass them, and calls the C entry point of the same
-name on the current HIP stream.  All computation happens in the library's HIP
+Every function here validates its tensors (dtype, shape, device), allocates
+outputs (and, where asked, a workspace) with torch when the caller does not
+pass them, and calls the C entry point of the same name on the current HIP
+stream.  All computation happens in the library's HIP
 kernels; there is no fallback of any kind.  If the library is missing or
 cannot be loaded, importing this module raises ImportError.
 """
@@ -71,9 +72,10 @@ def _load():
     lib.awq_quantize_pack.restype = ctypes.c_int
     lib.awq_linear.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32, vp]
     lib.awq_linear.restype = ctypes.c_int
-    lib.awq_linear_ex.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32, i32, vp]
+    lib.awq_linear_ex.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32, i32, vp,
+                                  ctypes.c_size_t, vp]
     lib.awq_linear_ex.restype = ctypes.c_int
-    lib.awq_linear_workspace_size.argtypes = [i64, i64, i64, awq_config]
+    lib.awq_linear_workspace_size.argtypes = [i64, i64, i64, awq_config, i32, i32]
     lib.awq_linear_workspace_size.restype = ctypes.c_size_t
     lib.awq_linear_ws.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32, vp,
                                   ctypes.c_size_t, vp]
@@ -110,20 +112,46 @@ def check(status: int, what: str) -> None:
 # ---------------------------------------------------------------------------
 # torch-facing wrappers
 # ---------------------------------------------------------------------------
+#
+# Every wrapper checks, before any C call: that each argument is a tensor of
+# the expected dtype and shape (so no kernel can read or write past an
+# allocation), then that all tensors sit on one GPU, contiguously.  Shape and
+# dtype errors raise TypeError / ValueError even on machines without a GPU.
 
 def _torch():
     import torch
     return torch
 
 
-def _dev_ptr(t, name):
+def _tensor(t, name, dtype=None, shape=None):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None:
+        ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+        if not ok:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _placed(*named):
+    """All (tensor, name) pairs on one GPU and contiguous; returns the device."""
+    dev = None
+    for t, name in named:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev} like the other tensors")
+    return dev
+
+
+def _ptr(t):
     return ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
 
 
@@ -152,80 +180,150 @@ def empty_packed(N: int, K: int, group_size: int, device):
             torch.empty((N, G), dtype=torch.uint8, device=device))
 
 
+def _check_packed(qweight, scales, zeros, K, group_size):
+    """Packed layer tensors for input width K; returns N."""
+    torch = _torch()
+    if group_size <= 0 or K % group_size or K % 8:
+        raise ValueError(f"K={K} must be a multiple of 8 and of group_size={group_size}")
+    _tensor(qweight, "qweight", torch.int32)
+    if qweight.dim() != 2:
+        raise ValueError("qweight must be 2-D [N][K/8]")
+    N = qweight.shape[0]
+    _tensor(qweight, "qweight", shape=(N, K // 8))
+    _tensor(scales, "scales", torch.float16, (N, K // group_size))
+    _tensor(zeros, "zeros", torch.uint8, (N, K // group_size))
+    return N
+
+
 def awq_quantize_pack(W, group_size: int = 128, s=None, nonfinite_count=None, out=None):
     """Quantize and pack W (fp16 [N][K], on the GPU).  Returns (qweight, scales, zeros)."""
     torch = _torch()
-    if W.dtype != torch.float16 or W.dim() != 2:
-        raise TypeError("W must be a 2-D float16 tensor")
+    _tensor(W, "W", torch.float16)
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [N][K]")
     N, K = W.shape
-    qw, sc, zr = out if out is not None else empty_packed(N, K, group_size, W.device)
+    if group_size <= 0 or K % group_size or K % 8:
+        raise ValueError(f"K={K} must be a multiple of 8 and of group_size={group_size}")
+    if out is not None:
+        qw, sc, zr = out
+        if _check_packed(qw, sc, zr, K, group_size) != N:
+            raise ValueError("out's packed tensors are not for N rows")
+    named = [(W, "W")]
     sp = ctypes.c_void_p(0)
     if s is not None:
-        if s.dtype != torch.float32 or s.shape != (K,):
-            raise TypeError("s must be float32 of shape (K,)")
-        sp = _dev_ptr(s, "s")
+        _tensor(s, "s", torch.float32, (K,))
+        named.append((s, "s"))
+        sp = _ptr(s)
     cp = ctypes.c_void_p(0)
     if nonfinite_count is not None:
-        if nonfinite_count.dtype != torch.int32:
-            raise TypeError("nonfinite_count must be int32")
-        cp = _dev_ptr(nonfinite_count, "nonfinite_count")
-    st = lib.awq_quantize_pack(_dev_ptr(W, "W"), N, K, config(group_size), sp,
-                               _dev_ptr(qw, "qweight"), _dev_ptr(sc, "scales"),
-                               _dev_ptr(zr, "zeros"), cp, _stream(W.device))
+        _tensor(nonfinite_count, "nonfinite_count", torch.int32)
+        if nonfinite_count.numel() < 1:
+            raise ValueError("nonfinite_count must hold one element")
+        named.append((nonfinite_count, "nonfinite_count"))
+        cp = _ptr(nonfinite_count)
+    dev = _placed(*named)
+    if out is None:
+        qw, sc, zr = empty_packed(N, K, group_size, dev)
+    _placed((W, "W"), (qw, "qweight"), (sc, "scales"), (zr, "zeros"))
+    st = lib.awq_quantize_pack(_ptr(W), N, K, config(group_size), sp, _ptr(qw), _ptr(sc),
+                               _ptr(zr), cp, _stream(dev))
     check(st, "awq_quantize_pack")
     return qw, sc, zr
 
 
-def awq_linear_ex(X, qweight, scales, zeros, kernel: int = AWQ_KERNEL_AUTO, group_size: int = 128,
-                  out_dtype=None, out=None):
-    """Y = X * deq(W)^T with an explicit kernel choice (AWQ_KERNEL_*)."""
+def _linear_args(X, qweight, scales, zeros, group_size, out_dtype, out):
+    """Validate a linear call; returns (M, N, K, out, device)."""
     torch = _torch()
+    _tensor(X, "X", (torch.float16, torch.bfloat16))
     if X.dim() != 2:
-        raise TypeError("X must be 2-D")
+        raise ValueError("X must be 2-D [M][K]")
     M, K = X.shape
-    N = qweight.shape[0]
-    if qweight.shape != (N, K // 8) or scales.shape != (N, K // group_size) or zeros.shape != scales.shape:
-        raise ValueError("packed weight shapes do not match X and group_size")
+    N = _check_packed(qweight, scales, zeros, K, group_size)
+    ydt = (torch.float16, torch.bfloat16, torch.float32)
+    if out is not None:
+        _tensor(out, "out", ydt, (M, N))
+    elif out_dtype is not None and out_dtype not in ydt:
+        raise TypeError(f"out_dtype {out_dtype} is not float16, bfloat16 or float32")
+    dev = _placed((X, "X"), (qweight, "qweight"), (scales, "scales"), (zeros, "zeros"))
     if out is None:
-        odt = X.dtype if out_dtype is None else out_dtype
-        out = torch.empty((M, N), dtype=odt, device=X.device)
-    st = lib.awq_linear_ex(_dev_ptr(X, "X"), _dtype_code(X.dtype), _dev_ptr(qweight, "qweight"),
-                           _dev_ptr(scales, "scales"), _dev_ptr(zeros, "zeros"), M, N, K,
-                           config(group_size), _dev_ptr(out, "Y"), _dtype_code(out.dtype),
-                           int(kernel), _stream(X.device))
+        out = torch.empty((M, N), dtype=X.dtype if out_dtype is None else out_dtype, device=dev)
+    _placed((X, "X"), (out, "out"))
+    return M, N, K, out, dev
+
+
+def awq_linear_workspace_size(M: int, N: int, K: int, group_size: int = 128,
+                              x_dtype=None, kernel: int = AWQ_KERNEL_AUTO) -> int:
+    """Workspace bytes the GEMM path needs (awq_linear_workspace_size); x_dtype
+    is a torch dtype (default float16)."""
+    torch = _torch()
+    xd = AWQ_F16 if x_dtype is None or x_dtype == torch.float16 else _dtype_code(x_dtype)
+    return int(lib.awq_linear_workspace_size(M, N, K, config(group_size), xd, int(kernel)))
+
+
+def _workspace_arg(workspace, need, dev):
+    torch = _torch()
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be a tensor, None or 'auto'")
+        if need == 0:
+            return None
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        return None
+    _tensor(workspace, "workspace")
+    _placed((workspace, "workspace"))
+    if workspace.device != dev:
+        raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
+    return workspace
+
+
+def awq_linear_ex(X, qweight, scales, zeros, kernel: int = AWQ_KERNEL_AUTO,
+                  group_size: int = 128, out_dtype=None, out=None, workspace="auto"):
+    """Y = X * deq(W)^T with an explicit kernel choice (AWQ_KERNEL_*).
+
+    ``workspace``: 'auto' (a torch-allocated buffer of
+    awq_linear_workspace_size bytes when the call needs one), a uint8 tensor
+    of at least that size (any contents), or None (the scratch-free plan, as
+    awq_linear)."""
+    if isinstance(workspace, str) and workspace != "auto":
+        raise ValueError("workspace must be a tensor, None or 'auto'")
+    if workspace is not None and not isinstance(workspace, str):
+        _tensor(workspace, "workspace")
+    M, N, K, out, dev = _linear_args(X, qweight, scales, zeros, group_size, out_dtype, out)
+    need = awq_linear_workspace_size(M, N, K, group_size, X.dtype, kernel)
+    ws = _workspace_arg(workspace, need, dev)
+    st = lib.awq_linear_ex(_ptr(X), _dtype_code(X.dtype), _ptr(qweight), _ptr(scales),
+                           _ptr(zeros), M, N, K, config(group_size), _ptr(out),
+                           _dtype_code(out.dtype), int(kernel),
+                           ctypes.c_void_p(0) if ws is None else _ptr(ws),
+                           0 if ws is None else ws.numel() * ws.element_size(), _stream(dev))
     check(st, "awq_linear_ex")
     return out
 
 
 def awq_linear(X, qweight, scales, zeros, group_size: int = 128, out_dtype=None, out=None):
-    """Y = X * deq(W)^T; small M runs the GEMV kernel, larger M the GEMM."""
-    return awq_linear_ex(X, qweight, scales, zeros, AWQ_KERNEL_AUTO, group_size, out_dtype, out)
-
-
-def awq_linear_workspace_size(M: int, N: int, K: int, group_size: int = 128) -> int:
-    return int(lib.awq_linear_workspace_size(M, N, K, config(group_size)))
+    """Y = X * deq(W)^T with no scratch memory (the C awq_linear): small M
+    runs the GEMV, larger M the GEMM without a K split; bf16 activations on
+    the GEMM path raise AwqError (use awq_linear_ex or awq_linear_ws)."""
+    M, N, K, out, dev = _linear_args(X, qweight, scales, zeros, group_size, out_dtype, out)
+    st = lib.awq_linear(_ptr(X), _dtype_code(X.dtype), _ptr(qweight), _ptr(scales), _ptr(zeros),
+                        M, N, K, config(group_size), _ptr(out), _dtype_code(out.dtype),
+                        _stream(dev))
+    check(st, "awq_linear")
+    return out
 
 
 def awq_linear_ws(X, qweight, scales, zeros, workspace, group_size: int = 128, out_dtype=None,
                   out=None):
     """awq_linear with a caller workspace (uint8 tensor of at least
     awq_linear_workspace_size bytes, any contents); the call allocates nothing."""
-    torch = _torch()
-    if X.dim() != 2:
-        raise TypeError("X must be 2-D")
-    M, K = X.shape
-    N = qweight.shape[0]
-    if qweight.shape != (N, K // 8) or scales.shape != (N, K // group_size) or zeros.shape != scales.shape:
-        raise ValueError("packed weight shapes do not match X and group_size")
-    if out is None:
-        odt = X.dtype if out_dtype is None else out_dtype
-        out = torch.empty((M, N), dtype=odt, device=X.device)
-    wp = ctypes.c_void_p(0) if workspace is None else _dev_ptr(workspace, "workspace")
-    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.awq_linear_ws(_dev_ptr(X, "X"), _dtype_code(X.dtype), _dev_ptr(qweight, "qweight"),
-                           _dev_ptr(scales, "scales"), _dev_ptr(zeros, "zeros"), M, N, K,
-                           config(group_size), _dev_ptr(out, "Y"), _dtype_code(out.dtype), wp, wb,
-                           _stream(X.device))
+    M, N, K, out, dev = _linear_args(X, qweight, scales, zeros, group_size, out_dtype, out)
+    ws = _workspace_arg(workspace, 0, dev)
+    st = lib.awq_linear_ws(_ptr(X), _dtype_code(X.dtype), _ptr(qweight), _ptr(scales),
+                           _ptr(zeros), M, N, K, config(group_size), _ptr(out),
+                           _dtype_code(out.dtype),
+                           ctypes.c_void_p(0) if ws is None else _ptr(ws),
+                           0 if ws is None else ws.numel() * ws.element_size(), _stream(dev))
     check(st, "awq_linear_ws")
     return out
 
@@ -239,28 +337,45 @@ def awq_scale_search(X, W, group_size: int = 128, alphas=None, workspace=None, o
     """Alpha-grid scale search.  Returns a dict with best_index, losses (numpy
     fp64), s (fp32 [K] tensor) and the packed weights for the chosen s."""
     torch = _torch()
+    _tensor(X, "X", torch.float16)
+    _tensor(W, "W", torch.float16)
+    if X.dim() != 2 or W.dim() != 2:
+        raise ValueError("X must be [M][K] and W [N][K]")
     M, K = X.shape
     N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError(f"W has {W.shape[1]} input channels, X has {K}")
     n_alpha = 20 if alphas is None else len(alphas)
     need = awq_scale_search_workspace_size(M, N, K, group_size, n_alpha)
     if need == 0:
         check(AWQ_ERR_INVALID_ARG, "awq_scale_search_workspace_size")
+    if out is not None:
+        qw, sc, zr = out
+        if _check_packed(qw, sc, zr, K, group_size) != N:
+            raise ValueError("out's packed tensors are not for N rows")
+    if workspace is not None:
+        _tensor(workspace, "workspace")
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                             f"bytes, {need} needed")
+    dev = _placed((X, "X"), (W, "W"))
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
-    qw, sc, zr = out if out is not None else empty_packed(N, K, group_size, X.device)
-    best_s = torch.empty(K, dtype=torch.float32, device=X.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None:
+        qw, sc, zr = empty_packed(N, K, group_size, dev)
+    best_s = torch.empty(K, dtype=torch.float32, device=dev)
+    _placed((X, "X"), (workspace, "workspace"), (qw, "qweight"), (sc, "scales"), (zr, "zeros"))
     a_ptr = None
     if alphas is not None:
         a_arr = (ctypes.c_double * n_alpha)(*[float(a) for a in alphas])
         a_ptr = ctypes.cast(a_arr, ctypes.POINTER(ctypes.c_double))
     best = ctypes.c_int32(-1)
     losses = (ctypes.c_double * n_alpha)()
-    st = lib.awq_scale_search(_dev_ptr(X, "X"), _dev_ptr(W, "W"), M, N, K, config(group_size),
-                              a_ptr, n_alpha, _dev_ptr(workspace, "workspace"),
+    st = lib.awq_scale_search(_ptr(X), _ptr(W), M, N, K, config(group_size),
+                              a_ptr, n_alpha, _ptr(workspace),
                               workspace.numel() * workspace.element_size(),
-                              ctypes.byref(best), losses, _dev_ptr(best_s, "best_s"),
-                              _dev_ptr(qw, "qweight"), _dev_ptr(sc, "scales"),
-                              _dev_ptr(zr, "zeros"), _stream(X.device))
+                              ctypes.byref(best), losses, _ptr(best_s),
+                              _ptr(qw), _ptr(sc), _ptr(zr), _stream(dev))
     check(st, "awq_scale_search")
     return {"best_index": int(best.value), "losses": np.array(losses[:], dtype=np.float64),
             "s": best_s, "qweight": qw, "scales": sc, "zeros": zr}

@@ -74,13 +74,17 @@ def compile_one(src: str, obj: str, verbose: bool) -> None:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link LIB_PATH (always rebuilds)."""
+    """Compile every source (in parallel, one hipcc per translation unit) and
+    link LIB_PATH (always rebuilds)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     with tempfile.TemporaryDirectory(prefix="awq355_build_") as tmp:
-        objs = []
-        for src in SOURCES:
-            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            compile_one(src, obj, verbose)
-            objs.append(obj)
+        objs = [os.path.join(tmp, os.path.splitext(src)[0] + ".o") for src in SOURCES]
+        jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            for fut in [pool.submit(compile_one, src, obj, verbose)
+                        for src, obj in zip(SOURCES, objs)]:
+                fut.result()
         tmp_lib = os.path.join(tmp, LIB_NAME)
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         if verbose:

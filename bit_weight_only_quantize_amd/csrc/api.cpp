@@ -8,10 +8,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <map>
-#include <mutex>
-#include <utility>
-#include <vector>
 
 #include "../../include/awq355.h"
 #include "awq_internal.h"
@@ -40,47 +36,12 @@ awq_status hip_status(hipError_t e, const char *where) {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// GEMM scratch of awq_linear / awq_linear_ex (split-K partials, bf16 row
-// factors and converted rows), one per device, allocated the first time a
-// call needs it (or needs more).  A buffer is never freed: a larger one
-// replaces it for later calls, and HIP graphs captured with the old one stay
-// valid.  Its contents between calls do not matter.
-struct Scratch {
-  void *ptr = nullptr;
-  size_t bytes = 0;
-};
-std::mutex g_scratch_mu;
-std::map<int, Scratch> g_scratch;
-
-hipError_t linear_scratch(size_t bytes, void **out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  Scratch &s = g_scratch[dev];
-  if (s.bytes < bytes) {
-    const size_t want = bytes > 2 * s.bytes ? bytes : 2 * s.bytes;
-    void *p = nullptr;
-    e = hipMalloc(&p, want);
-    if (e != hipSuccess) return e;
-    s.ptr = p;
-    s.bytes = want;
-  }
-  *out = s.ptr;
-  return hipSuccess;
-}
-
-// Automatic kernel choice (measured on MI355X, fp16, graph replays): the GEMV
-// up to M = 8; from 9 to AWQ_GEMV_MAX_M rows only for layers of at most 5e7
-// weights.  Above that the GEMV, whose activation reads grow with M once the
-// rows no longer fit its LDS staging, is slower than the split-K GEMM (at
-// M = 16: 28.7 vs 22.0 us for 13824 x 5120; the GEMV stays ahead on the
-// 4096 x 4096 and 4096 x 11008 layers).
-// GEMV or GEMM, from measured times on 7B- and 13B-class layers: the GEMV
-// wins wherever it stages the activation rows in LDS; unstaged, its
-// activation reads grow with M, and it loses where each wave walks a long
-// chain of groups (> 8), beyond M = 8, or beyond M = 12 on layers of at most
-// 5e7 weights.
+// Automatic kernel choice, from measured times (fp16, graph replays) on 7B-
+// and 13B-class layers: the GEMV wins wherever it stages the activation rows
+// in LDS; unstaged, its activation reads grow with M, and it loses to the
+// split-K GEMM where each wave walks a long chain of groups (> 8), beyond
+// M = 8, or beyond M = 12 on layers of at most 5e7 weights (at M = 16: 28.7
+// vs 22.0 us for 13824 x 5120).
 bool auto_gemv(int64_t M, int64_t N, int64_t K, int g) {
   if (M > AWQ_GEMV_MAX_M || !awq::gemv_supported(M, N, K, g)) return false;
   if (awq::gemv_stages_activations(M, N, K)) return true;
@@ -233,48 +194,50 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
 
 namespace {
 
-// awq_linear_ex with an optional caller workspace (NULL: the library scratch).
-awq_status linear_impl(const void *X, int32_t x_dtype, const uint32_t *qweight,
+// Whether the automatic choice (or the explicit `kernel`) runs the GEMV.
+bool runs_gemv(int64_t M, int64_t N, int64_t K, int gs, int32_t kernel) {
+  return kernel == AWQ_KERNEL_GEMV || (kernel == AWQ_KERNEL_AUTO && auto_gemv(M, N, K, gs));
+}
+
+// The linear layer with the GEMM's scratch from the caller's workspace, or
+// (workspace == NULL) with a scratch-free plan.
+awq_status linear_impl(const char *who, const void *X, int32_t x_dtype, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
                        int64_t K, awq_config cfg, void *Y, int32_t y_dtype, int32_t kernel,
-                       void *workspace, size_t workspace_bytes, bool caller_ws,
-                       awq_stream_t stream) {
+                       void *workspace, size_t workspace_bytes, awq_stream_t stream) {
   awq_status st =
       check_linear(X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype, kernel);
   if (st != AWQ_OK) return st;
-  const awq::XType xt = x_dtype == AWQ_F16 ? awq::XType::F16 : awq::XType::BF16;
-  const awq::GemmPlan plan = awq::gemm_plan(M > 0 ? M : 1, N > 0 ? N : 1, K, xt);
-  const bool gemv_ok = awq::gemv_supported(M, N > 0 ? N : 1, K, cfg.group_size);
-  if (kernel == AWQ_KERNEL_GEMV && !gemv_ok)
-    return fail(AWQ_ERR_UNSUPPORTED, "GEMV kernel cannot serve K=%lld", (long long)K);
-  const bool gemv = kernel == AWQ_KERNEL_GEMV ||
-                    (kernel == AWQ_KERNEL_AUTO && auto_gemv(M, N, K, cfg.group_size));
-  if (caller_ws && !gemv && plan.workspace_bytes > 0) {
-    if (!workspace) return fail(AWQ_ERR_INVALID_ARG, "this shape needs a workspace");
-    if (!aligned(workspace, 256)) return fail(AWQ_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-    // The documented minimum (awq_linear_workspace_size) covers both
-    // activation types.
-    const size_t need = awq::gemm_workspace_bytes(M, N, K);
-    if (workspace_bytes < need)
-      return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-  }
+  if (kernel == AWQ_KERNEL_GEMV && !awq::gemv_supported(M, N > 0 ? N : 1, K, cfg.group_size))
+    return fail(AWQ_ERR_UNSUPPORTED, "%s: the GEMV kernel cannot serve K=%lld", who,
+                (long long)K);
+  if (workspace && !aligned(workspace, kAlign))
+    return fail(AWQ_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", who);
   if (M == 0 || N == 0) return ok();
+  const awq::XType xt = x_dtype == AWQ_F16 ? awq::XType::F16 : awq::XType::BF16;
   const awq::YType yt = y_dtype == AWQ_F16    ? awq::YType::F16
                         : y_dtype == AWQ_BF16 ? awq::YType::BF16
                                               : awq::YType::F32;
   const hipStream_t hs = as_stream(stream);
-  if (gemv)
+  if (runs_gemv(M, N, K, cfg.group_size, kernel))
     return hip_status(awq::launch_gemv(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size, Y,
                                        yt, hs),
-                      "awq_linear (gemv)");
-  void *scratch = caller_ws ? workspace : nullptr;
-  if (!caller_ws && plan.workspace_bytes > 0) {
-    const hipError_t e = linear_scratch(plan.workspace_bytes, &scratch);
-    if (e != hipSuccess) return hip_status(e, "awq_linear (split-K scratch)");
+                      who);
+  const awq::GemmPlan plan =
+      awq::gemm_plan(M, N, K, xt, workspace ? awq::Scratch::Full : awq::Scratch::None);
+  if (plan.workspace_bytes > 0) {
+    if (!workspace)
+      return fail(AWQ_ERR_WORKSPACE,
+                  "%s: bf16 activations on the GEMM path need a workspace of %zu bytes "
+                  "(awq_linear_workspace_size)",
+                  who, plan.workspace_bytes);
+    if (workspace_bytes < plan.workspace_bytes)
+      return fail(AWQ_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who,
+                  workspace_bytes, plan.workspace_bytes);
   }
   return hip_status(awq::launch_gemm(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size, Y,
-                                     yt, scratch, hs),
-                    "awq_linear (gemm)");
+                                     yt, plan, workspace, hs),
+                    who);
 }
 
 }  // namespace
@@ -282,31 +245,37 @@ awq_status linear_impl(const void *X, int32_t x_dtype, const uint32_t *qweight,
 awq_status awq_linear_ex(const void *X, int32_t x_dtype, const uint32_t *qweight,
                          const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
                          int64_t K, awq_config cfg, void *Y, int32_t y_dtype, int32_t kernel,
-                         awq_stream_t stream) {
-  return linear_impl(X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype, kernel,
-                     nullptr, 0, false, stream);
+                         void *workspace, size_t workspace_bytes, awq_stream_t stream) {
+  return linear_impl("awq_linear_ex", X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y,
+                     y_dtype, kernel, workspace, workspace_bytes, stream);
 }
 
-size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg) {
+size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg,
+                                 int32_t x_dtype, int32_t kernel) {
   if (check_config(cfg, K) != AWQ_OK || M < 0 || N < 0) return 0;
-  if (M == 0 || N == 0) return 0;
-  if (auto_gemv(M, N, K, cfg.group_size)) return 0;
-  return awq::gemm_workspace_bytes(M, N, K);
+  if (M > ((int64_t)1 << 31) || N > ((int64_t)1 << 31)) return 0;
+  if (x_dtype != AWQ_F16 && x_dtype != AWQ_BF16) return 0;
+  if (kernel != AWQ_KERNEL_AUTO && kernel != AWQ_KERNEL_GEMV && kernel != AWQ_KERNEL_GEMM)
+    return 0;
+  if (M == 0 || N == 0 || runs_gemv(M, N, K, cfg.group_size, kernel)) return 0;
+  if (!awq::gemm_supported(N, K, false)) return 0;
+  const awq::XType xt = x_dtype == AWQ_F16 ? awq::XType::F16 : awq::XType::BF16;
+  return awq::gemm_plan(M, N, K, xt, awq::Scratch::Full).workspace_bytes;
 }
 
 awq_status awq_linear_ws(const void *X, int32_t x_dtype, const uint32_t *qweight,
                          const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
                          int64_t K, awq_config cfg, void *Y, int32_t y_dtype, void *workspace,
                          size_t workspace_bytes, awq_stream_t stream) {
-  return linear_impl(X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype,
-                     AWQ_KERNEL_AUTO, workspace, workspace_bytes, true, stream);
+  return linear_impl("awq_linear_ws", X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y,
+                     y_dtype, AWQ_KERNEL_AUTO, workspace, workspace_bytes, stream);
 }
 
 awq_status awq_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,
                       const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
                       int64_t K, awq_config cfg, void *Y, int32_t y_dtype, awq_stream_t stream) {
-  return awq_linear_ex(X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype,
-                       AWQ_KERNEL_AUTO, stream);
+  return linear_impl("awq_linear", X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype,
+                     AWQ_KERNEL_AUTO, nullptr, 0, stream);
 }
 
 size_t awq_scale_search_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg,

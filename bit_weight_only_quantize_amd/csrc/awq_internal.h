@@ -38,6 +38,18 @@ struct SplitK {
 };
 
 // ---- the quantized GEMM (any M) -------------------------------------------------
+// What scratch memory a GEMM plan may use.
+enum class Scratch : int {
+  Full = 0,     // K split when the tiles cannot fill the CUs; bf16: row factors, and a
+                // converted fp16 copy of X (M * K * 2 bytes) for the 256-row tile
+  Bounded = 1,  // as Full, but bf16 input never takes the 256-row tile (no copy of X):
+                // at most kBoundedPartialBytes of partials plus M * 4 bytes of factors
+  None = 2,     // nothing: K is never split; bf16 input still needs its row factors
+};
+// Upper bound of a plan's split-K partials: tiles * splits <= 256 slots of at
+// most 128 x 256 fp32.
+constexpr size_t kBoundedPartialBytes = (size_t)256 * 128 * 256 * 4;
+
 // Row tile (16 * mt rows), K split and workspace of a quantized GEMM
 // (gemm_f16.hip; gemm_plan and the wrappers below are in linear_gemm.hip).
 struct GemmPlan {
@@ -47,24 +59,23 @@ struct GemmPlan {
   size_t xh_offset;        // bf16 input, 256-row tile: X scaled to fp16 ([M][K]), else 0
   size_t workspace_bytes;  // 0 when splits == 1 and the input is fp16; partials first
 };
-// The plan of the kernel that serves activations of type xt (fp16: the
-// kernel of gemm_f16.hip).
-GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, XType xt);
-// Workspace that serves either activation type.
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
-// `workspace` (gemm_plan(...).workspace_bytes, 256-byte aligned; its contents
-// on entry are ignored) is needed only when the plan's workspace_bytes > 0.
+// The plan of the kernel that serves activations of type xt.
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, XType xt, Scratch sc);
+// Runs `plan` (from gemm_plan with the same M, N, K and xt).  `workspace`
+// (plan.workspace_bytes, 256-byte aligned; its contents on entry are ignored)
+// is needed only when plan.workspace_bytes > 0.
 hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M,
                        int64_t N, int64_t K, int gs, void *Y, YType yt,
-                       void *workspace, hipStream_t st);
+                       const GemmPlan &plan, void *workspace, hipStream_t st);
 
 // ---- gemm_f16.hip (the quantized GEMM: fp16, or bf16 converted to fp16) ---------------
 // Row tile (16 * mt rows), K split and workspace of the GEMM.
-GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16);
+GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16, Scratch sc);
 hipError_t launch_gemm_f16(const uint16_t *X, bool bf16, const uint32_t *qweight,
                            const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
-                           int64_t K, int gs, void *Y, YType yt, void *workspace, hipStream_t st);
+                           int64_t K, int gs, void *Y, YType yt, const GemmPlan &plan,
+                           void *workspace, hipStream_t st);
 
 // linear_gemm.hip: the search's reference GEMM, X * W^T with W fp16 [N][K],
 // fp32 output.

@@ -48,46 +48,25 @@ __device__ __forceinline__ int nibble_of_channel(int i) { return (i >> 1) + 4 * 
 // DeqRegs per kernel, outside the loops (the empty asm statements only hide
 // the constant values from the optimizer so that they stay in registers).
 struct DeqRegs {
-  uint32_t lo, hi;            // 0x000F000F, 0x00F000F0
-  uint32_t e1024, e64, e128;  // fp16 1024.0, fp16 64.0, bf16 128.0 in both halves
+  uint32_t lo, hi;      // 0x000F000F, 0x00F000F0
+  uint32_t e1024, e64;  // fp16 1024.0 and fp16 64.0 in both halves
   __device__ __forceinline__ DeqRegs()
-      : lo(0x000F000Fu), hi(0x00F000F0u), e1024(0x64006400u), e64(0x54005400u),
-        e128(0x43004300u) {
+      : lo(0x000F000Fu), hi(0x00F000F0u), e1024(0x64006400u), e64(0x54005400u) {
     asm volatile("" : "+v"(lo));
     asm volatile("" : "+v"(hi));
     asm volatile("" : "+s"(e1024));
     asm volatile("" : "+s"(e64));
-    asm volatile("" : "+s"(e128));
   }
 };
 
-// fp16, biased codes of word w as the B operand of one 16x16x32 MFMA slot:
-// OR-ing a code held in bits 0..3 of a half into the mantissa of 1024.0
-// (0x6400) gives 1024 + q exactly; a code held in bits 4..7 OR-ed into 64.0
-// (0x5400) gives 64 + q exactly.  Channel pairs (0,1) and (4,5) come out as
-// 1024 + q, pairs (2,3) and (6,7) as 64 + q.  Five VALU instructions per
-// 8 weights.
-__device__ __forceinline__ u32x4 deq_f16_biased(uint32_t w, const DeqRegs &r) {
-  const uint32_t w8 = w >> 8;
-  return u32x4{(w & r.lo) | r.e1024, (w & r.hi) | r.e64, (w8 & r.lo) | r.e1024,
-               (w8 & r.hi) | r.e64};
-}
-
-// The B operand that removes the bias and the zero point from
-// deq_f16_biased: -(1024 + z) and -(64 + z) in the matching slots, built from
-// the fp16 bit patterns directly (0xE400 | z is -(1024 + z); 0xD400 + 16 z is
-// -(64 + z)).  mfma(a, deq_f16_biased(w)) + mfma(a, corr_f16(z)) is the
-// product of a with the exact integers q - z.
-__device__ __forceinline__ u32x4 corr_f16(uint32_t z) {
-  const uint32_t a = 0xE400u | z;
-  const uint32_t b = 0xD400u + (z << 4);
-  const uint32_t A = a | (a << 16), B = b | (b << 16);
-  return u32x4{A, B, A, B};
-}
-
 // fp16: the exact integers (q - z) for the 8 channels of word w, as 8 fp16 in
-// channel order (biased codes minus (1024 + z) or (64 + z) in packed half
-// arithmetic: exact, since every value is an integer of at most 11 bits).
+// channel order.  OR-ing a code held in bits 0..3 of a half into the mantissa
+// of 1024.0 (0x6400) gives 1024 + q exactly, a code held in bits 4..7 OR-ed
+// into 64.0 (0x5400) gives 64 + q exactly (channel pairs (0,1) and (4,5) come
+// out as 1024 + q, pairs (2,3) and (6,7) as 64 + q); a packed half
+// subtraction of 1024 + z or 64 + z then leaves q - z, exactly, since every
+// value involved is an integer of at most 11 bits.  Nine VALU instructions
+// per 8 weights (a shift, four and-or, four packed subtractions).
 struct DeqF16 {
   uint32_t nz1024, nz64;  // -(1024 + z), -(64 + z) in both halves (fp16 bits)
   __device__ __forceinline__ explicit DeqF16(uint32_t z) {
@@ -111,25 +90,24 @@ struct DeqF16 {
   }
 };
 
-// bf16: 128 + q exactly (OR into the mantissa of 128.0 = 0x4300).  gfx950 has
-// no packed bf16 add, so the zero point is removed after the product, either
-// with an MFMA against corr_bf16(z) or with a row-sum MFMA:
-// sum_k a_k (q_k - z) = sum_k a_k (128 + q_k) - (128 + z) sum_k a_k.
-__device__ __forceinline__ u32x4 deq_bf16_biased(uint32_t w, const DeqRegs &r) {
-  return u32x4{(w & r.lo) | r.e128, ((w >> 4) & r.lo) | r.e128, ((w >> 8) & r.lo) | r.e128,
-               ((w >> 12) & r.lo) | r.e128};
-}
-
-// -(128 + z) in all 8 bf16 slots (0xC300 | z; exact, 128 + z < 256).
-__device__ __forceinline__ u32x4 corr_bf16(uint32_t z) {
-  const uint32_t a = 0xC300u | z;
-  const uint32_t A = a | (a << 16);
-  return u32x4{A, A, A, A};
-}
-
-// bf16 1.0 in all 8 slots: an MFMA against it yields the row sums of A.
-__device__ __forceinline__ u32x4 bf16_ones() {
-  return u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+// bf16: the exact integers (q - z) as 8 bf16 in channel order, from the fp16
+// ones.  gfx950 has no packed bf16 arithmetic; widening each fp16 half to
+// fp32 is exact, and an integer of at most 4 significant bits has zero low
+// 16 bits in fp32, so the upper half of its fp32 pattern is its bf16
+// encoding.  Three VALU operations per pair (two conversions and one byte
+// permute) on top of DeqF16.
+__device__ __forceinline__ u32x4 f16_pairs_to_bf16(u32x4 h) {
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t hi = h[i];
+    const f16x2 p = __builtin_bit_cast(f16x2, hi);
+    const uint32_t lo32 = __builtin_bit_cast(uint32_t, (float)p[0]);
+    const uint32_t hi32 = __builtin_bit_cast(uint32_t, (float)p[1]);
+    // bytes 2,3 of lo32 -> bytes 0,1; bytes 2,3 of hi32 -> bytes 2,3
+    out[i] = __builtin_amdgcn_perm(hi32, lo32, 0x07060302u);
+  }
+  return out;
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {

@@ -4,13 +4,15 @@
 // The GEMM variant of the quantized linear layer ("AWQ Advanced Usage Guide",
 // "WQLinear Kernel Variants": batch sizes above one), Y = X * deq(W)^T with
 // deq = (q - z) * s per group of g input channels (the pages' zero-point,
-// group-wise int4 configuration).  Like the GEMM kernels the pages describe,
-// it dequantizes each weight to fp16 and runs an fp16 matrix product with
-// fp32 accumulation: the B operand is fp16((q - z) * s), the exact integer
-// q - z times the group's fp16 scale rounded once (relative error at most
-// 2^-11 per weight).  The search's loss variant (EPI = 1) keeps B the exact
-// integer q - z, scales each group's fp32 sum, and reduces (Yref - Y)^2 of
-// its tile instead of storing Y.
+// group-wise int4 configuration).  The pages do not say how a kernel
+// dequantizes.  Tiles of 64 rows and more (MFMA-bound from M = 256 on) use
+// the B operand fp16((q - z) * s), the exact integer q - z times the group's
+// fp16 scale rounded once (relative error at most 2^-11 per weight, within
+// the output tolerance on the layer configurations: about 3e-4 relative
+// Frobenius error), so the MFMAs accumulate straight into the tile.  The
+// 32-row tile and the search's loss variant (EPI = 1) keep B the exact
+// integer q - z and scale each group's fp32 sum; the loss variant reduces
+// (Yref - Y)^2 of its tile instead of storing Y.
 //
 // Work split, chosen from measured MI355X rates (one wave keeps the MFMA unit
 // busy when it issues about two VALU operations or fewer per 16x16x32 MFMA;
@@ -112,9 +114,12 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 
 }  // namespace
 
-// EPI: 0 stores Y with fp16-dequantized weights; 1 (the search's loss) uses
-// the exact integer q - z with the group scale on fp32 group sums and reduces
-// (Yref - Y)^2 of the tile to one fp64 partial instead of storing Y.
+// EPI: 0 stores Y; 1 (the search's loss) reduces (Yref - Y)^2 of the tile to
+// one fp64 partial instead of storing Y.  The B operand is the exact integer
+// q - z with the group scale applied to fp32 group sums for the loss and for
+// the 32-row tile (batched decode, where the VALU work per MFMA is highest
+// anyway and exact products keep the error independent of the activations'
+// mean); larger tiles use fp16((q - z) * s).
 template <int GS, int YT, int MT, bool KTAIL, bool BF16X, int EPI>
 __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
                                               const uint32_t *__restrict__ qweight,
@@ -124,7 +129,7 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
                                               const float *__restrict__ rowf,
                                               const float *__restrict__ Yref,
                                               double *__restrict__ partials) {
-  constexpr bool kExact = EPI == 1;
+  constexpr bool kExact = EPI == 1 || MT <= 2;
   constexpr int kBM = 16 * MT;
   constexpr int kWpl = GS / 32;      // packed words per lane per group and column
   constexpr int kGPB = kBK / GS;     // groups per K block
@@ -722,8 +727,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 
 // Per-row activation factor for bf16 input: the power of two that brings the
 // row's largest magnitude into [2^14, 2^15), so every value of the row is
-// within fp16's range and those within 2^38 of the largest keep their full
-// precision (exponent capped to stay a normal fp32); 1 for rows that are all
+// within fp16's range.  Scaled values of at least 2^-17 (every value at least
+// 2^-31 times the row's largest) are fp16 numbers and keep their full 8-bit
+// precision; smaller ones fall on fp16's subnormal grid (spacing 2^-24) and
+// are truncated, with an absolute error below 2^-38 times the row's largest
+// magnitude (exponent capped to stay a normal fp32); 1 for rows that are all
 // zero or hold inf or NaN.  One workgroup per row.  With Xh, the row is also
 // written there multiplied by its factor and converted to fp16 (round toward
 // zero, as the GEMM's own staging does), for the 256-row tile.
@@ -868,22 +876,26 @@ hipError_t f16_go(const uint16_t *X, const uint32_t *qw, const uint16_t *sc, con
 
 // Row tile and K split.  M <= 32 and M <= 64 take 32- and 64-row tiles (the
 // weight stream dominates there), larger M the 128-row tile, and shapes whose
-// 256-row tiles fill every CU without a K split the 256-row tile.  When the
-// tiles cannot give every CU a workgroup, K is split into as many parts as
-// still fit in one round (at most 8, at least two K blocks each), with the
+// 256-row tiles fill every CU without a K split the 256-row tile (not for
+// bf16 input under Scratch::Bounded, which has no room for its converted
+// copy of X).  When the tiles cannot give every CU a workgroup, K is split
+// (unless Scratch::None) into as many parts as still fit in one round (up to
+// 8 with at least two K blocks each, up to 16 with at least four), with the
 // fp32 partial tiles in the workspace.  bf16 input adds one fp32 activation
 // factor per row, and with the 256-row tile its fp16 copy scaled by them.
-GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16) {
+GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16, Scratch sc) {
   GemmPlan p{};
   p.mt = M <= 32 ? 2 : M <= 64 ? 4 : 8;
   // 256-row tiles that alone fill every CU: the 256-row tile (each
   // dequantized weight then feeds 16 MFMAs instead of 8)
-  if (K % kBK == 0 && ((M + 255) / 256) * ((N + kBN - 1) / kBN) >= kSlots) p.mt = 16;
+  if (K % kBK == 0 && ((M + 255) / 256) * ((N + kBN - 1) / kBN) >= kSlots &&
+      !(bf16 && sc == Scratch::Bounded))
+    p.mt = 16;
   const int64_t bm = 16 * p.mt;
   p.tiles = ((M + bm - 1) / bm) * ((N + kBN - 1) / kBN);
   const int64_t nkb = (K + kBK - 1) / kBK;
   p.splits = 1;
-  if (p.tiles < kSlots) {
+  if (p.tiles < kSlots && sc != Scratch::None) {
     int64_t sp = kSlots / p.tiles;
     // at least 2 K blocks per split up to 8 splits, at least 4 beyond (up to
     // 16): a split of few blocks is mostly pipeline fill and drain
@@ -909,9 +921,9 @@ GemmPlan gemm_f16_plan(int64_t M, int64_t N, int64_t K, bool bf16) {
 
 hipError_t launch_gemm_f16(const uint16_t *X, bool bf16, const uint32_t *qweight,
                            const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
-                           int64_t K, int gs, void *Y, YType yt, void *workspace, hipStream_t st) {
+                           int64_t K, int gs, void *Y, YType yt, const GemmPlan &p,
+                           void *workspace, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  const GemmPlan p = gemm_f16_plan(M, N, K, bf16);
   if (p.workspace_bytes > 0 && !workspace) return hipErrorInvalidValue;
   SplitK sk{1, nullptr};
   if (p.splits > 1) {

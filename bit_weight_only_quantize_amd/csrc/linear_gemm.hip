@@ -206,22 +206,16 @@ bool gemm_supported(int64_t N, int64_t K, bool dense) {
   return (dense ? N * K * 2 : N * K / 2) <= lim && rows_per_launch(N, K, 256) > 0;
 }
 
-GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, XType xt) {
-  return gemm_f16_plan(M, N, K, xt == XType::BF16);
-}
-
-// The bf16 plan adds the row factors (and the converted rows) to the fp16
-// plan's workspace, so it serves either activation type.
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  return gemm_f16_plan(M, N, K, true).workspace_bytes;
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, XType xt, Scratch sc) {
+  return gemm_f16_plan(M, N, K, xt == XType::BF16, sc);
 }
 
 hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
-                       int64_t K, int gs, void *Y, YType yt, void *workspace,
-                       hipStream_t st) {
+                       int64_t K, int gs, void *Y, YType yt, const GemmPlan &plan,
+                       void *workspace, hipStream_t st) {
   return launch_gemm_f16(reinterpret_cast<const uint16_t *>(X), xt == XType::BF16, qweight,
-                         scales, zeros, M, N, K, gs, Y, yt, workspace, st);
+                         scales, zeros, M, N, K, gs, Y, yt, plan, workspace, st);
 }
 
 hipError_t launch_gemm_dense_f32(const uint16_t *X, const uint16_t *W, int64_t M, int64_t N,

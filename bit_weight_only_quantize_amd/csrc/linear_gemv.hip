@@ -13,10 +13,12 @@
 // kq = l >> 4) reads 16 bytes (32 codes) of column c per group and the
 // contraction runs on the 16x16x32 MFMA with the activation rows padded to
 // 16: the matrix core does the multiply-adds, leaving the VALU only the
-// dequantization (about 9 instructions per 8 weights).  The per-group scale is
-// applied to the fp32 partial of each group, so the B operand is the exact
-// integer q - z and no rounding of dequantized weights ever happens.
-// Partials of the NW waves are combined through LDS in a fixed order.
+// dequantization (9 instructions per 8 weights for fp16 activations, 21 for
+// bf16).  The B operand is the exact integer q - z, so every product
+// a * (q - z) is exact in fp32 and the only roundings are those of the fp32
+// sums; the group's fp16 scale multiplies the fp32 sum of each group once.
+// No dequantized weight is ever rounded.  Partials of the NW waves are
+// combined through LDS in a fixed order.
 
 #include "awq_internal.h"
 #include "device_common.h"
@@ -230,18 +232,17 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
       const uint32_t zr = zs[gs];
       const uint16_t sb = ss[gs];
       const float sc = g < G ? half_bits_to_float(sb) : 0.0f;
-      // Biased codes times a, plus a times the bias-and-zero correction: two
-      // independent MFMA chains, summed once per group.
-      const u32x4 corr = kBF16 ? corr_bf16(zr) : corr_f16(zr);
-      f32x4 t = {0.f, 0.f, 0.f, 0.f}, tc = {0.f, 0.f, 0.f, 0.f};
+      // The exact integers q - z times a, summed in fp32 over the group
+      // (every product is exact), then scaled once.
+      const DeqF16 deq(zr);
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < kWpl; ++j) {
-        const u32x4 b = kBF16 ? deq_bf16_biased(cur.raw[u][j], dq) : deq_f16_biased(cur.raw[u][j], dq);
-        t = mfma32<XT>(a[j], b, t);
-        tc = mfma32<XT>(a[j], corr, tc);
+        const u32x4 h = deq(cur.raw[u][j], dq);
+        t = mfma32<XT>(a[j], kBF16 ? f16_pairs_to_bf16(h) : h, t);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(t[e] + tc[e], sc, acc[e]);
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(t[e], sc, acc[e]);
     }
     cur = nxt;
   }

@@ -10,6 +10,7 @@
 
 #include "awq_internal.h"
 #include "device_common.h"
+#include "exact_quotient.h"
 
 namespace awq {
 
@@ -17,7 +18,9 @@ namespace awq {
 // An fp16 magnitude is an integer number of units of 2^-24 (below 2^40), so the
 // column sums are accumulated as 64-bit integers: exact for any M < 2^24 and
 // independent of the order in which the atomics land.  The mean is then the
-// correctly rounded quotient of the exact sum by M.
+// correctly rounded quotient of the exact sum by M (rn_quotient_u64, exact
+// also for sums beyond 2^53, where a conversion to fp64 first would round
+// twice), times 2^-24.
 // A workgroup of 16 waves sums a block of 512 columns by 128 rows: each wave
 // takes every 16th row of the block (8 rows, all loads in flight at once),
 // the waves' sums meet in LDS, and one 64-bit atomic per column and block
@@ -84,10 +87,10 @@ __global__ __launch_bounds__(64 * kAbsWaves) void abs_colsum_kernel(
 }
 
 __global__ __launch_bounds__(256) void mean_from_units_kernel(const uint64_t *__restrict__ units,
-                                                              int64_t n, double m,
+                                                              int64_t n, uint32_t m,
                                                               double *__restrict__ xbar) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) xbar[i] = ((double)units[i] * 0x1p-24) / m;
+  if (i < n) xbar[i] = rn_quotient_u64(units[i], m) * 0x1p-24;
 }
 
 hipError_t launch_mean_abs(const uint16_t *X, int64_t M, int64_t K, uint64_t *units,
@@ -98,7 +101,7 @@ hipError_t launch_mean_abs(const uint16_t *X, int64_t M, int64_t K, uint64_t *un
   const dim3 grid((unsigned)((K + kAbsCols - 1) / kAbsCols), (unsigned)(blocks < 4096 ? blocks : 4096));
   abs_colsum_kernel<<<grid, 64 * kAbsWaves, 0, st>>>(X, M, K,
                                                      reinterpret_cast<unsigned long long *>(units));
-  mean_from_units_kernel<<<gk, 256, 0, st>>>(units, K, (double)M, xbar);
+  mean_from_units_kernel<<<gk, 256, 0, st>>>(units, K, (uint32_t)M, xbar);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@
  * Conventions for every entry point
  *  - Pointers marked "device" point to memory of the current HIP device; the
  *    caller owns every buffer.  The library keeps no state and allocates no
- *    memory except where an entry point says otherwise.
+ *    memory: scratch comes from workspaces the caller passes in.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued on it and the call returns without waiting, unless the
  *    entry point says it synchronizes.
@@ -119,23 +119,20 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
  * otherwise, unless K / group_size exceeds 8 times its waves per workgroup
  * (16 when N <= 4096, else 8), for M <= 8, and for M <= 12 when
  * N * K <= 5e7; else the MFMA GEMM.
- * GEMV: products of the exact integer (code - zero) and the 16-bit
- * activation, accumulated in fp32 within a group, multiplied by the group's
- * scale and accumulated in fp32 across groups.  GEMM: the dequantized weight
- * (code - zero) * scale is rounded once to fp16 (relative error <= 2^-11),
- * as the pages' GEMM kernels dequantize to fp16, and the products are
- * accumulated in fp32; bf16 activations are scaled per row by a power of two
- * into fp16's range (exact) and the row's output divided by it.  Y is rounded
- * once to y_dtype.  When its tiles alone cannot fill the GPU, the GEMM splits K
- * across workgroups and needs a scratch buffer (see awq_linear_ws); bf16
- * activations need one too (a factor per row, and for shapes large enough
- * for the 256-row tile an fp16 copy of X, M * K * 2 bytes): awq_linear
- * and awq_linear_ex take it from a per-device buffer the library allocates the
- * first time a shape needs it (or needs more) and keeps until the process
- * ends.  Consequently (a) inside a HIP-graph capture, first call the same
- * shape once outside the capture; (b) calls on one device that need the
- * scratch and may overlap in time (different streams) share that buffer and
- * must instead use awq_linear_ws with a workspace each.
+ * Arithmetic.  The GEMV and the GEMM's 32-row tile (M <= 32) multiply the
+ * activations by the exact integers (code - zero), so every product is exact
+ * in fp32; each group's fp32 sum is multiplied by the group's scale and
+ * accumulated in fp32.  The GEMM's larger tiles (M > 32) multiply by the
+ * dequantized weight (code - zero) * scale rounded once to fp16 (relative
+ * error <= 2^-11 per weight; chosen for throughput, within the 1e-3
+ * relative Frobenius tolerance) and accumulate in fp32; an output's extra
+ * error is then at most 2^-11 * sum_k |x_k * w_k|.  bf16 activations on the
+ * GEMM are scaled per row by a power of two into fp16's range (exact) and
+ * the row's output divided by it.  Y is rounded once to y_dtype.
+ * Allocation: none.  awq_linear uses no scratch memory: the GEMM runs without
+ * splitting K (slower for small M than awq_linear_ws), and bf16 activations
+ * on the GEMM path, which need a per-row factor in scratch memory, return
+ * AWQ_ERR_WORKSPACE (use awq_linear_ws or awq_linear_ex with a workspace).
  * Requirements: M, N >= 0, K > 0, K % g == 0.  M == 0 or N == 0 is a no-op.
  */
 awq_status awq_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,
@@ -144,36 +141,49 @@ awq_status awq_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,
                       int32_t y_dtype, awq_stream_t stream);
 
 /*
- * awq_linear_ex - awq_linear with an explicit kernel choice (AWQ_KERNEL_*),
- * so the GEMV and GEMM paths can be compared on the same call (the pages
- * quote GEMV as faster than GEMM at batch size 1: "WQLinear Kernel Variants").
- * AWQ_KERNEL_GEMV requires M <= AWQ_GEMV_MAX_M (else AWQ_ERR_INVALID_ARG).
+ * awq_linear_ex - awq_linear with an explicit kernel choice (AWQ_KERNEL_*)
+ * and an optional workspace, so the GEMV and GEMM paths can be compared on
+ * the same call (the pages quote GEMV as faster than GEMM at batch size 1:
+ * "WQLinear Kernel Variants").
+ *
+ *   kernel     AWQ_KERNEL_AUTO (awq_linear's choice), AWQ_KERNEL_GEMV
+ *            (requires M <= AWQ_GEMV_MAX_M, else AWQ_ERR_INVALID_ARG) or
+ *            AWQ_KERNEL_GEMM.
+ *   workspace  device, 256-byte aligned, at least
+ *            awq_linear_workspace_size(M, N, K, cfg, x_dtype, kernel) bytes,
+ *            or NULL for awq_linear's scratch-free behaviour.  Scratch only:
+ *            its contents on entry are ignored and on return unspecified.
+ *            Calls that share a workspace must not overlap in time.
+ * Allocation: none.  Errors: AWQ_ERR_WORKSPACE when workspace_bytes is too
+ * small; otherwise as awq_linear.
  */
 awq_status awq_linear_ex(const void *X, int32_t x_dtype, const uint32_t *qweight,
                          const uint16_t *scales, const uint8_t *zeros, int64_t M,
                          int64_t N, int64_t K, awq_config cfg, void *Y,
-                         int32_t y_dtype, int32_t kernel, awq_stream_t stream);
+                         int32_t y_dtype, int32_t kernel, void *workspace,
+                         size_t workspace_bytes, awq_stream_t stream);
 
 /*
- * awq_linear_workspace_size - bytes of device workspace awq_linear_ws needs
- * for this shape, for either activation type (0: none; also 0 on invalid
- * arguments).
+ * awq_linear_workspace_size - bytes of device workspace the GEMM path needs
+ * for this shape, activation type and kernel choice: fp32 partial tiles when
+ * the output tiles alone cannot fill the GPU (K is then split across
+ * workgroups and a second kernel sums the parts in a fixed order), and for
+ * bf16 activations a factor per row (and, for shapes large enough for the
+ * 256-row tile, an fp16 copy of X, M * K * 2 bytes).  0 when the call needs
+ * none (the GEMV, or an fp16 GEMM that fills the GPU unsplit), and 0 on
+ * invalid arguments.
  */
-size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg);
+size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg,
+                                 int32_t x_dtype, int32_t kernel);
 
 /*
  * awq_linear_ws - awq_linear (automatic kernel choice) with a caller-owned
- * workspace instead of the library's scratch; allocates nothing.
+ * workspace: awq_linear_ex(..., AWQ_KERNEL_AUTO, workspace, workspace_bytes,
+ * stream).  Allocates nothing.
  * Cites: as awq_linear.
- *
- *   workspace  device, at least awq_linear_workspace_size() bytes, 256-byte
- *            aligned.  Scratch only: its contents on entry are ignored and
- *            on return are unspecified, so it needs no clearing and can be
- *            reused by later calls of any shape.  May be NULL when the size
- *            is 0.
- *   Calls that share a workspace must not overlap in time.
- * Errors: AWQ_ERR_WORKSPACE when workspace_bytes is too small; otherwise as
- * awq_linear.
+ *   workspace  device, at least awq_linear_workspace_size(M, N, K, cfg,
+ *            x_dtype, AWQ_KERNEL_AUTO) bytes, 256-byte aligned; may be NULL
+ *            when that size is 0.  Scratch as for awq_linear_ex.
  */
 awq_status awq_linear_ws(const void *X, int32_t x_dtype, const uint32_t *qweight,
                          const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,

@@ -17,9 +17,10 @@ What the pages fix
 
 What the pages leave open, and the reading taken here
 -----------------------------------------------------
-* Statistic: xbar_k = (1/M) sum_m |X_mk| in fp64.  For fp16 inputs every term
-  is a multiple of 2^-24 below 2^16, so for M <= 8192 the sum is exact and does
-  not depend on summation order.
+* Statistic: xbar_k = (1/M) sum_m |X_mk|: the exact sum (every fp16 magnitude
+  is an integer number of units of 2^-24, below 2^40, so the sum is an exact
+  integer for M < 2^24 and does not depend on summation order), divided by M
+  and rounded once to fp64.
 * Candidate scalings: s_k = t_k / sqrt(max_k t * min_k t), t_k =
   max(xbar_k, 2^-24)^alpha, alpha on the grid {0, 0.05, ..., 0.95}, computed
   in fp64 and rounded once to fp32.  alpha = 0 gives s = 1 exactly (plain
@@ -60,10 +61,20 @@ STAT_FLOOR = 2.0 ** -24
 
 
 def activation_mean_abs(X):
-    """xbar[k] = mean over rows m of |X[m][k]|, in fp64."""
+    """xbar[k] = mean over rows m of |X[m][k]|: the exact column sum divided by
+    M, rounded once to fp64 (X fp16, M < 2^24)."""
     X = np.asarray(X)
+    if X.dtype != F16:
+        raise TypeError("X must be float16")
     M = X.shape[0]
-    return np.abs(X.astype(F64)).sum(axis=0) / F64(M)
+    if not 0 < M < 2 ** 24:
+        raise ValueError("M must be in [1, 2^24)")
+    # |x| * 2^24 is an integer below 2^40 and exact in fp64; the uint64 column
+    # sums stay below 2^64.
+    units = (np.abs(X.astype(F64)) * 2.0 ** 24).astype(np.uint64)
+    sums = units.sum(axis=0, dtype=np.uint64)
+    # Python's int / int is the correctly rounded quotient; * 2^-24 is exact.
+    return np.array([(int(t) / M) * 2.0 ** -24 for t in sums], dtype=F64)
 
 
 def scale_vector(xbar, alpha: float):

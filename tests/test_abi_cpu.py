@@ -68,8 +68,9 @@ def test_quantize_pack_validation():
     assert lib.awq_last_error().decode() == ""
 
 
-def _lin(X=FAKE, xt=0, M=3, N=64, K=256, c=None, Y=FAKE, yt=0, kernel=0):
-    return lib.awq_linear_ex(X, xt, FAKE, FAKE, FAKE, M, N, K, c or cfg(128), Y, yt, kernel, NULL)
+def _lin(X=FAKE, xt=0, M=3, N=64, K=256, c=None, Y=FAKE, yt=0, kernel=0, ws=NULL, ws_bytes=0):
+    return lib.awq_linear_ex(X, xt, FAKE, FAKE, FAKE, M, N, K, c or cfg(128), Y, yt, kernel, ws,
+                             ws_bytes, NULL)
 
 
 def test_linear_validation():
@@ -84,38 +85,69 @@ def test_linear_validation():
     assert _lin(X=ctypes.c_void_p(0x10002)) == binding.AWQ_ERR_INVALID_ARG
     assert _lin(Y=ctypes.c_void_p(0x10002), yt=2) == binding.AWQ_ERR_INVALID_ARG
     assert lib.awq_linear_ex(FAKE, 0, FAKE, ctypes.c_void_p(0x10001), FAKE, 3, 64, 256, cfg(128),
-                             FAKE, 0, 0, NULL) == binding.AWQ_ERR_INVALID_ARG   # odd scales
+                             FAKE, 0, 0, NULL, 0, NULL) == binding.AWQ_ERR_INVALID_ARG  # odd scales
+    assert _lin(ws=ctypes.c_void_p(0x10010), ws_bytes=1 << 20) == binding.AWQ_ERR_INVALID_ARG
     assert _lin(M=0) == binding.AWQ_OK
     assert _lin(N=0, X=NULL) == binding.AWQ_OK
     assert lib.awq_linear(FAKE, 0, FAKE, FAKE, FAKE, 3, 64, 200, cfg(128), FAKE, 0, NULL) \
         == binding.AWQ_ERR_INVALID_ARG
 
 
+def _wsz(M, N, K, g=128, xd=0, kernel=0):
+    return lib.awq_linear_workspace_size(M, N, K, cfg(g), xd, kernel)
+
+
 def test_linear_workspace_size_and_validation():
     # one row of a 4096-wide layer runs the GEMV: no workspace
-    assert lib.awq_linear_workspace_size(1, 4096, 4096, cfg(128)) == 0
+    assert _wsz(1, 4096, 4096) == 0
+    # ... unless the GEMM is forced: its 16 column tiles split K
+    assert _wsz(1, 4096, 4096, kernel=binding.AWQ_KERNEL_GEMM) > 0
     # a batch of 64 splits K across workgroups: fp32 partial tiles
-    ws = lib.awq_linear_workspace_size(64, 13824, 5120, cfg(128))
+    ws = _wsz(64, 13824, 5120)
     assert ws >= 64 * 13824 * 4
-    assert lib.awq_linear_workspace_size(64, 13824, 100, cfg(128)) == 0     # invalid K
-    assert lib.awq_linear_workspace_size(0, 13824, 5120, cfg(128)) == 0
+    # bf16 adds one fp32 factor per row
+    assert _wsz(64, 13824, 5120, xd=1) >= ws + 64 * 4
+    # the prefill shapes fill the GPU unsplit: nothing for fp16, the row
+    # factors and an fp16 copy of X for bf16
+    assert _wsz(4096, 28672, 8192) == 0
+    assert _wsz(4096, 28672, 8192, xd=1) >= 4096 * 8192 * 2 + 4096 * 4
+    assert _wsz(64, 13824, 100) == 0           # invalid K
+    assert _wsz(0, 13824, 5120) == 0
+    assert _wsz(64, 13824, 5120, xd=2) == 0    # fp32 activations are not W4A16
+    assert _wsz(64, 13824, 5120, kernel=7) == 0
 
     def call(ws_ptr=FAKE, ws_bytes=ws, M=64, N=13824, K=5120):
         return lib.awq_linear_ws(FAKE, 0, FAKE, FAKE, FAKE, M, N, K, cfg(128), FAKE, 0, ws_ptr,
                                  ws_bytes, NULL)
     assert call(ws_bytes=ws - 1) == binding.AWQ_ERR_WORKSPACE
-    assert call(ws_ptr=NULL) == binding.AWQ_ERR_INVALID_ARG
+    assert "needed" in lib.awq_last_error().decode()
     assert call(ws_ptr=ctypes.c_void_p(0x10010)) == binding.AWQ_ERR_INVALID_ARG
     assert call(M=0, ws_ptr=NULL, ws_bytes=0) == binding.AWQ_OK
+
+
+def test_scratch_free_calls():
+    """awq_linear (and awq_linear_ex without a workspace) allocate nothing and
+    use no scratch: a bf16 GEMM, which needs per-row factors in scratch
+    memory, is refused before any HIP call."""
+    bf = lib.awq_linear(FAKE, 1, FAKE, FAKE, FAKE, 64, 13824, 5120, cfg(128), FAKE, 2, NULL)
+    assert bf == binding.AWQ_ERR_WORKSPACE
+    assert "workspace" in lib.awq_last_error().decode()
+    assert _lin(xt=1, M=64, N=13824, K=5120, kernel=binding.AWQ_KERNEL_GEMM) \
+        == binding.AWQ_ERR_WORKSPACE
+    # a workspace one byte short of the bf16 plan's is refused too
+    need = _wsz(64, 13824, 5120, xd=1, kernel=binding.AWQ_KERNEL_GEMM)
+    assert _lin(xt=1, M=64, N=13824, K=5120, kernel=binding.AWQ_KERNEL_GEMM,
+                ws=ctypes.c_void_p(0x10000), ws_bytes=need - 1) == binding.AWQ_ERR_WORKSPACE
 
 
 def test_linear_dispatch_rule():
     """awq_linear's GEMV/GEMM choice (host logic, no GPU): the GEMV, which
     needs no workspace, wherever its activation rows fit in LDS (64 KiB, or
-    128 KiB when N <= 4096); unstaged, the GEMM (split K, so a workspace)
-    where a GEMV wave would walk more than 8 groups, else the GEMV up to
-    M = 8, or 12 for layers of at most 5e7 weights."""
-    ws = lambda M, N, K: lib.awq_linear_workspace_size(M, N, K, cfg(128))
+    128 KiB when N <= 4096); unstaged, the GEMM where a GEMV wave would walk
+    more than 8 groups, else the GEMV up to M = 8, or 12 for layers of at
+    most 5e7 weights.  (A bf16 GEMM always needs a workspace, so a zero size
+    means the GEMV.)"""
+    ws = lambda M, N, K: _wsz(M, N, K, xd=1)
     assert ws(2, 5120, 13824) == 0          # 55 KiB of rows: staged
     assert ws(4, 5120, 13824) > 0           # unstaged, 108 groups over 8 waves
     assert ws(8, 11008, 4096) == 0          # 64 KiB: staged
@@ -158,3 +190,54 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     runtimes = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
     assert len(runtimes) == 1, runtimes
+
+
+# --- the binding checks dtypes and shapes before any C call -------------------------
+
+def _raises(exc, fn, *a, **k):
+    with pytest.raises(exc) as e:
+        fn(*a, **k)
+    return str(e.value)
+
+
+def test_binding_rejects_mismatched_tensors():
+    """Wrong dtypes or shapes raise in the binding (on CPU tensors, before the
+    device check and before any launch): an `out` that is too small, a
+    narrower W, packed tensors of the wrong dtype or group count."""
+    import torch
+    M, N, K, g = 4, 64, 256, 128
+    X = torch.zeros((M, K), dtype=torch.float16)
+    qw = torch.zeros((N, K // 8), dtype=torch.int32)
+    sc = torch.zeros((N, K // g), dtype=torch.float16)
+    zr = torch.zeros((N, K // g), dtype=torch.uint8)
+    lin = binding.awq_linear
+    assert "out" in _raises(ValueError, lin, X, qw, sc, zr, out=torch.empty((M, N - 1), dtype=torch.float16))
+    assert "out" in _raises(TypeError, lin, X, qw, sc, zr, out=torch.empty((M, N), dtype=torch.int16))
+    assert "qweight" in _raises(TypeError, lin, X, qw.to(torch.int64), sc, zr)
+    assert "qweight" in _raises(ValueError, lin, X, qw[:, :-1], sc, zr)
+    assert "scales" in _raises(TypeError, lin, X, qw, sc.float(), zr)
+    assert "scales" in _raises(ValueError, lin, X, qw, sc, zr, group_size=64)
+    assert "zeros" in _raises(TypeError, lin, X, qw, sc, zr.to(torch.int8))
+    assert "zeros" in _raises(ValueError, lin, X, qw, sc, zr[:-1])
+    assert "X" in _raises(TypeError, lin, X.float(), qw, sc, zr)
+    assert "out_dtype" in _raises(TypeError, lin, X, qw, sc, zr, out_dtype=torch.int32)
+    assert "K=" in _raises(ValueError, lin, X[:, :200], qw, sc, zr)
+    # everything well-formed, but on the CPU: refused for placement
+    assert "GPU" in _raises(ValueError, lin, X, qw, sc, zr)
+    ex = binding.awq_linear_ex
+    assert "workspace" in _raises(ValueError, ex, X, qw, sc, zr, workspace="big")
+
+    W = torch.zeros((N, K), dtype=torch.float16)
+    qp = binding.awq_quantize_pack
+    assert "W" in _raises(TypeError, qp, W.float())
+    assert "s" in _raises(ValueError, qp, W, s=torch.ones(K - 8, dtype=torch.float32))
+    assert "s" in _raises(TypeError, qp, W, s=torch.ones(K, dtype=torch.float64))
+    assert "N rows" in _raises(ValueError, qp, W, out=(qw[:-1], sc[:-1], zr[:-1]))
+    assert "GPU" in _raises(ValueError, qp, W)
+
+    ss = binding.awq_scale_search
+    assert "input channels" in _raises(ValueError, ss, X, W[:, :128])
+    assert "W" in _raises(TypeError, ss, X, W.float())
+    assert "X" in _raises(TypeError, ss, X.to(torch.bfloat16), W)
+    assert "workspace" in _raises(ValueError, ss, X, W, workspace=torch.empty(16, dtype=torch.uint8))
+    assert "GPU" in _raises(ValueError, ss, X, W)

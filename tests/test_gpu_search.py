@@ -29,6 +29,25 @@ def _gpu_search(X, W, g=128, alphas=None):
     return res
 
 
+def _every_candidate_bitwise(X, W, g, alphas, grid_losses=None):
+    """Each candidate alone (a one-value grid): its s vector and its packed
+    weights are bit-identical to the oracle's, and (when the grid's losses are
+    given) its loss equals the grid's entry bitwise, since a candidate's loss
+    does not depend on the others."""
+    xbar = activation_mean_abs(X)
+    for j, a in enumerate(alphas):
+        res = _gpu_search(X, W, g, [float(a)])
+        assert res["best_index"] == 0
+        s_ref = scale_vector(xbar, a)
+        assert np.array_equal(to_np(res["s"]).view(np.uint32), s_ref.view(np.uint32)), f"s, alpha {a}"
+        qw, sc, zr = quantize_pack(W, QuantConfig(group_size=g), s_ref)
+        assert np.array_equal(to_np(res["qweight"]), qw), f"codes, alpha {a}"
+        assert np.array_equal(to_np(res["scales"]).view(np.uint16), sc.view(np.uint16))
+        assert np.array_equal(to_np(res["zeros"]), zr)
+        if grid_losses is not None:
+            assert res["losses"][0] == grid_losses[j], f"loss, alpha {a}"
+
+
 def _check_against(res, ref, what):
     gap = np.sort(ref["losses"])[:2]
     say(what, "best", ref["best_index"], "runner-up gap", float((gap[1] - gap[0]) / gap[0]))
@@ -49,6 +68,7 @@ def test_small_search_matches_oracle(M, N, K, g):
     res = _gpu_search(X, W, g)
     ref = scale_search(X, W, QuantConfig(group_size=g))
     _check_against(res, ref, f"search {M}x{N}x{K}")
+    _every_candidate_bitwise(X, W, g, DEFAULT_ALPHAS, res["losses"])
 
 
 def test_custom_alpha_grid():
@@ -83,7 +103,64 @@ def test_full_search_layer_against_stored_oracle():
     assert _sha(to_np(res["qweight"])) == gold["sha256_qweight"]
     assert _sha(to_np(res["scales"]).view(np.uint16)) == gold["sha256_scales"]
     assert _sha(to_np(res["zeros"])) == gold["sha256_zeros"]
-    # the whole s-table: every candidate's s vector is bit-identical to the oracle's
+    # the winning candidate's s recomputed by the oracle
     xbar = activation_mean_abs(X)
     s_best = scale_vector(xbar, DEFAULT_ALPHAS[gold["best_index"]])
     assert np.array_equal(to_np(res["s"]), s_best)
+
+
+def test_full_search_every_candidate_bitwise():
+    """The whole s-table on the 4096 x 4096 layer: every candidate's s vector
+    and packed weights are bit-identical to the oracle's (each candidate run
+    alone through a one-value grid), and each candidate's loss equals the
+    full grid's entry bitwise."""
+    case = wl.search_case()
+    X = case.activation()
+    W = case.weight()
+    say("search full 4096^3, every candidate")
+    res = _gpu_search(X, W)
+    _every_candidate_bitwise(X, W, 128, DEFAULT_ALPHAS, res["losses"])
+
+
+@pytest.mark.parametrize("grid,want", [([0.35, 0.35], 0), ([0.9, 0.35, 0.35], 1),
+                                       ([0.35, 0.9, 0.35], 0), ([0.9, 0.9, 0.35, 0.35], 2)])
+def test_tie_break_takes_the_first_minimum(grid, want):
+    """A repeated alpha gives bit-identical losses; the chosen index is the
+    first that attains the minimum (a last-minimum rule would return the later
+    copy).  The oracle fixes the expected index and confirms L(0.35) < L(0.9)
+    on these inputs."""
+    X = wl.gen_activation(256, 512, 150, 151)
+    W = wl.gen_weight(192, 512, 152)
+    ref = scale_search(X, W, QuantConfig(), np.array(grid))
+    assert ref["best_index"] == want
+    say("tie-break", grid)
+    res = _gpu_search(X, W, 128, grid)
+    assert res["best_index"] == want
+    L = res["losses"]
+    for i, a in enumerate(grid):
+        for j, b in enumerate(grid):
+            if a == b:
+                assert L[i] == L[j]
+    assert np.all(np.abs(L - ref["losses"]) <= LOSS_RTOL * ref["losses"])
+
+
+def test_search_statistic_beyond_2_53_units():
+    """34278 calibration rows, half the channels near fp16's maximum with a
+    few subnormal magnitudes mixed in: their column sums pass 2^53 units of
+    2^-24, where the statistic needs the exact integer quotient (a conversion
+    to fp64 before dividing would round twice).  Every candidate's s is
+    bit-identical to the oracle's."""
+    M, K, N = 34278, 128, 16
+    rng = np.random.default_rng(0)
+    X = rng.standard_normal((M, K))
+    X[:, :64] = 65504.0
+    for k in range(64):
+        X[rng.integers(0, M, size=int(rng.integers(1, 40))), k] = rng.integers(1, 1024) * 2.0 ** -24
+        X[rng.integers(0, M, size=3), k] = 65504.0 - 32 * rng.integers(1, 60)
+    X = X.astype(np.float16)
+    W = wl.gen_weight(N, K, 160)
+    say("search statistic beyond 2^53 units", M, K, N)
+    res = _gpu_search(X, W, 128, [0.0, 0.25, 0.5, 0.75, 1.0])
+    ref = scale_search(X, W, QuantConfig(), np.array([0.0, 0.25, 0.5, 0.75, 1.0]))
+    _check_against(res, ref, "large M")
+    _every_candidate_bitwise(X, W, 128, [0.1, 0.35, 0.6, 0.95], None)

@@ -22,6 +22,30 @@ def test_mean_abs_is_order_independent():
     assert np.array_equal(a, b) and np.array_equal(a, c)
 
 
+def test_mean_abs_exact_beyond_fp64_summation():
+    """Column sums of ~34000 rows near fp16's maximum exceed 2^53 units of
+    2^-24, where fp64 accumulation stops being exact; a few subnormal
+    magnitudes mixed in make plain fp64 summation round differently.  The
+    statistic must still be the exact mean rounded once (compared with exact
+    rational arithmetic), and the naive fp64 sum must miss it on some column
+    (so this pin separates the two)."""
+    from fractions import Fraction
+    M, K = 34278, 8
+    rng = np.random.default_rng(0)
+    X = np.full((M, K), 65504.0)
+    for k in range(K):
+        X[rng.integers(0, M, size=int(rng.integers(1, 40))), k] = rng.integers(1, 1024) * 2.0 ** -24
+        X[rng.integers(0, M, size=3), k] = 65504.0 - 32 * rng.integers(1, 60)
+    X[::7, 2] *= -1.0                        # magnitudes, not values
+    X = X.astype(np.float16)
+    got = activation_mean_abs(X)
+    naive = np.abs(X.astype(np.float64)).sum(axis=0) / np.float64(M)
+    for k in range(K):
+        exact = sum((Fraction(abs(float(v))) for v in X[:, k]), Fraction(0)) / M
+        assert got[k] == float(exact), k
+    assert np.any(naive != got)
+
+
 def test_two_channel_scale_closed_form():
     xbar = np.array([1.0, 4.0])
     # alpha = 1/2: t = (1, 2), sqrt(max*min) = sqrt(2): s = (2^-1/2, 2^1/2)
@@ -156,3 +180,23 @@ def test_reference_output_blocked():
     W = gen_weight(70, 128, 93)
     assert np.array_equal(reference_output(X, W, block=16),
                           X.astype(np.float64) @ W.astype(np.float64).T)
+
+
+@pytest.mark.parametrize("grid,want", [([0.35, 0.35], 0), ([0.9, 0.35, 0.35], 1),
+                                       ([0.35, 0.9, 0.35], 0), ([0.9, 0.9, 0.35, 0.35], 2)])
+def test_tie_break_takes_the_first_minimum(grid, want):
+    """Reading R16: the smallest index attaining the minimum.  A repeated alpha
+    gives bit-identical losses (the loss is a deterministic function of alpha),
+    so a rule that kept the last minimum would return the later copy.  The
+    data give L(0.35) < L(0.9) (checked), so 0.35's first copy must win."""
+    X = gen_activation(256, 512, 150, 151)
+    W = gen_weight(192, 512, 152)
+    res = scale_search(X, W, QuantConfig(), np.array(grid))
+    L = res["losses"]
+    xbar = activation_mean_abs(X)
+    l35 = search_loss(X, W, scale_vector(xbar, 0.35))[0]
+    l90 = search_loss(X, W, scale_vector(xbar, 0.9))[0]
+    assert l35 < l90
+    for i, a in enumerate(grid):
+        assert L[i] == (l35 if a == 0.35 else l90)
+    assert res["best_index"] == want

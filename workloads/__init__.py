@@ -94,6 +94,31 @@ def gen_activation(M: int, K: int, seed: int, outlier_seed: int, dtype: str = "f
     return out
 
 
+#: Activation distributions with a non-zero mean (stress inputs for the
+#: linear layer's accuracy: outputs grow with the mean, and so do the rounding
+#: errors of any kernel that rounds dequantized weights or cancels large sums).
+SHIFTED_KINDS = ("abs", "mean3", "mean40")
+
+
+def gen_activation_shifted(M: int, K: int, seed: int, kind: str, dtype: str = "f16") -> np.ndarray:
+    """X[M][K] = |N(0,1)| ('abs'), N(3,1) ('mean3') or N(0,1) + 40 ('mean40'),
+    without outlier channels; 'f16' returns float16, 'bf16' uint16 bf16 bits."""
+    z = np.random.default_rng(seed).standard_normal((M, K))
+    if kind == "abs":
+        x = np.abs(z)
+    elif kind == "mean3":
+        x = z + 3.0
+    elif kind == "mean40":
+        x = z + 40.0
+    else:
+        raise ValueError(kind)
+    if dtype == "f16":
+        return x.astype(np.float16)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x.astype(np.float32))
+    raise ValueError(dtype)
+
+
 @dataclass(frozen=True)
 class Case:
     """One layer shape with its seeds."""
