@@ -36,6 +36,7 @@ EXPORTS = (
     "awq_linear_ex",
     "awq_linear_workspace_size",
     "awq_linear_ws",
+    "awq_linear_noalloc",
     "awq_scale_search_workspace_size",
     "awq_scale_search",
     "awq_status_string",
@@ -80,6 +81,9 @@ def _load():
     lib.awq_linear_ws.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32, vp,
                                   ctypes.c_size_t, vp]
     lib.awq_linear_ws.restype = ctypes.c_int
+    lib.awq_linear_noalloc.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32,
+                                       vp]
+    lib.awq_linear_noalloc.restype = ctypes.c_int
     lib.awq_scale_search_workspace_size.argtypes = [i64, i64, i64, awq_config, i32]
     lib.awq_scale_search_workspace_size.restype = ctypes.c_size_t
     lib.awq_scale_search.argtypes = [vp, vp, i64, i64, i64, awq_config,
@@ -325,6 +329,19 @@ def awq_linear_ws(X, qweight, scales, zeros, workspace, group_size: int = 128, o
                            ctypes.c_void_p(0) if ws is None else _ptr(ws),
                            0 if ws is None else ws.numel() * ws.element_size(), _stream(dev))
     check(st, "awq_linear_ws")
+    return out
+
+
+def awq_linear_noalloc(X, qweight, scales, zeros, group_size: int = 128, out_dtype=None,
+                       out=None):
+    """awq_linear_ws with the library's static device scratch instead of a
+    workspace: allocates nothing (pass `out` to allocate nothing here either).
+    Calls that may overlap in time on one GPU must not be made."""
+    M, N, K, out, dev = _linear_args(X, qweight, scales, zeros, group_size, out_dtype, out)
+    st = lib.awq_linear_noalloc(_ptr(X), _dtype_code(X.dtype), _ptr(qweight), _ptr(scales),
+                                _ptr(zeros), M, N, K, config(group_size), _ptr(out),
+                                _dtype_code(out.dtype), _stream(dev))
+    check(st, "awq_linear_noalloc")
     return out
 
 

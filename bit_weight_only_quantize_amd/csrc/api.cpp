@@ -9,6 +9,8 @@
 #include <cstdio>
 #include <cstring>
 
+#include <mutex>
+
 #include "../../include/awq355.h"
 #include "awq_internal.h"
 
@@ -276,6 +278,83 @@ awq_status awq_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,
                       int64_t K, awq_config cfg, void *Y, int32_t y_dtype, awq_stream_t stream) {
   return linear_impl("awq_linear", X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype,
                      AWQ_KERNEL_AUTO, nullptr, 0, stream);
+}
+
+}  // extern "C"
+
+// ---- awq_linear_noalloc: the GEMM's scratch in a static device array -----------
+namespace {
+
+// The GEMM scratch of awq_linear_noalloc: split-K partials (at most
+// kBoundedPartialBytes) and, for bf16 activations, one fp32 factor per row.
+// One copy per GPU, in the library's code object; it lives until the process
+// ends.  Host code must never pass `scratch` itself to a kernel (in host code
+// the name is only a stand-in): the device address comes from
+// hipGetSymbolAddress, once per device.
+constexpr size_t kStaticScratchBytes = AWQ_NOALLOC_SCRATCH_BYTES;
+static_assert(kStaticScratchBytes >= awq::kBoundedPartialBytes + 256, "scratch too small");
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with that device current).
+awq_status static_scratch(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "awq_linear_noalloc (hipGetDevice)");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(AWQ_ERR_UNSUPPORTED, "awq_linear_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "awq_linear_noalloc (hipGetSymbolAddress)");
+    if (!p) return fail(AWQ_ERR_HIP, "awq_linear_noalloc: no device address for the scratch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return AWQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+awq_status awq_linear_noalloc(const void *X, int32_t x_dtype, const uint32_t *qweight,
+                              const uint16_t *scales, const uint8_t *zeros, int64_t M,
+                              int64_t N, int64_t K, awq_config cfg, void *Y, int32_t y_dtype,
+                              awq_stream_t stream) {
+  const char *who = "awq_linear_noalloc";
+  awq_status st = check_linear(X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype,
+                               AWQ_KERNEL_AUTO);
+  if (st != AWQ_OK) return st;
+  if (M == 0 || N == 0) return ok();
+  const awq::XType xt = x_dtype == AWQ_F16 ? awq::XType::F16 : awq::XType::BF16;
+  const awq::YType yt = y_dtype == AWQ_F16    ? awq::YType::F16
+                        : y_dtype == AWQ_BF16 ? awq::YType::BF16
+                                              : awq::YType::F32;
+  const hipStream_t hs = as_stream(stream);
+  if (runs_gemv(M, N, K, cfg.group_size, AWQ_KERNEL_AUTO))
+    return hip_status(awq::launch_gemv(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size, Y,
+                                       yt, hs),
+                      who);
+  const awq::GemmPlan plan = awq::gemm_plan(M, N, K, xt, awq::Scratch::Bounded);
+  if (plan.workspace_bytes > kStaticScratchBytes)
+    return fail(AWQ_ERR_WORKSPACE,
+                "%s: this call needs %zu bytes of scratch, beyond the static %zu (bf16 "
+                "activations need one fp32 factor per row)",
+                who, plan.workspace_bytes, kStaticScratchBytes);
+  void *ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    st = static_scratch(&ws);
+    if (st != AWQ_OK) return st;
+  }
+  return hip_status(awq::launch_gemm(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size, Y,
+                                     yt, plan, ws, hs),
+                    who);
 }
 
 size_t awq_scale_search_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg,

@@ -190,6 +190,34 @@ awq_status awq_linear_ws(const void *X, int32_t x_dtype, const uint32_t *qweight
                          int64_t K, awq_config cfg, void *Y, int32_t y_dtype, void *workspace,
                          size_t workspace_bytes, awq_stream_t stream);
 
+/* Bytes of device scratch behind awq_linear_noalloc, per GPU: the largest
+ * split-K partials of a plan (256 tiles of 128 x 256 fp32, 32 MiB) plus 1 MiB
+ * of per-row factors for bf16 activations. */
+#define AWQ_NOALLOC_SCRATCH_BYTES ((size_t)33 << 20)
+
+/*
+ * awq_linear_noalloc - awq_linear_ws without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code under HIP-graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The GEMM's scratch is a static device array of
+ * AWQ_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held until the
+ * process ends.  Same kernel choice and results as awq_linear_ws (bf16
+ * activations never take the 256-row tile here, which needs an fp16 copy
+ * of X; the 128-row tile computes the same values).
+ * Errors: AWQ_ERR_WORKSPACE when the call needs more scratch than the
+ * static array holds (only bf16 activations on the GEMM path with more than
+ * about 8.6 million rows, 4 bytes each); otherwise as awq_linear.
+ * Concurrency: every call on a GPU shares that GPU's array.  Calls on one
+ * GPU that may overlap in time (different streams, or concurrent graph
+ * replays) race on it and must not be made; calls ordered on one stream are
+ * safe.  The array carries nothing from one call to the next (each call
+ * writes every scratch element it reads), so it needs no clearing.
+ */
+awq_status awq_linear_noalloc(const void *X, int32_t x_dtype, const uint32_t *qweight,
+                              const uint16_t *scales, const uint8_t *zeros, int64_t M,
+                              int64_t N, int64_t K, awq_config cfg, void *Y,
+                              int32_t y_dtype, awq_stream_t stream);
+
 /*
  * awq_scale_search_workspace_size - bytes of device workspace that
  * awq_scale_search needs for these sizes (0 on invalid arguments).

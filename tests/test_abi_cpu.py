@@ -140,6 +140,19 @@ def test_scratch_free_calls():
                 ws=ctypes.c_void_p(0x10000), ws_bytes=need - 1) == binding.AWQ_ERR_WORKSPACE
 
 
+def test_noalloc_rejects_beyond_its_static_scratch():
+    """awq_linear_noalloc refuses, before any HIP call, a call whose scratch
+    exceeds its static array: bf16 activations on the GEMM path take one fp32
+    factor per row, so 9 million rows need 36 MB of the 33 MiB."""
+    assert binding.lib.awq_linear_noalloc(FAKE, 1, FAKE, FAKE, FAKE, 9_000_000, 4096, 4096,
+                                          cfg(128), FAKE, 2, NULL) == binding.AWQ_ERR_WORKSPACE
+    assert "static" in lib.awq_last_error().decode()
+    assert binding.lib.awq_linear_noalloc(FAKE, 0, FAKE, FAKE, FAKE, 0, 4096, 4096, cfg(128),
+                                          FAKE, 2, NULL) == binding.AWQ_OK
+    assert binding.lib.awq_linear_noalloc(FAKE, 0, FAKE, FAKE, FAKE, 4, 4096, 4096, cfg(96),
+                                          FAKE, 2, NULL) == binding.AWQ_ERR_UNSUPPORTED
+
+
 def test_linear_dispatch_rule():
     """awq_linear's GEMV/GEMM choice (host logic, no GPU): the GEMV, which
     needs no workspace, wherever its activation rows fit in LDS (64 KiB, or
