@@ -30,6 +30,7 @@ Parity status per function is listed in each module header.
 
 from .quant import (  # noqa: F401
     ORDER,
+    SYM_ZERO,
     QuantConfig,
     quantize_groups,
     pack_codes,

@@ -40,10 +40,11 @@ def linear64(X, qweight, scales, zeros, group_size: int = 128, rows=None, cols=N
     K = X.shape[1]
     qweight = np.asarray(qweight)
     scales = np.asarray(scales)
-    zeros = np.asarray(zeros)
+    zeros = None if zeros is None else np.asarray(zeros)
     if cols is not None:
         cols = np.asarray(cols)
-        qweight, scales, zeros = qweight[cols], scales[cols], zeros[cols]
+        qweight, scales = qweight[cols], scales[cols]
+        zeros = None if zeros is None else zeros[cols]
     if rows is not None:
         X = X[np.asarray(rows)]
     deq = _deq_from_packed(qweight, scales, zeros, K, group_size)
@@ -51,7 +52,8 @@ def linear64(X, qweight, scales, zeros, group_size: int = 128, rows=None, cols=N
 
 
 def linear_naive(X, q, scales, zeros, group_size: int = 128):
-    """Pure-Python loops over (m, n, k); for tiny shapes only."""
+    """Pure-Python loops over (m, n, k); for tiny shapes only (zeros=None:
+    the symmetric grid, zero 8)."""
     X = np.asarray(X).astype(np.float64)
     M, K = X.shape
     N = q.shape[0]
@@ -62,7 +64,8 @@ def linear_naive(X, q, scales, zeros, group_size: int = 128):
             acc = 0.0
             for k in range(K):
                 grp = k // g
-                w = (float(q[n][k]) - float(zeros[n][grp])) * float(scales[n][grp])
+                z = 8.0 if zeros is None else float(zeros[n][grp])
+                w = (float(q[n][k]) - z) * float(scales[n][grp])
                 acc += float(X[m][k]) * w
             Y[m][n] = acc
     return np.array(Y, dtype=np.float64)

@@ -30,6 +30,17 @@ quantisation with an integer zero point, written out below step by step:
 
 rint is round-half-to-even, every division is IEEE fp32 and correctly rounded.
 
+Without a zero point ("Zero-Point Quantization": zero_point=False is the
+symmetric variant; the pages give no formula), the plainest symmetric reading
+is a grid centred on zero whose extremes are +-7 steps, so that the group's
+largest magnitude lands exactly on a level:
+
+  amax   = max_g |v|
+  s32    = amax / 7                  fp32 division
+  s_h    = fp16_rne(max(s32, 2^-14))
+  q      = clamp(rint(v / s_h), -8, 7), stored as the code q + 8 (0..15)
+  deq    = (code - 8) * s_h          (a fixed zero point of 8; no zeros array)
+
 Packing (a layout of this project, not of the pages): qweight[n][c] is a u32
 whose nibble p (bits 4p..4p+3) holds q[n][8c + ORDER[p]], ORDER =
 (0, 2, 4, 6, 1, 3, 5, 7).  So nibble i and nibble i+4 of a word hold the pair
@@ -56,6 +67,9 @@ ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
 #: Smallest stored scale: the smallest normal fp16 value.
 SCALE_FLOOR = F32(2.0 ** -14)
 
+#: Code of the symmetric grid's zero (codes are q + 8 for q in [-8, 7]).
+SYM_ZERO = 8
+
 
 @dataclass(frozen=True)
 class QuantConfig:
@@ -68,20 +82,20 @@ class QuantConfig:
     def check(self, K: int) -> None:
         if self.w_bit != 4:
             raise ValueError("only w_bit=4 is defined")
-        if not self.zero_point:
-            raise ValueError("only zero_point=True is defined")
         if self.group_size <= 0 or K % self.group_size:
             raise ValueError("K must be a multiple of group_size")
         if K % 8:
             raise ValueError("K must be a multiple of 8")
 
 
-def quantize_groups(W, group_size: int = 128, s=None):
+def quantize_groups(W, group_size: int = 128, s=None, zero_point: bool = True):
     """Quantize W[N][K] (fp16) group-wise along K.
 
-    Returns (q uint8 [N][K], scales fp16 [N][K/g], zeros uint8 [N][K/g]).
-    ``s`` is an optional fp32 per-input-channel scale vector of length K; when
-    given, the values quantized are fp32(s_k * W_nk) (the sW of Y=(X/s)(sW)).
+    Returns (q uint8 [N][K], scales fp16 [N][K/g], zeros uint8 [N][K/g]), or
+    with zero_point=False the symmetric codes, the scales and None (every
+    group's zero is SYM_ZERO).  ``s`` is an optional fp32 per-input-channel
+    scale vector of length K; when given, the values quantized are
+    fp32(s_k * W_nk) (the sW of Y=(X/s)(sW)).
     """
     W = np.asarray(W)
     if W.dtype != F16:
@@ -100,6 +114,15 @@ def quantize_groups(W, group_size: int = 128, s=None):
             raise TypeError("s must be float32 of shape (K,)")
         v = s[None, :] * v                      # one correctly-rounded fp32 product
     vg = v.reshape(N, G, g)
+
+    if not zero_point:
+        # Symmetric: the step puts the largest magnitude on level +-7.
+        amax = np.abs(vg).max(axis=-1)
+        s32 = amax / F32(7.0)
+        s_h = np.maximum(s32, SCALE_FLOOR).astype(F16)
+        sf = s_h.astype(F32)
+        q = np.clip(np.rint(vg / sf[..., None]), F32(-8.0), F32(7.0)) + F32(SYM_ZERO)
+        return q.reshape(N, K).astype(np.uint8), s_h, None
 
     # Step 2: the range of each group, widened to include 0.
     lo = np.minimum(vg.min(axis=-1), F32(0.0))
@@ -141,18 +164,22 @@ def unpack_codes(qweight, K: int):
 
 
 def dequantize(q, scales, zeros, group_size: int = 128):
-    """deq[n][k] = (q[n][k] - z[n][k//g]) * s_h[n][k//g], in fp64 (exact)."""
+    """deq[n][k] = (q[n][k] - z[n][k//g]) * s_h[n][k//g], in fp64 (exact).
+    zeros=None is the symmetric grid: z = SYM_ZERO for every group."""
     q = np.asarray(q)
     N, K = q.shape
     g = int(group_size)
+    if zeros is None:
+        zeros = np.full(np.asarray(scales).shape, SYM_ZERO, dtype=np.uint8)
     zr = np.repeat(np.asarray(zeros).astype(np.float64), g, axis=1)
     sc = np.repeat(np.asarray(scales).astype(np.float64), g, axis=1)
     return (q.astype(np.float64) - zr) * sc
 
 
 def quantize_pack(W, cfg: QuantConfig = QuantConfig(), s=None):
-    """Quantize and pack: returns (qweight u32 [N][K/8], scales f16 [N][G], zeros u8 [N][G])."""
+    """Quantize and pack: returns (qweight u32 [N][K/8], scales f16 [N][G],
+    zeros u8 [N][G] or None for the symmetric grid)."""
     W = np.asarray(W)
     cfg.check(W.shape[1])
-    q, sc, zr = quantize_groups(W, cfg.group_size, s)
+    q, sc, zr = quantize_groups(W, cfg.group_size, s, cfg.zero_point)
     return pack_codes(q), sc, zr

@@ -113,12 +113,13 @@ def search_loss(X, W, s, cfg: QuantConfig = QuantConfig(), Y_ref=None, block: in
     W = np.asarray(W)
     if Y_ref is None:
         Y_ref = reference_output(X, W, block)
-    q, sc, zr = quantize_groups(W, cfg.group_size, s)
+    q, sc, zr = quantize_groups(W, cfg.group_size, s, cfg.zero_point)
     A64 = scaled_activation(X, s).astype(F64)
     N = W.shape[0]
     total = F64(0.0)
     for n0 in range(0, N, block):
-        deq = dequantize(q[n0:n0 + block], sc[n0:n0 + block], zr[n0:n0 + block], cfg.group_size)
+        deq = dequantize(q[n0:n0 + block], sc[n0:n0 + block],
+                         None if zr is None else zr[n0:n0 + block], cfg.group_size)
         E = Y_ref[:, n0:n0 + block] - A64 @ deq.T
         total += np.sum(E * E)
     return float(total), (q, sc, zr)

@@ -70,3 +70,15 @@ def test_error_vs_unquantized_is_small(g):
     Yr = X.astype(np.float64) @ W.astype(np.float64).T
     rel = np.linalg.norm(Y - Yr) / np.linalg.norm(Yr)
     assert 0.01 < rel < 0.2
+
+
+def test_symmetric_grid_matches_python_loops():
+    """Without zero points (zeros=None: every zero is 8) the fp64 product
+    equals a pure-Python loop over (code - 8) * scale."""
+    W = _w(12, 256, 77)
+    X = (np.random.default_rng(78).standard_normal((3, 256))).astype(np.float16)
+    q, sc, zr = quantize_groups(W, 64, zero_point=False)
+    assert zr is None
+    got = linear64(X, pack_codes(q), sc, None, 64)
+    ref = linear_naive(X, q, sc, None, 64)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))

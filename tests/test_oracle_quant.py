@@ -174,7 +174,99 @@ def test_config_validation():
         QuantConfig(w_bit=3).check(128)
     with pytest.raises(ValueError):
         QuantConfig(group_size=128).check(192)
-    with pytest.raises(ValueError):
-        QuantConfig(zero_point=False).check(128)
+    QuantConfig(zero_point=False).check(128)
     qw, sc, zr = quantize_pack(_random_w(3, 256, 0), QuantConfig(group_size=64))
     assert qw.shape == (3, 32) and sc.shape == (3, 4) and zr.shape == (3, 4)
+    qw, sc, zr = quantize_pack(_random_w(3, 256, 0), QuantConfig(group_size=64, zero_point=False))
+    assert qw.shape == (3, 32) and sc.shape == (3, 4) and zr is None
+
+
+# --- the symmetric grid (zero_point=False) --------------------------------------------
+
+SYM = json.load(open(os.path.join(HERE, "golden", "hand_worked_symmetric.json")))
+
+
+@pytest.mark.parametrize("grp", SYM["groups"], ids=[g["name"] for g in SYM["groups"]])
+def test_symmetric_hand_worked_group(grp):
+    g = SYM["group_size"]
+    W = _group_array(grp["values"], g)
+    q, sc, zr = quantize_groups(W, g, zero_point=False)
+    assert zr is None and sc.shape == (1, 1)
+    assert int(sc.view(np.uint16)[0, 0]) == grp["scale_fp16_bits"]
+    assert float(sc[0, 0]) == grp["scale"]
+    n = len(grp["codes"])
+    assert q[0, :n].tolist() == grp["codes"]
+    assert np.all(q[0, n:] == 8)
+    if "dequant" in grp:
+        assert dequantize(q, sc, None, g)[0, :n].tolist() == grp["dequant"]
+
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_symmetric_roundtrip_bound_and_extremes(g):
+    """Half a step for every weight (no level is ever clamped: |v|/s <= 7
+    (1 + 2^-11) < 7.5), the largest magnitude of each group on level +-7, and
+    code 0 (level -8) never used."""
+    W = _random_w(64, 512, 12)
+    q, sc, zr = quantize_groups(W, g, zero_point=False)
+    deq = dequantize(q, sc, None, g)
+    s_rep = np.repeat(sc.astype(np.float64), g, axis=1)
+    v = W.astype(np.float64)
+    assert np.all(np.abs(v - deq) <= 0.5 * s_rep * (1 + 2.0 ** -20))
+    assert q.min() >= 1 and q.max() <= 15
+    vg = np.abs(v).reshape(64, -1, g)
+    arg = vg.argmax(axis=-1)
+    qg = q.reshape(64, -1, g).astype(int) - 8
+    ext = np.take_along_axis(qg, arg[..., None], axis=-1)[..., 0]
+    assert np.all(np.abs(ext) == 7)
+    assert np.all(deq[q == 8] == 0.0)
+
+
+def test_symmetric_brute_force_nearest_level():
+    """Every code is the nearest of the 16 levels (c - 8) * s, ties going to
+    an even q, except within fp32's rounding of the quotient at near-ties."""
+    g = 8
+    W = _random_w(40, 64, 13, sigma=1.0)
+    q, sc, _ = quantize_groups(W, g, zero_point=False)
+    v = W.astype(np.float64)
+    for n in range(W.shape[0]):
+        for k in range(W.shape[1]):
+            s = float(sc[n, k // g])
+            levels = (np.arange(16) - 8) * s
+            d = np.abs(v[n, k] - levels)
+            best = np.flatnonzero(d == d.min())
+            if len(best) == 2:
+                best = [b for b in best if (b - 8) % 2 == 0]
+            if q[n, k] != best[0]:
+                srt = np.sort(d)
+                assert srt[1] - srt[0] <= 2.0 ** -20 * s * 16
+
+
+def test_symmetric_negation_and_scaling():
+    """Negating W maps code c to 16 - c (q to -q) with the same steps; a power
+    of two on W scales the steps exactly and keeps the codes.  A one-sided
+    (asymmetric) or off-by-one grid breaks the first."""
+    W = _random_w(16, 256, 14)
+    q, sc, _ = quantize_groups(W, 128, zero_point=False)
+    qn, scn, _ = quantize_groups(-W, 128, zero_point=False)
+    assert np.array_equal(qn.astype(int), 16 - q.astype(int))
+    assert np.array_equal(scn, sc)
+    for e in (-3, 2):
+        W2 = (W.astype(np.float32) * np.float32(2.0 ** e)).astype(np.float16)
+        q2, sc2, _ = quantize_groups(W2, 128, zero_point=False)
+        assert np.array_equal(q2, q)
+        assert np.array_equal(sc2.astype(np.float64), sc.astype(np.float64) * 2.0 ** e)
+
+
+def test_symmetric_scaled_input_channels():
+    """With s on the input channels, v = fp32(s * W) is what gets quantized:
+    a lossless symmetric grid divided by s comes back exactly."""
+    rng = np.random.default_rng(15)
+    N, K, g = 5, 256, 128
+    q = rng.integers(1, 16, size=(N, K)).astype(np.uint8)
+    q[:, ::g] = 1                      # -7: the largest magnitude of each group
+    s = np.array([1.0, 0.5, 2.0, 1.0] * (K // 4), dtype=np.float32)
+    grid = (q.astype(np.float64) - 8) * 2.0 ** -6
+    W = (grid / s[None, :].astype(np.float64)).astype(np.float16)
+    q2, sc, _ = quantize_groups(W, g, s, zero_point=False)
+    assert np.array_equal(q2, q)
+    assert np.all(sc == np.float16(2.0 ** -6))

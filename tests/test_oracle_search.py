@@ -200,3 +200,20 @@ def test_tie_break_takes_the_first_minimum(grid, want):
     for i, a in enumerate(grid):
         assert L[i] == (l35 if a == 0.35 else l90)
     assert res["best_index"] == want
+
+
+def test_symmetric_search_alpha_zero_is_plain_symmetric_rounding():
+    """zero_point=False runs the same search over the symmetric grid: alpha 0
+    reproduces the plain symmetric quantizer, the packed result carries no
+    zero points, and the loss matches a direct evaluation."""
+    X = gen_activation(32, 256, 171, 172)
+    W = gen_weight(16, 256, 173)
+    cfg = QuantConfig(zero_point=False)
+    res = scale_search(X, W, cfg)
+    assert res["zeros"] is None
+    L0, (q0, sc0, zr0) = search_loss(X, W, np.ones(256, np.float32), cfg)
+    q_plain, sc_plain, _ = quantize_groups(W, 128, zero_point=False)
+    assert zr0 is None and np.array_equal(q0, q_plain) and np.array_equal(sc0, sc_plain)
+    assert res["losses"][0] == L0
+    qw, sc, zr = quantize_pack(W, cfg, res["s"])
+    assert np.array_equal(res["qweight"], qw) and zr is None
