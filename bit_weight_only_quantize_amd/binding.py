@@ -175,17 +175,19 @@ def _dtype_code(dt):
     raise TypeError(f"unsupported dtype {dt}")
 
 
-def empty_packed(N: int, K: int, group_size: int, device):
-    """Allocate (qweight int32 [N][K/8], scales fp16 [N][K/g], zeros uint8 [N][K/g])."""
+def empty_packed(N: int, K: int, group_size: int, device, zero_point: bool = True):
+    """Allocate (qweight int32 [N][K/8], scales fp16 [N][K/g], zeros uint8 [N][K/g]);
+    zeros is None for the symmetric grid (zero_point=False)."""
     torch = _torch()
     G = K // group_size
     return (torch.empty((N, K // 8), dtype=torch.int32, device=device),
             torch.empty((N, G), dtype=torch.float16, device=device),
-            torch.empty((N, G), dtype=torch.uint8, device=device))
+            torch.empty((N, G), dtype=torch.uint8, device=device) if zero_point else None)
 
 
 def _check_packed(qweight, scales, zeros, K, group_size):
-    """Packed layer tensors for input width K; returns N."""
+    """Packed layer tensors for input width K (zeros None: the symmetric
+    grid); returns N."""
     torch = _torch()
     if group_size <= 0 or K % group_size or K % 8:
         raise ValueError(f"K={K} must be a multiple of 8 and of group_size={group_size}")
@@ -195,12 +197,19 @@ def _check_packed(qweight, scales, zeros, K, group_size):
     N = qweight.shape[0]
     _tensor(qweight, "qweight", shape=(N, K // 8))
     _tensor(scales, "scales", torch.float16, (N, K // group_size))
-    _tensor(zeros, "zeros", torch.uint8, (N, K // group_size))
+    if zeros is not None:
+        _tensor(zeros, "zeros", torch.uint8, (N, K // group_size))
     return N
 
 
-def awq_quantize_pack(W, group_size: int = 128, s=None, nonfinite_count=None, out=None):
-    """Quantize and pack W (fp16 [N][K], on the GPU).  Returns (qweight, scales, zeros)."""
+def _zp_ptr(zeros):
+    return ctypes.c_void_p(0) if zeros is None else _ptr(zeros)
+
+
+def awq_quantize_pack(W, group_size: int = 128, s=None, nonfinite_count=None, out=None,
+                      zero_point: bool = True):
+    """Quantize and pack W (fp16 [N][K], on the GPU).  Returns (qweight,
+    scales, zeros); zeros is None for the symmetric grid (zero_point=False)."""
     torch = _torch()
     _tensor(W, "W", torch.float16)
     if W.dim() != 2:
@@ -212,6 +221,8 @@ def awq_quantize_pack(W, group_size: int = 128, s=None, nonfinite_count=None, ou
         qw, sc, zr = out
         if _check_packed(qw, sc, zr, K, group_size) != N:
             raise ValueError("out's packed tensors are not for N rows")
+        if (zr is None) == bool(zero_point):
+            raise ValueError("out's zeros must be a tensor exactly when zero_point is set")
     named = [(W, "W")]
     sp = ctypes.c_void_p(0)
     if s is not None:
@@ -227,10 +238,10 @@ def awq_quantize_pack(W, group_size: int = 128, s=None, nonfinite_count=None, ou
         cp = _ptr(nonfinite_count)
     dev = _placed(*named)
     if out is None:
-        qw, sc, zr = empty_packed(N, K, group_size, dev)
-    _placed((W, "W"), (qw, "qweight"), (sc, "scales"), (zr, "zeros"))
-    st = lib.awq_quantize_pack(_ptr(W), N, K, config(group_size), sp, _ptr(qw), _ptr(sc),
-                               _ptr(zr), cp, _stream(dev))
+        qw, sc, zr = empty_packed(N, K, group_size, dev, zero_point)
+    _placed((W, "W"), (qw, "qweight"), (sc, "scales"), *([] if zr is None else [(zr, "zeros")]))
+    st = lib.awq_quantize_pack(_ptr(W), N, K, config(group_size, zero_point=zero_point), sp,
+                               _ptr(qw), _ptr(sc), _zp_ptr(zr), cp, _stream(dev))
     check(st, "awq_quantize_pack")
     return qw, sc, zr
 
@@ -248,7 +259,8 @@ def _linear_args(X, qweight, scales, zeros, group_size, out_dtype, out):
         _tensor(out, "out", ydt, (M, N))
     elif out_dtype is not None and out_dtype not in ydt:
         raise TypeError(f"out_dtype {out_dtype} is not float16, bfloat16 or float32")
-    dev = _placed((X, "X"), (qweight, "qweight"), (scales, "scales"), (zeros, "zeros"))
+    dev = _placed((X, "X"), (qweight, "qweight"), (scales, "scales"),
+                  *([] if zeros is None else [(zeros, "zeros")]))
     if out is None:
         out = torch.empty((M, N), dtype=X.dtype if out_dtype is None else out_dtype, device=dev)
     _placed((X, "X"), (out, "out"))
@@ -297,7 +309,8 @@ def awq_linear_ex(X, qweight, scales, zeros, kernel: int = AWQ_KERNEL_AUTO,
     need = awq_linear_workspace_size(M, N, K, group_size, X.dtype, kernel)
     ws = _workspace_arg(workspace, need, dev)
     st = lib.awq_linear_ex(_ptr(X), _dtype_code(X.dtype), _ptr(qweight), _ptr(scales),
-                           _ptr(zeros), M, N, K, config(group_size), _ptr(out),
+                           _zp_ptr(zeros), M, N, K,
+                           config(group_size, zero_point=zeros is not None), _ptr(out),
                            _dtype_code(out.dtype), int(kernel),
                            ctypes.c_void_p(0) if ws is None else _ptr(ws),
                            0 if ws is None else ws.numel() * ws.element_size(), _stream(dev))
@@ -310,9 +323,9 @@ def awq_linear(X, qweight, scales, zeros, group_size: int = 128, out_dtype=None,
     runs the GEMV, larger M the GEMM without a K split; bf16 activations on
     the GEMM path raise AwqError (use awq_linear_ex or awq_linear_ws)."""
     M, N, K, out, dev = _linear_args(X, qweight, scales, zeros, group_size, out_dtype, out)
-    st = lib.awq_linear(_ptr(X), _dtype_code(X.dtype), _ptr(qweight), _ptr(scales), _ptr(zeros),
-                        M, N, K, config(group_size), _ptr(out), _dtype_code(out.dtype),
-                        _stream(dev))
+    st = lib.awq_linear(_ptr(X), _dtype_code(X.dtype), _ptr(qweight), _ptr(scales),
+                        _zp_ptr(zeros), M, N, K, config(group_size, zero_point=zeros is not None),
+                        _ptr(out), _dtype_code(out.dtype), _stream(dev))
     check(st, "awq_linear")
     return out
 
@@ -324,7 +337,8 @@ def awq_linear_ws(X, qweight, scales, zeros, workspace, group_size: int = 128, o
     M, N, K, out, dev = _linear_args(X, qweight, scales, zeros, group_size, out_dtype, out)
     ws = _workspace_arg(workspace, 0, dev)
     st = lib.awq_linear_ws(_ptr(X), _dtype_code(X.dtype), _ptr(qweight), _ptr(scales),
-                           _ptr(zeros), M, N, K, config(group_size), _ptr(out),
+                           _zp_ptr(zeros), M, N, K,
+                           config(group_size, zero_point=zeros is not None), _ptr(out),
                            _dtype_code(out.dtype),
                            ctypes.c_void_p(0) if ws is None else _ptr(ws),
                            0 if ws is None else ws.numel() * ws.element_size(), _stream(dev))
@@ -339,20 +353,24 @@ def awq_linear_noalloc(X, qweight, scales, zeros, group_size: int = 128, out_dty
     Calls that may overlap in time on one GPU must not be made."""
     M, N, K, out, dev = _linear_args(X, qweight, scales, zeros, group_size, out_dtype, out)
     st = lib.awq_linear_noalloc(_ptr(X), _dtype_code(X.dtype), _ptr(qweight), _ptr(scales),
-                                _ptr(zeros), M, N, K, config(group_size), _ptr(out),
+                                _zp_ptr(zeros), M, N, K,
+                           config(group_size, zero_point=zeros is not None), _ptr(out),
                                 _dtype_code(out.dtype), _stream(dev))
     check(st, "awq_linear_noalloc")
     return out
 
 
 def awq_scale_search_workspace_size(M: int, N: int, K: int, group_size: int = 128,
-                                    n_alpha: int = 20) -> int:
-    return int(lib.awq_scale_search_workspace_size(M, N, K, config(group_size), n_alpha))
+                                    n_alpha: int = 20, zero_point: bool = True) -> int:
+    cfg = config(group_size, zero_point=zero_point)
+    return int(lib.awq_scale_search_workspace_size(M, N, K, cfg, n_alpha))
 
 
-def awq_scale_search(X, W, group_size: int = 128, alphas=None, workspace=None, out=None):
+def awq_scale_search(X, W, group_size: int = 128, alphas=None, workspace=None, out=None,
+                     zero_point: bool = True):
     """Alpha-grid scale search.  Returns a dict with best_index, losses (numpy
-    fp64), s (fp32 [K] tensor) and the packed weights for the chosen s."""
+    fp64), s (fp32 [K] tensor) and the packed weights for the chosen s (zeros
+    None for the symmetric grid, zero_point=False)."""
     torch = _torch()
     _tensor(X, "X", torch.float16)
     _tensor(W, "W", torch.float16)
@@ -363,13 +381,15 @@ def awq_scale_search(X, W, group_size: int = 128, alphas=None, workspace=None, o
     if W.shape[1] != K:
         raise ValueError(f"W has {W.shape[1]} input channels, X has {K}")
     n_alpha = 20 if alphas is None else len(alphas)
-    need = awq_scale_search_workspace_size(M, N, K, group_size, n_alpha)
+    need = awq_scale_search_workspace_size(M, N, K, group_size, n_alpha, zero_point)
     if need == 0:
         check(AWQ_ERR_INVALID_ARG, "awq_scale_search_workspace_size")
     if out is not None:
         qw, sc, zr = out
         if _check_packed(qw, sc, zr, K, group_size) != N:
             raise ValueError("out's packed tensors are not for N rows")
+        if (zr is None) == bool(zero_point):
+            raise ValueError("out's zeros must be a tensor exactly when zero_point is set")
     if workspace is not None:
         _tensor(workspace, "workspace")
         if workspace.numel() * workspace.element_size() < need:
@@ -379,20 +399,21 @@ def awq_scale_search(X, W, group_size: int = 128, alphas=None, workspace=None, o
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if out is None:
-        qw, sc, zr = empty_packed(N, K, group_size, dev)
+        qw, sc, zr = empty_packed(N, K, group_size, dev, zero_point)
     best_s = torch.empty(K, dtype=torch.float32, device=dev)
-    _placed((X, "X"), (workspace, "workspace"), (qw, "qweight"), (sc, "scales"), (zr, "zeros"))
+    _placed((X, "X"), (workspace, "workspace"), (qw, "qweight"), (sc, "scales"),
+            *([] if zr is None else [(zr, "zeros")]))
     a_ptr = None
     if alphas is not None:
         a_arr = (ctypes.c_double * n_alpha)(*[float(a) for a in alphas])
         a_ptr = ctypes.cast(a_arr, ctypes.POINTER(ctypes.c_double))
     best = ctypes.c_int32(-1)
     losses = (ctypes.c_double * n_alpha)()
-    st = lib.awq_scale_search(_ptr(X), _ptr(W), M, N, K, config(group_size),
+    st = lib.awq_scale_search(_ptr(X), _ptr(W), M, N, K, config(group_size, zero_point=zero_point),
                               a_ptr, n_alpha, _ptr(workspace),
                               workspace.numel() * workspace.element_size(),
                               ctypes.byref(best), losses, _ptr(best_s),
-                              _ptr(qw), _ptr(sc), _ptr(zr), _stream(dev))
+                              _ptr(qw), _ptr(sc), _zp_ptr(zr), _stream(dev))
     check(st, "awq_scale_search")
     return {"best_index": int(best.value), "losses": np.array(losses[:], dtype=np.float64),
             "s": best_s, "qweight": qw, "scales": sc, "zeros": zr}

@@ -53,8 +53,8 @@ bool auto_gemv(int64_t M, int64_t N, int64_t K, int g) {
 
 awq_status check_config(awq_config cfg, int64_t K) {
   if (cfg.w_bit != 4) return fail(AWQ_ERR_UNSUPPORTED, "w_bit=%d: only 4 is supported", cfg.w_bit);
-  if (cfg.zero_point != 1)
-    return fail(AWQ_ERR_UNSUPPORTED, "zero_point=%d: only 1 (asymmetric) is supported",
+  if (cfg.zero_point != 0 && cfg.zero_point != 1)
+    return fail(AWQ_ERR_INVALID_ARG, "zero_point=%d: must be 1 (asymmetric) or 0 (symmetric)",
                 cfg.zero_point);
   if (cfg.group_size != 64 && cfg.group_size != 128)
     return fail(AWQ_ERR_UNSUPPORTED, "group_size=%d: supported values are 64 and 128",
@@ -92,7 +92,7 @@ awq_status check_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,
   if (!awq::gemm_supported(N, K, false))
     return fail(AWQ_ERR_UNSUPPORTED, "layer of %lld x %lld exceeds 2 GiB of packed weights",
                 (long long)N, (long long)K);
-  if (!X || !qweight || !scales || !zeros || !Y)
+  if (!X || !qweight || !scales || (cfg.zero_point && !zeros) || !Y)
     return fail(AWQ_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(X, 16) || !aligned(qweight, 16))
     return fail(AWQ_ERR_INVALID_ARG, "X and qweight must be 16-byte aligned");
@@ -180,7 +180,7 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
   if (N < 0) return fail(AWQ_ERR_INVALID_ARG, "N=%lld is negative", (long long)N);
   if (N > ((int64_t)1 << 31)) return fail(AWQ_ERR_INVALID_ARG, "N too large");
   if (N == 0) return ok();
-  if (!W || !qweight || !scales || !zeros)
+  if (!W || !qweight || !scales || (cfg.zero_point && !zeros))
     return fail(AWQ_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(W, 16) || !aligned(qweight, 16))
     return fail(AWQ_ERR_INVALID_ARG, "W and qweight must be 16-byte aligned");
@@ -189,7 +189,8 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
   if (nonfinite_count && !aligned(nonfinite_count, 4))
     return fail(AWQ_ERR_INVALID_ARG, "nonfinite_count must be 4-byte aligned");
   return hip_status(awq::launch_quantize_pack(reinterpret_cast<const uint16_t *>(W), N, K,
-                                              cfg.group_size, s, qweight, scales, zeros,
+                                              cfg.group_size, s, qweight, scales,
+                                              cfg.zero_point ? zeros : nullptr,
                                               nonfinite_count, as_stream(stream)),
                     "awq_quantize_pack");
 }
@@ -222,7 +223,7 @@ awq_status linear_impl(const char *who, const void *X, int32_t x_dtype, const ui
                                               : awq::YType::F32;
   const hipStream_t hs = as_stream(stream);
   if (runs_gemv(M, N, K, cfg.group_size, kernel))
-    return hip_status(awq::launch_gemv(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size, Y,
+    return hip_status(awq::launch_gemv(X, xt, qweight, scales, cfg.zero_point ? zeros : nullptr, M, N, K, cfg.group_size, Y,
                                        yt, hs),
                       who);
   const awq::GemmPlan plan =
@@ -237,7 +238,7 @@ awq_status linear_impl(const char *who, const void *X, int32_t x_dtype, const ui
       return fail(AWQ_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who,
                   workspace_bytes, plan.workspace_bytes);
   }
-  return hip_status(awq::launch_gemm(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size, Y,
+  return hip_status(awq::launch_gemm(X, xt, qweight, scales, cfg.zero_point ? zeros : nullptr, M, N, K, cfg.group_size, Y,
                                      yt, plan, workspace, hs),
                     who);
 }
@@ -338,7 +339,7 @@ awq_status awq_linear_noalloc(const void *X, int32_t x_dtype, const uint32_t *qw
                                               : awq::YType::F32;
   const hipStream_t hs = as_stream(stream);
   if (runs_gemv(M, N, K, cfg.group_size, AWQ_KERNEL_AUTO))
-    return hip_status(awq::launch_gemv(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size, Y,
+    return hip_status(awq::launch_gemv(X, xt, qweight, scales, cfg.zero_point ? zeros : nullptr, M, N, K, cfg.group_size, Y,
                                        yt, hs),
                       who);
   const awq::GemmPlan plan = awq::gemm_plan(M, N, K, xt, awq::Scratch::Bounded);
@@ -352,7 +353,7 @@ awq_status awq_linear_noalloc(const void *X, int32_t x_dtype, const uint32_t *qw
     st = static_scratch(&ws);
     if (st != AWQ_OK) return st;
   }
-  return hip_status(awq::launch_gemm(X, xt, qweight, scales, zeros, M, N, K, cfg.group_size, Y,
+  return hip_status(awq::launch_gemm(X, xt, qweight, scales, cfg.zero_point ? zeros : nullptr, M, N, K, cfg.group_size, Y,
                                      yt, plan, ws, hs),
                     who);
 }
@@ -383,7 +384,8 @@ awq_status awq_scale_search(const void *X, const void *W, int64_t M, int64_t N, 
       grid[j] = alphas[j];
     }
   }
-  if (!X || !W || !workspace || !best_index || !best_s || !qweight || !scales || !zeros)
+  if (!X || !W || !workspace || !best_index || !best_s || !qweight || !scales ||
+      (cfg.zero_point && !zeros))
     return fail(AWQ_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(X, 16) || !aligned(W, 16) || !aligned(qweight, 16) || !aligned(best_s, 16))
     return fail(AWQ_ERR_INVALID_ARG, "X, W, qweight and best_s must be 16-byte aligned");
@@ -403,7 +405,7 @@ awq_status awq_scale_search(const void *X, const void *W, int64_t M, int64_t N, 
   auto *act = reinterpret_cast<uint16_t *>(ws + L.act);
   auto *qw = reinterpret_cast<uint32_t *>(ws + L.qw);
   auto *sc = reinterpret_cast<uint16_t *>(ws + L.sc);
-  auto *zr = reinterpret_cast<uint8_t *>(ws + L.zr);
+  auto *zr = cfg.zero_point ? reinterpret_cast<uint8_t *>(ws + L.zr) : nullptr;
   auto *yref = reinterpret_cast<float *>(ws + L.yref);
   auto *partials = reinterpret_cast<double *>(ws + L.partials);
   auto *dlosses = reinterpret_cast<double *>(ws + L.losses);
@@ -436,7 +438,8 @@ awq_status awq_scale_search(const void *X, const void *W, int64_t M, int64_t N, 
   const float *sbest = table + (size_t)hbest * K;
   e = hipMemcpyAsync(best_s, sbest, sizeof(float) * K, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
-    e = awq::launch_quantize_pack(w, N, K, gs, sbest, qweight, scales, zeros, nullptr, s);
+    e = awq::launch_quantize_pack(w, N, K, gs, sbest, qweight, scales,
+                                  cfg.zero_point ? zeros : nullptr, nullptr, s);
   if (e != hipSuccess) return hip_status(e, "awq_scale_search (final pack)");
   *best_index = hbest;
   if (losses) std::memcpy(losses, hlosses, sizeof(double) * n_alpha);

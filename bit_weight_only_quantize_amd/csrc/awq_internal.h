@@ -1,6 +1,8 @@
 // Internal launcher interface between the C ABI (api.cpp) and the HIP kernels.
 // Every launcher assumes its arguments were validated by the caller and
-// returns the hipError_t of the launch.
+// returns the hipError_t of the launch.  A null `zeros` pointer selects the
+// symmetric grid (zero_point = 0): no zero point is read or written, and
+// every group's zero is 8.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -213,7 +213,9 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // t = 64 * wave + 16 * j + c, so that lane (c, kq) reads its four column
   // tiles' values with one 16-byte LDS read per group.
   const rsrc_t rS = make_rsrc(scales, (uint32_t)N * (uint32_t)G * 2u);
-  const rsrc_t rZ = make_rsrc(zeros, (uint32_t)N * (uint32_t)G);
+  // no zeros (the symmetric grid): every zero load reads 0, and 8 is added
+  const rsrc_t rZ = make_rsrc(zeros, zeros ? (uint32_t)N * (uint32_t)G : 0u);
+  const uint32_t zfix = zeros ? 0u : (8u << 16);
   const uint32_t sz_col = (uint32_t)(col0 + tid) * (uint32_t)G;
   struct SZ {
     uint32_t sc;     // kGPB scales: u16, or two u16 in one u32 (g = 64)
@@ -242,13 +244,13 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   const int sz_slot = ((wave * 16 + c) * 4 + kq) * 4;   // this thread's column: j = kq
   auto store_sz = [&](uint32_t *buf, const SZ &r) {
     if constexpr (kGPB == 1) {
-      buf[sz_slot / 4] = ((uint32_t)(uint8_t)r.zr << 16) | (uint16_t)r.sc;
+      buf[sz_slot / 4] = (((uint32_t)(uint8_t)r.zr << 16) + zfix) | (uint16_t)r.sc;
     } else if constexpr (!KTAIL) {
-      buf[sz_slot / 4] = ((r.zr & 0xFFu) << 16) | (r.sc & 0xFFFFu);
-      buf[256 + sz_slot / 4] = ((r.zr & 0xFF00u) << 8) | (r.sc >> 16);
+      buf[sz_slot / 4] = (((r.zr & 0xFFu) << 16) + zfix) | (r.sc & 0xFFFFu);
+      buf[256 + sz_slot / 4] = (((r.zr & 0xFF00u) << 8) + zfix) | (r.sc >> 16);
     } else {
-      buf[sz_slot / 4] = ((uint32_t)(uint8_t)r.zr << 16) | (uint16_t)r.sc;
-      buf[256 + sz_slot / 4] = ((uint32_t)r.zr1 << 16) | (uint32_t)r.sc1;
+      buf[sz_slot / 4] = (((uint32_t)(uint8_t)r.zr << 16) + zfix) | (uint16_t)r.sc;
+      buf[256 + sz_slot / 4] = (((uint32_t)r.zr1 << 16) + zfix) | (uint32_t)r.sc1;
     }
   };
 

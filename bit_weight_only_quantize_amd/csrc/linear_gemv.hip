@@ -80,7 +80,7 @@ template <class XT, int GS, int NW, int U, bool STAGE_X>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
-    void *__restrict__ Y, int ytype) {
+    void *__restrict__ Y, int ytype, uint32_t zfix) {
   constexpr int kWpl = GS / 32;            // packed words per lane per group
   constexpr bool kBF16 = __is_same(XT, TagBF16);
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -96,7 +96,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 
   const rsrc_t rQ = make_rsrc(qweight, (uint32_t)N * (uint32_t)K / 2u);
   const rsrc_t rS = make_rsrc(scales, (uint32_t)N * (uint32_t)G * 2u);
-  const rsrc_t rZ = make_rsrc(zeros, (uint32_t)N * (uint32_t)G);
+  // no zeros (the symmetric grid): every load reads 0 and zfix = 8 is added
+  const rsrc_t rZ = make_rsrc(zeros, zeros ? (uint32_t)N * (uint32_t)G : 0u);
   const rsrc_t rX = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
 
   const uint32_t q_lane = (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(kq * kWpl * 4);
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
         else  // a group past the end loaded nothing: its stale registers may hold any bits
           a[j] = g < G ? cur.a[u][j] : u32x4{0u, 0u, 0u, 0u};
       }
-      const uint32_t zr = zs[gs];
+      const uint32_t zr = zs[gs] + zfix;
       const uint16_t sb = ss[gs];
       const float sc = g < G ? half_bits_to_float(sb) : 0.0f;
       // The exact integers q - z times a, summed in fp32 over the group
@@ -282,6 +283,7 @@ static void gemv_launch(const uint16_t *X, const uint32_t *qw, const uint16_t *s
   const dim3 grid((unsigned)((N + 15) / 16));
   const int G = (int)(K / GS);
   const bool stage = (uint64_t)M * (uint64_t)K * 2u <= gemv_stage_budget(NW);
+  const uint32_t zfix = zr ? 0u : 8u;
   const GemvSmem L = gemv_smem(M, (int)K, G, stage);
   // the reduction reuses the buffer: at least NW * 64 * 16 bytes
   const uint32_t bytes = L.total > 64u * NW * 16u ? L.total : 64u * NW * 16u;
@@ -289,13 +291,13 @@ static void gemv_launch(const uint16_t *X, const uint32_t *qw, const uint16_t *s
   // faster at 13.5 groups per wave, slower at 5 and below).
   if (stage && G > 8 * NW)
     gemv_kernel<XT, GS, NW, 2, true><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
-                                                                   (int)K, Y, (int)yt);
+                                                                   (int)K, Y, (int)yt, zfix);
   else if (stage)
     gemv_kernel<XT, GS, NW, 1, true><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
-                                                                   (int)K, Y, (int)yt);
+                                                                   (int)K, Y, (int)yt, zfix);
   else
     gemv_kernel<XT, GS, NW, 2, false><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
-                                                                    (int)K, Y, (int)yt);
+                                                                    (int)K, Y, (int)yt, zfix);
 }
 
 // Waves per workgroup.  Every workgroup of a launch should be resident at

@@ -9,7 +9,10 @@
 //   scale = fp16(max((hi - lo) / 15, 2^-14)); zero = clamp(rint(-lo/scale), 0, 15)
 //   code  = clamp(rint(v / scale) + zero, 0, 15)
 // with IEEE correctly rounded fp32 division and rint half-to-even, so the codes
-// are reproducible bit for bit on any IEEE machine.
+// are reproducible bit for bit on any IEEE machine.  Without a zero point
+// ("Zero-Point Quantization": zero_point = False, the symmetric variant):
+//   scale = fp16(max(max |v| / 7, 2^-14)); code = clamp(rint(v/scale), -8, 7) + 8
+// and no zero point is stored.
 //
 // Mapping: one lane per output word (8 input channels, 16 bytes of W);
 // g/8 consecutive lanes form a group and exchange min/max with DPP moves.
@@ -61,7 +64,7 @@ __device__ __forceinline__ float group_max(float v) {
 // Grid: x covers the words of one row in chunks of 256 (a multiple of the
 // group's word count, so no group straddles workgroups), y the rows (looped
 // when N exceeds the grid's y limit).  No per-lane 64-bit division.
-template <int GS>
+template <int GS, bool SYM>
 __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const uint16_t *__restrict__ W, int64_t N, int64_t K, const float *__restrict__ s,
     uint32_t *__restrict__ qweight, uint16_t *__restrict__ scales,
@@ -99,29 +102,40 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
       for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
 
-    float lo = 0.0f, hi = 0.0f;
+    float lo = 0.0f, hi = 0.0f, step;
+    if constexpr (SYM) {
+      // the largest magnitude of the group on level +-7: one IEEE division
+      // per lane and group
+      float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      lo = fminf(lo, v[i]);
-      hi = fmaxf(hi, v[i]);
-    }
-    lo = group_min<kLanesPerGroup>(lo);
-    hi = group_max<kLanesPerGroup>(hi);
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
+      amax = group_max<kLanesPerGroup>(amax);
+      step = amax / 7.0f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo = fminf(lo, v[i]);
+        hi = fmaxf(hi, v[i]);
+      }
+      lo = group_min<kLanesPerGroup>(lo);
+      hi = group_max<kLanesPerGroup>(hi);
 
-    // (hi - lo) / 15, correctly rounded, from the product with RN(1/15) and
-    // one exact-remainder correction (Markstein): checked against IEEE
-    // division for every non-negative finite fp32 dividend; an infinite
-    // dividend (the only other value hi - lo takes) passes through as the
-    // division would give it.
-    const float d = hi - lo;
-    const float q0 = d * 0x1.111112p-4f;
-    const float q1 = __builtin_fmaf(__builtin_fmaf(-15.0f, q0, d), 0x1.111112p-4f, q0);
-    const float step = d == __builtin_inff() ? d : q1;
+      // (hi - lo) / 15, correctly rounded, from the product with RN(1/15)
+      // and one exact-remainder correction (Markstein): checked against IEEE
+      // division for every non-negative finite fp32 dividend; an infinite
+      // dividend (the only other value hi - lo takes) passes through as the
+      // division would give it.
+      const float d = hi - lo;
+      const float q0 = d * 0x1.111112p-4f;
+      const float q1 = __builtin_fmaf(__builtin_fmaf(-15.0f, q0, d), 0x1.111112p-4f, q0);
+      step = d == __builtin_inff() ? d : q1;
+    }
     const _Float16 sh = (_Float16)fmaxf(step, 0x1p-14f);
     const float sf = (float)sh;
 
     // rint(v / sf) with the correctly rounded quotient q, without eight
-    // divisions: |v / sf| < 16 (|v| <= hi - lo <= 15 sf (1 + 2^-10)), so q
+    // divisions: |v / sf| < 16 (|v| <= hi - lo <= 15 sf (1 + 2^-10), or
+    // symmetric |v| <= max |v| <= 7 sf (1 + 2^-10)), so q
     // lies within 2^-20 of the exact v / sf, and y = fl(v * rcp(sf)), with
     // the hardware reciprocal (specified to 1 ulp; up to 7 ulp would do),
     // within 2^-16 - 2^-20.  Unless y is within 2^-16 of a half-integer, both
@@ -133,7 +147,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     // an inf in the group makes sf inf and rcp(sf) 0), so those lanes take
     // the slow path too, where they are counted.
     const float rs = __builtin_amdgcn_rcpf(sf);
-    const float zy = -lo * rs;
+    const float zy = -lo * rs;          // symmetric: lo = 0, so zq = 0
     float zq = __builtin_rintf(zy);
     bool near_half = !(__builtin_fabsf(zy - zq) <= 0.5f - 0x1p-16f);
     float qv[8];
@@ -145,18 +159,22 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
       near_half |= !(__builtin_fabsf(y - qv[i]) <= 0.5f - 0x1p-16f);
     }
     if (near_half) {
-      zq = __builtin_rintf(-lo / sf);
+      if constexpr (!SYM) zq = __builtin_rintf(-lo / sf);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         qv[i] = __builtin_rintf(v[i] / sf);
         bad += !__builtin_isfinite(v[i]);
       }
     }
-    const float zf = fminf(fmaxf(zq, 0.0f), 15.0f);
+    // asymmetric: codes rint(v/s) + z clamped to [0, 15]; symmetric:
+    // rint(v/s) clamped to [-8, 7], plus 8
+    const float zf = SYM ? 8.0f : fminf(fmaxf(zq, 0.0f), 15.0f);
+    const float qlo = SYM ? -8.0f : 0.0f, qhi = SYM ? 7.0f : 15.0f;
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float qf = fminf(fmaxf(qv[i] + zf, 0.0f), 15.0f);
+      const float qf = SYM ? fminf(fmaxf(qv[i], qlo), qhi) + zf
+                           : fminf(fmaxf(qv[i] + zf, qlo), qhi);
       word |= ((uint32_t)qf) << (4 * nibble_of_channel(i));
     }
 
@@ -165,7 +183,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
       if ((c % kLanesPerGroup) == 0) {
         const int64_t gi = n * (K / GS) + c / kLanesPerGroup;
         scales[gi] = __builtin_bit_cast(uint16_t, sh);
-        zeros[gi] = (uint8_t)zf;
+        if constexpr (!SYM) zeros[gi] = (uint8_t)zf;
       }
     }
   }
@@ -183,10 +201,17 @@ hipError_t launch_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int gs,
   if (N == 0) return hipSuccess;
   const int64_t wpr = K / 8;
   const dim3 grid((unsigned)((wpr + 255) / 256), (unsigned)(N < 65535 ? N : 65535));
-  if (gs == 128)
-    quantize_pack_kernel<128><<<grid, 256, 0, st>>>(W, N, K, s, qweight, scales, zeros, nonfinite);
-  else
-    quantize_pack_kernel<64><<<grid, 256, 0, st>>>(W, N, K, s, qweight, scales, zeros, nonfinite);
+  if (zeros == nullptr) {
+    if (gs == 128)
+      quantize_pack_kernel<128, true><<<grid, 256, 0, st>>>(W, N, K, s, qweight, scales, zeros, nonfinite);
+    else
+      quantize_pack_kernel<64, true><<<grid, 256, 0, st>>>(W, N, K, s, qweight, scales, zeros, nonfinite);
+  } else {
+    if (gs == 128)
+      quantize_pack_kernel<128, false><<<grid, 256, 0, st>>>(W, N, K, s, qweight, scales, zeros, nonfinite);
+    else
+      quantize_pack_kernel<64, false><<<grid, 256, 0, st>>>(W, N, K, s, qweight, scales, zeros, nonfinite);
+  }
   return hipGetLastError();
 }
 

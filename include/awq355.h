@@ -32,7 +32,8 @@
  *             the 4-bit code of input channel 8c + ORDER[p],
  *             ORDER = {0, 2, 4, 6, 1, 3, 5, 7}.
  *  - scales   fp16 bits [N][K/g]: step of group k/g of row n.
- *  - zeros    u8   [N][K/g]: zero point (0..15) of that group.
+ *  - zeros    u8   [N][K/g]: zero point (0..15) of that group; absent for
+ *             the symmetric grid (zero_point = 0), whose zero is 8.
  *  - weight(n, k) = (code - zero) * scale.
  */
 #ifndef AWQ355_H
@@ -46,8 +47,10 @@ extern "C" {
 #endif
 
 /* Mirror of the pages' quant_config fields (w_bit, q_group_size,
- * zero_point).  Supported: w_bit = 4, group_size in {64, 128},
- * zero_point = 1. */
+ * zero_point).  Supported: w_bit = 4, group_size in {64, 128}, zero_point =
+ * 1 (asymmetric, a zero point per group) or 0 (symmetric: "Zero-Point
+ * Quantization", no zero points; every entry point then ignores `zeros`,
+ * which may be NULL, and the code of 0.0 is 8). */
 typedef struct awq_config {
     int32_t w_bit;
     int32_t group_size;
@@ -87,7 +90,7 @@ typedef void *awq_stream_t;
  *   s        device, fp32 [K] per-input-channel scale, or NULL for s = 1.
  *   qweight  device, u32 [N][K/8], 16-byte aligned (layout above).
  *   scales   device, fp16 bits [N][K/g].
- *   zeros    device, u8 [N][K/g].
+ *   zeros    device, u8 [N][K/g] (zero_point = 1; ignored when 0).
  *   nonfinite_count  device int32 or NULL.  When given, the number of
  *            non-finite values among s_k * W_nk is ADDED to it (the caller
  *            clears it); outputs of groups holding such values are unspecified.
@@ -95,6 +98,8 @@ typedef void *awq_stream_t;
  * Per group of g consecutive k of one row, with v = fp32(s_k * W_nk):
  *   lo = min(min v, 0), hi = max(max v, 0), scale = fp16(max((hi-lo)/15, 2^-14)),
  *   zero = clamp(rint(-lo/scale), 0, 15), code = clamp(rint(v/scale) + zero, 0, 15),
+ * and with zero_point = 0 (no zeros written):
+ *   scale = fp16(max(max |v| / 7, 2^-14)), code = clamp(rint(v/scale), -8, 7) + 8,
  * fp32 correctly-rounded division, rint = round half to even.
  * Requirements: N >= 0, K > 0, K % g == 0.  N == 0 is a no-op.
  */

@@ -56,7 +56,12 @@ def test_quantize_pack_validation():
     assert _qp(c=cfg(128, w_bit=3)) == binding.AWQ_ERR_UNSUPPORTED
     assert "w_bit" in lib.awq_last_error().decode()
     assert _qp(c=cfg(96)) == binding.AWQ_ERR_UNSUPPORTED
-    assert _qp(c=cfg(128, zero_point=False)) == binding.AWQ_ERR_UNSUPPORTED
+    bad_zp = binding.awq_config(4, 128, 2)
+    assert _qp(c=bad_zp) == binding.AWQ_ERR_INVALID_ARG
+    assert "zero_point" in lib.awq_last_error().decode()
+    # the symmetric grid takes no zeros: NULL passes validation (N = 0: no launch)
+    assert _qp(c=cfg(128, zero_point=False), zr=NULL, N=0) == binding.AWQ_OK
+    assert _qp(zr=NULL) == binding.AWQ_ERR_INVALID_ARG      # asymmetric needs them
     assert _qp(K=192) == binding.AWQ_ERR_INVALID_ARG          # not a multiple of 128
     assert _qp(K=0) == binding.AWQ_ERR_INVALID_ARG
     assert _qp(N=-1) == binding.AWQ_ERR_INVALID_ARG

@@ -18,12 +18,14 @@ def _awq():
     return awq
 
 
-def _packed(W, g, chunk=4096):
-    """Oracle-packed weights (row chunks bound host memory), plus GPU copies."""
-    parts = [quantize_pack(W[r:r + chunk], QuantConfig(group_size=g))
+def _packed(W, g, chunk=4096, zero_point=True):
+    """Oracle-packed weights (row chunks bound host memory), plus GPU copies;
+    zeros are None for the symmetric grid."""
+    parts = [quantize_pack(W[r:r + chunk], QuantConfig(group_size=g, zero_point=zero_point))
              for r in range(0, W.shape[0], chunk)]
-    qw, sc, zr = (np.concatenate([p[i] for p in parts]) for i in range(3))
-    return qw, sc, zr, (to_dev(qw), to_dev(sc), to_dev(zr))
+    qw, sc = (np.concatenate([p[i] for p in parts]) for i in range(2))
+    zr = np.concatenate([p[2] for p in parts]) if zero_point else None
+    return qw, sc, zr, (to_dev(qw), to_dev(sc), None if zr is None else to_dev(zr))
 
 
 _PREFILL_CACHE = {}
@@ -467,3 +469,74 @@ def test_empty_inputs():
     X = torch.empty((0, 256), dtype=torch.float16, device=dev())
     Y = awq.awq_linear(X, *pd, group_size=128)
     assert Y.shape == (0, 32)
+
+
+# --- the symmetric grid (zero_point=False: no zero points, zero code 8) ---------------
+
+@pytest.mark.parametrize("path", ["gemv", "gemm32", "gemm_large"])
+def test_symmetric_one_hot_rows_are_exact(path):
+    torch = torch_mod()
+    N, K, g = 80, 512, 128
+    W = wl.gen_weight(N, K, 18)
+    qw, sc, zr, pd = _packed(W, g, zero_point=False)
+    assert zr is None and pd[2] is None
+    deq = dequantize(unpack_codes(qw, K), sc, None, g)
+    if path == "gemm_large":
+        deq = deq.astype(np.float16).astype(np.float64)
+    rows = {"gemv": 16, "gemm32": 32, "gemm_large": K}[path]
+    for k0 in range(0, K, rows):
+        sel = np.arange(k0, min(K, k0 + rows))
+        X = np.zeros((len(sel), K), np.float16)
+        X[np.arange(len(sel)), sel] = 1.0
+        say("symmetric one-hot", path, len(sel))
+        Y = out_to_f64(_run(X, "f16", pd, g, GEMV if path == "gemv" else GEMM, torch.float32))
+        assert np.array_equal(Y, deq[:, sel].T)
+
+
+@pytest.mark.parametrize("case", wl.gemv_cases(), ids=lambda c: c.name)
+def test_symmetric_decode_layers(case):
+    """The 7B-class decode layers without zero points at M = 1 and 4: the
+    automatic choice (GEMV) and the GEMM, against the fp64 oracle."""
+    torch = torch_mod()
+    W = case.weight()
+    X = case.activation()
+    qw, sc, zr, pd = _packed(W, 128, zero_point=False)
+    ref = linear64(X, qw, sc, None, 128)
+    for kern in (0, GEMM):
+        say("symmetric gemv layer", case.name, kern)
+        assert_close(out_to_f64(_run(X, "f16", pd, 128, kern)), ref, case.name)
+        assert_close(out_to_f64(_run(X, "f16", pd, 128, kern, torch.float32)), ref, case.name)
+
+
+@pytest.mark.parametrize("case", [c for c in wl.gemm_cases() if c.M in (16, 256)],
+                         ids=lambda c: c.name)
+def test_symmetric_batched_layers(case):
+    W = case.weight()
+    X = case.activation()
+    qw, sc, zr, pd = _packed(W, case.group_size, zero_point=False)
+    ref = linear64(X, qw, sc, None, case.group_size)
+    say("symmetric gemm layer", case.name)
+    assert_close(out_to_f64(_run(X, "f16", pd, case.group_size, 0)), ref, case.name)
+
+
+@pytest.mark.parametrize("M,N,K,g,dt", [(5, 130, 1024, 64, "bf16"), (33, 300, 2048, 128, "bf16"),
+                                        (77, 200, 384, 128, "f16"), (300, 32600, 384, 128, "bf16")])
+def test_symmetric_ragged(M, N, K, g, dt):
+    """Ragged symmetric layers through the GEMV, the split-K tiles and the
+    256-row tile, fp16 and bf16 activations, fp32 output; awq_linear_noalloc
+    gives the same bits as the workspace call."""
+    torch = torch_mod()
+    awq = _awq()
+    W = wl.gen_weight(N, K, 180 + N)
+    X = wl.gen_activation(M, K, 181 + M, 182, dt)
+    qw, sc, zr, pd = _packed(W, g, zero_point=False)
+    ref = linear64(_x_f64(X, dt), qw, sc, None, g)
+    for kern in [GEMM] + ([GEMV] if M <= 16 else []):
+        say("symmetric ragged", M, N, K, g, dt, kern)
+        Y = _run(X, dt, pd, g, kern, torch.float32)
+        assert_close(out_to_f64(Y), ref, f"sym {M}x{N}x{K}")
+    Xd = to_dev(X, bf16=(dt == "bf16"))
+    a = awq.awq_linear_ex(Xd, *pd, group_size=g, out_dtype=torch.float32)
+    b = awq.awq_linear_noalloc(Xd, *pd, group_size=g, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -20,17 +20,20 @@ def _awq():
     return awq
 
 
-def _gpu_pack(W, g, s=None):
+def _gpu_pack(W, g, s=None, zero_point=True):
     awq = _awq()
     qw, sc, zr = awq.awq_quantize_pack(to_dev(W), group_size=g,
-                                       s=None if s is None else to_dev(s))
+                                       s=None if s is None else to_dev(s), zero_point=zero_point)
     torch_mod().cuda.synchronize()
-    return to_np(qw), to_np(sc), to_np(zr)
+    return to_np(qw), to_np(sc), None if zr is None else to_np(zr)
 
 
 def _assert_same(gpu, ref, what):
     names = ("qweight", "scales", "zeros")
     for a, b, nm in zip(gpu, ref, names):
+        if a is None or b is None:
+            assert a is None and b is None, (what, nm)
+            continue
         a = np.asarray(a)
         b = np.asarray(b)
         if nm == "scales":
@@ -149,3 +152,44 @@ def test_empty_is_noop():
     W = torch.empty((0, 256), dtype=torch.float16, device=dev())
     qw, sc, zr = awq.awq_quantize_pack(W, 128)
     assert qw.shape == (0, 32)
+
+
+# --- the symmetric grid (zero_point=False) ----------------------------------------------
+
+def test_symmetric_hand_worked_groups_on_gpu():
+    gold = json.load(open(os.path.join(HERE, "golden", "hand_worked_symmetric.json")))
+    g = gold["group_size"]
+    W = np.zeros((len(gold["groups"]), g), dtype=np.float16)
+    for i, grp in enumerate(gold["groups"]):
+        W[i, : len(grp["values"])] = np.array(grp["values"], dtype=np.float16)
+    say("symmetric hand-worked groups", W.shape)
+    qw, sc, zr = _gpu_pack(W, g, zero_point=False)
+    assert zr is None
+    from oracle import unpack_codes
+    q = unpack_codes(qw, g)
+    for i, grp in enumerate(gold["groups"]):
+        n = len(grp["codes"])
+        assert q[i, :n].tolist() == grp["codes"], grp["name"]
+        assert np.all(q[i, n:] == 8), grp["name"]
+        assert int(sc.view(np.uint16)[i, 0]) == grp["scale_fp16_bits"], grp["name"]
+
+
+@pytest.mark.parametrize("N,K,g", SMALL)
+def test_symmetric_ragged_and_small(N, K, g):
+    W = wl.gen_weight(N, K, 1100 + N, row_seed=8)
+    cfg = QuantConfig(group_size=g, zero_point=False)
+    say("symmetric quantize ragged", N, K, g)
+    _assert_same(_gpu_pack(W, g, zero_point=False), quantize_pack(W, cfg), f"sym {N}x{K}g{g}")
+    s = np.exp(np.random.default_rng(N + 1).standard_normal(K)).astype(np.float32)
+    _assert_same(_gpu_pack(W, g, s, zero_point=False), quantize_pack(W, cfg, s),
+                 f"sym {N}x{K}g{g} scaled")
+
+
+@pytest.mark.parametrize("case", wl.gemv_cases(Ms=(1,)), ids=lambda c: c.name)
+def test_symmetric_decode_layers(case):
+    """The 7B-class layers quantized without zero points, every word, scale
+    and code bit-identical to the oracle's."""
+    W = case.weight()
+    say("symmetric quantize layer", case.name)
+    _assert_same(_gpu_pack(W, 128, zero_point=False),
+                 quantize_pack(W, QuantConfig(zero_point=False)), case.name)

@@ -23,8 +23,9 @@ def _awq():
     return awq
 
 
-def _gpu_search(X, W, g=128, alphas=None):
-    res = _awq().awq_scale_search(to_dev(X), to_dev(W), group_size=g, alphas=alphas)
+def _gpu_search(X, W, g=128, alphas=None, zero_point=True):
+    res = _awq().awq_scale_search(to_dev(X), to_dev(W), group_size=g, alphas=alphas,
+                                  zero_point=zero_point)
     torch_mod().cuda.synchronize()
     return res
 
@@ -57,7 +58,10 @@ def _check_against(res, ref, what):
     assert np.array_equal(to_np(res["s"]).view(np.uint32), ref["s"].view(np.uint32))
     assert np.array_equal(to_np(res["qweight"]), ref["qweight"])
     assert np.array_equal(to_np(res["scales"]).view(np.uint16), ref["scales"].view(np.uint16))
-    assert np.array_equal(to_np(res["zeros"]), ref["zeros"])
+    if ref["zeros"] is None:
+        assert res["zeros"] is None
+    else:
+        assert np.array_equal(to_np(res["zeros"]), ref["zeros"])
 
 
 @pytest.mark.parametrize("M,N,K,g", [(256, 192, 512, 128), (100, 77, 384, 64), (512, 256, 1024, 128)])
@@ -164,3 +168,15 @@ def test_search_statistic_beyond_2_53_units():
     ref = scale_search(X, W, QuantConfig(), np.array([0.0, 0.25, 0.5, 0.75, 1.0]))
     _check_against(res, ref, "large M")
     _every_candidate_bitwise(X, W, 128, [0.1, 0.35, 0.6, 0.95], None)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(256, 192, 512, 128), (100, 77, 384, 64)])
+def test_symmetric_search_matches_oracle(M, N, K, g):
+    """The search over the symmetric grid (zero_point=False): losses, the
+    chosen index, s and the packed result against the oracle."""
+    X = wl.gen_activation(M, K, 7 * M + 1, 8 * M + 1)
+    W = wl.gen_weight(N, K, 9 * N + 1)
+    say("symmetric search", M, N, K, g)
+    res = _gpu_search(X, W, g, zero_point=False)
+    ref = scale_search(X, W, QuantConfig(group_size=g, zero_point=False))
+    _check_against(res, ref, f"symmetric search {M}x{N}x{K}")
