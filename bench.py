@@ -200,6 +200,105 @@ def cpu_baseline(layers):
                       f"(unpack + fp64 dequant + fp64 GEMV), {dt:.1f} s"}
 
 
+def _blas_threads():
+    from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()
+                if i.get("internal_api") in ("openblas", "mkl", "blis")] + [1])
+
+
+def _timed(fn, min_s=2.0, max_reps=20):
+    """Seconds per call of fn, repeated until min_s has passed."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s or reps >= max_reps:
+            return dt / reps, reps
+
+
+def oracle_rows(rows):
+    """The CPU oracle, as it stands, on bounded samples of the quantize,
+    batched-GEMM, prefill and search rows, in each row's units, with the
+    GPU/CPU ratio.  Elementwise oracle steps run on one thread (NumPy); the
+    fp64 products on the BLAS threads."""
+    import workloads as wl
+    from oracle import (DEFAULT_ALPHAS, QuantConfig, activation_mean_abs, linear64,
+                        quantize_pack, reference_output, scale_vector, search_loss)
+    nt = _blas_threads()
+    out = {}
+
+    c = wl.gemv_cases(Ms=(1,))[1]
+    W = c.weight()
+    qbytes = c.N * c.K * 2 + c.weight_bytes
+    t, reps = _timed(lambda: quantize_pack(W, QuantConfig()), 3.0, 5)
+    gpu = rows.get("quantize_pack_4096x11008", {}).get("GB/s")
+    out["quantize_pack_4096x11008"] = {
+        "value": round(qbytes / t / 1e9, 4), "unit": "GB/s", "threads": 1,
+        "sample": f"the whole 4096x11008 layer, {reps} run(s), {t:.2f} s each",
+        "gpu_over_cpu": None if gpu is None else round(gpu / (qbytes / t / 1e9), 1)}
+    log("oracle quantize", out["quantize_pack_4096x11008"])
+    del W
+
+    case = [x for x in wl.gemm_cases() if x.M == 256 and x.group_size == 128][0]
+    qw, sc, zr = quantize_pack(case.weight(), QuantConfig())
+    X = case.activation()
+    t, reps = _timed(lambda: [linear64(X, qw[n0:n0 + 1024], sc[n0:n0 + 1024], zr[n0:n0 + 1024], 128)
+                              for n0 in range(0, case.N, 1024)], 2.0, 5)
+    tf = case.flops / t / 1e12
+    gpu = next((r["TFLOP/s"] for r in rows.get("batched_gemm", []) if r["layer"] == case.name), None)
+    out[case.name] = {"value": round(tf, 5), "unit": "TFLOP/s", "threads": nt,
+                      "sample": f"the whole layer in blocks of 1024 output columns (unpack, fp64 "
+                                f"dequant and product), {reps} run(s), {t:.2f} s each",
+                      "gpu_over_cpu": None if gpu is None else round(gpu / tf, 1)}
+    log("oracle", case.name, out[case.name])
+    del qw, sc, zr, X
+
+    case = wl.prefill_cases(dtypes=("f16",))[0]
+    Wb = wl.gen_weight(case.N, case.K, case.w_seed)[:2048]        # rows are quantized alone
+    qw, sc, zr = quantize_pack(Wb, QuantConfig())
+    X = case.activation()
+    blocks = 2
+    t0 = time.perf_counter()
+    for b in range(blocks):
+        linear64(X, qw[1024 * b:1024 * (b + 1)], sc[1024 * b:1024 * (b + 1)],
+                 zr[1024 * b:1024 * (b + 1)], 128)
+    dt = time.perf_counter() - t0
+    tf = 2.0 * case.M * case.K * 1024 * blocks / dt / 1e12
+    gpu = next((r["TFLOP/s"] for r in rows.get("prefill_gemm", []) if r["layer"] == case.name), None)
+    out[case.name] = {"value": round(tf, 5), "unit": "TFLOP/s", "threads": nt,
+                      "sample": f"{blocks} of the {case.N // 1024} blocks of 1024 output columns "
+                                f"(all 4096 rows), {dt:.2f} s; the full layer at this rate: "
+                                f"{dt * case.N / (1024 * blocks):.0f} s",
+                      "gpu_over_cpu": None if gpu is None else round(gpu / tf, 1)}
+    log("oracle", case.name, out[case.name])
+    del Wb, qw, sc, zr, X
+
+    case = wl.search_case()
+    X = case.activation()
+    W = case.weight()
+    t0 = time.perf_counter()
+    xbar = activation_mean_abs(X)
+    Y_ref = reference_output(X, W)
+    t_ref = time.perf_counter() - t0
+    n_alpha = 2
+    t0 = time.perf_counter()
+    for a in DEFAULT_ALPHAS[[0, 7]][:n_alpha]:
+        search_loss(X, W, scale_vector(xbar, a), QuantConfig(), Y_ref)
+    t_a = (time.perf_counter() - t0) / n_alpha
+    full = t_ref + 20 * t_a
+    flops = 21 * 2 * case.M * case.N * case.K
+    gpu = rows.get("scale_search_4096", {}).get("ms")
+    out["scale_search_4096"] = {
+        "value": round(full * 1e3, 1), "unit": "ms (20 alphas)", "threads": nt,
+        "effective_TFLOP/s": round(flops / full / 1e12, 5),
+        "sample": f"statistic and fp64 reference product ({t_ref:.1f} s) plus {n_alpha} of the "
+                  f"20 candidates ({t_a:.1f} s each), extrapolated to 20",
+        "gpu_over_cpu": None if gpu is None else round(full * 1e3 / gpu, 1)}
+    log("oracle search", out["scale_search_4096"])
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -310,6 +409,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         cpu = cpu_baseline(host_layers)
+        if args.rows == "all":
+            rows["cpu_oracle"] = oracle_rows(rows)
 
     out = {
         "metric": "W4A16 GEMV weight GB/s (M=1) & GEMM TFLOP/s (M>=256), % of MI355X roofline",
@@ -490,3 +591,10 @@ def measure_search_row(awq, torch, wl):
 
 if __name__ == "__main__":
     main()
+    # The result line is out.  bench.py starts no child process; what remains
+    # is teardown (the HIP runtime releasing about a hundred captured graphs
+    # and several GB of device buffers, the BLAS thread pool), which can keep
+    # the process alive for seconds after the line.  Flush and end it here.
+    sys.stdout.flush()
+    sys.stderr.flush()
+    os._exit(0)
