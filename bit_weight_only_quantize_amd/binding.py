@@ -27,16 +27,21 @@ AWQ_ERR_NONFINITE = 5
 
 AWQ_F16, AWQ_BF16, AWQ_F32 = 0, 1, 2
 AWQ_KERNEL_AUTO, AWQ_KERNEL_GEMV, AWQ_KERNEL_GEMM = 0, 1, 2
+AWQ_EPILOGUE_NONE, AWQ_EPILOGUE_SILU_MUL = 0, 1
+AWQ_MAX_PARTS = 4
 AWQ_GEMV_MAX_M = 16
 
 #: Every symbol include/awq355.h declares.
 EXPORTS = (
     "awq_quantize_pack",
+    "awq_dequantize",
     "awq_linear",
     "awq_linear_ex",
     "awq_linear_workspace_size",
     "awq_linear_ws",
     "awq_linear_noalloc",
+    "awq_linear_fused_workspace_size",
+    "awq_linear_fused",
     "awq_scale_search_workspace_size",
     "awq_scale_search",
     "awq_status_string",
@@ -48,6 +53,11 @@ EXPORTS = (
 class awq_config(ctypes.Structure):
     _fields_ = [("w_bit", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("zero_point", ctypes.c_int32)]
+
+
+class awq_linear_part(ctypes.Structure):
+    _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("N", ctypes.c_int64), ("Y", ctypes.c_void_p)]
 
 
 class AwqError(RuntimeError):
@@ -71,6 +81,8 @@ def _load():
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.awq_quantize_pack.argtypes = [vp, i64, i64, awq_config, vp, vp, vp, vp, vp, vp]
     lib.awq_quantize_pack.restype = ctypes.c_int
+    lib.awq_dequantize.argtypes = [vp, vp, vp, i64, i64, awq_config, vp, i32, vp]
+    lib.awq_dequantize.restype = ctypes.c_int
     lib.awq_linear.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32, vp]
     lib.awq_linear.restype = ctypes.c_int
     lib.awq_linear_ex.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32, i32, vp,
@@ -81,6 +93,12 @@ def _load():
     lib.awq_linear_ws.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32, vp,
                                   ctypes.c_size_t, vp]
     lib.awq_linear_ws.restype = ctypes.c_int
+    pp = ctypes.POINTER(awq_linear_part)
+    lib.awq_linear_fused_workspace_size.argtypes = [pp, i32, i64, i64, awq_config, i32, i32, i32]
+    lib.awq_linear_fused_workspace_size.restype = ctypes.c_size_t
+    lib.awq_linear_fused.argtypes = [vp, i32, pp, i32, i64, i64, awq_config, i32, vp, i32, i32,
+                                     vp, ctypes.c_size_t, vp]
+    lib.awq_linear_fused.restype = ctypes.c_int
     lib.awq_linear_noalloc.argtypes = [vp, i32, vp, vp, vp, i64, i64, i64, awq_config, vp, i32,
                                        vp]
     lib.awq_linear_noalloc.restype = ctypes.c_int
@@ -246,6 +264,30 @@ def awq_quantize_pack(W, group_size: int = 128, s=None, nonfinite_count=None, ou
     return qw, sc, zr
 
 
+def awq_dequantize(qweight, scales, zeros, K: int, group_size: int = 128, out_dtype=None,
+                   out=None):
+    """(code - zero) * scale as a [N][K] tensor: float32 (exact, the default)
+    or float16 (rounded once); zeros None for the symmetric grid."""
+    torch = _torch()
+    N = _check_packed(qweight, scales, zeros, K, group_size)
+    odt = torch.float32 if out_dtype is None else out_dtype
+    if out is not None:
+        _tensor(out, "out", (torch.float16, torch.float32), (N, K))
+        odt = out.dtype
+    elif odt not in (torch.float16, torch.float32):
+        raise TypeError(f"out_dtype {odt} is not float16 or float32")
+    dev = _placed((qweight, "qweight"), (scales, "scales"),
+                  *([] if zeros is None else [(zeros, "zeros")]))
+    if out is None:
+        out = torch.empty((N, K), dtype=odt, device=dev)
+    _placed((qweight, "qweight"), (out, "out"))
+    st = lib.awq_dequantize(_ptr(qweight), _ptr(scales), _zp_ptr(zeros), N, K,
+                            config(group_size, zero_point=zeros is not None), _ptr(out),
+                            _dtype_code(odt), _stream(dev))
+    check(st, "awq_dequantize")
+    return out
+
+
 def _linear_args(X, qweight, scales, zeros, group_size, out_dtype, out):
     """Validate a linear call; returns (M, N, K, out, device)."""
     torch = _torch()
@@ -358,6 +400,78 @@ def awq_linear_noalloc(X, qweight, scales, zeros, group_size: int = 128, out_dty
                                 _dtype_code(out.dtype), _stream(dev))
     check(st, "awq_linear_noalloc")
     return out
+
+
+def awq_linear_fused(X, parts, epilogue: str = "none", group_size: int = 128, out_dtype=None,
+                     outs=None, kernel: int = AWQ_KERNEL_AUTO, workspace="auto"):
+    """Several projections of one X (each part a (qweight, scales, zeros)
+    tuple of the same K, group size and zero-point mode).  epilogue 'none'
+    returns [X W_i^T for each part]; 'silu_mul' takes (gate, up) and returns
+    silu(X Wg^T) * (X Wu^T).  `outs` optionally gives the output tensors (a
+    list for 'none', one tensor for 'silu_mul')."""
+    torch = _torch()
+    if epilogue not in ("none", "silu_mul"):
+        raise ValueError("epilogue must be 'none' or 'silu_mul'")
+    if not 1 <= len(parts) <= AWQ_MAX_PARTS:
+        raise ValueError(f"1 to {AWQ_MAX_PARTS} parts")
+    pair = epilogue == "silu_mul"
+    if pair and len(parts) != 2:
+        raise ValueError("'silu_mul' takes exactly two parts (gate, up)")
+    if isinstance(workspace, str) and workspace != "auto":
+        raise ValueError("workspace must be a tensor, None or 'auto'")
+    _tensor(X, "X", (torch.float16, torch.bfloat16))
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [M][K]")
+    M, K = X.shape
+    Ns = [_check_packed(qw, sc, zr, K, group_size) for (qw, sc, zr) in parts]
+    zp = parts[0][2] is not None
+    if any((zr is not None) != zp for (_, _, zr) in parts):
+        raise ValueError("all parts must share the zero-point mode")
+    if pair and Ns[0] != Ns[1]:
+        raise ValueError("gate and up must have the same N")
+    ydt = (torch.float16, torch.bfloat16, torch.float32)
+    odt = X.dtype if out_dtype is None else out_dtype
+    if odt not in ydt:
+        raise TypeError(f"out_dtype {odt} is not float16, bfloat16 or float32")
+    if outs is not None:
+        outl = [outs] if pair else list(outs)
+        if len(outl) != (1 if pair else len(parts)):
+            raise ValueError("one output per part ('none') or one H ('silu_mul')")
+        for o, n in zip(outl, Ns[:len(outl)]):
+            _tensor(o, "out", ydt, (M, n))
+        if len({o.dtype for o in outl}) != 1:
+            raise TypeError("every output must have the same dtype")
+        odt = outl[0].dtype
+    named = [(X, "X")]
+    for i, (qw, sc, zr) in enumerate(parts):
+        named += [(qw, f"parts[{i}].qweight"), (sc, f"parts[{i}].scales")]
+        if zr is not None:
+            named.append((zr, f"parts[{i}].zeros"))
+    dev = _placed(*named)
+    if outs is None:
+        outl = [torch.empty((M, n), dtype=odt, device=dev) for n in (Ns[:1] if pair else Ns)]
+    _placed(*[(o, "out") for o in outl])
+    arr = (awq_linear_part * len(parts))()
+    for i, (qw, sc, zr) in enumerate(parts):
+        arr[i] = awq_linear_part(qw.data_ptr() if qw.numel() else None,
+                                 sc.data_ptr() if sc.numel() else None,
+                                 None if zr is None or not zr.numel() else zr.data_ptr(), Ns[i],
+                                 None if pair else (outl[i].data_ptr() if outl[i].numel() else None))
+    cfg = config(group_size, zero_point=zp)
+    epi = AWQ_EPILOGUE_SILU_MUL if pair else AWQ_EPILOGUE_NONE
+    xd = _dtype_code(X.dtype)
+    need = int(lib.awq_linear_fused_workspace_size(arr, len(parts), M, K, cfg, xd, epi,
+                                                   int(kernel)))
+    if workspace is not None and not isinstance(workspace, str):
+        _tensor(workspace, "workspace")
+    ws = _workspace_arg(workspace, need, dev)
+    H = outl[0] if pair else None
+    st = lib.awq_linear_fused(_ptr(X), xd, arr, len(parts), M, K, cfg, epi,
+                              ctypes.c_void_p(0) if H is None else _ptr(H), _dtype_code(odt),
+                              int(kernel), ctypes.c_void_p(0) if ws is None else _ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size(), _stream(dev))
+    check(st, "awq_linear_fused")
+    return H if pair else outl
 
 
 def awq_scale_search_workspace_size(M: int, N: int, K: int, group_size: int = 128,

@@ -195,6 +195,26 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
                     "awq_quantize_pack");
 }
 
+awq_status awq_dequantize(const uint32_t *qweight, const uint16_t *scales, const uint8_t *zeros,
+                          int64_t N, int64_t K, awq_config cfg, void *out, int32_t out_dtype,
+                          awq_stream_t stream) {
+  awq_status st = check_config(cfg, K);
+  if (st != AWQ_OK) return st;
+  if (N < 0) return fail(AWQ_ERR_INVALID_ARG, "N=%lld is negative", (long long)N);
+  if (N > ((int64_t)1 << 31)) return fail(AWQ_ERR_INVALID_ARG, "N too large");
+  if (out_dtype != AWQ_F16 && out_dtype != AWQ_F32)
+    return fail(AWQ_ERR_INVALID_ARG, "out_dtype=%d: must be AWQ_F16 or AWQ_F32", out_dtype);
+  if (N == 0) return ok();
+  if (!qweight || !scales || (cfg.zero_point && !zeros) || !out)
+    return fail(AWQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(out, 16) || !aligned(qweight, 4) || !aligned(scales, 2))
+    return fail(AWQ_ERR_INVALID_ARG, "out must be 16-byte aligned, qweight 4, scales 2");
+  return hip_status(awq::launch_dequantize(qweight, scales, cfg.zero_point ? zeros : nullptr, N, K,
+                                           cfg.group_size, out, out_dtype == AWQ_F32,
+                                           as_stream(stream)),
+                    "awq_dequantize");
+}
+
 namespace {
 
 // Whether the automatic choice (or the explicit `kernel`) runs the GEMV.
@@ -279,6 +299,130 @@ awq_status awq_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,
                       int64_t K, awq_config cfg, void *Y, int32_t y_dtype, awq_stream_t stream) {
   return linear_impl("awq_linear", X, x_dtype, qweight, scales, zeros, M, N, K, cfg, Y, y_dtype,
                      AWQ_KERNEL_AUTO, nullptr, 0, stream);
+}
+
+}  // extern "C"
+
+// ---- awq_linear_fused: projections that share one input ------------------------
+namespace {
+
+// Workspace layout of a fused call on the GEMM path.
+struct FusedLayout {
+  bool gemv;
+  size_t gemm_ws, gate_off, up_off, scratch_off, total;
+};
+
+awq_status check_fused(const void *X, int32_t x_dtype, const awq_linear_part *parts,
+                       int32_t n_parts, int64_t M, int64_t K, awq_config cfg, int32_t epilogue,
+                       const void *H, int32_t y_dtype, int32_t kernel, bool need_ptrs) {
+  if (n_parts < 1 || n_parts > AWQ_MAX_PARTS || !parts)
+    return fail(AWQ_ERR_INVALID_ARG, "n_parts=%d: must be in [1, %d]", n_parts, AWQ_MAX_PARTS);
+  if (epilogue != AWQ_EPILOGUE_NONE && epilogue != AWQ_EPILOGUE_SILU_MUL)
+    return fail(AWQ_ERR_INVALID_ARG, "epilogue=%d: unknown", epilogue);
+  if (epilogue == AWQ_EPILOGUE_SILU_MUL && (n_parts != 2 || parts[0].N != parts[1].N))
+    return fail(AWQ_ERR_INVALID_ARG, "the SiLU-mul epilogue takes 2 parts of equal N");
+  for (int i = 0; i < n_parts; ++i) {
+    // each part is checked as a linear call of its own (the output pointer
+    // is H for the SiLU-mul epilogue)
+    const void *y = epilogue == AWQ_EPILOGUE_SILU_MUL ? H : parts[i].Y;
+    awq_status st = check_linear(need_ptrs ? X : (const void *)16, x_dtype,
+                                 need_ptrs ? parts[i].qweight : (const uint32_t *)16,
+                                 need_ptrs ? parts[i].scales : (const uint16_t *)16,
+                                 need_ptrs ? parts[i].zeros : (const uint8_t *)16, M, parts[i].N, K,
+                                 cfg, need_ptrs ? y : (const void *)16, y_dtype, kernel);
+    if (st != AWQ_OK) return st;
+  }
+  return AWQ_OK;
+}
+
+FusedLayout fused_layout(const awq_linear_part *parts, int32_t n_parts, int64_t M, int64_t K,
+                         awq_config cfg, awq::XType xt, int32_t epilogue, int32_t kernel) {
+  FusedLayout L{};
+  const bool pair = epilogue == AWQ_EPILOGUE_SILU_MUL;
+  int64_t ntot = 0, nmax = 0, tiles = 0;
+  for (int i = 0; i < n_parts; ++i) {
+    ntot += parts[i].N;
+    nmax = parts[i].N > nmax ? parts[i].N : nmax;
+    if (!pair || i == 0) tiles += (parts[i].N + 15) / 16;   // the GEMV's workgroups
+  }
+  L.gemv = M > 0 && ntot > 0 && kernel != AWQ_KERNEL_GEMM &&
+           awq::gemv_supported(M, 16 * tiles, K, cfg.group_size, pair ? 2 : 1) &&
+           (kernel == AWQ_KERNEL_GEMV || auto_gemv(M, ntot, K, cfg.group_size));
+  if (L.gemv || M == 0 || ntot == 0) return L;
+  for (int i = 0; i < n_parts; ++i) {
+    if (parts[i].N == 0) continue;
+    const size_t b = awq::gemm_plan(M, parts[i].N, K, xt, awq::Scratch::Full).workspace_bytes;
+    L.gemm_ws = b > L.gemm_ws ? b : L.gemm_ws;
+  }
+  if (pair) {
+    L.gate_off = 0;
+    L.up_off = round_up(sizeof(float) * (size_t)M * nmax);
+    L.scratch_off = L.up_off + round_up(sizeof(float) * (size_t)M * nmax);
+  }
+  L.total = L.scratch_off + L.gemm_ws;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t awq_linear_fused_workspace_size(const awq_linear_part *parts, int32_t n_parts, int64_t M,
+                                       int64_t K, awq_config cfg, int32_t x_dtype,
+                                       int32_t epilogue, int32_t kernel) {
+  if (check_fused(nullptr, x_dtype, parts, n_parts, M, K, cfg, epilogue, nullptr, AWQ_F32, kernel,
+                  false) != AWQ_OK)
+    return 0;
+  const awq::XType xt = x_dtype == AWQ_F16 ? awq::XType::F16 : awq::XType::BF16;
+  return fused_layout(parts, n_parts, M, K, cfg, xt, epilogue, kernel).total;
+}
+
+awq_status awq_linear_fused(const void *X, int32_t x_dtype, const awq_linear_part *parts,
+                            int32_t n_parts, int64_t M, int64_t K, awq_config cfg,
+                            int32_t epilogue, void *H, int32_t y_dtype, int32_t kernel,
+                            void *workspace, size_t workspace_bytes, awq_stream_t stream) {
+  const char *who = "awq_linear_fused";
+  awq_status st =
+      check_fused(X, x_dtype, parts, n_parts, M, K, cfg, epilogue, H, y_dtype, kernel, true);
+  if (st != AWQ_OK) return st;
+  if (workspace && !aligned(workspace, kAlign))
+    return fail(AWQ_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", who);
+  const awq::XType xt = x_dtype == AWQ_F16 ? awq::XType::F16 : awq::XType::BF16;
+  const awq::YType yt = y_dtype == AWQ_F16    ? awq::YType::F16
+                        : y_dtype == AWQ_BF16 ? awq::YType::BF16
+                                              : awq::YType::F32;
+  const FusedLayout L = fused_layout(parts, n_parts, M, K, cfg, xt, epilogue, kernel);
+  if (kernel == AWQ_KERNEL_GEMV && M > 0 && !L.gemv)
+    return fail(AWQ_ERR_UNSUPPORTED, "%s: the GEMV kernel cannot serve these parts", who);
+  if (L.total > 0 && (!workspace || workspace_bytes < L.total))
+    return fail(AWQ_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed "
+                "(awq_linear_fused_workspace_size)", who, workspace ? workspace_bytes : 0, L.total);
+  if (M == 0) return ok();
+  const bool pair = epilogue == AWQ_EPILOGUE_SILU_MUL;
+  awq::LinearPart lp[AWQ_MAX_PARTS];
+  for (int i = 0; i < n_parts; ++i)
+    lp[i] = awq::LinearPart{parts[i].qweight, parts[i].scales,
+                            cfg.zero_point ? parts[i].zeros : nullptr, parts[i].N,
+                            pair ? H : parts[i].Y};
+  const hipStream_t hs = as_stream(stream);
+  if (L.gemv)
+    return hip_status(awq::launch_gemv_parts(X, xt, lp, n_parts, pair, M, K, cfg.group_size, yt, hs),
+                      who);
+  char *ws = reinterpret_cast<char *>(workspace);
+  void *scratch = L.gemm_ws ? ws + L.scratch_off : nullptr;
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < n_parts && e == hipSuccess; ++i) {
+    if (lp[i].N == 0) continue;
+    const awq::GemmPlan plan = awq::gemm_plan(M, lp[i].N, K, xt, awq::Scratch::Full);
+    void *y = pair ? (void *)(ws + (i == 0 ? L.gate_off : L.up_off)) : lp[i].Y;
+    e = awq::launch_gemm(X, xt, lp[i].qweight, lp[i].scales, lp[i].zeros, M, lp[i].N, K,
+                         cfg.group_size, y, pair ? awq::YType::F32 : yt, plan, scratch, hs);
+  }
+  if (e == hipSuccess && pair)
+    e = awq::launch_silu_mul(reinterpret_cast<const float *>(ws + L.gate_off),
+                             reinterpret_cast<const float *>(ws + L.up_off), M * parts[0].N, H,
+                             yt, hs);
+  return hip_status(e, who);
 }
 
 }  // extern "C"

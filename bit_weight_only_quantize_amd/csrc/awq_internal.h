@@ -19,9 +19,23 @@ hipError_t launch_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int gs,
                                 uint16_t *scales, uint8_t *zeros,
                                 int32_t *nonfinite, hipStream_t st);
 
+// W'[n][k] = (q - z) * s as fp32 (f32) or fp16 [N][K] (quantize_pack.hip).
+hipError_t launch_dequantize(const uint32_t *qweight, const uint16_t *scales, const uint8_t *zeros,
+                             int64_t N, int64_t K, int gs, void *out, bool f32, hipStream_t st);
+
+// One weight set of a fused launch: packed [N][K] weights and its output [M][N].
+struct LinearPart {
+  const uint32_t *qweight;
+  const uint16_t *scales;
+  const uint8_t *zeros;
+  int64_t N;
+  void *Y;
+};
+
 // ---- linear_gemv.hip (M <= 16) -------------------------------------------------
-// Whether the GEMV kernel can serve this shape (M <= 16, its LDS fits).
-bool gemv_supported(int64_t M, int64_t N, int64_t K, int gs);
+// Whether the GEMV kernel can serve this shape (M <= 16, its LDS fits) with
+// np weight sets per workgroup (1, or 2 for the gate/up pair).
+bool gemv_supported(int64_t M, int64_t N, int64_t K, int gs, int np = 1);
 // Whether the GEMV stages the M activation rows in LDS (its fast path).
 bool gemv_stages_activations(int64_t M, int64_t N, int64_t K);
 // Groups of K each GEMV wave walks in sequence.
@@ -30,6 +44,12 @@ hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M,
                        int64_t N, int64_t K, int gs, void *Y, YType yt,
                        hipStream_t st);
+// Up to 4 weight sets sharing X in one launch (each writes its own Y); with
+// silu_mul, exactly 2 of equal N and Y of part 0 receives silu(X W0^T) *
+// (X W1^T).  The zero-point mode of part 0 holds for all parts.
+hipError_t launch_gemv_parts(const void *X, XType xt, const LinearPart *parts, int count,
+                             bool silu_mul, int64_t M, int64_t K, int gs, YType yt,
+                             hipStream_t st);
 
 // ---- split K (gemm_f16.hip) ---------------------------------------------------------
 // Split-K bookkeeping of one launch: `splits` workgroups per output tile, each
@@ -78,6 +98,10 @@ hipError_t launch_gemm_f16(const uint16_t *X, bool bf16, const uint32_t *qweight
                            const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
                            int64_t K, int gs, void *Y, YType yt, const GemmPlan &plan,
                            void *workspace, hipStream_t st);
+
+// linear_gemm.hip: H = silu(A) * B elementwise over n fp32 values, rounded to yt.
+hipError_t launch_silu_mul(const float *A, const float *B, int64_t n, void *H, YType yt,
+                           hipStream_t st);
 
 // linear_gemm.hip: the search's reference GEMM, X * W^T with W fp16 [N][K],
 // fp32 output.

@@ -218,6 +218,43 @@ hipError_t launch_gemm(const void *X, XType xt, const uint32_t *qweight,
                          scales, zeros, M, N, K, gs, Y, yt, plan, workspace, st);
 }
 
+// ---- SiLU(gate) * up: the epilogue of the fused gate/up projections on the GEMM
+// path ("AWQ Advanced Usage Guide", "Layer Fusion": gate and up projections fused).
+// H[i] = silu(A[i]) * B[i] over fp32 A (gate) and B (up), rounded once to yt;
+// silu(x) = x / (1 + e^-x).  HBM-bound: 8 bytes in, 2 or 4 out per element.
+__global__ __launch_bounds__(256) void silu_mul_kernel(const float *__restrict__ A,
+                                                       const float *__restrict__ B, int64_t n,
+                                                       void *__restrict__ H, int yt) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  float v[4];
+  if (i4 + 4 <= n) {
+    const float4 a = *reinterpret_cast<const float4 *>(A + i4);
+    const float4 b = *reinterpret_cast<const float4 *>(B + i4);
+    const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = av[e] / (1.0f + __expf(-av[e])) * bv[e];
+  } else {
+    for (int e = 0; e < 4; ++e) v[e] = i4 + e < n ? A[i4 + e] / (1.0f + __expf(-A[i4 + e])) * B[i4 + e] : 0.0f;
+  }
+  for (int e = 0; e < 4 && i4 + e < n; ++e) {
+    if (yt == (int)YType::F32)
+      reinterpret_cast<float *>(H)[i4 + e] = v[e];
+    else if (yt == (int)YType::BF16)
+      reinterpret_cast<uint16_t *>(H)[i4 + e] = float_to_bf16_bits(v[e]);
+    else
+      reinterpret_cast<uint16_t *>(H)[i4 + e] = float_to_half_bits(v[e]);
+  }
+}
+
+hipError_t launch_silu_mul(const float *A, const float *B, int64_t n, void *H, YType yt,
+                           hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int64_t threads = (n + 3) / 4;
+  silu_mul_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(A, B, n, H, (int)yt);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_dense_f32(const uint16_t *X, const uint16_t *W, int64_t M, int64_t N,
                                  int64_t K, float *Y, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;

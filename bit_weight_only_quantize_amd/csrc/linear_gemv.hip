@@ -41,8 +41,9 @@ constexpr int kGemvMaxSZ = 4096;
 // memory instead.
 constexpr uint32_t kGemvStageBytes = 64u * 1024u;
 constexpr uint32_t kGemvStageBytesSolo = 128u * 1024u;
-// Waves per workgroup for N output columns (see gemv_dispatch).
-__host__ __device__ constexpr int gemv_waves(int64_t N) { return (N + 15) / 16 <= 256 ? 16 : 8; }
+// Waves per workgroup for a grid of column tiles (see gemv_dispatch).
+__host__ __device__ constexpr int gemv_waves_for_tiles(int64_t tiles) { return tiles <= 256 ? 16 : 8; }
+__host__ __device__ constexpr int gemv_waves(int64_t N) { return gemv_waves_for_tiles((N + 15) / 16); }
 __host__ __device__ constexpr uint32_t gemv_stage_budget(int nw) {
   return nw == 16 ? kGemvStageBytesSolo : kGemvStageBytes;
 }
@@ -50,37 +51,62 @@ __host__ __device__ constexpr uint32_t gemv_stage_budget(int nw) {
 // LDS layout (dynamic shared memory, byte offsets; every region starts on a
 // 1 KiB boundary):
 //   [0, xbytes)              activation rows 0..M-1 (when staged)
-//   [soff, ...)              scales of the 16 columns, fp16 bits, [16][G]
-//   [zoff, ...)              zero points of the 16 columns, u8, [16][G]
+//   [soff[i], ...)           scales of the 16 columns of weight set i, fp16 bits, [16][G]
+//   [zoff[i], ...)           zero points of those columns, u8, [16][G]
 // The cross-wave reduction reuses the start of the buffer after the loop.
 
 struct GemvSmem {
   uint32_t xrow;     // bytes per activation row (K * 2)
-  uint32_t soff, zoff, total;
+  uint32_t soff[2], zoff[2], total;
 };
 
 __host__ __device__ inline uint32_t kib_up(uint32_t b) { return (b + 1023u) & ~1023u; }
 
-__host__ __device__ inline GemvSmem gemv_smem(int M, int K, int G, bool stage_x) {
+// np weight sets per workgroup (2: the gate/up pair of awq_linear_fused).
+__host__ __device__ inline GemvSmem gemv_smem(int M, int K, int G, bool stage_x, int np) {
   GemvSmem L;
   L.xrow = (uint32_t)K * 2u;
-  L.soff = stage_x ? kib_up(L.xrow * (uint32_t)M) : 0u;
-  L.zoff = L.soff + kib_up(32u * (uint32_t)G);
-  L.total = L.zoff + kib_up(16u * (uint32_t)G);
+  uint32_t off = stage_x ? kib_up(L.xrow * (uint32_t)M) : 0u;
+  for (int i = 0; i < 2; ++i) {
+    L.soff[i] = off;
+    if (i < np) off += kib_up(32u * (uint32_t)G);
+    L.zoff[i] = off;
+    if (i < np) off += kib_up(16u * (uint32_t)G);
+  }
+  L.total = off;
   return L;
 }
 
+// The weight sets of one launch ("AWQ Advanced Usage Guide", "Layer Fusion":
+// projections that share an input, such as Q, K and V, run as one launch).
+// Workgroup b serves 16 columns of part p, where tile_end[p-1] <= b <
+// tile_end[p] (cumulative 16-column tiles).  In the paired mode (NP = 2) the
+// workgroups tile part 0 and each serves the same 16 columns of parts 0 and 1
+// (gate and up), and stores silu(gate) * up.
+constexpr int kGemvMaxParts = 4;
+struct GemvParts {
+  const uint32_t *qw[kGemvMaxParts];
+  const uint16_t *sc[kGemvMaxParts];
+  const uint8_t *zr[kGemvMaxParts];
+  void *y[kGemvMaxParts];
+  int n[kGemvMaxParts];
+  int tile_end[kGemvMaxParts];
+  int count;
+};
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
 // Memory instructions are the scarce resource here (each one occupies the
 // CU's address unit for tens of cycles), so per group a wave issues exactly
-// one: the 16-byte packed-weight load of each lane.  Activations (staged by
-// the workgroup once when M*K*2 fits the LDS budget), scales and zero points
-// come from LDS.  All global reads use buffer resources, so rows
-// >= M, columns >= N and groups >= G read zero without branches.
-template <class XT, int GS, int NW, int U, bool STAGE_X>
-__global__ __launch_bounds__(64 * NW) void gemv_kernel(
-    const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
-    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
-    void *__restrict__ Y, int ytype, uint32_t zfix) {
+// one per weight set: the 16-byte packed-weight load of each lane.
+// Activations (staged by the workgroup once when M*K*2 fits the LDS budget),
+// scales and zero points come from LDS.  All global reads use buffer
+// resources, so rows >= M, columns >= N and groups >= G read zero without
+// branches.
+template <class XT, int GS, int NW, int U, bool STAGE_X, int NP>
+__global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restrict__ X,
+                                                       GemvParts parts, int M, int K, int ytype,
+                                                       uint32_t zfix) {
   constexpr int kWpl = GS / 32;            // packed words per lane per group
   constexpr bool kBF16 = __is_same(XT, TagBF16);
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -89,21 +115,32 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15;
   const int kq = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  // this workgroup's part and column tile (uniform)
+  int part = 0;
+  if constexpr (NP == 1) {
+    while (part + 1 < parts.count && (int)blockIdx.x >= parts.tile_end[part]) ++part;
+  }
+  const int tile = (int)blockIdx.x - (part ? parts.tile_end[part - 1] : 0);
+  const int N = parts.n[part];
+  const int n0 = tile * 16;
   const int n = n0 + c;
   const int G = K / GS;
-  const GemvSmem L = gemv_smem(M, K, G, STAGE_X);
+  const GemvSmem L = gemv_smem(M, K, G, STAGE_X, NP);
 
-  const rsrc_t rQ = make_rsrc(qweight, (uint32_t)N * (uint32_t)K / 2u);
-  const rsrc_t rS = make_rsrc(scales, (uint32_t)N * (uint32_t)G * 2u);
-  // no zeros (the symmetric grid): every load reads 0 and zfix = 8 is added
-  const rsrc_t rZ = make_rsrc(zeros, zeros ? (uint32_t)N * (uint32_t)G : 0u);
+  rsrc_t rQ[NP], rS[NP], rZ[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    rQ[i] = make_rsrc(parts.qw[part + i], (uint32_t)N * (uint32_t)K / 2u);
+    rS[i] = make_rsrc(parts.sc[part + i], (uint32_t)N * (uint32_t)G * 2u);
+    // no zeros (the symmetric grid): every load reads 0 and zfix = 8 is added
+    rZ[i] = make_rsrc(parts.zr[part + i], parts.zr[part + i] ? (uint32_t)N * (uint32_t)G : 0u);
+  }
   const rsrc_t rX = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
 
   const uint32_t q_lane = (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(kq * kWpl * 4);
   const uint32_t x_lane = (uint32_t)c * (uint32_t)K * 2u + (uint32_t)(kq * kWpl * 16);
   struct Batch {
-    uint32_t raw[U][kWpl];
+    uint32_t raw[NP][U][kWpl];
     u32x4 a[U][kWpl];      // used only when activations are not staged
   };
   // Packed weights (and, without staging, activations) of groups
@@ -116,14 +153,17 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
       const int g = g0 + u * NW;
       if (g >= G) continue;
       const uint32_t qo = q_lane + (uint32_t)g * (GS / 2);
-      if constexpr (kWpl == 4) {
-        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo, 0, 0));
 #pragma unroll
-        for (int j = 0; j < kWpl; ++j) b.raw[u][j] = v[j];
-      } else {
-        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rQ, qo, 0, 0));
+      for (int i = 0; i < NP; ++i) {
+        if constexpr (kWpl == 4) {
+          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ[i], qo, 0, 0));
 #pragma unroll
-        for (int j = 0; j < kWpl; ++j) b.raw[u][j] = v[j];
+          for (int j = 0; j < kWpl; ++j) b.raw[i][u][j] = v[j];
+        } else {
+          const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rQ[i], qo, 0, 0));
+#pragma unroll
+          for (int j = 0; j < kWpl; ++j) b.raw[i][u][j] = v[j];
+        }
       }
       if constexpr (!STAGE_X) {
         const uint32_t xo = x_lane + (uint32_t)g * (GS * 2);
@@ -151,7 +191,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
   const int nsz = (16 * G + 64 * NW - 1) / (64 * NW);   // uniform: rounds needed
   const uint32_t xbytes = STAGE_X ? (uint32_t)M * L.xrow : 0u;
   const int nxr = (int)((xbytes + 64u * NW * 16u - 1u) / (64u * NW * 16u));
-  uint32_t sreg[kSZ], zreg[kSZ];
+  uint32_t sreg[NP][kSZ], zreg[NP][kSZ];
   u32x4 xreg[kXR];
   {
     const uint32_t base = (uint32_t)n0 * (uint32_t)G;
@@ -160,8 +200,11 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
       if (r >= nsz) break;
       const uint32_t i = (uint32_t)(tid + r * 64 * NW);
       const uint32_t o = i < 16u * (uint32_t)G ? base + i : 0x7FFFFFF0u;
-      sreg[r] = __builtin_amdgcn_raw_buffer_load_b16(rS, o * 2u, 0, 0);
-      zreg[r] = __builtin_amdgcn_raw_buffer_load_b8(rZ, o, 0, 0);
+#pragma unroll
+      for (int s = 0; s < NP; ++s) {
+        sreg[s][r] = __builtin_amdgcn_raw_buffer_load_b16(rS[s], o * 2u, 0, 0);
+        zreg[s][r] = __builtin_amdgcn_raw_buffer_load_b8(rZ[s], o, 0, 0);
+      }
     }
     if constexpr (STAGE_X) {
 #pragma unroll
@@ -180,15 +223,16 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
   load_batch(wave, cur);
   __builtin_amdgcn_sched_barrier(0);
   {
-    uint16_t *ss = reinterpret_cast<uint16_t *>(smem + L.soff);
-    uint8_t *zs = reinterpret_cast<uint8_t *>(smem + L.zoff);
 #pragma unroll
     for (int r = 0; r < kSZ; ++r) {
       if (r >= nsz) break;
       const int i = tid + r * 64 * NW;
       if (i < 16 * G) {
-        ss[i] = (uint16_t)sreg[r];
-        zs[i] = (uint8_t)zreg[r];
+#pragma unroll
+        for (int s = 0; s < NP; ++s) {
+          reinterpret_cast<uint16_t *>(smem + L.soff[s])[i] = (uint16_t)sreg[s][r];
+          reinterpret_cast<uint8_t *>(smem + L.zoff[s])[i] = (uint8_t)zreg[s][r];
+        }
       }
     }
     if constexpr (STAGE_X) {
@@ -207,10 +251,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
   // alone, and result rows >= M are never stored, so the padding rows may
   // hold any values.
   const char *xlds = smem + (c < M ? (uint32_t)c * L.xrow : 0u) + (uint32_t)(kq * kWpl * 16);
-  const uint16_t *ss = reinterpret_cast<const uint16_t *>(smem + L.soff) + c * G;
-  const uint8_t *zs = reinterpret_cast<const uint8_t *>(smem + L.zoff) + c * G;
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NP];
+#pragma unroll
+  for (int s = 0; s < NP; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const DeqRegs dq;
 
   // Software pipeline: the next batch's loads are in flight while this batch
@@ -230,90 +274,97 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
         else  // a group past the end loaded nothing: its stale registers may hold any bits
           a[j] = g < G ? cur.a[u][j] : u32x4{0u, 0u, 0u, 0u};
       }
-      const uint32_t zr = zs[gs] + zfix;
-      const uint16_t sb = ss[gs];
-      const float sc = g < G ? half_bits_to_float(sb) : 0.0f;
-      // The exact integers q - z times a, summed in fp32 over the group
-      // (every product is exact), then scaled once.
-      const DeqF16 deq(zr);
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < kWpl; ++j) {
-        const u32x4 h = deq(cur.raw[u][j], dq);
-        t = mfma32<XT>(a[j], kBF16 ? f16_pairs_to_bf16(h) : h, t);
+      for (int s = 0; s < NP; ++s) {
+        const uint32_t zr = reinterpret_cast<const uint8_t *>(smem + L.zoff[s])[c * G + gs] + zfix;
+        const uint16_t sb = reinterpret_cast<const uint16_t *>(smem + L.soff[s])[c * G + gs];
+        const float sc = g < G ? half_bits_to_float(sb) : 0.0f;
+        // The exact integers q - z times a, summed in fp32 over the group
+        // (every product is exact), then scaled once.
+        const DeqF16 deq(zr);
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kWpl; ++j) {
+          const u32x4 h = deq(cur.raw[s][u][j], dq);
+          t = mfma32<XT>(a[j], kBF16 ? f16_pairs_to_bf16(h) : h, t);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[s][e] = __builtin_fmaf(t[e], sc, acc[s][e]);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(t[e], sc, acc[e]);
     }
     cur = nxt;
   }
 
   __syncthreads();
   f32x4 *red = reinterpret_cast<f32x4 *>(smem);
-  red[wave * 64 + lane] = acc;
+#pragma unroll
+  for (int s = 0; s < NP; ++s) red[(s * NW + wave) * 64 + lane] = acc[s];
   __syncthreads();
   if (wave != 0) return;
-  f32x4 sum = red[lane];
+  f32x4 sum[NP];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    const f32x4 o = red[w * 64 + lane];
+  for (int s = 0; s < NP; ++s) {
+    sum[s] = red[s * NW * 64 + lane];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sum[e] += o[e];
+    for (int w = 1; w < NW; ++w) {
+      const f32x4 o = red[(s * NW + w) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[s][e] += o[e];
+    }
   }
   if (n >= N) return;
+  void *Y = parts.y[part];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int m = 4 * kq + e;
     if (m >= M) continue;
     const int64_t o = (int64_t)m * N + n;
+    const float v = NP == 2 ? silu(sum[0][e]) * sum[1][e] : sum[0][e];
     if (ytype == (int)YType::F16)
-      reinterpret_cast<uint16_t *>(Y)[o] = float_to_half_bits(sum[e]);
+      reinterpret_cast<uint16_t *>(Y)[o] = float_to_half_bits(v);
     else if (ytype == (int)YType::BF16)
-      reinterpret_cast<uint16_t *>(Y)[o] = float_to_bf16_bits(sum[e]);
+      reinterpret_cast<uint16_t *>(Y)[o] = float_to_bf16_bits(v);
     else
-      reinterpret_cast<float *>(Y)[o] = sum[e];
+      reinterpret_cast<float *>(Y)[o] = v;
   }
 }
 
 
-template <class XT, int GS, int NW>
-static void gemv_launch(const uint16_t *X, const uint32_t *qw, const uint16_t *sc,
-                        const uint8_t *zr, int M, int64_t N, int64_t K, void *Y, YType yt,
-                        hipStream_t st) {
-  const dim3 grid((unsigned)((N + 15) / 16));
+template <class XT, int GS, int NW, int NP>
+static void gemv_launch(const uint16_t *X, const GemvParts &parts, int tiles, int M, int64_t K,
+                        YType yt, uint32_t zfix, hipStream_t st) {
+  const dim3 grid((unsigned)tiles);
   const int G = (int)(K / GS);
   const bool stage = (uint64_t)M * (uint64_t)K * 2u <= gemv_stage_budget(NW);
-  const uint32_t zfix = zr ? 0u : 8u;
-  const GemvSmem L = gemv_smem(M, (int)K, G, stage);
-  // the reduction reuses the buffer: at least NW * 64 * 16 bytes
-  const uint32_t bytes = L.total > 64u * NW * 16u ? L.total : 64u * NW * 16u;
+  const GemvSmem L = gemv_smem(M, (int)K, G, stage, NP);
+  // the reduction reuses the buffer: at least NP * NW * 64 * 16 bytes
+  const uint32_t need = (uint32_t)NP * 64u * NW * 16u;
+  const uint32_t bytes = L.total > need ? L.total : need;
   // Two batches in flight once a wave walks more than 8 groups (measured 7%
   // faster at 13.5 groups per wave, slower at 5 and below).
   if (stage && G > 8 * NW)
-    gemv_kernel<XT, GS, NW, 2, true><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
-                                                                   (int)K, Y, (int)yt, zfix);
+    gemv_kernel<XT, GS, NW, 2, true, NP><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
   else if (stage)
-    gemv_kernel<XT, GS, NW, 1, true><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
-                                                                   (int)K, Y, (int)yt, zfix);
+    gemv_kernel<XT, GS, NW, 1, true, NP><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
   else
-    gemv_kernel<XT, GS, NW, 2, false><<<grid, 64 * NW, bytes, st>>>(X, qw, sc, zr, M, (int)N,
-                                                                    (int)K, Y, (int)yt, zfix);
+    gemv_kernel<XT, GS, NW, 2, false, NP><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
 }
 
 // Waves per workgroup.  Every workgroup of a launch should be resident at
 // once (a second partial round of workgroups costs a whole extra memory
-// latency): with at most one workgroup per CU (N <= 16 * 256) the workgroup
-// takes 16 waves, otherwise 8.  One group per wave is in flight ahead of the
-// one being computed: deeper windows were measured slower on MI355X (every
-// wave's staging loads then queue behind more weight traffic).
-template <class XT, int GS>
-static void gemv_dispatch(const uint16_t *X, const uint32_t *qw, const uint16_t *sc,
-                          const uint8_t *zr, int M, int64_t N, int64_t K, void *Y, YType yt,
-                          hipStream_t st) {
-  if (gemv_waves(N) == 16)
-    gemv_launch<XT, GS, 16>(X, qw, sc, zr, M, N, K, Y, yt, st);
+// latency): with at most one workgroup per CU (at most 256 column tiles) the
+// workgroup takes 16 waves, otherwise 8.  One group per wave is in flight ahead
+// of the one being computed: deeper windows were measured slower on MI355X
+// (every wave's staging loads then queue behind more weight traffic).
+template <class XT, int GS, int NP>
+static void gemv_dispatch(const uint16_t *X, const GemvParts &parts, int tiles, int M, int64_t K,
+                          YType yt, uint32_t zfix, hipStream_t st) {
+  // the gate/up pair always takes 8 waves: with 16, its two sets of staging
+  // registers spill under the 1024-thread register budget
+  if (NP == 1 && gemv_waves_for_tiles(tiles) == 16)
+    gemv_launch<XT, GS, 16, NP>(X, parts, tiles, M, K, yt, zfix, st);
   else
-    gemv_launch<XT, GS, 8>(X, qw, sc, zr, M, N, K, Y, yt, st);
+    gemv_launch<XT, GS, 8, NP>(X, parts, tiles, M, K, yt, zfix, st);
 }
 
 int64_t gemv_groups_per_wave(int64_t N, int64_t K, int gs) {
@@ -324,27 +375,58 @@ bool gemv_stages_activations(int64_t M, int64_t N, int64_t K) {
   return (uint64_t)M * (uint64_t)K * 2u <= gemv_stage_budget(gemv_waves(N));
 }
 
-bool gemv_supported(int64_t M, int64_t N, int64_t K, int gs) {
+bool gemv_supported(int64_t M, int64_t N, int64_t K, int gs, int np) {
   const int64_t G = K / gs;
-  const bool stage = gemv_stages_activations(M, N, K);
-  const GemvSmem L = gemv_smem((int)M, (int)K, (int)G, stage);
-  const uint32_t lds = gemv_waves(N) == 16 ? 160u * 1024u : 80u * 1024u;
-  return M <= 16 && 16 * G <= kGemvMaxSZ && L.total <= lds;
+  const int nw = np == 2 ? 8 : gemv_waves(N);
+  const bool stage = (uint64_t)M * (uint64_t)K * 2u <= gemv_stage_budget(nw);
+  const GemvSmem L = gemv_smem((int)M, (int)K, (int)G, stage, np);
+  const uint32_t lds = nw == 16 ? 160u * 1024u : 80u * 1024u;
+  return M <= 16 && 16 * G <= kGemvMaxSZ && L.total <= lds && N * K / 2 < 0x7FFFFFF0;
 }
+
+namespace {
+template <int NP>
+hipError_t gemv_go(const void *X, XType xt, const GemvParts &parts, int tiles, int64_t M,
+                   int64_t K, int gs, YType yt, uint32_t zfix, hipStream_t st) {
+  const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
+  if (xt == XType::F16) {
+    if (gs == 128) gemv_dispatch<TagF16, 128, NP>(x, parts, tiles, (int)M, K, yt, zfix, st);
+    else gemv_dispatch<TagF16, 64, NP>(x, parts, tiles, (int)M, K, yt, zfix, st);
+  } else {
+    if (gs == 128) gemv_dispatch<TagBF16, 128, NP>(x, parts, tiles, (int)M, K, yt, zfix, st);
+    else gemv_dispatch<TagBF16, 64, NP>(x, parts, tiles, (int)M, K, yt, zfix, st);
+  }
+  return hipGetLastError();
+}
+}  // namespace
 
 hipError_t launch_gemv(const void *X, XType xt, const uint32_t *qweight,
                        const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
                        int64_t K, int gs, void *Y, YType yt, hipStream_t st) {
-  if (M == 0 || N == 0) return hipSuccess;
-  const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
-  if (xt == XType::F16) {
-    if (gs == 128) gemv_dispatch<TagF16, 128>(x, qweight, scales, zeros, (int)M, N, K, Y, yt, st);
-    else gemv_dispatch<TagF16, 64>(x, qweight, scales, zeros, (int)M, N, K, Y, yt, st);
-  } else {
-    if (gs == 128) gemv_dispatch<TagBF16, 128>(x, qweight, scales, zeros, (int)M, N, K, Y, yt, st);
-    else gemv_dispatch<TagBF16, 64>(x, qweight, scales, zeros, (int)M, N, K, Y, yt, st);
+  const LinearPart one{qweight, scales, zeros, N, Y};
+  return launch_gemv_parts(X, xt, &one, 1, false, M, K, gs, yt, st);
+}
+
+hipError_t launch_gemv_parts(const void *X, XType xt, const LinearPart *p, int count,
+                             bool silu_mul, int64_t M, int64_t K, int gs, YType yt,
+                             hipStream_t st) {
+  if (M == 0 || count <= 0) return hipSuccess;
+  GemvParts parts{};
+  int tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    parts.qw[i] = p[i].qweight;
+    parts.sc[i] = p[i].scales;
+    parts.zr[i] = p[i].zeros;
+    parts.y[i] = p[i].Y;
+    parts.n[i] = (int)p[i].N;
+    if (!silu_mul || i == 0) tiles += (int)((p[i].N + 15) / 16);
+    parts.tile_end[i] = tiles;
   }
-  return hipGetLastError();
+  parts.count = count;
+  if (tiles == 0) return hipSuccess;
+  const uint32_t zfix = p[0].zeros ? 0u : 8u;
+  if (silu_mul) return gemv_go<2>(X, xt, parts, tiles, M, K, gs, yt, zfix, st);
+  return gemv_go<1>(X, xt, parts, tiles, M, K, gs, yt, zfix, st);
 }
 
 }  // namespace awq

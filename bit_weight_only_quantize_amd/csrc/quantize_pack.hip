@@ -216,3 +216,58 @@ hipError_t launch_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int gs,
 }
 
 }  // namespace awq
+
+namespace awq {
+
+// ---- dequantize: packed codes back to weights --------------------------------------
+// The pseudo-quantization step of the pages' pipeline (ai.lansai.wang explainer,
+// four-stage table, "伪量化评测" row: simulate the low-bit weights without the
+// target kernel): W'[n][k] = (q - z) * s, the value the linear kernels multiply
+// by, written as fp32 (exact) or fp16 (rounded once).  One lane per packed word
+// (8 weights): 4 bytes of codes in, 16 or 32 bytes out; a 2-D grid as above.
+template <int GS, bool F32OUT>
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restrict__ qweight,
+                                                         const uint16_t *__restrict__ scales,
+                                                         const uint8_t *__restrict__ zeros,
+                                                         int64_t N, int64_t K, void *__restrict__ out) {
+  const int wpr = (int)(K / 8);
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= wpr) return;
+  for (int64_t n = blockIdx.y; n < N; n += gridDim.y) {
+    const uint32_t w = qweight[n * wpr + c];
+    const int64_t gi = n * (K / GS) + (c * 8) / GS;
+    const float s = half_bits_to_float(scales[gi]);
+    const float z = zeros ? (float)zeros[gi] : 8.0f;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ((float)((w >> (4 * nibble_of_channel(i))) & 0xFu) - z) * s;
+    if constexpr (F32OUT) {
+      float4 *o = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + n * K + (int64_t)c * 8);
+      o[0] = float4{v[0], v[1], v[2], v[3]};
+      o[1] = float4{v[4], v[5], v[6], v[7]};
+    } else {
+      u32x4 h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        h[i] = (uint32_t)float_to_half_bits(v[2 * i]) | ((uint32_t)float_to_half_bits(v[2 * i + 1]) << 16);
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(out) + n * K + (int64_t)c * 8) = h;
+    }
+  }
+}
+
+hipError_t launch_dequantize(const uint32_t *qweight, const uint16_t *scales, const uint8_t *zeros,
+                             int64_t N, int64_t K, int gs, void *out, bool f32, hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  const int64_t wpr = K / 8;
+  const dim3 grid((unsigned)((wpr + 255) / 256), (unsigned)(N < 65535 ? N : 65535));
+  if (gs == 128) {
+    if (f32) dequantize_kernel<128, true><<<grid, 256, 0, st>>>(qweight, scales, zeros, N, K, out);
+    else dequantize_kernel<128, false><<<grid, 256, 0, st>>>(qweight, scales, zeros, N, K, out);
+  } else {
+    if (f32) dequantize_kernel<64, true><<<grid, 256, 0, st>>>(qweight, scales, zeros, N, K, out);
+    else dequantize_kernel<64, false><<<grid, 256, 0, st>>>(qweight, scales, zeros, N, K, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace awq

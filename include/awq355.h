@@ -109,6 +109,25 @@ awq_status awq_quantize_pack(const void *W, int64_t N, int64_t K, awq_config cfg
                              awq_stream_t stream);
 
 /*
+ * awq_dequantize - the packed weights back as floating-point weights: the
+ * pseudo-quantized layer.
+ * Cites: ai.lansai.wang explainer, four-stage table, "伪量化评测" row
+ * (pseudo-quantized evaluation: simulate the low-bit weights without
+ * depending on the target kernel).
+ *
+ *   qweight, scales, zeros: as produced by awq_quantize_pack for [N][K]
+ *            (zeros ignored when cfg.zero_point = 0).
+ *   out      device, [N][K] of out_dtype, 16-byte aligned: AWQ_F32 gives
+ *            (code - zero) * scale exactly; AWQ_F16 rounds it once (nearest
+ *            even).
+ * awq_quantize_pack followed by awq_dequantize is the pseudo-quantization
+ * of W (with s: of s * W).  Requirements: N >= 0, K > 0, K % g == 0.
+ */
+awq_status awq_dequantize(const uint32_t *qweight, const uint16_t *scales, const uint8_t *zeros,
+                          int64_t N, int64_t K, awq_config cfg, void *out, int32_t out_dtype,
+                          awq_stream_t stream);
+
+/*
  * awq_linear - Y = X * deq(W)^T, the W4A16 linear layer.
  * Cites: "AWQ Advanced Usage Guide", "WQLinear Kernel Variants" (GEMM for
  * batch > 1, GEMV for single-token decode); ai.lansai.wang explainer, table
@@ -194,6 +213,62 @@ awq_status awq_linear_ws(const void *X, int32_t x_dtype, const uint32_t *qweight
                          const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
                          int64_t K, awq_config cfg, void *Y, int32_t y_dtype, void *workspace,
                          size_t workspace_bytes, awq_stream_t stream);
+
+/* One projection of awq_linear_fused: packed weights for [N][K] (as from
+ * awq_quantize_pack) and its output Y [M][N]. */
+typedef struct awq_linear_part {
+    const uint32_t *qweight;
+    const uint16_t *scales;
+    const uint8_t *zeros;
+    int64_t N;
+    void *Y;
+} awq_linear_part;
+
+#define AWQ_MAX_PARTS 4
+
+/* Epilogues of awq_linear_fused (int32_t in signatures). */
+enum { AWQ_EPILOGUE_NONE = 0, AWQ_EPILOGUE_SILU_MUL = 1 };
+
+/*
+ * awq_linear_fused_workspace_size - bytes of device workspace awq_linear_fused
+ * needs for these parts (their qweight/scales/zeros/Y may be NULL here), M,
+ * K, activation type, epilogue and kernel choice; 0 when none is needed
+ * (the GEMV path) and on invalid arguments.
+ */
+size_t awq_linear_fused_workspace_size(const awq_linear_part *parts, int32_t n_parts, int64_t M,
+                                       int64_t K, awq_config cfg, int32_t x_dtype,
+                                       int32_t epilogue, int32_t kernel);
+
+/*
+ * awq_linear_fused - several W4A16 projections of one input X.
+ * Cites: "AWQ Advanced Usage Guide", "Layer Fusion", "What Gets Fused"
+ * (attention: Q, K and V projections combined; MLP: gate and up projections
+ * fused).
+ *
+ *   X        device, [M][K] of x_dtype, 16-byte aligned; shared by all parts.
+ *   parts    host array of n_parts (1..AWQ_MAX_PARTS) projections of the
+ *            same K, group size and zero-point mode.
+ *   epilogue AWQ_EPILOGUE_NONE: parts[i].Y = X * deq(W_i)^T for every part.
+ *            AWQ_EPILOGUE_SILU_MUL: two parts of equal N (gate, up) and
+ *            H = silu(X * deq(W_0)^T) * (X * deq(W_1)^T), silu(x) = x / (1 +
+ *            e^-x), computed in fp32 and rounded once; parts[i].Y are ignored.
+ *   H        device [M][N] of y_dtype (SILU_MUL only; else ignored).
+ *   kernel   AWQ_KERNEL_AUTO, _GEMV or _GEMM, as in awq_linear_ex; the
+ *            choice uses the parts' total N.
+ *   workspace  device, 256-byte aligned, at least
+ *            awq_linear_fused_workspace_size() bytes (NULL when that is 0).
+ * The GEMV path serves every part in one launch: each workgroup serves 16
+ * columns of one part (with SILU_MUL, the same 16 columns of gate and up,
+ * combined in its epilogue), so X is staged once per workgroup and no
+ * intermediate reaches memory.  The GEMM path (large M, where each
+ * projection fills the GPU by itself) runs the layer kernel once per part; with
+ * SILU_MUL gate and up go to fp32 in the workspace and an elementwise kernel
+ * writes H.  Arithmetic, requirements and errors per part as awq_linear_ex.
+ */
+awq_status awq_linear_fused(const void *X, int32_t x_dtype, const awq_linear_part *parts,
+                            int32_t n_parts, int64_t M, int64_t K, awq_config cfg,
+                            int32_t epilogue, void *H, int32_t y_dtype, int32_t kernel,
+                            void *workspace, size_t workspace_bytes, awq_stream_t stream);
 
 /* Bytes of device scratch behind awq_linear_noalloc, per GPU: the largest
  * split-K partials of a plan (256 tiles of 128 x 256 fp32, 32 MiB) plus 1 MiB

@@ -38,7 +38,7 @@ from .quant import (  # noqa: F401
     dequantize,
     quantize_pack,
 )
-from .linear import linear64, linear_naive  # noqa: F401
+from .linear import gate_up_silu64, linear64, linear_naive, silu64  # noqa: F401
 from .search import (  # noqa: F401
     DEFAULT_ALPHAS,
     activation_mean_abs,

@@ -69,3 +69,21 @@ def linear_naive(X, q, scales, zeros, group_size: int = 128):
                 acc += float(X[m][k]) * w
             Y[m][n] = acc
     return np.array(Y, dtype=np.float64)
+
+
+def silu64(x):
+    """silu(x) = x * sigmoid(x) = x / (1 + e^-x), in fp64.
+
+    The fused gate/up projections ("AWQ Advanced Usage Guide", "Layer
+    Fusion": "Gate and Up projections fused") feed the MLP's gated activation,
+    silu(gate) * up; the page names the fusion, not the activation, and the
+    plainest reading is the SiLU-gated MLP of the Llama-class models the pages
+    quantize."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def gate_up_silu64(X, gate, up, group_size: int = 128):
+    """silu(X * deq(Wg)^T) * (X * deq(Wu)^T) in fp64; gate and up are
+    (qweight, scales, zeros) of the same [N][K]."""
+    return silu64(linear64(X, *gate, group_size)) * linear64(X, *up, group_size)

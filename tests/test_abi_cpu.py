@@ -73,6 +73,46 @@ def test_quantize_pack_validation():
     assert lib.awq_last_error().decode() == ""
 
 
+def test_dequantize_validation():
+    dq = lambda **k: lib.awq_dequantize(k.get("qw", FAKE), FAKE, k.get("zr", FAKE), k.get("N", 4),
+                                        k.get("K", 256), k.get("c", cfg(128)), k.get("out", FAKE),
+                                        k.get("dt", 2), NULL)
+    assert dq(dt=1) == binding.AWQ_ERR_INVALID_ARG           # bf16 output is not offered
+    assert dq(K=200) == binding.AWQ_ERR_INVALID_ARG
+    assert dq(N=-1) == binding.AWQ_ERR_INVALID_ARG
+    assert dq(zr=NULL) == binding.AWQ_ERR_INVALID_ARG        # asymmetric needs zeros
+    assert dq(out=ctypes.c_void_p(0x10008)) == binding.AWQ_ERR_INVALID_ARG
+    assert dq(N=0) == binding.AWQ_OK
+    assert dq(N=0, zr=NULL, c=cfg(128, zero_point=False)) == binding.AWQ_OK
+
+
+def test_fused_validation():
+    P = binding.awq_linear_part
+    arr = (P * 5)()
+    for i in range(5):
+        arr[i] = P(0x10000, 0x10000, 0x10000, 64, 0x10000)
+
+    def call(n=2, epi=0, H=NULL, kernel=0, M=3, K=256, ws=NULL, wsb=0, xt=0):
+        return lib.awq_linear_fused(FAKE, xt, arr, n, M, K, cfg(128), epi, H, 0, kernel, ws, wsb,
+                                    NULL)
+    assert call(n=0) == binding.AWQ_ERR_INVALID_ARG
+    assert call(n=5) == binding.AWQ_ERR_INVALID_ARG
+    assert call(epi=2) == binding.AWQ_ERR_INVALID_ARG
+    assert call(n=3, epi=1, H=FAKE) == binding.AWQ_ERR_INVALID_ARG     # the pair is 2 parts
+    arr[1].N = 65
+    assert call(epi=1, H=FAKE) == binding.AWQ_ERR_INVALID_ARG          # of equal N
+    arr[1].N = 64
+    assert call(epi=1) == binding.AWQ_ERR_INVALID_ARG                  # H is required
+    assert call(K=200) == binding.AWQ_ERR_INVALID_ARG
+    assert call(kernel=1, M=17) == binding.AWQ_ERR_INVALID_ARG        # GEMV serves M <= 16
+    # the GEMM path of a pair needs fp32 gate/up in the workspace
+    need = lib.awq_linear_fused_workspace_size(arr, 2, 64, 256, cfg(128), 0, 1, 2)
+    assert need >= 2 * 64 * 64 * 4
+    assert call(epi=1, H=FAKE, kernel=2, M=64, ws=FAKE, wsb=need - 1) == binding.AWQ_ERR_WORKSPACE
+    assert lib.awq_linear_fused_workspace_size(arr, 2, 1, 256, cfg(128), 0, 1, 0) == 0  # GEMV
+    assert call(M=0) == binding.AWQ_OK
+
+
 def _lin(X=FAKE, xt=0, M=3, N=64, K=256, c=None, Y=FAKE, yt=0, kernel=0, ws=NULL, ws_bytes=0):
     return lib.awq_linear_ex(X, xt, FAKE, FAKE, FAKE, M, N, K, c or cfg(128), Y, yt, kernel, ws,
                              ws_bytes, NULL)

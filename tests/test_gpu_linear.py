@@ -5,8 +5,8 @@ import pytest
 
 import workloads as wl
 from gpu_common import (REL_FRO, assert_close, dev, out_to_f64, say, to_dev, to_np, torch_mod)
-from oracle import (QuantConfig, bf16_bits_to_f32, dequantize, linear64, quantize_pack,
-                    unpack_codes)
+from oracle import (QuantConfig, bf16_bits_to_f32, dequantize, gate_up_silu64, linear64,
+                    quantize_pack, unpack_codes)
 
 pytestmark = pytest.mark.gpu
 
@@ -540,3 +540,86 @@ def test_symmetric_ragged(M, N, K, g, dt):
     b = awq.awq_linear_noalloc(Xd, *pd, group_size=g, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# --- fused projections (awq_linear_fused) -----------------------------------------------
+
+@pytest.mark.parametrize("M,kernel", [(1, 0), (4, 0), (16, 1), (40, 0), (300, 0), (3, GEMM)])
+@pytest.mark.parametrize("zp", [True, False])
+def test_fused_qkv_parts(M, kernel, zp):
+    """Q, K and V projections of one input (N = 4096, 1024 and 1000, the last
+    ragged) in one call: each output against the fp64 oracle.  M <= 16 runs
+    all three in one GEMV launch, larger M one GEMM per part."""
+    torch = torch_mod()
+    awq = _awq()
+    K, g = 4096, 128
+    Ns = (4096, 1024, 1000)
+    X = wl.gen_activation(M, K, 190 + M, 191)
+    packs = [_packed(wl.gen_weight(n, K, 192 + i), g, zero_point=zp) for i, n in enumerate(Ns)]
+    say("fused qkv", M, kernel, zp)
+    Ys = awq.awq_linear_fused(to_dev(X), [p[3] for p in packs], group_size=g,
+                              out_dtype=torch.float32, kernel=kernel)
+    torch.cuda.synchronize()
+    for Y, (qw, sc, zr, _) in zip(Ys, packs):
+        assert_close(out_to_f64(Y), linear64(X, qw, sc, zr, g), f"qkv M={M}")
+
+
+@pytest.mark.parametrize("M,kernel,dt", [(1, 0, "f16"), (4, 0, "f16"), (4, 0, "bf16"), (16, GEMV, "f16"),
+                                         (64, 0, "f16"), (300, 0, "bf16"), (2, GEMM, "f16")])
+def test_fused_gate_up_silu(M, kernel, dt):
+    """The 7B-class MLP's gate and up projections (N = 11008, K = 4096) with
+    the SiLU-mul epilogue: H = silu(X Wg^T) * (X Wu^T) against the fp64 oracle,
+    fp32 and 16-bit output (the 16-bit output is the fp32 result rounded once)."""
+    torch = torch_mod()
+    awq = _awq()
+    K, N, g = 4096, 11008, 128
+    X = wl.gen_activation(M, K, 200 + M, 201, dt)
+    gate = _packed(wl.gen_weight(N, K, 202), g)
+    up = _packed(wl.gen_weight(N, K, 203), g)
+    ref = gate_up_silu64(_x_f64(X, dt), gate[:3], up[:3], g)
+    Xd = to_dev(X, bf16=(dt == "bf16"))
+    say("fused gate/up silu", M, kernel, dt)
+    H32 = awq.awq_linear_fused(Xd, [gate[3], up[3]], "silu_mul", g, torch.float32, kernel=kernel)
+    H16 = awq.awq_linear_fused(Xd, [gate[3], up[3]], "silu_mul", g, kernel=kernel)
+    torch.cuda.synchronize()
+    got = out_to_f64(H32)
+    assert torch.equal(H16, H32.to(H16.dtype))
+    if M <= 32:
+        # the GEMV and the 32-row tile multiply by exact q - z
+        rel, mx = assert_close(got, ref, f"gate/up M={M}")
+        say("  rel_fro %.2e max_abs %.2e" % (rel, mx))
+        return
+    # Larger GEMM tiles round dequantized weights to fp16: each of gate and
+    # up is then off by at most e = 2^-11 sum_k |x_k w_k| (their stated bound),
+    # and H = silu(g) u by at most |silu'(g) u| e_g + |silu(g)| e_u (plus
+    # second-order and fp32 terms).
+    x64 = _x_f64(X, dt)
+    dg = dequantize(unpack_codes(gate[0], K), gate[1], gate[2], g)
+    du = dequantize(unpack_codes(up[0], K), up[1], up[2], g)
+    yg, yu = x64 @ dg.T, x64 @ du.T
+    eg = 2.0 ** -11 * (np.abs(x64) @ np.abs(dg).T)
+    eu = 2.0 ** -11 * (np.abs(x64) @ np.abs(du).T)
+    sig = 1.0 / (1.0 + np.exp(-yg))
+    dsilu = sig * (1.0 + yg * (1.0 - sig))
+    bound = np.abs(dsilu * yu) * eg + np.abs(yg * sig) * eu
+    err = np.abs(got - ref)
+    assert np.all(err <= 1.01 * bound + 1e-3 * eg * eu + 1e-5), float(np.max(err - bound))
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel <= REL_FRO
+    say("  rel_fro %.2e max_abs %.2e (bound holds)" % (rel, float(err.max())))
+
+
+def test_fused_ragged_and_symmetric_pair():
+    """A ragged gate/up pair (N = 200, g64, symmetric grid) through both paths."""
+    torch = torch_mod()
+    awq = _awq()
+    K, N, g = 640, 200, 64
+    gate = _packed(wl.gen_weight(N, K, 210), g, zero_point=False)
+    up = _packed(wl.gen_weight(N, K, 211), g, zero_point=False)
+    for M, kernel in ((3, 0), (3, GEMM), (50, 0)):
+        X = wl.gen_activation(M, K, 212 + M, 213)
+        say("fused ragged pair", M, kernel)
+        H = awq.awq_linear_fused(to_dev(X), [gate[3], up[3]], "silu_mul", g, torch.float32,
+                                 kernel=kernel)
+        torch.cuda.synchronize()
+        assert_close(out_to_f64(H), gate_up_silu64(X, gate[:3], up[:3], g), f"pair M={M}")

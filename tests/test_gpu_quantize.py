@@ -193,3 +193,25 @@ def test_symmetric_decode_layers(case):
     say("symmetric quantize layer", case.name)
     _assert_same(_gpu_pack(W, 128, zero_point=False),
                  quantize_pack(W, QuantConfig(zero_point=False)), case.name)
+
+
+# --- dequantize (the pseudo-quantized weights) --------------------------------------------
+
+@pytest.mark.parametrize("N,K,g,zp", [(77, 192, 64, True), (300, 1024, 128, False),
+                                      (4096, 4096, 128, True), (11008, 4096, 128, False)])
+def test_dequantize_bit_exact(N, K, g, zp):
+    """awq_dequantize of packed weights: fp32 output equals the oracle's exact
+    (q - z) * s; fp16 output equals it rounded once to fp16 (nearest even)."""
+    from oracle import dequantize, unpack_codes
+    awq = _awq()
+    torch = torch_mod()
+    W = wl.gen_weight(N, K, 1200 + N, row_seed=9)
+    qw, sc, zr = quantize_pack(W, QuantConfig(group_size=g, zero_point=zp))
+    ref = dequantize(unpack_codes(qw, K), sc, zr, g)
+    pd = (to_dev(qw), to_dev(sc), None if zr is None else to_dev(zr))
+    say("dequantize", N, K, g, zp)
+    o32 = awq.awq_dequantize(*pd, K, group_size=g)
+    o16 = awq.awq_dequantize(*pd, K, group_size=g, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert np.array_equal(o32.cpu().numpy().astype(np.float64), ref)
+    assert np.array_equal(to_np(o16).view(np.uint16), ref.astype(np.float16).view(np.uint16))

@@ -82,3 +82,31 @@ def test_symmetric_grid_matches_python_loops():
     got = linear64(X, pack_codes(q), sc, None, 64)
     ref = linear_naive(X, q, sc, None, 64)
     assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_silu_identities():
+    """silu(x) - silu(-x) = x (sigmoid(x) + sigmoid(-x) = 1), silu(0) = 0, the
+    large-|x| limits, and agreement with x * scipy's logistic function."""
+    from scipy.special import expit
+    from oracle import silu64
+    x = np.linspace(-30, 30, 6001)
+    assert np.allclose(silu64(x) - silu64(-x), x, rtol=1e-14, atol=1e-14)
+    assert silu64(0.0) == 0.0
+    assert abs(silu64(40.0) - 40.0) < 1e-15 and abs(silu64(-40.0)) < 1e-15
+    assert np.allclose(silu64(x), x * expit(x), rtol=1e-15, atol=1e-300)
+
+
+def test_gate_up_silu_matches_loops():
+    """The fused gate/up oracle equals silu applied to a pure-Python loop's
+    gate product, times the loop's up product."""
+    from oracle import gate_up_silu64, silu64
+    Wg, Wu = _w(6, 128, 91), _w(6, 128, 92)
+    X = (np.random.default_rng(93).standard_normal((2, 128))).astype(np.float16)
+    gq, gs, gz = quantize_groups(Wg, 64)
+    uq, us, uz = quantize_groups(Wu, 64)
+    got = gate_up_silu64(X, (pack_codes(gq), gs, gz), (pack_codes(uq), us, uz), 64)
+    yg = linear_naive(X, gq, gs, gz, 64)
+    yu = linear_naive(X, uq, us, uz, 64)
+    ref = np.array([[float(a) / (1.0 + np.exp(-float(a))) * float(b) for a, b in zip(ra, rb)]
+                    for ra, rb in zip(yg, yu)])
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
