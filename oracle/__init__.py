@@ -40,8 +40,13 @@ from .quant import (  # noqa: F401
 )
 from .linear import gate_up_silu64, linear64, linear_naive, silu64  # noqa: F401
 from .search import (  # noqa: F401
+    CLIP_GRID,
     DEFAULT_ALPHAS,
     activation_mean_abs,
+    clip_search,
+    group_gram,
+    quantize_group_clipped,
+    weight_mean_abs,
     scale_vector,
     scale_table,
     scaled_activation,

@@ -77,15 +77,30 @@ def activation_mean_abs(X):
     return np.array([(int(t) / M) * 2.0 ** -24 for t in sums], dtype=F64)
 
 
-def scale_vector(xbar, alpha: float):
-    """One candidate scaling: fp32 s[k] from the fp64 statistic and one alpha."""
+def weight_mean_abs(W):
+    """wbar[k] = mean over output rows n of |W[n][k]| (fp16 W): the exact
+    column sum divided by N, rounded once to fp64 (the same statistic as
+    activation_mean_abs, taken over the weights)."""
+    return activation_mean_abs(W)
+
+
+def scale_vector(xbar, alpha: float, wbar=None):
+    """One candidate scaling: fp32 s[k] from the fp64 statistic and one alpha.
+
+    With ``wbar`` (duo scaling, "Calibration Parameters": duo_scaling scales
+    by weights and activations; the page gives no formula): t_k = xbar_k^alpha
+    / wbar_k^(1 - alpha), both floored at 2^-24, so alpha = 1 is the
+    activation-only candidate and alpha = 0 the one that equalizes weight
+    magnitudes.  Without it: t_k = xbar_k^alpha."""
     t = np.power(np.maximum(np.asarray(xbar, dtype=F64), STAT_FLOOR), F64(alpha))
+    if wbar is not None:
+        t = t / np.power(np.maximum(np.asarray(wbar, dtype=F64), STAT_FLOOR), F64(1.0) - F64(alpha))
     s = t / np.sqrt(t.max() * t.min())
     return s.astype(F32)
 
 
-def scale_table(xbar, alphas=DEFAULT_ALPHAS):
-    return np.stack([scale_vector(xbar, a) for a in alphas]).astype(F32)
+def scale_table(xbar, alphas=DEFAULT_ALPHAS, wbar=None):
+    return np.stack([scale_vector(xbar, a, wbar) for a in alphas]).astype(F32)
 
 
 def scaled_activation(X, s):
@@ -125,31 +140,115 @@ def search_loss(X, W, s, cfg: QuantConfig = QuantConfig(), Y_ref=None, block: in
     return float(total), (q, sc, zr)
 
 
-def scale_search(X, W, cfg: QuantConfig = QuantConfig(), alphas=DEFAULT_ALPHAS, block: int = 1024):
+def scale_search(X, W, cfg: QuantConfig = QuantConfig(), alphas=DEFAULT_ALPHAS, block: int = 1024,
+                 duo_scaling: bool = False, apply_clip: bool = False):
     """Grid search over alpha.  Returns a dict with the chosen index, all losses,
-    the statistic, the chosen fp32 scale vector and the packed weights for it."""
+    the statistic, the chosen fp32 scale vector and the packed weights for it
+    (with apply_clip, the packed weights of the per-group clipping search,
+    clip_search, on the chosen scaling; the losses are those of the unclipped
+    candidates)."""
     X = np.asarray(X)
     W = np.asarray(W)
     cfg.check(W.shape[1])
     xbar = activation_mean_abs(X)
+    wbar = weight_mean_abs(W) if duo_scaling else None
     Y_ref = reference_output(X, W, block)
     losses = np.empty(len(alphas), dtype=F64)
     best = None
     best_codes = None
     best_s = None
     for j, a in enumerate(alphas):
-        s = scale_vector(xbar, a)
+        s = scale_vector(xbar, a, wbar)
         L, codes = search_loss(X, W, s, cfg, Y_ref, block)
         losses[j] = L
         if best is None or L < losses[best]:       # strict: the first minimum wins
             best, best_codes, best_s = j, codes, s
-    q, sc, zr = best_codes
-    return {
-        "best_index": int(best),
-        "losses": losses,
-        "xbar": xbar,
-        "s": best_s,
-        "qweight": pack_codes(q),
-        "scales": sc,
-        "zeros": zr,
-    }
+    out = {"best_index": int(best), "losses": losses, "xbar": xbar, "wbar": wbar, "s": best_s}
+    if apply_clip:
+        clip = clip_search(X, W, best_s, cfg)
+        out.update(qweight=pack_codes(clip["q"]), scales=clip["scales"], zeros=clip["zeros"],
+                   clip_index=clip["clip_index"])
+    else:
+        q, sc, zr = best_codes
+        out.update(qweight=pack_codes(q), scales=sc, zeros=zr)
+    return out
+
+
+# ---- weight clipping ----------------------------------------------------------------
+#: Shrink factors of the clipping search: c_i = 1 - i/40, i = 0..19 (1 down to
+#: 0.525), each rounded once to fp32.  ("Calibration Parameters" names
+#: apply_clip, "Apply weight clipping", and no grid; this one mirrors the
+#: alpha grid's 20 points and shrinks a range to at most about half.)
+CLIP_GRID = (1.0 - np.arange(20, dtype=F64) / 40.0).astype(F32)
+
+
+def quantize_group_clipped(v, c, group_size: int, zero_point: bool = True):
+    """Quantize fp32 values v[..., g] (groups along the last axis) with each
+    group's range shrunk by the fp32 factor c: the asymmetric range becomes
+    [fp32(c * lo), fp32(c * hi)] (lo, hi as in quantize_groups), the symmetric
+    one +-fp32(c * max|v|); then the step, zero point and codes follow
+    quantize_groups exactly, so values beyond the shrunk range take the
+    extreme codes.  c = 1 reproduces quantize_groups.  Returns (q, s_h, z)."""
+    v = np.asarray(v, dtype=F32)
+    c = F32(c)
+    if zero_point:
+        lo = np.minimum(v.min(axis=-1), F32(0.0)) * c
+        hi = np.maximum(v.max(axis=-1), F32(0.0)) * c
+        s32 = (hi - lo) / F32(15.0)
+        s_h = np.maximum(s32, F32(2.0 ** -14)).astype(np.float16)
+        sf = s_h.astype(F32)
+        z = np.clip(np.rint(-lo / sf), F32(0.0), F32(15.0))
+        q = np.clip(np.rint(v / sf[..., None]) + z[..., None], F32(0.0), F32(15.0))
+        return q, s_h, z
+    amax = np.abs(v).max(axis=-1) * c
+    s32 = amax / F32(7.0)
+    s_h = np.maximum(s32, F32(2.0 ** -14)).astype(np.float16)
+    sf = s_h.astype(F32)
+    q = np.clip(np.rint(v / sf[..., None]), F32(-8.0), F32(7.0)) + F32(8.0)
+    return q, s_h, np.full(s_h.shape, F32(8.0))
+
+
+def group_gram(A, group_size: int):
+    """C[g] = A_g^T A_g in fp64 for the column groups of A (fp16 [M][K]): the
+    products of fp16 values are exact in fp64."""
+    A64 = np.asarray(A).astype(F64)
+    M, K = A64.shape
+    Ag = A64.reshape(M, K // group_size, group_size)
+    return np.einsum("mgi,mgj->gij", Ag, Ag)
+
+
+def clip_search(X, W, s, cfg: QuantConfig = QuantConfig(), grid=CLIP_GRID):
+    """Per (row n, group g), the shrink factor of `grid` whose quantization
+    minimizes the group's contribution to the output error on the
+    calibration inputs,
+        E_c = || A_g (v_g - deq_c(v_g)) ||^2 = d^T C_g d,   d = v_g - deq_c(v_g),
+    where A = fp16(X / s) is the activation the quantized layer sees, v =
+    fp32(s * W) the weights it quantizes and C_g = A_g^T A_g (the objective of
+    "How AWQ Works", restricted to one group of one output).  d is exact in
+    fp64, E in fp64; the first minimum wins.  Returns dict(clip_index u8
+    [N][G], q u8 [N][K], scales fp16 [N][G], zeros u8 [N][G] or None)."""
+    W = np.asarray(W)
+    N, K = W.shape
+    g = cfg.group_size
+    G = K // g
+    s = np.asarray(s, dtype=F32)
+    v = (s[None, :] * W.astype(F32)).reshape(N, G, g)
+    C = group_gram(scaled_activation(X, s), g)
+    best_E = np.full((N, G), np.inf)
+    best_i = np.zeros((N, G), dtype=np.uint8)
+    q_out = np.zeros((N, G, g), dtype=F32)
+    s_out = np.zeros((N, G), dtype=np.float16)
+    z_out = np.zeros((N, G), dtype=F32)
+    for i, c in enumerate(np.asarray(grid, dtype=F32)):
+        q, s_h, z = quantize_group_clipped(v, c, g, cfg.zero_point)
+        deq = (q.astype(F64) - z.astype(F64)[..., None]) * s_h.astype(F64)[..., None]
+        d = v.astype(F64) - deq
+        E = np.einsum("ngi,gij,ngj->ng", d, C, d)
+        take = E < best_E                          # strict: the first minimum wins
+        best_E = np.where(take, E, best_E)
+        best_i[take] = i
+        q_out[take] = q[take]
+        s_out[take] = s_h[take]
+        z_out[take] = z[take]
+    return {"clip_index": best_i, "q": q_out.reshape(N, K).astype(np.uint8), "scales": s_out,
+            "zeros": z_out.astype(np.uint8) if cfg.zero_point else None, "errors": best_E}

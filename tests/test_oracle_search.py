@@ -217,3 +217,115 @@ def test_symmetric_search_alpha_zero_is_plain_symmetric_rounding():
     assert res["losses"][0] == L0
     qw, sc, zr = quantize_pack(W, cfg, res["s"])
     assert np.array_equal(res["qweight"], qw) and zr is None
+
+
+# --- duo scaling -----------------------------------------------------------------------
+
+def test_duo_scaling_closed_forms():
+    from oracle import weight_mean_abs
+    W = np.array([[1.0, -4.0], [-3.0, 2.0]], dtype=np.float16)
+    assert weight_mean_abs(W).tolist() == [2.0, 3.0]
+    # xbar = (1, 4), wbar = (4, 1), alpha = 1/2: t = (1/2, 2), sqrt(max*min) = 1
+    s = scale_vector(np.array([1.0, 4.0]), 0.5, np.array([4.0, 1.0]))
+    assert s.tolist() == [0.5, 2.0]
+    # alpha = 1 ignores the weights exactly (wbar^0 = 1)
+    X = gen_activation(64, 256, 301, 302)
+    Wr = gen_weight(32, 256, 303)
+    xbar, wbar = activation_mean_abs(X), weight_mean_abs(Wr)
+    assert np.array_equal(scale_vector(xbar, 1.0, wbar), scale_vector(xbar, 1.0))
+    # alpha = 0 equalizes the weight magnitudes: s_k * wbar_k is one constant
+    s0 = scale_vector(xbar, 0.0, wbar).astype(np.float64)
+    prod = s0 * wbar
+    assert np.max(np.abs(prod / prod[0] - 1.0)) < 2.0 ** -22
+    # a factor 4 on every weight magnitude scales t by 4^-(1/2) = 1/2 at alpha
+    # 1/2, which the normalization removes exactly
+    assert np.array_equal(scale_vector(xbar, 0.5, 4.0 * wbar), scale_vector(xbar, 0.5, wbar))
+
+
+def test_duo_search_uses_both_statistics():
+    """The duo search's candidate j equals scale_vector(xbar, alpha_j, wbar);
+    its alpha-1 candidate coincides with the plain search's."""
+    from oracle import weight_mean_abs
+    X = gen_activation(64, 256, 311, 312)
+    W = gen_weight(24, 256, 313)
+    duo = scale_search(X, W, duo_scaling=True)
+    plain = scale_search(X, W, alphas=np.array([1.0]))
+    one = scale_search(X, W, alphas=np.array([1.0]), duo_scaling=True)
+    assert one["losses"][0] == plain["losses"][0]
+    s = scale_vector(activation_mean_abs(X), DEFAULT_ALPHAS[duo["best_index"]], weight_mean_abs(W))
+    assert np.array_equal(duo["s"], s)
+
+
+# --- weight clipping ------------------------------------------------------------------
+
+@pytest.mark.parametrize("zp", [True, False])
+def test_clip_factor_one_is_plain_quantization(zp):
+    from oracle import clip_search, quantize_group_clipped
+    W = gen_weight(16, 256, 321)
+    v = W.astype(np.float32).reshape(16, 2, 128)
+    q, s_h, z = quantize_group_clipped(v, np.float32(1.0), 128, zp)
+    qr, sr, zr = quantize_groups(W, 128, zero_point=zp)
+    assert np.array_equal(q.reshape(16, 256).astype(np.uint8), qr) and np.array_equal(s_h, sr)
+    X = gen_activation(32, 256, 322, 323)
+    ones = np.ones(256, np.float32)
+    r = clip_search(X, W, ones, QuantConfig(zero_point=zp), grid=np.array([1.0], np.float32))
+    assert np.all(r["clip_index"] == 0) and np.array_equal(r["q"], qr)
+
+
+@pytest.mark.parametrize("zp", [True, False])
+def test_clip_choice_against_direct_output_error(zp):
+    """The chosen factor minimizes ||A_g (v - deq_c(v))||^2 computed directly
+    by loops over tokens (not through the Gram matrix), and the errors agree."""
+    from oracle import CLIP_GRID, clip_search, quantize_group_clipped
+    M, N, K, g = 24, 6, 128, 64
+    X = gen_activation(M, K, 331, 332)
+    W = gen_weight(N, K, 333)
+    s = scale_vector(activation_mean_abs(X), 0.5)
+    r = clip_search(X, W, s, QuantConfig(group_size=g, zero_point=zp))
+    A = scaled_activation(X, s).astype(np.float64)
+    v = (s[None, :] * W.astype(np.float32)).reshape(N, K // g, g)
+    for n in range(N):
+        for gi in range(K // g):
+            errs = []
+            for c in CLIP_GRID:
+                q, s_h, z = quantize_group_clipped(v[n:n + 1, gi:gi + 1], c, g, zp)
+                d = v[n, gi].astype(np.float64) - (q[0, 0].astype(np.float64) - float(z[0, 0])) * float(s_h[0, 0])
+                e = 0.0
+                for m in range(M):
+                    t = sum(float(A[m, gi * g + k]) * float(d[k]) for k in range(g))
+                    e += t * t
+                errs.append(e)
+            errs = np.array(errs)
+            i = int(r["clip_index"][n, gi])
+            assert abs(r["errors"][n, gi] - errs[i]) <= 1e-9 * errs[i] + 1e-300
+            assert errs[i] <= errs.min() * (1 + 1e-12)
+            assert i == int(np.flatnonzero(errs <= errs.min() * (1 + 1e-12))[0])
+
+
+def test_clip_prefers_shrinking_an_unused_outlier():
+    """A group whose largest weight meets an input channel that is always zero:
+    shrinking the range costs nothing there and refines every other weight, so
+    a factor below 1 wins, and with all activations zero every error is 0 and
+    the first factor (1) wins."""
+    from oracle import clip_search
+    rng = np.random.default_rng(341)
+    W = (rng.standard_normal((4, 128)) * 0.02).astype(np.float16)
+    W[:, 5] = np.float16(0.5)
+    X = rng.standard_normal((64, 128)).astype(np.float16)
+    X[:, 5] = 0
+    ones = np.ones(128, np.float32)
+    r = clip_search(X, W, ones, QuantConfig())
+    assert np.all(r["clip_index"] > 0)
+    r0 = clip_search(np.zeros((8, 128), np.float16), W, ones, QuantConfig())
+    assert np.all(r0["clip_index"] == 0) and np.all(r0["errors"] == 0)
+
+
+def test_search_with_clip_packs_the_clipped_codes():
+    from oracle import clip_search, pack_codes
+    X = gen_activation(64, 256, 351, 352)
+    W = gen_weight(16, 256, 353)
+    r = scale_search(X, W, apply_clip=True)
+    c = clip_search(X, W, r["s"], QuantConfig())
+    assert np.array_equal(r["qweight"], pack_codes(c["q"])) and np.array_equal(r["clip_index"], c["clip_index"])
+    plain = scale_search(X, W)
+    assert np.array_equal(r["losses"], plain["losses"]) and r["best_index"] == plain["best_index"]
