@@ -586,6 +586,22 @@ def measure_search_row(awq, torch, wl):
                                  "frac_mfma": round(flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
                                  "best_index": r["best_index"]}
     log("search", rows["scale_search_4096"])
+    # the calibration options: duo scaling, and the per-group clipping search
+    for key, kw in (("scale_search_4096_duo", dict(duo_scaling=True)),
+                    ("scale_search_4096_clip", dict(apply_clip=True))):
+        ws2 = torch.empty(awq.awq_scale_search_workspace_size(case.M, case.N, case.K, **kw),
+                          dtype=torch.uint8, device="cuda")
+        awq.awq_scale_search(Xd, Wd, workspace=ws2, **kw)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            awq.awq_scale_search(Xd, Wd, workspace=ws2, **kw)
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        rows[key] = {"ms": round(min(ts) * 1e3, 3)}
+        log(key, rows[key])
+        del ws2
     return rows
 
 

@@ -44,6 +44,8 @@ EXPORTS = (
     "awq_linear_fused",
     "awq_scale_search_workspace_size",
     "awq_scale_search",
+    "awq_scale_search_workspace_size_ex",
+    "awq_scale_search_ex",
     "awq_status_string",
     "awq_last_error",
     "awq_version",
@@ -58,6 +60,10 @@ class awq_config(ctypes.Structure):
 class awq_linear_part(ctypes.Structure):
     _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("zeros", ctypes.c_void_p), ("N", ctypes.c_int64), ("Y", ctypes.c_void_p)]
+
+
+class awq_search_options(ctypes.Structure):
+    _fields_ = [("duo_scaling", ctypes.c_int32), ("apply_clip", ctypes.c_int32)]
 
 
 class AwqError(RuntimeError):
@@ -109,6 +115,14 @@ def _load():
                                      ctypes.POINTER(ctypes.c_int32),
                                      ctypes.POINTER(ctypes.c_double), vp, vp, vp, vp, vp]
     lib.awq_scale_search.restype = ctypes.c_int
+    po = ctypes.POINTER(awq_search_options)
+    lib.awq_scale_search_workspace_size_ex.argtypes = [i64, i64, i64, awq_config, i32, po]
+    lib.awq_scale_search_workspace_size_ex.restype = ctypes.c_size_t
+    lib.awq_scale_search_ex.argtypes = [vp, vp, i64, i64, i64, awq_config,
+                                        ctypes.POINTER(ctypes.c_double), i32, po, vp,
+                                        ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ctypes.c_double), vp, vp, vp, vp, vp, vp]
+    lib.awq_scale_search_ex.restype = ctypes.c_int
     lib.awq_status_string.argtypes = [ctypes.c_int]
     lib.awq_status_string.restype = ctypes.c_char_p
     lib.awq_last_error.argtypes = []
@@ -475,16 +489,20 @@ def awq_linear_fused(X, parts, epilogue: str = "none", group_size: int = 128, ou
 
 
 def awq_scale_search_workspace_size(M: int, N: int, K: int, group_size: int = 128,
-                                    n_alpha: int = 20, zero_point: bool = True) -> int:
+                                    n_alpha: int = 20, zero_point: bool = True,
+                                    duo_scaling: bool = False, apply_clip: bool = False) -> int:
     cfg = config(group_size, zero_point=zero_point)
-    return int(lib.awq_scale_search_workspace_size(M, N, K, cfg, n_alpha))
+    opts = awq_search_options(int(bool(duo_scaling)), int(bool(apply_clip)))
+    return int(lib.awq_scale_search_workspace_size_ex(M, N, K, cfg, n_alpha, ctypes.byref(opts)))
 
 
 def awq_scale_search(X, W, group_size: int = 128, alphas=None, workspace=None, out=None,
-                     zero_point: bool = True):
-    """Alpha-grid scale search.  Returns a dict with best_index, losses (numpy
-    fp64), s (fp32 [K] tensor) and the packed weights for the chosen s (zeros
-    None for the symmetric grid, zero_point=False)."""
+                     zero_point: bool = True, duo_scaling: bool = False,
+                     apply_clip: bool = False):
+    """Alpha-grid scale search (awq_scale_search_ex).  Returns a dict with
+    best_index, losses (numpy fp64), s (fp32 [K] tensor) and the packed
+    weights for the chosen s (zeros None for the symmetric grid,
+    zero_point=False); with apply_clip also clip_index (uint8 [N][K/g])."""
     torch = _torch()
     _tensor(X, "X", torch.float16)
     _tensor(W, "W", torch.float16)
@@ -495,7 +513,8 @@ def awq_scale_search(X, W, group_size: int = 128, alphas=None, workspace=None, o
     if W.shape[1] != K:
         raise ValueError(f"W has {W.shape[1]} input channels, X has {K}")
     n_alpha = 20 if alphas is None else len(alphas)
-    need = awq_scale_search_workspace_size(M, N, K, group_size, n_alpha, zero_point)
+    need = awq_scale_search_workspace_size(M, N, K, group_size, n_alpha, zero_point, duo_scaling,
+                                           apply_clip)
     if need == 0:
         check(AWQ_ERR_INVALID_ARG, "awq_scale_search_workspace_size")
     if out is not None:
@@ -523,11 +542,19 @@ def awq_scale_search(X, W, group_size: int = 128, alphas=None, workspace=None, o
         a_ptr = ctypes.cast(a_arr, ctypes.POINTER(ctypes.c_double))
     best = ctypes.c_int32(-1)
     losses = (ctypes.c_double * n_alpha)()
-    st = lib.awq_scale_search(_ptr(X), _ptr(W), M, N, K, config(group_size, zero_point=zero_point),
-                              a_ptr, n_alpha, _ptr(workspace),
-                              workspace.numel() * workspace.element_size(),
-                              ctypes.byref(best), losses, _ptr(best_s),
-                              _ptr(qw), _ptr(sc), _zp_ptr(zr), _stream(dev))
-    check(st, "awq_scale_search")
-    return {"best_index": int(best.value), "losses": np.array(losses[:], dtype=np.float64),
-            "s": best_s, "qweight": qw, "scales": sc, "zeros": zr}
+    opts = awq_search_options(int(bool(duo_scaling)), int(bool(apply_clip)))
+    clip = (torch.empty((N, K // group_size), dtype=torch.uint8, device=dev)
+            if apply_clip else None)
+    st = lib.awq_scale_search_ex(_ptr(X), _ptr(W), M, N, K,
+                                 config(group_size, zero_point=zero_point), a_ptr, n_alpha,
+                                 ctypes.byref(opts), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 ctypes.byref(best), losses, _ptr(best_s), _ptr(qw), _ptr(sc),
+                                 _zp_ptr(zr), ctypes.c_void_p(0) if clip is None else _ptr(clip),
+                                 _stream(dev))
+    check(st, "awq_scale_search_ex")
+    res = {"best_index": int(best.value), "losses": np.array(losses[:], dtype=np.float64),
+           "s": best_s, "qweight": qw, "scales": sc, "zeros": zr}
+    if clip is not None:
+        res["clip_index"] = clip
+    return res

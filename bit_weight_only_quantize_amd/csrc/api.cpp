@@ -106,13 +106,16 @@ constexpr size_t kAlign = 256;
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace layout of the scale search (each region 256-byte aligned).
+// Workspace layout of the scale search (each region 256-byte aligned; the
+// duo-scaling and clipping regions only when those options are on).
 struct SearchLayout {
-  size_t units, xbar, table, act, qw, sc, zr, yref, partials, losses, best, total;
+  size_t units, xbar, table, act, qw, sc, zr, yref, partials, losses, best;
+  size_t wunits, wbar, gram_partial, gram, total;
   int64_t tiles;
 };
 
-SearchLayout search_layout(int64_t M, int64_t N, int64_t K, int gs, int n_alpha) {
+SearchLayout search_layout(int64_t M, int64_t N, int64_t K, int gs, int n_alpha, bool duo,
+                           bool clip) {
   SearchLayout L{};
   const int64_t G = K / gs;
   L.tiles = awq::gemm_tile_count(M, N);
@@ -133,16 +136,31 @@ SearchLayout search_layout(int64_t M, int64_t N, int64_t K, int gs, int n_alpha)
   L.partials = take(sizeof(double) * (size_t)n_alpha * L.tiles);
   L.losses = take(sizeof(double) * 64);
   L.best = take(sizeof(int32_t));
+  if (duo) {
+    L.wunits = take(sizeof(uint64_t) * K);
+    L.wbar = take(sizeof(double) * K);
+  }
+  if (clip) {
+    L.gram_partial = take(sizeof(double) * (size_t)G * awq::gram_parts(M) * gs * gs);
+    L.gram = take(sizeof(double) * (size_t)G * gs * (gs + 1) / 2);
+  }
   L.total = off;
   return L;
 }
 
-awq_status check_search(int64_t M, int64_t N, int64_t K, awq_config cfg, int32_t n_alpha) {
+awq_status check_search(int64_t M, int64_t N, int64_t K, awq_config cfg, int32_t n_alpha,
+                        const awq_search_options *opts = nullptr) {
   awq_status st = check_config(cfg, K);
   if (st != AWQ_OK) return st;
   if (M < 1 || N < 1) return fail(AWQ_ERR_INVALID_ARG, "M and N must be >= 1");
   if (M > ((int64_t)1 << 24) - 1)
     return fail(AWQ_ERR_INVALID_ARG, "M=%lld exceeds 2^24-1 calibration rows", (long long)M);
+  if (opts && (opts->duo_scaling != 0 && opts->duo_scaling != 1))
+    return fail(AWQ_ERR_INVALID_ARG, "duo_scaling=%d: must be 0 or 1", opts->duo_scaling);
+  if (opts && (opts->apply_clip != 0 && opts->apply_clip != 1))
+    return fail(AWQ_ERR_INVALID_ARG, "apply_clip=%d: must be 0 or 1", opts->apply_clip);
+  if (opts && opts->duo_scaling && N > ((int64_t)1 << 24) - 1)
+    return fail(AWQ_ERR_INVALID_ARG, "duo scaling: N=%lld exceeds 2^24-1 rows", (long long)N);
   if (N > ((int64_t)1 << 31)) return fail(AWQ_ERR_INVALID_ARG, "N too large");
   if (n_alpha < 1 || n_alpha > 64)
     return fail(AWQ_ERR_INVALID_ARG, "n_alpha=%d must be in [1, 64]", n_alpha);
@@ -504,8 +522,15 @@ awq_status awq_linear_noalloc(const void *X, int32_t x_dtype, const uint32_t *qw
 
 size_t awq_scale_search_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg,
                                        int32_t n_alpha) {
-  if (check_search(M, N, K, cfg, n_alpha) != AWQ_OK) return 0;
-  return search_layout(M, N, K, cfg.group_size, n_alpha).total;
+  return awq_scale_search_workspace_size_ex(M, N, K, cfg, n_alpha, nullptr);
+}
+
+size_t awq_scale_search_workspace_size_ex(int64_t M, int64_t N, int64_t K, awq_config cfg,
+                                          int32_t n_alpha, const awq_search_options *opts) {
+  if (check_search(M, N, K, cfg, n_alpha, opts) != AWQ_OK) return 0;
+  return search_layout(M, N, K, cfg.group_size, n_alpha, opts && opts->duo_scaling,
+                       opts && opts->apply_clip)
+      .total;
 }
 
 awq_status awq_scale_search(const void *X, const void *W, int64_t M, int64_t N, int64_t K,
@@ -513,8 +538,20 @@ awq_status awq_scale_search(const void *X, const void *W, int64_t M, int64_t N, 
                             void *workspace, size_t workspace_bytes, int32_t *best_index,
                             double *losses, float *best_s, uint32_t *qweight,
                             uint16_t *scales, uint8_t *zeros, awq_stream_t stream) {
-  awq_status st = check_search(M, N, K, cfg, n_alpha);
+  return awq_scale_search_ex(X, W, M, N, K, cfg, alphas, n_alpha, nullptr, workspace,
+                             workspace_bytes, best_index, losses, best_s, qweight, scales, zeros,
+                             nullptr, stream);
+}
+
+awq_status awq_scale_search_ex(const void *X, const void *W, int64_t M, int64_t N, int64_t K,
+                               awq_config cfg, const double *alphas, int32_t n_alpha,
+                               const awq_search_options *opts, void *workspace,
+                               size_t workspace_bytes, int32_t *best_index, double *losses,
+                               float *best_s, uint32_t *qweight, uint16_t *scales,
+                               uint8_t *zeros, uint8_t *clip_index, awq_stream_t stream) {
+  awq_status st = check_search(M, N, K, cfg, n_alpha, opts);
   if (st != AWQ_OK) return st;
+  const bool duo = opts && opts->duo_scaling, clip = opts && opts->apply_clip;
   double grid[64];
   if (alphas == nullptr) {
     if (n_alpha != 20)
@@ -536,7 +573,7 @@ awq_status awq_scale_search(const void *X, const void *W, int64_t M, int64_t N, 
   if (!aligned(workspace, kAlign))
     return fail(AWQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (!aligned(scales, 2)) return fail(AWQ_ERR_INVALID_ARG, "scales must be 2-byte aligned");
-  const SearchLayout L = search_layout(M, N, K, cfg.group_size, n_alpha);
+  const SearchLayout L = search_layout(M, N, K, cfg.group_size, n_alpha, duo, clip);
   if (workspace_bytes < L.total)
     return fail(AWQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu required", workspace_bytes,
                 L.total);
@@ -558,8 +595,11 @@ awq_status awq_scale_search(const void *X, const void *W, int64_t M, int64_t N, 
   const auto *w = reinterpret_cast<const uint16_t *>(W);
   const int gs = cfg.group_size;
 
+  auto *wbar = duo ? reinterpret_cast<double *>(ws + L.wbar) : nullptr;
   hipError_t e = awq::launch_mean_abs(x, M, K, units, xbar, s);
-  if (e == hipSuccess) e = awq::launch_scale_table(xbar, K, grid, n_alpha, table, s);
+  if (e == hipSuccess && duo)   // the weights' statistic: the same kernel over the N rows of W
+    e = awq::launch_mean_abs(w, N, K, reinterpret_cast<uint64_t *>(ws + L.wunits), wbar, s);
+  if (e == hipSuccess) e = awq::launch_scale_table(xbar, wbar, K, grid, n_alpha, table, s);
   if (e == hipSuccess) e = awq::launch_gemm_dense_f32(x, w, M, N, K, yref, s);
   for (int j = 0; j < n_alpha && e == hipSuccess; ++j) {
     const float *sj = table + (size_t)j * K;
@@ -581,9 +621,18 @@ awq_status awq_scale_search(const void *X, const void *W, int64_t M, int64_t N, 
 
   const float *sbest = table + (size_t)hbest * K;
   e = hipMemcpyAsync(best_s, sbest, sizeof(float) * K, hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess)
+  if (e == hipSuccess && !clip)
     e = awq::launch_quantize_pack(w, N, K, gs, sbest, qweight, scales,
                                   cfg.zero_point ? zeros : nullptr, nullptr, s);
+  if (e == hipSuccess && clip) {
+    // the clipping search on the chosen scaling, with A = fp16(X / s)
+    e = awq::launch_scale_activation(x, sbest, M, K, act, s);
+    if (e == hipSuccess)
+      e = awq::launch_clip_search(w, sbest, act, M, N, K, gs,
+                                  reinterpret_cast<double *>(ws + L.gram_partial),
+                                  reinterpret_cast<double *>(ws + L.gram), qweight, scales,
+                                  cfg.zero_point ? zeros : nullptr, clip_index, s);
+  }
   if (e != hipSuccess) return hip_status(e, "awq_scale_search (final pack)");
   *best_index = hbest;
   if (losses) std::memcpy(losses, hlosses, sizeof(double) * n_alpha);

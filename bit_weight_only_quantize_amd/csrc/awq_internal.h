@@ -124,9 +124,20 @@ bool gemm_supported(int64_t N, int64_t K, bool dense);
 // xbar[k] = sum_m |X[m][k]| / M in fp64 (exact sum; `units` is K u64 scratch).
 hipError_t launch_mean_abs(const uint16_t *X, int64_t M, int64_t K, uint64_t *units,
                            double *xbar, hipStream_t st);
-// s_table[j][k] for n_alpha alphas (device fp64 array).
-hipError_t launch_scale_table(const double *xbar, int64_t K, const double *alphas,
-                              int n_alpha, float *s_table, hipStream_t st);
+// s_table[j][k] for n_alpha alphas (host fp64 array); wbar (device, or NULL)
+// enables duo scaling.
+hipError_t launch_scale_table(const double *xbar, const double *wbar, int64_t K,
+                              const double *alphas, int n_alpha, float *s_table, hipStream_t st);
+// Weight clipping: points of the shrink grid, Gram partials per group
+// (gram_parts(M) of GS*GS fp64 each), then per (row, group) the factor of
+// least output error; writes the packed result for it (zeros NULL: symmetric)
+// and, if clip_index is given, the chosen index (u8 [N][K/gs]).
+constexpr int kClipPoints = 20;
+int64_t gram_parts(int64_t M);
+hipError_t launch_clip_search(const uint16_t *W, const float *s, const uint16_t *A, int64_t M,
+                              int64_t N, int64_t K, int gs, double *gram_partial, double *gram,
+                              uint32_t *qweight, uint16_t *scales, uint8_t *zeros,
+                              uint8_t *clip_index, hipStream_t st);
 // A = fp16(fp32(X) / s).
 hipError_t launch_scale_activation(const uint16_t *X, const float *s, int64_t M,
                                    int64_t K, uint16_t *A, hipStream_t st);

@@ -112,17 +112,24 @@ struct Alphas {
 
 constexpr int kTableThreads = 1024;
 
-__device__ __forceinline__ double stat_pow(double xbar, double alpha) {
-  return pow(fmax(xbar, 0x1p-24), alpha);
+// t = max(xbar, 2^-24)^alpha, and with duo scaling ("Calibration Parameters":
+// duo_scaling scales by weights and activations) divided by
+// max(wbar, 2^-24)^(1 - alpha), wbar the mean |W| of the input channel.
+__device__ __forceinline__ double stat_pow(const double *xbar, const double *wbar, int64_t k,
+                                           double alpha) {
+  double t = pow(fmax(xbar[k], 0x1p-24), alpha);
+  if (wbar) t = t / pow(fmax(wbar[k], 0x1p-24), 1.0 - alpha);
+  return t;
 }
 
 __global__ __launch_bounds__(kTableThreads) void scale_table_kernel(
-    const double *__restrict__ xbar, int64_t K, Alphas alphas, float *__restrict__ table) {
+    const double *__restrict__ xbar, const double *__restrict__ wbar, int64_t K, Alphas alphas,
+    float *__restrict__ table) {
   const int j = blockIdx.x;
   const double alpha = alphas.a[j];
   double tmax = 0.0, tmin = __builtin_huge_val();
   for (int64_t k = threadIdx.x; k < K; k += kTableThreads) {
-    const double t = stat_pow(xbar[k], alpha);
+    const double t = stat_pow(xbar, wbar, k, alpha);
     tmax = fmax(tmax, t);
     tmin = fmin(tmin, t);
   }
@@ -150,14 +157,275 @@ __global__ __launch_bounds__(kTableThreads) void scale_table_kernel(
   __syncthreads();
   const double norm = sqrt(smax[0] * smin[0]);
   for (int64_t k = threadIdx.x; k < K; k += kTableThreads)
-    table[j * K + k] = (float)(stat_pow(xbar[k], alpha) / norm);
+    table[j * K + k] = (float)(stat_pow(xbar, wbar, k, alpha) / norm);
 }
 
-hipError_t launch_scale_table(const double *xbar, int64_t K, const double *alphas, int n_alpha,
-                              float *s_table, hipStream_t st) {
+hipError_t launch_scale_table(const double *xbar, const double *wbar, int64_t K,
+                              const double *alphas, int n_alpha, float *s_table, hipStream_t st) {
   Alphas a;
   for (int j = 0; j < 64; ++j) a.a[j] = j < n_alpha ? alphas[j] : 0.0;
-  scale_table_kernel<<<n_alpha, kTableThreads, 0, st>>>(xbar, K, a, s_table);
+  scale_table_kernel<<<n_alpha, kTableThreads, 0, st>>>(xbar, wbar, K, a, s_table);
+  return hipGetLastError();
+}
+
+// ---- weight clipping ------------------------------------------------------------------
+// "Calibration Parameters": apply_clip, "Apply weight clipping".  Per output
+// row n and group g of the chosen scaling, the shrink factor c of a 20-point
+// grid whose quantization minimizes the group's output error on the
+// calibration inputs, E_c = ||A_g d||^2 = d^T C_g d with A = fp16(X / s), d =
+// v - deq_c(v), v = fp32(s * W) and C_g = A_g^T A_g.  C is accumulated in fp64
+// (products of fp16 values are exact), d is exact in fp32 (deq is 0 or within
+// a factor 2 of v, and has at most 15 significant bits), E is fp64: the
+// choice differs from an exact evaluation only at fp64 near-ties.
+
+constexpr int kGramRows = 512;     // calibration rows per partial Gram matrix
+constexpr int kGramTile = 32;      // rows staged in LDS at a time
+
+// Partial Gram matrices: grid (G, P); workgroup (g, p) sums rows
+// [p * kGramRows, (p + 1) * kGramRows) of group g.  Thread t owns the 8 x 8
+// block (t / 16, t % 16) of a 128 x 128 matrix (g = 64: 4 x 4 blocks of the
+// 64 x 64 one, threads 0..255 as 16 x 16 blocks).
+template <int GS>
+__global__ __launch_bounds__(256) void gram_partial_kernel(const uint16_t *__restrict__ A,
+                                                           int64_t M, int64_t K,
+                                                           double *__restrict__ partial) {
+  constexpr int kB = GS / 16;                       // block edge: 8 (g128) or 4 (g64)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kGramTile][GS];
+  const int g = blockIdx.x, p = blockIdx.y, P = gridDim.y;
+  const int t = threadIdx.x, bi = t / 16, bj = t % 16;
+  double acc[kB][kB];
+#pragma unroll
+  for (int i = 0; i < kB; ++i)
+#pragma unroll
+    for (int j = 0; j < kB; ++j) acc[i][j] = 0.0;
+  const int64_t m0 = (int64_t)p * kGramRows, m1 = m0 + kGramRows < M ? m0 + kGramRows : M;
+  for (int64_t mt = m0; mt < m1; mt += kGramTile) {
+    __syncthreads();
+    // stage kGramTile rows x GS columns (16 bytes per thread and round)
+    for (int e = t; e < kGramTile * GS / 8; e += 256) {
+      const int r = e / (GS / 8), ch = e % (GS / 8);
+      const int64_t m = mt + r;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (m < m1) v = *reinterpret_cast<const u32x4 *>(A + m * K + (int64_t)g * GS + ch * 8);
+      *reinterpret_cast<u32x4 *>(&tile[r][ch * 8]) = v;
+    }
+    __syncthreads();
+    const int rows = m1 - mt < kGramTile ? (int)(m1 - mt) : kGramTile;
+    for (int r = 0; r < rows; ++r) {
+      double a[kB], b[kB];
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {
+        a[i] = (double)half_bits_to_float(tile[r][bi * kB + i]);
+        b[i] = (double)half_bits_to_float(tile[r][bj * kB + i]);
+      }
+#pragma unroll
+      for (int i = 0; i < kB; ++i)
+#pragma unroll
+        for (int j = 0; j < kB; ++j) acc[i][j] = __builtin_fma(a[i], b[j], acc[i][j]);
+    }
+  }
+  double *out = partial + ((int64_t)g * P + p) * GS * GS;
+#pragma unroll
+  for (int i = 0; i < kB; ++i)
+#pragma unroll
+    for (int j = 0; j < kB; ++j) out[(bi * kB + i) * GS + bj * kB + j] = acc[i][j];
+}
+
+// C[g] = sum of the P partials in index order, written as the packed upper
+// triangle (row i holds columns i..GS-1).
+template <int GS>
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const double *__restrict__ partial,
+                                                          int P, double *__restrict__ gram) {
+  const int g = blockIdx.x;
+  for (int e = threadIdx.x; e < GS * GS; e += 256) {
+    const int i = e / GS, j = e % GS;
+    if (j < i) continue;
+    double v = 0.0;
+    for (int p = 0; p < P; ++p) v += partial[((int64_t)g * P + p) * GS * GS + e];
+    gram[(int64_t)g * (GS * (GS + 1) / 2) + i * GS - i * (i - 1) / 2 + (j - i)] = v;
+  }
+}
+
+struct ClipGrid {
+  float c[kClipPoints];
+};
+
+// Quantization of value v with shrink factor c: the step (fp16 bits) and the
+// zero point of the group (lo, hi, amax over the group), then code(v).  The
+// arithmetic of quantize_pack_kernel with the range scaled by c, written
+// with IEEE divisions (this kernel is not bound by them).
+template <bool SYM>
+__device__ __forceinline__ void clip_params(float lo, float hi, float amax, float c, float &sf,
+                                            float &zf, uint16_t &sbits) {
+  float step;
+  if constexpr (SYM) {
+    step = (amax * c) / 7.0f;
+  } else {
+    step = (hi * c - lo * c) / 15.0f;
+  }
+  const _Float16 sh = (_Float16)fmaxf(step, 0x1p-14f);
+  sbits = __builtin_bit_cast(uint16_t, sh);
+  sf = (float)sh;
+  zf = SYM ? 8.0f : fminf(fmaxf(__builtin_rintf(-(lo * c) / sf), 0.0f), 15.0f);
+}
+template <bool SYM>
+__device__ __forceinline__ float clip_code(float v, float sf, float zf) {
+  const float q = __builtin_rintf(v / sf);
+  return SYM ? fminf(fmaxf(q, -8.0f), 7.0f) + 8.0f : fminf(fmaxf(q + zf, 0.0f), 15.0f);
+}
+
+// One wave per (row n, group g); a workgroup of 4 waves serves rows of one
+// group, with the group's packed Gram matrix in LDS (fp64) and each wave's
+// candidate errors d_c in LDS (fp32, [k][c]).  Lane l owns the elements
+// k = l * (GS/64) .. of the group: it computes u_c(k) = sum_j C[k][j] d_c[j]
+// for its k and all candidates, then E_c = sum_k d_c(k) u_c(k) summed over the
+// lanes in a fixed order.  The first minimum wins; the wave then writes the
+// group's codes, scale and zero point for it (and the chosen index).
+constexpr int kClipWaves = 4;
+template <int GS, bool SYM>
+__global__ __launch_bounds__(64 * kClipWaves) void clip_select_kernel(
+    const uint16_t *__restrict__ W, const float *__restrict__ s, int64_t N, int64_t K,
+    const double *__restrict__ gram, ClipGrid grid, int rows_per_block,
+    uint32_t *__restrict__ qweight, uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros,
+    uint8_t *__restrict__ clip_index) {
+  constexpr int kE = GS / 64;                          // elements per lane: 2 or 1
+  constexpr int kTri = GS * (GS + 1) / 2;
+  constexpr int kC = kClipPoints;
+  __shared__ double sC[kTri];
+  __shared__ float sD[kClipWaves][GS][kC];
+  const int g = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = (int)(K / GS);
+  for (int e = threadIdx.x; e < kTri; e += 64 * kClipWaves) sC[e] = gram[(int64_t)g * kTri + e];
+  __syncthreads();
+  auto cij = [&](int i, int j) {
+    const int a = i < j ? i : j, b = i < j ? j : i;
+    return sC[a * GS - a * (a - 1) / 2 + (b - a)];
+  };
+  const int64_t nb = (int64_t)blockIdx.y * rows_per_block;
+  for (int r = wave; r < rows_per_block; r += kClipWaves) {
+    const int64_t n = nb + r;
+    if (n >= N) break;                                  // uniform per wave
+    // this lane's values v = fp32(s * W)
+    float v[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int64_t k = (int64_t)g * GS + lane * kE + e;
+      v[e] = s[k] * half_bits_to_float(W[n * K + k]);
+    }
+    float lo = 0.0f, hi = 0.0f, amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      lo = fminf(lo, v[e]);
+      hi = fmaxf(hi, v[e]);
+      amax = fmaxf(amax, __builtin_fabsf(v[e]));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, off, 64));
+      hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    }
+    // d_c for this lane's elements, to LDS (exact in fp32)
+#pragma unroll
+    for (int ci = 0; ci < kC; ++ci) {
+      float sf, zf;
+      uint16_t sb;
+      clip_params<SYM>(lo, hi, amax, grid.c[ci], sf, zf, sb);
+#pragma unroll
+      for (int e = 0; e < kE; ++e) {
+        const float q = clip_code<SYM>(v[e], sf, zf);
+        sD[wave][lane * kE + e][ci] = v[e] - (q - zf) * sf;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes landed
+    __builtin_amdgcn_wave_barrier();
+    double u[kE][kC];
+#pragma unroll
+    for (int e = 0; e < kE; ++e)
+#pragma unroll
+      for (int ci = 0; ci < kC; ++ci) u[e][ci] = 0.0;
+    for (int j = 0; j < GS; ++j) {
+      double cj[kE];
+#pragma unroll
+      for (int e = 0; e < kE; ++e) cj[e] = cij(lane * kE + e, j);
+#pragma unroll
+      for (int ci = 0; ci < kC; ++ci) {
+        const double dj = (double)sD[wave][j][ci];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) u[e][ci] = __builtin_fma(cj[e], dj, u[e][ci]);
+      }
+    }
+    double E[kC];
+#pragma unroll
+    for (int ci = 0; ci < kC; ++ci) {
+      double t = 0.0;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) t = __builtin_fma((double)sD[wave][lane * kE + e][ci], u[e][ci], t);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
+      E[ci] = t;
+    }
+    int best = 0;
+    double ebest = E[0];
+    float cbest = grid.c[0];
+#pragma unroll
+    for (int ci = 1; ci < kC; ++ci) {
+      if (E[ci] < ebest) {                 // strict: the first minimum wins
+        ebest = E[ci];
+        best = ci;
+        cbest = grid.c[ci];
+      }
+    }
+    // codes, scale and zero point of the chosen factor: lane l < GS/8 packs word l
+    float sf, zf;
+    uint16_t sb;
+    clip_params<SYM>(lo, hi, amax, cbest, sf, zf, sb);
+    if (lane < GS / 8) {
+      const int64_t k0 = (int64_t)g * GS + lane * 8;
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float vi = s[k0 + i] * half_bits_to_float(W[n * K + k0 + i]);
+        word |= ((uint32_t)clip_code<SYM>(vi, sf, zf)) << (4 * nibble_of_channel(i));
+      }
+      qweight[n * (K / 8) + k0 / 8] = word;
+    }
+    if (lane == 0) {
+      scales[n * G + g] = sb;
+      if constexpr (!SYM) zeros[n * G + g] = (uint8_t)zf;
+      if (clip_index) clip_index[n * G + g] = (uint8_t)best;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+int64_t gram_parts(int64_t M) { return (M + kGramRows - 1) / kGramRows; }
+
+hipError_t launch_clip_search(const uint16_t *W, const float *s, const uint16_t *A, int64_t M,
+                              int64_t N, int64_t K, int gs, double *gram_partial, double *gram,
+                              uint32_t *qweight, uint16_t *scales, uint8_t *zeros,
+                              uint8_t *clip_index, hipStream_t st) {
+  const int64_t G = K / gs, P = gram_parts(M);
+  ClipGrid grid;
+  for (int i = 0; i < kClipPoints; ++i) grid.c[i] = (float)(1.0 - (double)i / 40.0);
+  const int rpb = 64;
+  const dim3 cgrid((unsigned)G, (unsigned)((N + rpb - 1) / rpb));
+  if (gs == 128) {
+    gram_partial_kernel<128><<<dim3((unsigned)G, (unsigned)P), 256, 0, st>>>(A, M, K, gram_partial);
+    gram_reduce_kernel<128><<<(unsigned)G, 256, 0, st>>>(gram_partial, (int)P, gram);
+    if (zeros)
+      clip_select_kernel<128, false><<<cgrid, 64 * kClipWaves, 0, st>>>(W, s, N, K, gram, grid, rpb, qweight, scales, zeros, clip_index);
+    else
+      clip_select_kernel<128, true><<<cgrid, 64 * kClipWaves, 0, st>>>(W, s, N, K, gram, grid, rpb, qweight, scales, zeros, clip_index);
+  } else {
+    gram_partial_kernel<64><<<dim3((unsigned)G, (unsigned)P), 256, 0, st>>>(A, M, K, gram_partial);
+    gram_reduce_kernel<64><<<(unsigned)G, 256, 0, st>>>(gram_partial, (int)P, gram);
+    if (zeros)
+      clip_select_kernel<64, false><<<cgrid, 64 * kClipWaves, 0, st>>>(W, s, N, K, gram, grid, rpb, qweight, scales, zeros, clip_index);
+    else
+      clip_select_kernel<64, true><<<cgrid, 64 * kClipWaves, 0, st>>>(W, s, N, K, gram, grid, rpb, qweight, scales, zeros, clip_index);
+  }
   return hipGetLastError();
 }
 

@@ -341,6 +341,47 @@ awq_status awq_scale_search(const void *X, const void *W, int64_t M, int64_t N,
                             uint16_t *scales, uint8_t *zeros,
                             awq_stream_t stream);
 
+/* Options of awq_scale_search_ex, mirroring the pages' calibration
+ * parameters ("AWQ Advanced Usage Guide", "Calibration Parameters"):
+ *  duo_scaling  1: candidate t_k = xbar_k^alpha / wbar_k^(1 - alpha), wbar_k
+ *               the mean |W_nk| over the N rows (exact sum, rounded once;
+ *               N < 2^24), both floored at 2^-24 ("Scale weights and
+ *               activations"); 0: t_k = xbar_k^alpha.
+ *  apply_clip   1: after the alpha search, each (row, group) of the chosen
+ *               scaling takes the range shrink factor c_i = 1 - i/40, i =
+ *               0..19 (rounded to fp32: the group's [lo, hi], or +-max|v|,
+ *               times c) that minimizes the group's output error
+ *               ||A_g (v - deq_c(v))||^2, A = fp16(X / s), v = fp32(s * W),
+ *               evaluated in fp64 through A_g^T A_g; the first minimum wins
+ *               ("Apply weight clipping").  The packed result is that of the
+ *               chosen factors; the losses stay those of the unclipped
+ *               candidates. */
+typedef struct awq_search_options {
+    int32_t duo_scaling;
+    int32_t apply_clip;
+} awq_search_options;
+
+/* awq_scale_search_workspace_size for awq_scale_search_ex with `opts` (NULL:
+ * both options off). */
+size_t awq_scale_search_workspace_size_ex(int64_t M, int64_t N, int64_t K, awq_config cfg,
+                                          int32_t n_alpha, const awq_search_options *opts);
+
+/*
+ * awq_scale_search_ex - awq_scale_search with the calibration options above.
+ * Cites: as awq_scale_search, and "Calibration Parameters" (duo_scaling,
+ * apply_clip).
+ *   opts        host, or NULL (both off: exactly awq_scale_search).
+ *   clip_index  device u8 [N][K/g] or NULL: with apply_clip, the chosen
+ *               shrink index of every (row, group).
+ * Everything else as awq_scale_search.
+ */
+awq_status awq_scale_search_ex(const void *X, const void *W, int64_t M, int64_t N, int64_t K,
+                               awq_config cfg, const double *alphas, int32_t n_alpha,
+                               const awq_search_options *opts, void *workspace,
+                               size_t workspace_bytes, int32_t *best_index, double *losses,
+                               float *best_s, uint32_t *qweight, uint16_t *scales,
+                               uint8_t *zeros, uint8_t *clip_index, awq_stream_t stream);
+
 /* Static description of a status code. */
 const char *awq_status_string(awq_status status);
 

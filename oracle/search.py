@@ -213,11 +213,12 @@ def group_gram(A, group_size: int):
     products of fp16 values are exact in fp64."""
     A64 = np.asarray(A).astype(F64)
     M, K = A64.shape
-    Ag = A64.reshape(M, K // group_size, group_size)
-    return np.einsum("mgi,mgj->gij", Ag, Ag)
+    G = K // group_size
+    return np.stack([A64[:, g * group_size:(g + 1) * group_size].T
+                     @ A64[:, g * group_size:(g + 1) * group_size] for g in range(G)])
 
 
-def clip_search(X, W, s, cfg: QuantConfig = QuantConfig(), grid=CLIP_GRID):
+def clip_search(X, W, s, cfg: QuantConfig = QuantConfig(), grid=CLIP_GRID, all_errors=False):
     """Per (row n, group g), the shrink factor of `grid` whose quantization
     minimizes the group's contribution to the output error on the
     calibration inputs,
@@ -239,16 +240,23 @@ def clip_search(X, W, s, cfg: QuantConfig = QuantConfig(), grid=CLIP_GRID):
     q_out = np.zeros((N, G, g), dtype=F32)
     s_out = np.zeros((N, G), dtype=np.float16)
     z_out = np.zeros((N, G), dtype=F32)
+    errors = []
     for i, c in enumerate(np.asarray(grid, dtype=F32)):
         q, s_h, z = quantize_group_clipped(v, c, g, cfg.zero_point)
         deq = (q.astype(F64) - z.astype(F64)[..., None]) * s_h.astype(F64)[..., None]
         d = v.astype(F64) - deq
-        E = np.einsum("ngi,gij,ngj->ng", d, C, d)
+        # E[n][g] = d[n,g]^T C[g] d[n,g]
+        E = np.stack([np.sum((d[:, gi] @ C[gi]) * d[:, gi], axis=1) for gi in range(G)], axis=1)
+        if all_errors:
+            errors.append(E)
         take = E < best_E                          # strict: the first minimum wins
         best_E = np.where(take, E, best_E)
         best_i[take] = i
         q_out[take] = q[take]
         s_out[take] = s_h[take]
         z_out[take] = z[take]
-    return {"clip_index": best_i, "q": q_out.reshape(N, K).astype(np.uint8), "scales": s_out,
-            "zeros": z_out.astype(np.uint8) if cfg.zero_point else None, "errors": best_E}
+    out = {"clip_index": best_i, "q": q_out.reshape(N, K).astype(np.uint8), "scales": s_out,
+           "zeros": z_out.astype(np.uint8) if cfg.zero_point else None, "errors": best_E}
+    if all_errors:
+        out["all_errors"] = np.stack(errors)
+    return out

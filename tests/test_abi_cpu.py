@@ -242,6 +242,25 @@ def test_search_workspace_and_validation():
     assert best.value == -1      # nothing written on error
 
 
+def test_search_options_validation():
+    O = binding.awq_search_options
+    size = lambda M, N, o: lib.awq_scale_search_workspace_size_ex(M, N, 4096, cfg(128), 20,
+                                                                 ctypes.byref(o))
+    plain = lib.awq_scale_search_workspace_size(4096, 4096, 4096, cfg(128), 20)
+    assert size(4096, 4096, O(0, 0)) == plain
+    # duo adds the weights' statistic; clipping the Gram matrices (fp64)
+    assert size(4096, 4096, O(1, 0)) > plain
+    assert size(4096, 4096, O(0, 1)) >= plain + 32 * 128 * 128 * 8
+    assert size(4096, 4096, O(2, 0)) == 0
+    assert size(4096, 1 << 24, O(1, 0)) == 0         # duo: N < 2^24 rows of W
+    best = ctypes.c_int32(-1)
+    o = O(0, 3)
+    st = lib.awq_scale_search_ex(FAKE, FAKE, 64, 64, 256, cfg(128), None, 20, ctypes.byref(o),
+                                 FAKE, 1 << 40, ctypes.byref(best), None, FAKE, FAKE, FAKE, FAKE,
+                                 NULL, NULL)
+    assert st == binding.AWQ_ERR_INVALID_ARG and best.value == -1
+
+
 def test_single_hip_runtime_in_process():
     """torch bundles a HIP runtime with the same soname; the binding must bind
     the library to that copy, never map a second runtime next to it."""

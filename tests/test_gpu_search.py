@@ -23,9 +23,10 @@ def _awq():
     return awq
 
 
-def _gpu_search(X, W, g=128, alphas=None, zero_point=True):
+def _gpu_search(X, W, g=128, alphas=None, zero_point=True, duo_scaling=False, apply_clip=False):
     res = _awq().awq_scale_search(to_dev(X), to_dev(W), group_size=g, alphas=alphas,
-                                  zero_point=zero_point)
+                                  zero_point=zero_point, duo_scaling=duo_scaling,
+                                  apply_clip=apply_clip)
     torch_mod().cuda.synchronize()
     return res
 
@@ -180,3 +181,88 @@ def test_symmetric_search_matches_oracle(M, N, K, g):
     res = _gpu_search(X, W, g, zero_point=False)
     ref = scale_search(X, W, QuantConfig(group_size=g, zero_point=False))
     _check_against(res, ref, f"symmetric search {M}x{N}x{K}")
+
+
+# --- duo scaling and weight clipping (awq_scale_search_ex) ------------------------------
+
+@pytest.mark.parametrize("M,N,K,g", [(256, 192, 512, 128), (100, 77, 384, 64)])
+def test_duo_scaling_search_matches_oracle(M, N, K, g):
+    """duo_scaling: every candidate's s (activation and weight statistics) and
+    codes bitwise, the losses, the chosen index and the packed result."""
+    from oracle import weight_mean_abs
+    X = wl.gen_activation(M, K, 400 + M, 401)
+    W = wl.gen_weight(N, K, 402 + N)
+    say("duo search", M, N, K, g)
+    res = _gpu_search(X, W, g, duo_scaling=True)
+    ref = scale_search(X, W, QuantConfig(group_size=g), duo_scaling=True)
+    _check_against(res, ref, "duo")
+    xbar, wbar = activation_mean_abs(X), weight_mean_abs(W)
+    for a in DEFAULT_ALPHAS[::3]:
+        one = _gpu_search(X, W, g, [float(a)], duo_scaling=True)
+        assert np.array_equal(to_np(one["s"]).view(np.uint32), scale_vector(xbar, a, wbar).view(np.uint32))
+
+
+def _check_clip(res, ref, what):
+    """The GPU's clip choice equals the oracle's except where the oracle's
+    errors of the two choices agree to fp64 rounding (a near-tie); the packed
+    result equals the oracle's quantization for the GPU's choice."""
+    from oracle import CLIP_GRID, quantize_group_clipped, pack_codes
+    gi = to_np(res["clip_index"]).astype(np.int64)
+    oi = ref["clip_index"].astype(np.int64)
+    diff = np.argwhere(gi != oi)
+    say(what, "clip choices differing from the oracle:", len(diff), "of", gi.size,
+        "histogram", np.bincount(oi.ravel(), minlength=20).tolist())
+    E = ref["all_errors"]
+    for n, g in diff:
+        a, b = E[gi[n, g], n, g], E[oi[n, g], n, g]
+        assert abs(a - b) <= 1e-12 * max(b, 1e-300), (what, int(n), int(g), a, b)
+    if len(diff) == 0:
+        assert np.array_equal(to_np(res["qweight"]), pack_codes(ref["q"]))
+        assert np.array_equal(to_np(res["scales"]).view(np.uint16), ref["scales"].view(np.uint16))
+        if ref["zeros"] is not None:
+            assert np.array_equal(to_np(res["zeros"]), ref["zeros"])
+
+
+@pytest.mark.parametrize("M,N,K,g,zp", [(256, 192, 512, 128, True), (100, 77, 384, 64, True),
+                                        (256, 130, 512, 128, False), (64, 40, 640, 64, False)])
+def test_clip_search_matches_oracle(M, N, K, g, zp):
+    """apply_clip: the per-group shrink choice and the packed result against
+    the oracle's clipping search on the oracle's chosen scaling."""
+    from oracle import clip_search
+    X = wl.gen_activation(M, K, 410 + M, 411)
+    W = wl.gen_weight(N, K, 412 + N)
+    cfg = QuantConfig(group_size=g, zero_point=zp)
+    say("clip search", M, N, K, g, zp)
+    res = _gpu_search(X, W, g, zero_point=zp, apply_clip=True)
+    ref = scale_search(X, W, cfg)
+    assert res["best_index"] == ref["best_index"]
+    assert np.array_equal(to_np(res["s"]).view(np.uint32), ref["s"].view(np.uint32))
+    _check_clip(res, clip_search(X, W, ref["s"], cfg, all_errors=True), "clip small")
+
+
+def test_clip_search_full_layer():
+    """Clipping on the 4096 x 4096 layer (4096 calibration rows, g128): every
+    one of the 131072 (row, group) choices against the oracle, on the scaling
+    the oracle chose (stored golden index)."""
+    from oracle import clip_search
+    gold = json.load(open(os.path.join(HERE, "golden", "search_4096.json")))
+    case = wl.search_case()
+    X = case.activation()
+    W = case.weight()
+    say("clip search full 4096^3")
+    res = _gpu_search(X, W, apply_clip=True)
+    assert res["best_index"] == gold["best_index"]
+    s_ref = scale_vector(activation_mean_abs(X), DEFAULT_ALPHAS[gold["best_index"]])
+    _check_clip(res, clip_search(X, W, s_ref, QuantConfig(), all_errors=True), "clip full")
+
+
+def test_duo_and_clip_together():
+    from oracle import clip_search
+    X = wl.gen_activation(128, 512, 420, 421)
+    W = wl.gen_weight(96, 512, 422)
+    say("duo + clip")
+    res = _gpu_search(X, W, duo_scaling=True, apply_clip=True)
+    ref = scale_search(X, W, QuantConfig(), duo_scaling=True)
+    assert res["best_index"] == ref["best_index"]
+    assert np.array_equal(to_np(res["s"]).view(np.uint32), ref["s"].view(np.uint32))
+    _check_clip(res, clip_search(X, W, ref["s"], QuantConfig(), all_errors=True), "duo+clip")
