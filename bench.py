@@ -13,7 +13,8 @@ ten rotation steps back to back (the timed region runs exactly --steps steps).
 Also measured after the timed region ("rows"): quantize/pack, GEMV at M=4,
 GEMM at M=1 (for the GEMV-vs-GEMM comparison), batched GEMM at M=16/64/256
 (13B-class MLP, g64 and g128), prefill GEMM at M=4096 (70B-class, fp16 and
-bf16) and the full alpha search on a 4096^3 layer.
+bf16), fused QKV and gate/up projections at M=1, and the full alpha search on
+a 4096^3 layer (plain, with duo scaling, with weight clipping).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows all|none]
 """
@@ -456,7 +457,51 @@ def measure_rows(awq, torch, wl, L, decode_layers, R_dec, only_gemm=False):
         rows.update(measure_decode_extra_rows(awq, torch, wl, L, decode_layers, R_dec))
     rows.update(measure_gemm_rows(awq, torch, wl, L))
     if not only_gemm:
+        rows.update(measure_fused_rows(awq, torch, wl, L))
         rows.update(measure_search_row(awq, torch, wl))
+    return rows
+
+
+def measure_fused_rows(awq, torch, wl, L):
+    """Fused projections at M=1 on 7B-class shapes: Q, K and V (three 4096 x
+    4096 parts) in one launch against three single launches, and gate/up (two
+    4096 -> 11008 parts) with silu(g)*u in one launch against the two plain
+    projections alone (no activation kernel counted for them)."""
+    rows = {}
+    K = 4096
+    X = torch.from_numpy(wl.gen_activation(1, K, seed=71, outlier_seed=72)).cuda()
+    for key, Ns, epi in (("fused_qkv_m1", (4096, 4096, 4096), "none"),
+                         ("fused_gate_up_silu_m1", (11008, 11008), "silu_mul")):
+        base = []
+        for i, N in enumerate(Ns):
+            W = torch.from_numpy(wl.gen_weight(N, K, seed=80 + i)).cuda()
+            base.append(awq.awq_quantize_pack(W, 128))
+            del W
+        nbytes = sum(qw.numel() * 4 + sc.numel() * 2 + zr.numel() for (qw, sc, zr) in base)
+        R = copies_for(nbytes)
+        copies = [base] + [[tuple(t.clone() for t in p) for p in base] for _ in range(R - 1)]
+        torch.cuda.synchronize()
+        if epi == "none":
+            outs = [torch.empty((1, N), dtype=torch.float16, device="cuda") for N in Ns]
+        else:
+            outs = torch.empty((1, Ns[0]), dtype=torch.float16, device="cuda")
+        Ys = [torch.empty((1, N), dtype=torch.float16, device="cuda") for N in Ns]
+
+        def ff(copies=copies, outs=outs, epi=epi):
+            for parts in copies:
+                awq.awq_linear_fused(X, parts, epi, 128, outs=outs, workspace=None)
+
+        def fs(copies=copies, Ys=Ys):
+            for parts in copies:
+                for p, Y in zip(parts, Ys):
+                    L.linear(X, p, Y, 128, awq.AWQ_KERNEL_AUTO)
+        t_f = time_graph(torch, make_graph(torch, ff), 10, R)
+        t_s = time_graph(torch, make_graph(torch, fs), 10, R)
+        rows[key] = {"fused_us": round(t_f * 1e6, 3), "separate_us": round(t_s * 1e6, 3),
+                     "fused_GB/s": round(nbytes / t_f / 1e9, 1),
+                     "frac_hbm": round(nbytes / t_f / 1e9 / HBM_PEAK_GBS, 4)}
+        log(key, rows[key])
+        del copies, base
     return rows
 
 
