@@ -142,7 +142,7 @@ SearchLayout search_layout(int64_t M, int64_t N, int64_t K, int gs, int n_alpha,
   }
   if (clip) {
     L.gram_partial = take(sizeof(double) * (size_t)G * awq::gram_parts(M) * gs * gs);
-    L.gram = take(sizeof(double) * (size_t)G * gs * (gs + 1) / 2);
+    L.gram = take(sizeof(double) * (size_t)G * awq::clip_gram_doubles(gs));
   }
   L.total = off;
   return L;
@@ -162,6 +162,9 @@ awq_status check_search(int64_t M, int64_t N, int64_t K, awq_config cfg, int32_t
   if (opts && opts->duo_scaling && N > ((int64_t)1 << 24) - 1)
     return fail(AWQ_ERR_INVALID_ARG, "duo scaling: N=%lld exceeds 2^24-1 rows", (long long)N);
   if (N > ((int64_t)1 << 31)) return fail(AWQ_ERR_INVALID_ARG, "N too large");
+  if (opts && opts->apply_clip && K / cfg.group_size > 65535)
+    return fail(AWQ_ERR_UNSUPPORTED, "weight clipping: K/g=%lld exceeds 65535 groups",
+                (long long)(K / cfg.group_size));
   if (n_alpha < 1 || n_alpha > 64)
     return fail(AWQ_ERR_INVALID_ARG, "n_alpha=%d must be in [1, 64]", n_alpha);
   if (!awq::gemm_supported(N, K, true))

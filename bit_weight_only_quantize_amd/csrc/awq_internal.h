@@ -134,6 +134,9 @@ hipError_t launch_scale_table(const double *xbar, const double *wbar, int64_t K,
 // and, if clip_index is given, the chosen index (u8 [N][K/gs]).
 constexpr int kClipPoints = 20;
 int64_t gram_parts(int64_t M);
+// fp64 entries of one group's Gram matrix as the clip selection reads it
+// (the 16 x 16 blocks on and above the diagonal, in MFMA operand order).
+constexpr int64_t clip_gram_doubles(int gs) { return (gs / 16) * (gs / 16 + 1) / 2 * 256; }
 hipError_t launch_clip_search(const uint16_t *W, const float *s, const uint16_t *A, int64_t M,
                               int64_t N, int64_t K, int gs, double *gram_partial, double *gram,
                               uint32_t *qweight, uint16_t *scales, uint8_t *zeros,

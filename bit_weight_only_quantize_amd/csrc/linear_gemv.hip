@@ -103,7 +103,10 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 // scales and zero points come from LDS.  All global reads use buffer
 // resources, so rows >= M, columns >= N and groups >= G read zero without
 // branches.
-template <class XT, int GS, int NW, int U, bool STAGE_X, int NP>
+//
+// MULTI: more than one part (a single part reads its pointers at fixed
+// argument offsets, with no dependent lookup before the first load).
+template <class XT, int GS, int NW, int U, bool STAGE_X, int NP, bool MULTI>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restrict__ X,
                                                        GemvParts parts, int M, int K, int ytype,
                                                        uint32_t zfix) {
@@ -117,11 +120,15 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
   const int kq = lane >> 4;
   // this workgroup's part and column tile (uniform)
   int part = 0;
-  if constexpr (NP == 1) {
+  if constexpr (NP == 1 && MULTI) {
     while (part + 1 < parts.count && (int)blockIdx.x >= parts.tile_end[part]) ++part;
   }
   const int tile = (int)blockIdx.x - (part ? parts.tile_end[part - 1] : 0);
   const int N = parts.n[part];
+  // read the output pointer with the other arguments: left to its use after
+  // the reduction, its argument load was measured to cost 2-5% per launch
+  void *const Y = parts.y[part];
+  asm volatile("" : : "s"(Y));
   const int n0 = tile * 16;
   const int n = n0 + c;
   const int G = K / GS;
@@ -313,7 +320,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
     }
   }
   if (n >= N) return;
-  void *Y = parts.y[part];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int m = 4 * kq + e;
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
 }
 
 
-template <class XT, int GS, int NW, int NP>
+template <class XT, int GS, int NW, int NP, bool MULTI>
 static void gemv_launch(const uint16_t *X, const GemvParts &parts, int tiles, int M, int64_t K,
                         YType yt, uint32_t zfix, hipStream_t st) {
   const dim3 grid((unsigned)tiles);
@@ -343,11 +349,11 @@ static void gemv_launch(const uint16_t *X, const GemvParts &parts, int tiles, in
   // Two batches in flight once a wave walks more than 8 groups (measured 7%
   // faster at 13.5 groups per wave, slower at 5 and below).
   if (stage && G > 8 * NW)
-    gemv_kernel<XT, GS, NW, 2, true, NP><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
+    gemv_kernel<XT, GS, NW, 2, true, NP, MULTI><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
   else if (stage)
-    gemv_kernel<XT, GS, NW, 1, true, NP><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
+    gemv_kernel<XT, GS, NW, 1, true, NP, MULTI><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
   else
-    gemv_kernel<XT, GS, NW, 2, false, NP><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
+    gemv_kernel<XT, GS, NW, 2, false, NP, MULTI><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
 }
 
 // Waves per workgroup.  Every workgroup of a launch should be resident at
@@ -361,10 +367,16 @@ static void gemv_dispatch(const uint16_t *X, const GemvParts &parts, int tiles, 
                           YType yt, uint32_t zfix, hipStream_t st) {
   // the gate/up pair always takes 8 waves: with 16, its two sets of staging
   // registers spill under the 1024-thread register budget
-  if (NP == 1 && gemv_waves_for_tiles(tiles) == 16)
-    gemv_launch<XT, GS, 16, NP>(X, parts, tiles, M, K, yt, zfix, st);
+  if (NP == 2)
+    gemv_launch<XT, GS, 8, NP, false>(X, parts, tiles, M, K, yt, zfix, st);
+  else if (parts.count > 1 && gemv_waves_for_tiles(tiles) == 16)
+    gemv_launch<XT, GS, 16, NP, true>(X, parts, tiles, M, K, yt, zfix, st);
+  else if (parts.count > 1)
+    gemv_launch<XT, GS, 8, NP, true>(X, parts, tiles, M, K, yt, zfix, st);
+  else if (gemv_waves_for_tiles(tiles) == 16)
+    gemv_launch<XT, GS, 16, NP, false>(X, parts, tiles, M, K, yt, zfix, st);
   else
-    gemv_launch<XT, GS, 8, NP>(X, parts, tiles, M, K, yt, zfix, st);
+    gemv_launch<XT, GS, 8, NP, false>(X, parts, tiles, M, K, yt, zfix, st);
 }
 
 int64_t gemv_groups_per_wave(int64_t N, int64_t K, int gs) {

@@ -231,19 +231,34 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const uint16_t *__res
     for (int j = 0; j < kB; ++j) out[(bi * kB + i) * GS + bj * kB + j] = acc[i][j];
 }
 
-// C[g] = sum of the P partials in index order, written as the packed upper
-// triangle (row i holds columns i..GS-1).
+// The clip selection multiplies 16 x 16 blocks of C on the matrix cores
+// (mfma_f64_16x16x4: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]
+// and holds D[4 r + l / 16][l % 16] in its r-th result, r = 0..3; measured
+// on gfx950 with single-entry operands).  Block pair (I, J), I <= J,
+// is pair index I*NB - I(I-1)/2 + (J - I); its operand for k-step s is
+//   frag[pair][s][l] = C'[16 I + l % 16][16 J + 4 s + l / 16],
+// C' = C on the diagonal blocks and 2C above them (exact), so that
+//   d^T C d = sum_I d_I^T (sum_{J >= I} C'_IJ d_J).
+// gram_frag_kernel sums the P partials of each element in index order and
+// writes it there.  Grid (G, pairs), 256 threads: thread s * 64 + l.
 template <int GS>
-__global__ __launch_bounds__(256) void gram_reduce_kernel(const double *__restrict__ partial,
-                                                          int P, double *__restrict__ gram) {
-  const int g = blockIdx.x;
-  for (int e = threadIdx.x; e < GS * GS; e += 256) {
-    const int i = e / GS, j = e % GS;
-    if (j < i) continue;
-    double v = 0.0;
-    for (int p = 0; p < P; ++p) v += partial[((int64_t)g * P + p) * GS * GS + e];
-    gram[(int64_t)g * (GS * (GS + 1) / 2) + i * GS - i * (i - 1) / 2 + (j - i)] = v;
+__global__ __launch_bounds__(256) void gram_frag_kernel(const double *__restrict__ partial,
+                                                        int P, double *__restrict__ frag) {
+  constexpr int NB = GS / 16;
+  const int g = blockIdx.x, pair = blockIdx.y;
+  int I = 0, rem = pair;
+  while (rem >= NB - I) {
+    rem -= NB - I;
+    ++I;
   }
+  const int J = I + rem;
+  const int st = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int i = 16 * I + (l & 15), j = 16 * J + 4 * st + (l >> 4);
+  const double *src = partial + (int64_t)g * P * GS * GS + i * GS + j;
+  double v = 0.0;
+  for (int p = 0; p < P; ++p) v += src[(int64_t)p * GS * GS];
+  if (I < J) v *= 2.0;
+  frag[(int64_t)g * clip_gram_doubles(GS) + (int64_t)pair * 256 + threadIdx.x] = v;
 }
 
 struct ClipGrid {
@@ -274,129 +289,178 @@ __device__ __forceinline__ float clip_code(float v, float sf, float zf) {
   return SYM ? fminf(fmaxf(q, -8.0f), 7.0f) + 8.0f : fminf(fmaxf(q + zf, 0.0f), 15.0f);
 }
 
-// One wave per (row n, group g); a workgroup of 4 waves serves rows of one
-// group, with the group's packed Gram matrix in LDS (fp64) and each wave's
-// candidate errors d_c in LDS (fp32, [k][c]).  Lane l owns the elements
-// k = l * (GS/64) .. of the group: it computes u_c(k) = sum_j C[k][j] d_c[j]
-// for its k and all candidates, then E_c = sum_k d_c(k) u_c(k) summed over the
-// lanes in a fixed order.  The first minimum wins; the wave then writes the
-// group's codes, scale and zero point for it (and the chosen index).
-constexpr int kClipWaves = 4;
+// Grid point ci (lane-varying) without a dynamic index into the argument block.
+__device__ __forceinline__ float clip_factor(const ClipGrid &grid, int ci) {
+  float c = grid.c[0];
+#pragma unroll
+  for (int i = 1; i < kClipPoints; ++i) c = ci == i ? grid.c[i] : c;
+  return c;
+}
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// Per group g and 32 rows of W: E[r][c] = d^T C_g d for each row r and grid
+// point c, d = v - deq_c(v) (exact in fp32), in fp64 on the matrix cores.
+// The 640 columns (row, c) form 40 blocks of 16 (block b: rows 16 (b / 20)
+// .. + 15, point b % 20); wave w takes blocks 10 w .. 10 w + 9, two at a
+// time.  Per pair of blocks it builds the B operands d_J (every j, in
+// registers) and, for each row block I, U_I = sum_{J >= I} C'_IJ d_J and
+// E += d_I . U_I (lane-wise, then over the four lanes of a column in a fixed
+// order).  Then each row takes the first minimum over c (strict <, in grid
+// order) and packs its codes, scale and zero point for it.
+constexpr int kClipRowsPerBlock = 32;
 template <int GS, bool SYM>
-__global__ __launch_bounds__(64 * kClipWaves) void clip_select_kernel(
+__global__ __launch_bounds__(256) void clip_select_kernel(
     const uint16_t *__restrict__ W, const float *__restrict__ s, int64_t N, int64_t K,
-    const double *__restrict__ gram, ClipGrid grid, int rows_per_block,
-    uint32_t *__restrict__ qweight, uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros,
-    uint8_t *__restrict__ clip_index) {
-  constexpr int kE = GS / 64;                          // elements per lane: 2 or 1
-  constexpr int kTri = GS * (GS + 1) / 2;
-  constexpr int kC = kClipPoints;
-  __shared__ double sC[kTri];
-  __shared__ float sD[kClipWaves][GS][kC];
-  const int g = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const double *__restrict__ frag, ClipGrid grid, uint32_t *__restrict__ qweight,
+    uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros, uint8_t *__restrict__ clip_index) {
+  constexpr int NB = GS / 16;
+  constexpr int kPairs = NB * (NB + 1) / 2;
+  constexpr int R = kClipRowsPerBlock;
+  __shared__ __attribute__((aligned(16))) double sC[kPairs * 256];
+  // rows padded by 4 floats: a column's 16 lanes (16 rows) hit distinct banks
+  __shared__ __attribute__((aligned(16))) float sV[R][GS + 4];
+  __shared__ float sStat[R][3];
+  __shared__ double sE[R][kClipPoints];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.y;
   const int G = (int)(K / GS);
-  for (int e = threadIdx.x; e < kTri; e += 64 * kClipWaves) sC[e] = gram[(int64_t)g * kTri + e];
+  const int64_t row0 = (int64_t)blockIdx.x * R;
+
+  // this group's operand blocks, and v = fp32(s * W) of the block's rows
+  // (rows past N repeat row N - 1; nothing of theirs is stored)
+  {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(frag + (int64_t)g * (kPairs * 256));
+    u32x4 *dst = reinterpret_cast<u32x4 *>(sC);
+    for (int e = tid; e < kPairs * 128; e += 256) dst[e] = src[e];
+  }
+  for (int e = tid; e < R * GS / 8; e += 256) {
+    const int r = e / (GS / 8), k8 = e % (GS / 8);
+    const int64_t n = row0 + r < N ? row0 + r : N - 1;
+    const u32x4 wv = *reinterpret_cast<const u32x4 *>(W + n * K + (int64_t)g * GS + k8 * 8);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint16_t h = (uint16_t)(wv[q >> 1] >> (16 * (q & 1)));
+      sV[r][k8 * 8 + q] = s[(int64_t)g * GS + k8 * 8 + q] * half_bits_to_float(h);
+    }
+  }
   __syncthreads();
-  auto cij = [&](int i, int j) {
-    const int a = i < j ? i : j, b = i < j ? j : i;
-    return sC[a * GS - a * (a - 1) / 2 + (b - a)];
-  };
-  const int64_t nb = (int64_t)blockIdx.y * rows_per_block;
-  for (int r = wave; r < rows_per_block; r += kClipWaves) {
-    const int64_t n = nb + r;
-    if (n >= N) break;                                  // uniform per wave
-    // this lane's values v = fp32(s * W)
-    float v[kE];
-#pragma unroll
-    for (int e = 0; e < kE; ++e) {
-      const int64_t k = (int64_t)g * GS + lane * kE + e;
-      v[e] = s[k] * half_bits_to_float(W[n * K + k]);
-    }
+  // row statistics: 8 threads per row
+  {
+    const int r = tid >> 3, part = tid & 7;
     float lo = 0.0f, hi = 0.0f, amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < kE; ++e) {
-      lo = fminf(lo, v[e]);
-      hi = fmaxf(hi, v[e]);
-      amax = fmaxf(amax, __builtin_fabsf(v[e]));
+    for (int k = part; k < GS; k += 8) {
+      const float v = sV[r][k];
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+      amax = fmaxf(amax, __builtin_fabsf(v));
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
+    for (int off = 1; off < 8; off <<= 1) {
       lo = fminf(lo, __shfl_xor(lo, off, 64));
       hi = fmaxf(hi, __shfl_xor(hi, off, 64));
       amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     }
-    // d_c for this lane's elements, to LDS (exact in fp32)
+    if (part == 0) {
+      sStat[r][0] = lo;
+      sStat[r][1] = hi;
+      sStat[r][2] = amax;
+    }
+  }
+  __syncthreads();
+
+  const int q = lane & 15, kq = lane >> 4;
+  const int half = wave >> 1;                         // rows 16 half .. 16 half + 15
+  const int rl = 16 * half + q;                        // this lane's row within the block
+  const float lo = sStat[rl][0], hi = sStat[rl][1], amax = sStat[rl][2];
+  for (int t = 0; t < 5; ++t) {
+    const int ca = (wave & 1) * 10 + 2 * t, cb = ca + 1;
+    float sfa, zfa, sfb, zfb;
+    uint16_t sbits;
+    clip_params<SYM>(lo, hi, amax, grid.c[ca], sfa, zfa, sbits);
+    clip_params<SYM>(lo, hi, amax, grid.c[cb], sfb, zfb, sbits);
+    auto dd = [&](int j, float sf, float zf) {
+      const float v = sV[rl][j];
+      return (double)(v - (clip_code<SYM>(v, sf, zf) - zf) * sf);
+    };
+    double bA[NB][4], bB[NB][4];
 #pragma unroll
-    for (int ci = 0; ci < kC; ++ci) {
-      float sf, zf;
-      uint16_t sb;
-      clip_params<SYM>(lo, hi, amax, grid.c[ci], sf, zf, sb);
+    for (int J = 0; J < NB; ++J)
 #pragma unroll
-      for (int e = 0; e < kE; ++e) {
-        const float q = clip_code<SYM>(v[e], sf, zf);
-        sD[wave][lane * kE + e][ci] = v[e] - (q - zf) * sf;
+      for (int st = 0; st < 4; ++st) {
+        bA[J][st] = dd(16 * J + 4 * st + kq, sfa, zfa);
+        bB[J][st] = dd(16 * J + 4 * st + kq, sfb, zfb);
+      }
+    double eA = 0.0, eB = 0.0;
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      // one row block at a time: keeps the compiler from hoisting every
+      // block's operand reads and error terms at once (register spills)
+      __builtin_amdgcn_sched_barrier(0);
+      f64x4 uA = {0.0, 0.0, 0.0, 0.0}, uB = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int J = I; J < NB; ++J) {
+        const int pair = I * NB - I * (I - 1) / 2 + (J - I);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const double a = sC[(pair * 4 + st) * 64 + lane];
+          uA = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bA[J][st], uA, 0, 0, 0);
+          uB = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bB[J][st], uB, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * r + kq;
+        eA = __builtin_fma(dd(i, sfa, zfa), uA[r], eA);
+        eB = __builtin_fma(dd(i, sfb, zfb), uB[r], eB);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes landed
-    __builtin_amdgcn_wave_barrier();
-    double u[kE][kC];
-#pragma unroll
-    for (int e = 0; e < kE; ++e)
-#pragma unroll
-      for (int ci = 0; ci < kC; ++ci) u[e][ci] = 0.0;
-    for (int j = 0; j < GS; ++j) {
-      double cj[kE];
-#pragma unroll
-      for (int e = 0; e < kE; ++e) cj[e] = cij(lane * kE + e, j);
-#pragma unroll
-      for (int ci = 0; ci < kC; ++ci) {
-        const double dj = (double)sD[wave][j][ci];
-#pragma unroll
-        for (int e = 0; e < kE; ++e) u[e][ci] = __builtin_fma(cj[e], dj, u[e][ci]);
-      }
+    eA += __shfl_xor(eA, 16, 64);
+    eB += __shfl_xor(eB, 16, 64);
+    eA += __shfl_xor(eA, 32, 64);
+    eB += __shfl_xor(eB, 32, 64);
+    if (kq == 0) {
+      sE[rl][ca] = eA;
+      sE[rl][cb] = eB;
     }
-    double E[kC];
+  }
+  __syncthreads();
+
+  // per row (8 threads each): first minimum over the grid, then the row's
+  // codes for it, GS/64 packed words per thread
+  constexpr int kWordsPerRow = GS / 8;
+  constexpr int kThreadsPerRow = 256 / R;              // 8
+  constexpr int kWordsPerThread = kWordsPerRow / kThreadsPerRow;
+  const int r = tid / kThreadsPerRow, part = tid % kThreadsPerRow;
+  const int64_t n = row0 + r;
+  if (n >= N) return;
+  int best = 0;
+  double ebest = sE[r][0];
 #pragma unroll
-    for (int ci = 0; ci < kC; ++ci) {
-      double t = 0.0;
-#pragma unroll
-      for (int e = 0; e < kE; ++e) t = __builtin_fma((double)sD[wave][lane * kE + e][ci], u[e][ci], t);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
-      E[ci] = t;
+  for (int ci = 1; ci < kClipPoints; ++ci) {
+    const double e = sE[r][ci];
+    if (e < ebest) {                                   // strict: the first minimum wins
+      ebest = e;
+      best = ci;
     }
-    int best = 0;
-    double ebest = E[0];
-    float cbest = grid.c[0];
+  }
+  float sf, zf;
+  uint16_t sb;
+  clip_params<SYM>(sStat[r][0], sStat[r][1], sStat[r][2], clip_factor(grid, best), sf, zf, sb);
 #pragma unroll
-    for (int ci = 1; ci < kC; ++ci) {
-      if (E[ci] < ebest) {                 // strict: the first minimum wins
-        ebest = E[ci];
-        best = ci;
-        cbest = grid.c[ci];
-      }
-    }
-    // codes, scale and zero point of the chosen factor: lane l < GS/8 packs word l
-    float sf, zf;
-    uint16_t sb;
-    clip_params<SYM>(lo, hi, amax, cbest, sf, zf, sb);
-    if (lane < GS / 8) {
-      const int64_t k0 = (int64_t)g * GS + lane * 8;
-      uint32_t word = 0;
+  for (int u = 0; u < kWordsPerThread; ++u) {
+    const int wi = part * kWordsPerThread + u;
+    uint32_t word = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float vi = s[k0 + i] * half_bits_to_float(W[n * K + k0 + i]);
-        word |= ((uint32_t)clip_code<SYM>(vi, sf, zf)) << (4 * nibble_of_channel(i));
-      }
-      qweight[n * (K / 8) + k0 / 8] = word;
-    }
-    if (lane == 0) {
-      scales[n * G + g] = sb;
-      if constexpr (!SYM) zeros[n * G + g] = (uint8_t)zf;
-      if (clip_index) clip_index[n * G + g] = (uint8_t)best;
-    }
-    __builtin_amdgcn_wave_barrier();
+    for (int e = 0; e < 8; ++e)
+      word |= ((uint32_t)clip_code<SYM>(sV[r][wi * 8 + e], sf, zf)) << (4 * nibble_of_channel(e));
+    qweight[n * (K / 8) + (int64_t)g * (GS / 8) + wi] = word;
+  }
+  if (part == 0) {
+    scales[n * G + g] = sb;
+    if constexpr (!SYM) zeros[n * G + g] = (uint8_t)zf;
+    if (clip_index) clip_index[n * G + g] = (uint8_t)best;
   }
 }
 
@@ -409,22 +473,22 @@ hipError_t launch_clip_search(const uint16_t *W, const float *s, const uint16_t 
   const int64_t G = K / gs, P = gram_parts(M);
   ClipGrid grid;
   for (int i = 0; i < kClipPoints; ++i) grid.c[i] = (float)(1.0 - (double)i / 40.0);
-  const int rpb = 64;
-  const dim3 cgrid((unsigned)G, (unsigned)((N + rpb - 1) / rpb));
+  const dim3 cgrid((unsigned)((N + kClipRowsPerBlock - 1) / kClipRowsPerBlock), (unsigned)G);
+  const unsigned pairs = (unsigned)(clip_gram_doubles(gs) / 256);
   if (gs == 128) {
     gram_partial_kernel<128><<<dim3((unsigned)G, (unsigned)P), 256, 0, st>>>(A, M, K, gram_partial);
-    gram_reduce_kernel<128><<<(unsigned)G, 256, 0, st>>>(gram_partial, (int)P, gram);
+    gram_frag_kernel<128><<<dim3((unsigned)G, pairs), 256, 0, st>>>(gram_partial, (int)P, gram);
     if (zeros)
-      clip_select_kernel<128, false><<<cgrid, 64 * kClipWaves, 0, st>>>(W, s, N, K, gram, grid, rpb, qweight, scales, zeros, clip_index);
+      clip_select_kernel<128, false><<<cgrid, 256, 0, st>>>(W, s, N, K, gram, grid, qweight, scales, zeros, clip_index);
     else
-      clip_select_kernel<128, true><<<cgrid, 64 * kClipWaves, 0, st>>>(W, s, N, K, gram, grid, rpb, qweight, scales, zeros, clip_index);
+      clip_select_kernel<128, true><<<cgrid, 256, 0, st>>>(W, s, N, K, gram, grid, qweight, scales, zeros, clip_index);
   } else {
     gram_partial_kernel<64><<<dim3((unsigned)G, (unsigned)P), 256, 0, st>>>(A, M, K, gram_partial);
-    gram_reduce_kernel<64><<<(unsigned)G, 256, 0, st>>>(gram_partial, (int)P, gram);
+    gram_frag_kernel<64><<<dim3((unsigned)G, pairs), 256, 0, st>>>(gram_partial, (int)P, gram);
     if (zeros)
-      clip_select_kernel<64, false><<<cgrid, 64 * kClipWaves, 0, st>>>(W, s, N, K, gram, grid, rpb, qweight, scales, zeros, clip_index);
+      clip_select_kernel<64, false><<<cgrid, 256, 0, st>>>(W, s, N, K, gram, grid, qweight, scales, zeros, clip_index);
     else
-      clip_select_kernel<64, true><<<cgrid, 64 * kClipWaves, 0, st>>>(W, s, N, K, gram, grid, rpb, qweight, scales, zeros, clip_index);
+      clip_select_kernel<64, true><<<cgrid, 256, 0, st>>>(W, s, N, K, gram, grid, qweight, scales, zeros, clip_index);
   }
   return hipGetLastError();
 }

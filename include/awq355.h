@@ -355,7 +355,8 @@ awq_status awq_scale_search(const void *X, const void *W, int64_t M, int64_t N,
  *               evaluated in fp64 through A_g^T A_g; the first minimum wins
  *               ("Apply weight clipping").  The packed result is that of the
  *               chosen factors; the losses stay those of the unclipped
- *               candidates. */
+ *               candidates.  K/g must not exceed 65535 (else
+ *               AWQ_ERR_UNSUPPORTED). */
 typedef struct awq_search_options {
     int32_t duo_scaling;
     int32_t apply_clip;

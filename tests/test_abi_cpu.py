@@ -253,6 +253,10 @@ def test_search_options_validation():
     assert size(4096, 4096, O(0, 1)) >= plain + 32 * 128 * 128 * 8
     assert size(4096, 4096, O(2, 0)) == 0
     assert size(4096, 1 << 24, O(1, 0)) == 0         # duo: N < 2^24 rows of W
+    # clipping: at most 65535 groups (K = 65536 * 128 has one too many)
+    assert lib.awq_scale_search_workspace_size_ex(64, 1, 65536 * 128, cfg(128), 20,
+                                                  ctypes.byref(O(0, 1))) == 0
+    assert b"65535 groups" in lib.awq_last_error()
     best = ctypes.c_int32(-1)
     o = O(0, 3)
     st = lib.awq_scale_search_ex(FAKE, FAKE, 64, 64, 256, cfg(128), None, 20, ctypes.byref(o),
