@@ -13,7 +13,8 @@ _API = (
     "awq_linear_workspace_size", "awq_scale_search",
     "awq_scale_search_workspace_size", "AwqError", "config", "empty_packed", "lib",
     "AWQ_F16", "AWQ_BF16", "AWQ_F32", "AWQ_KERNEL_AUTO", "AWQ_KERNEL_GEMV",
-    "AWQ_KERNEL_GEMM", "AWQ_GEMV_MAX_M", "EXPORTS", "LIB_PATH",
+    "AWQ_KERNEL_GEMM", "AWQ_KERNEL_BATCHED", "AWQ_GEMV_MAX_M", "AWQ_BATCHED_MAX_M", "EXPORTS",
+    "LIB_PATH",
 )
 
 __all__ = list(_API)

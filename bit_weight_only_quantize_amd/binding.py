@@ -26,10 +26,11 @@ AWQ_ERR_HIP = 4
 AWQ_ERR_NONFINITE = 5
 
 AWQ_F16, AWQ_BF16, AWQ_F32 = 0, 1, 2
-AWQ_KERNEL_AUTO, AWQ_KERNEL_GEMV, AWQ_KERNEL_GEMM = 0, 1, 2
+AWQ_KERNEL_AUTO, AWQ_KERNEL_GEMV, AWQ_KERNEL_GEMM, AWQ_KERNEL_BATCHED = 0, 1, 2, 3
 AWQ_EPILOGUE_NONE, AWQ_EPILOGUE_SILU_MUL = 0, 1
 AWQ_MAX_PARTS = 4
 AWQ_GEMV_MAX_M = 16
+AWQ_BATCHED_MAX_M = 64
 
 #: Every symbol include/awq355.h declares.
 EXPORTS = (

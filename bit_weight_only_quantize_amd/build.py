@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = [
     "quantize_pack.hip",
     "linear_gemv.hip",
+    "linear_batched.hip",
     "linear_gemm.hip",
     "gemm_f16.hip",
     "search.hip",

@@ -51,6 +51,22 @@ bool auto_gemv(int64_t M, int64_t N, int64_t K, int g) {
   return M <= 8 || (M <= 12 && N * K <= 50000000);
 }
 
+// Automatic choice of the batched-decode kernel (with scratch for its
+// partials): where the GEMV cannot stage the activation rows, for 2 <= M <= 32
+// on layers of at least 4e7 weights and 5000 columns.  Same-box graph replays
+// (us; batched / GEMV / GEMM, g = 128 unless noted): 13824 x 5120 at M = 8
+// 17.0 / 21.2 / 20.5 and M = 16 17.4 / 28.0 / 20.9; 5120 x 13824 at M = 4
+// 18.7 / 22.4 / 21.1 and M = 16 19.0 / 34.5 / 21.6; g = 64, 13824 x 5120 at
+// M = 32 25.9 / - / 29.5; 11008 x 4096 at M = 16 15.3 / 17.9 / 16.6.  On 4096
+// x 4096 and 4096 x 11008 (N = 4096) the GEMV or the GEMM was as fast or
+// faster, and at M = 64 the GEMM (whose splits need fewer workgroups).
+bool auto_batched(int64_t M, int64_t N, int64_t K, int g) {
+  if (M < 2 || M > 32 || N < 5000 || N * K < 40000000) return false;
+  if (!awq::batched_gemv_supported(M, N, K, g)) return false;
+  return !(M <= AWQ_GEMV_MAX_M && awq::gemv_supported(M, N, K, g) &&
+           awq::gemv_stages_activations(M, N, K));
+}
+
 awq_status check_config(awq_config cfg, int64_t K) {
   if (cfg.w_bit != 4) return fail(AWQ_ERR_UNSUPPORTED, "w_bit=%d: only 4 is supported", cfg.w_bit);
   if (cfg.zero_point != 0 && cfg.zero_point != 1)
@@ -83,11 +99,15 @@ awq_status check_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,
   if (y_dtype != AWQ_F16 && y_dtype != AWQ_BF16 && y_dtype != AWQ_F32)
     return fail(AWQ_ERR_INVALID_ARG, "y_dtype=%d: must be AWQ_F16, AWQ_BF16 or AWQ_F32",
                 y_dtype);
-  if (kernel != AWQ_KERNEL_AUTO && kernel != AWQ_KERNEL_GEMV && kernel != AWQ_KERNEL_GEMM)
+  if (kernel != AWQ_KERNEL_AUTO && kernel != AWQ_KERNEL_GEMV && kernel != AWQ_KERNEL_GEMM &&
+      kernel != AWQ_KERNEL_BATCHED)
     return fail(AWQ_ERR_INVALID_ARG, "kernel=%d: unknown kernel selector", kernel);
   if (kernel == AWQ_KERNEL_GEMV && M > AWQ_GEMV_MAX_M)
     return fail(AWQ_ERR_INVALID_ARG, "GEMV kernel serves M <= %d, got M=%lld", AWQ_GEMV_MAX_M,
                 (long long)M);
+  if (kernel == AWQ_KERNEL_BATCHED && M > AWQ_BATCHED_MAX_M)
+    return fail(AWQ_ERR_INVALID_ARG, "batched kernel serves M <= %d, got M=%lld",
+                AWQ_BATCHED_MAX_M, (long long)M);
   if (M == 0 || N == 0) return AWQ_OK;
   if (!awq::gemm_supported(N, K, false))
     return fail(AWQ_ERR_UNSUPPORTED, "layer of %lld x %lld exceeds 2 GiB of packed weights",
@@ -238,9 +258,19 @@ awq_status awq_dequantize(const uint32_t *qweight, const uint16_t *scales, const
 
 namespace {
 
-// Whether the automatic choice (or the explicit `kernel`) runs the GEMV.
-bool runs_gemv(int64_t M, int64_t N, int64_t K, int gs, int32_t kernel) {
-  return kernel == AWQ_KERNEL_GEMV || (kernel == AWQ_KERNEL_AUTO && auto_gemv(M, N, K, gs));
+// Whether the automatic choice (or the explicit `kernel`) runs the batched-
+// decode kernel.  The automatic choice takes it only with scratch for its
+// split-K partials (awq_linear, which has none, never splits K).
+bool runs_batched(int64_t M, int64_t N, int64_t K, int gs, int32_t kernel, bool has_scratch) {
+  if (kernel == AWQ_KERNEL_BATCHED) return true;
+  return kernel == AWQ_KERNEL_AUTO && has_scratch && auto_batched(M, N, K, gs);
+}
+
+// Whether it runs the GEMV (the batched kernel, when chosen, comes first).
+bool runs_gemv(int64_t M, int64_t N, int64_t K, int gs, int32_t kernel, bool has_scratch) {
+  if (kernel == AWQ_KERNEL_GEMV) return true;
+  return kernel == AWQ_KERNEL_AUTO && !runs_batched(M, N, K, gs, kernel, has_scratch) &&
+         auto_gemv(M, N, K, gs);
 }
 
 // The linear layer with the GEMM's scratch from the caller's workspace, or
@@ -263,10 +293,26 @@ awq_status linear_impl(const char *who, const void *X, int32_t x_dtype, const ui
                         : y_dtype == AWQ_BF16 ? awq::YType::BF16
                                               : awq::YType::F32;
   const hipStream_t hs = as_stream(stream);
-  if (runs_gemv(M, N, K, cfg.group_size, kernel))
+  if (runs_gemv(M, N, K, cfg.group_size, kernel, workspace != nullptr))
     return hip_status(awq::launch_gemv(X, xt, qweight, scales, cfg.zero_point ? zeros : nullptr, M, N, K, cfg.group_size, Y,
                                        yt, hs),
                       who);
+  if (runs_batched(M, N, K, cfg.group_size, kernel, workspace != nullptr)) {
+    const awq::BatchedPlan bp = awq::batched_gemv_plan(
+        M, N, K, cfg.group_size, workspace ? awq::Scratch::Full : awq::Scratch::None);
+    if (bp.partial_bytes > 0 && !workspace)
+      return fail(AWQ_ERR_WORKSPACE,
+                  "%s: the batched kernel splits this K and needs a workspace of %zu bytes "
+                  "(awq_linear_workspace_size)",
+                  who, bp.partial_bytes);
+    if (bp.partial_bytes > workspace_bytes)
+      return fail(AWQ_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who,
+                  workspace_bytes, bp.partial_bytes);
+    return hip_status(awq::launch_batched_gemv(X, xt, qweight, scales,
+                                               cfg.zero_point ? zeros : nullptr, M, N, K,
+                                               cfg.group_size, Y, yt, bp, workspace, hs),
+                      who);
+  }
   const awq::GemmPlan plan =
       awq::gemm_plan(M, N, K, xt, workspace ? awq::Scratch::Full : awq::Scratch::None);
   if (plan.workspace_bytes > 0) {
@@ -299,10 +345,14 @@ size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg
   if (check_config(cfg, K) != AWQ_OK || M < 0 || N < 0) return 0;
   if (M > ((int64_t)1 << 31) || N > ((int64_t)1 << 31)) return 0;
   if (x_dtype != AWQ_F16 && x_dtype != AWQ_BF16) return 0;
-  if (kernel != AWQ_KERNEL_AUTO && kernel != AWQ_KERNEL_GEMV && kernel != AWQ_KERNEL_GEMM)
+  if (kernel != AWQ_KERNEL_AUTO && kernel != AWQ_KERNEL_GEMV && kernel != AWQ_KERNEL_GEMM &&
+      kernel != AWQ_KERNEL_BATCHED)
     return 0;
-  if (M == 0 || N == 0 || runs_gemv(M, N, K, cfg.group_size, kernel)) return 0;
+  if (kernel == AWQ_KERNEL_BATCHED && M > AWQ_BATCHED_MAX_M) return 0;
+  if (M == 0 || N == 0 || runs_gemv(M, N, K, cfg.group_size, kernel, true)) return 0;
   if (!awq::gemm_supported(N, K, false)) return 0;
+  if (runs_batched(M, N, K, cfg.group_size, kernel, true))
+    return awq::batched_gemv_plan(M, N, K, cfg.group_size, awq::Scratch::Full).partial_bytes;
   const awq::XType xt = x_dtype == AWQ_F16 ? awq::XType::F16 : awq::XType::BF16;
   return awq::gemm_plan(M, N, K, xt, awq::Scratch::Full).workspace_bytes;
 }
@@ -342,6 +392,8 @@ awq_status check_fused(const void *X, int32_t x_dtype, const awq_linear_part *pa
     return fail(AWQ_ERR_INVALID_ARG, "epilogue=%d: unknown", epilogue);
   if (epilogue == AWQ_EPILOGUE_SILU_MUL && (n_parts != 2 || parts[0].N != parts[1].N))
     return fail(AWQ_ERR_INVALID_ARG, "the SiLU-mul epilogue takes 2 parts of equal N");
+  if (kernel == AWQ_KERNEL_BATCHED)
+    return fail(AWQ_ERR_INVALID_ARG, "fused projections take AWQ_KERNEL_AUTO, _GEMV or _GEMM");
   for (int i = 0; i < n_parts; ++i) {
     // each part is checked as a linear call of its own (the output pointer
     // is H for the SiLU-mul epilogue)
@@ -503,10 +555,23 @@ awq_status awq_linear_noalloc(const void *X, int32_t x_dtype, const uint32_t *qw
                         : y_dtype == AWQ_BF16 ? awq::YType::BF16
                                               : awq::YType::F32;
   const hipStream_t hs = as_stream(stream);
-  if (runs_gemv(M, N, K, cfg.group_size, AWQ_KERNEL_AUTO))
+  if (runs_gemv(M, N, K, cfg.group_size, AWQ_KERNEL_AUTO, true))
     return hip_status(awq::launch_gemv(X, xt, qweight, scales, cfg.zero_point ? zeros : nullptr, M, N, K, cfg.group_size, Y,
                                        yt, hs),
                       who);
+  if (runs_batched(M, N, K, cfg.group_size, AWQ_KERNEL_AUTO, true)) {
+    const awq::BatchedPlan bp =
+        awq::batched_gemv_plan(M, N, K, cfg.group_size, awq::Scratch::Bounded);
+    void *ws = nullptr;
+    if (bp.partial_bytes > 0) {
+      st = static_scratch(&ws);
+      if (st != AWQ_OK) return st;
+    }
+    return hip_status(awq::launch_batched_gemv(X, xt, qweight, scales,
+                                               cfg.zero_point ? zeros : nullptr, M, N, K,
+                                               cfg.group_size, Y, yt, bp, ws, hs),
+                      who);
+  }
   const awq::GemmPlan plan = awq::gemm_plan(M, N, K, xt, awq::Scratch::Bounded);
   if (plan.workspace_bytes > kStaticScratchBytes)
     return fail(AWQ_ERR_WORKSPACE,

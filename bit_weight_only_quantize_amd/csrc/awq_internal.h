@@ -99,6 +99,21 @@ hipError_t launch_gemm_f16(const uint16_t *X, bool bf16, const uint32_t *qweight
                            int64_t K, int gs, void *Y, YType yt, const GemmPlan &plan,
                            void *workspace, hipStream_t st);
 
+// ---- linear_batched.hip (batched decode, M <= 64) ---------------------------------
+// Workgroups of 256 columns over a range of gps groups of K (a split); with
+// splits > 1 each writes fp32 partials ([split][M][N], partial_bytes of
+// workspace) that a second kernel sums in split order.
+struct BatchedPlan {
+  int splits, gps;
+  size_t partial_bytes;    // 0 when splits == 1
+};
+bool batched_gemv_supported(int64_t M, int64_t N, int64_t K, int gs);
+BatchedPlan batched_gemv_plan(int64_t M, int64_t N, int64_t K, int gs, Scratch sc);
+hipError_t launch_batched_gemv(const void *X, XType xt, const uint32_t *qweight,
+                               const uint16_t *scales, const uint8_t *zeros, int64_t M, int64_t N,
+                               int64_t K, int gs, void *Y, YType yt, const BatchedPlan &plan,
+                               void *workspace, hipStream_t st);
+
 // linear_gemm.hip: H = silu(A) * B elementwise over n fp32 values, rounded to yt.
 hipError_t launch_silu_mul(const float *A, const float *B, int64_t n, void *H, YType yt,
                            hipStream_t st);

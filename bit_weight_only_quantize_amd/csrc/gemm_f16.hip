@@ -617,6 +617,59 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   }
   constexpr int ysz = YT == (int)YType::F32 ? 4 : 2;
   const rsrc_t rY = make_rsrc(Y, (uint32_t)M * (uint32_t)N * (uint32_t)ysz);
+  if constexpr (YT != (int)YType::F32 && MT >= 8) {
+    // 16-bit output of the 128- and 256-row tiles through LDS: an MFMA result
+    // lane holds 4 rows of one column, so direct stores write 32-byte pieces
+    // of 4 rows each (measured about twice the bytes of Y reaching HBM).
+    // Each wave turns its 64 columns, half the rows at a time, into rows of
+    // 128 bytes in LDS (rows 144 bytes apart: the 4 row groups of a store
+    // start 16 banks apart) and stores them as whole 16-byte pieces, 8 lanes
+    // per row.  Waves 0-1 use sA0, waves 2-3 sA1, once every wave is past
+    // the main loop.
+    constexpr int kRowB = 64 * 2 + 16;
+    constexpr int kHalf = kBM / 2;
+    static_assert(2 * kHalf * kRowB <= kBM * kBK * 2, "epilogue staging exceeds the A buffers");
+    __syncthreads();
+    char *region = reinterpret_cast<char *>(wave < 2 ? sA0 : sA1) + (wave & 1) * kHalf * kRowB;
+    const int nb = col0 + wave * 64;
+    const bool vec = (N & 7) == 0;                      // 16-byte aligned rows of Y
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = h * (MT / 2); i < (h + 1) * (MT / 2); ++i)
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = (i - h * (MT / 2)) * 16 + 4 * kq + e;
+            const float v = acc[i][j][e];
+            *reinterpret_cast<uint16_t *>(region + r * kRowB + (16 * j + c) * 2) =
+                YT == (int)YType::F16 ? float_to_half_bits(v) : float_to_bf16_bits(v);
+          }
+      __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): this wave's writes landed
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < kHalf / 8; ++it) {
+        const int r = it * 8 + (lane >> 3), q = lane & 7;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(region + r * kRowB + q * 16);
+        const int m = row0 + h * kHalf + r, n = nb + 8 * q;
+        if (m >= M || n >= N) continue;
+        const uint32_t o = ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u;
+        if (vec && n + 8 <= N) {
+          __builtin_amdgcn_raw_buffer_store_b128(v, rY, o, 0, 0);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (n + t < N)
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(v[t >> 1] >> (16 * (t & 1))), rY,
+                                                    o + 2u * t, 0, 0);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);                // reads done before the next half
+      __builtin_amdgcn_wave_barrier();
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < kNT; ++j) {
     const int n = col0 + wave * 64 + j * 16 + c;

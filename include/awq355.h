@@ -70,14 +70,19 @@ typedef enum awq_status {
 enum { AWQ_F16 = 0, AWQ_BF16 = 1, AWQ_F32 = 2 };
 
 /* Kernel selection for awq_linear_ex (int32_t in signatures).  The pages'
- * `version` knob (GEMM / GEMV) becomes a dispatch on M in awq_linear. */
-enum { AWQ_KERNEL_AUTO = 0, AWQ_KERNEL_GEMV = 1, AWQ_KERNEL_GEMM = 2 };
+ * `version` knob (GEMM / GEMV) becomes a dispatch on M in awq_linear.
+ * AWQ_KERNEL_BATCHED is the batched-decode kernel between the two (M <=
+ * AWQ_BATCHED_MAX_M): the GEMV's exact arithmetic with 256 output columns
+ * per workgroup sharing each staged chunk of activations. */
+enum { AWQ_KERNEL_AUTO = 0, AWQ_KERNEL_GEMV = 1, AWQ_KERNEL_GEMM = 2, AWQ_KERNEL_BATCHED = 3 };
 
 typedef void *awq_stream_t;
 
 /* Upper bound on M for the GEMV kernel (awq_linear dispatches M <= this to
  * it; awq_linear_ex(AWQ_KERNEL_GEMV) rejects larger M). */
 #define AWQ_GEMV_MAX_M 16
+/* Upper bound on M for AWQ_KERNEL_BATCHED. */
+#define AWQ_BATCHED_MAX_M 64
 
 /*
  * awq_quantize_pack - scale, group-quantize and pack a weight matrix.
@@ -171,7 +176,12 @@ awq_status awq_linear(const void *X, int32_t x_dtype, const uint32_t *qweight,
  * "WQLinear Kernel Variants").
  *
  *   kernel     AWQ_KERNEL_AUTO (awq_linear's choice), AWQ_KERNEL_GEMV
- *            (requires M <= AWQ_GEMV_MAX_M, else AWQ_ERR_INVALID_ARG) or
+ *            (requires M <= AWQ_GEMV_MAX_M, else AWQ_ERR_INVALID_ARG),
+ *            AWQ_KERNEL_BATCHED (requires M <= AWQ_BATCHED_MAX_M, else
+ *            AWQ_ERR_INVALID_ARG; it splits K into ranges of at most
+ *            2048 / (g * ceil(M / 16)) groups, more when that leaves CUs
+ *            idle, and its fp32 partials need the workspace: without one,
+ *            a layer of more than one range returns AWQ_ERR_WORKSPACE) or
  *            AWQ_KERNEL_GEMM.
  *   workspace  device, 256-byte aligned, at least
  *            awq_linear_workspace_size(M, N, K, cfg, x_dtype, kernel) bytes,
@@ -193,9 +203,10 @@ awq_status awq_linear_ex(const void *X, int32_t x_dtype, const uint32_t *qweight
  * the output tiles alone cannot fill the GPU (K is then split across
  * workgroups and a second kernel sums the parts in a fixed order), and for
  * bf16 activations a factor per row (and, for shapes large enough for the
- * 256-row tile, an fp16 copy of X, M * K * 2 bytes).  0 when the call needs
- * none (the GEMV, or an fp16 GEMM that fills the GPU unsplit), and 0 on
- * invalid arguments.
+ * 256-row tile, an fp16 copy of X, M * K * 2 bytes).  The batched-decode
+ * kernel needs splits * M * N * 4 bytes of fp32 partials when it splits K.
+ * 0 when the call needs none (the GEMV, or an fp16 GEMM that fills the GPU
+ * unsplit), and 0 on invalid arguments.
  */
 size_t awq_linear_workspace_size(int64_t M, int64_t N, int64_t K, awq_config cfg,
                                  int32_t x_dtype, int32_t kernel);

@@ -98,6 +98,7 @@ def test_fused_validation():
     assert call(n=0) == binding.AWQ_ERR_INVALID_ARG
     assert call(n=5) == binding.AWQ_ERR_INVALID_ARG
     assert call(epi=2) == binding.AWQ_ERR_INVALID_ARG
+    assert call(kernel=binding.AWQ_KERNEL_BATCHED) == binding.AWQ_ERR_INVALID_ARG
     assert call(n=3, epi=1, H=FAKE) == binding.AWQ_ERR_INVALID_ARG     # the pair is 2 parts
     arr[1].N = 65
     assert call(epi=1, H=FAKE) == binding.AWQ_ERR_INVALID_ARG          # of equal N
@@ -123,6 +124,7 @@ def test_linear_validation():
     assert _lin(yt=7) == binding.AWQ_ERR_INVALID_ARG
     assert _lin(kernel=5) == binding.AWQ_ERR_INVALID_ARG
     assert _lin(M=17, kernel=binding.AWQ_KERNEL_GEMV) == binding.AWQ_ERR_INVALID_ARG
+    assert _lin(M=65, kernel=binding.AWQ_KERNEL_BATCHED) == binding.AWQ_ERR_INVALID_ARG
     assert _lin(M=-2) == binding.AWQ_ERR_INVALID_ARG
     assert _lin(K=100) == binding.AWQ_ERR_INVALID_ARG
     assert _lin(c=cfg(128, w_bit=8)) == binding.AWQ_ERR_UNSUPPORTED
@@ -156,6 +158,10 @@ def test_linear_workspace_size_and_validation():
     # factors and an fp16 copy of X for bf16
     assert _wsz(4096, 28672, 8192) == 0
     assert _wsz(4096, 28672, 8192, xd=1) >= 4096 * 8192 * 2 + 4096 * 4
+    # the batched-decode kernel splits K into fp32 partials [split][M][N]
+    bw = _wsz(16, 13824, 5120, kernel=binding.AWQ_KERNEL_BATCHED)
+    assert bw > 0 and bw % (16 * 13824 * 4) == 0
+    assert _wsz(65, 13824, 5120, kernel=binding.AWQ_KERNEL_BATCHED) == 0
     assert _wsz(64, 13824, 100) == 0           # invalid K
     assert _wsz(0, 13824, 5120) == 0
     assert _wsz(64, 13824, 5120, xd=2) == 0    # fp32 activations are not W4A16
@@ -199,23 +205,38 @@ def test_noalloc_rejects_beyond_its_static_scratch():
 
 
 def test_linear_dispatch_rule():
-    """awq_linear's GEMV/GEMM choice (host logic, no GPU): the GEMV, which
-    needs no workspace, wherever its activation rows fit in LDS (64 KiB, or
-    128 KiB when N <= 4096); unstaged, the GEMM where a GEMV wave would walk
-    more than 8 groups, else the GEMV up to M = 8, or 12 for layers of at
-    most 5e7 weights.  (A bf16 GEMM always needs a workspace, so a zero size
-    means the GEMV.)"""
-    ws = lambda M, N, K: _wsz(M, N, K, xd=1)
-    assert ws(2, 5120, 13824) == 0          # 55 KiB of rows: staged
-    assert ws(4, 5120, 13824) > 0           # unstaged, 108 groups over 8 waves
-    assert ws(8, 11008, 4096) == 0          # 64 KiB: staged
-    assert ws(12, 11008, 4096) == 0         # unstaged, 4.5e7 weights, M <= 12
-    assert ws(16, 11008, 4096) > 0          # unstaged, 4.5e7 weights, M > 12
-    assert ws(12, 13824, 5120) > 0          # unstaged, 7.1e7 weights, M > 8
-    assert ws(8, 13824, 5120) == 0          # unstaged, M <= 8, 5 groups per wave
-    assert ws(16, 4096, 4096) == 0          # 128 KiB: staged (16-wave workgroups)
-    assert ws(6, 4096, 11008) == 0          # unstaged, 4.5e7 weights
-    assert ws(17, 4096, 4096) > 0           # beyond the GEMV's 16 rows
+    """The automatic kernel choice of a call with scratch (awq_linear_ws,
+    awq_linear_ex with a workspace; host logic, no GPU): the GEMV wherever its
+    activation rows fit in LDS (64 KiB, or 128 KiB when N <= 4096); else the
+    batched-decode kernel for 2 <= M <= 32 on layers of at least 4e7 weights
+    and 5000 columns; else, unstaged, the GEMM where a GEMV wave would walk
+    more than 8 groups, the GEMV up to M = 8 (12 on layers of at most 5e7
+    weights), the GEMM beyond.  The kernel is read off the workspace size
+    (bf16 activations: the GEMM always needs one, the GEMV none, the batched
+    kernel exactly its own)."""
+    B = binding.AWQ_KERNEL_BATCHED
+
+    def kind(M, N, K):
+        a = _wsz(M, N, K, xd=1)
+        if a == 0:
+            return "gemv"
+        if a == _wsz(M, N, K, xd=1, kernel=B):
+            return "batched"
+        assert a == _wsz(M, N, K, xd=1, kernel=binding.AWQ_KERNEL_GEMM)
+        return "gemm"
+    assert kind(2, 5120, 13824) == "gemv"       # 55 KiB of rows: staged
+    assert kind(4, 5120, 13824) == "batched"    # unstaged, 7.1e7 weights
+    assert kind(8, 11008, 4096) == "gemv"       # 64 KiB: staged
+    assert kind(12, 11008, 4096) == "batched"   # unstaged, 4.5e7 weights, N >= 5000
+    assert kind(8, 13824, 5120) == "batched"
+    assert kind(32, 13824, 5120) == "batched"
+    assert kind(33, 13824, 5120) == "gemm"      # beyond 32 rows
+    assert kind(16, 4096, 4096) == "gemv"       # 128 KiB: staged (16-wave workgroups)
+    assert kind(6, 4096, 11008) == "gemv"       # N < 5000: unstaged GEMV, M <= 8
+    assert kind(16, 4096, 11008) == "gemm"      # N < 5000, M > 12
+    assert kind(17, 4096, 4096) == "gemm"       # beyond the GEMV's 16 rows
+    assert kind(12, 3000, 20480) == "gemm"      # N < 5000: 10 groups per GEMV wave
+    assert kind(4, 6000, 4096) == "gemv"        # 2.5e7 weights: staged
 
 
 def test_search_workspace_and_validation():

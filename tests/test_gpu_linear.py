@@ -10,7 +10,7 @@ from oracle import (QuantConfig, bf16_bits_to_f32, dequantize, gate_up_silu64, l
 
 pytestmark = pytest.mark.gpu
 
-GEMV, GEMM = 1, 2
+GEMV, GEMM, BATCHED = 1, 2, 3
 
 
 def _awq():
@@ -45,15 +45,17 @@ def _run(X, dt, packed_dev, g, kernel, out_dtype=None):
 
 # --- exactness pin: one-hot activations reproduce dequantized weights -------------
 
-@pytest.mark.parametrize("path", ["gemv", "gemm32", "gemm_large"])
+@pytest.mark.parametrize("path", ["gemv", "gemm32", "gemm_large", "batched"])
 @pytest.mark.parametrize("g", [64, 128])
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_one_hot_rows_are_exact(path, g, dt):
-    """X = rows of the identity.  GEMV and the GEMM's 32-row tile (batches of
-    up to 32 rows): Y[r][n] = deq[n][k_r] exactly in fp32 (their B operand is
-    the exact integer q - z, the scale applied to fp32 sums).  Larger GEMM
-    tiles: Y[r][n] = fp16(deq[n][k_r]) exactly, the dequantized weight
-    rounded once to fp16 (their B operand)."""
+    """X = rows of the identity.  GEMV, the batched-decode kernel (also
+    through its split-K partials: every other group contributes an exact 0)
+    and the GEMM's 32-row tile (batches of up to 32 rows): Y[r][n] =
+    deq[n][k_r] exactly in fp32 (their B operand is the exact integer q - z,
+    the scale applied to fp32 sums).  Larger GEMM tiles: Y[r][n] =
+    fp16(deq[n][k_r]) exactly, the dequantized weight rounded once to fp16
+    (their B operand)."""
     torch = torch_mod()
     N, K = 80, 512
     W = wl.gen_weight(N, K, 17)
@@ -61,8 +63,8 @@ def test_one_hot_rows_are_exact(path, g, dt):
     deq = dequantize(unpack_codes(qw, K), sc, zr, g)
     if path == "gemm_large":
         deq = deq.astype(np.float16).astype(np.float64)
-    rows = {"gemv": 16, "gemm32": 32, "gemm_large": K}[path]
-    kernel = GEMV if path == "gemv" else GEMM
+    rows = {"gemv": 16, "gemm32": 32, "gemm_large": K, "batched": 64}[path]
+    kernel = {"gemv": GEMV, "batched": BATCHED}.get(path, GEMM)
     ks = np.arange(0, K, 37) if path == "gemv" else np.arange(K)
     for k0 in range(0, len(ks), rows):
         sel = ks[k0:k0 + rows]
@@ -101,9 +103,9 @@ def test_ragged_shapes(M, N, K, g, dt):
     X = wl.gen_activation(M, K, 50 + M, 51, dt)
     qw, sc, zr, pd = _packed(W, g)
     ref = linear64(_x_f64(X, dt), qw, sc, zr, g)
-    kernels = [GEMM] + ([GEMV] if M <= 16 else [])
+    kernels = [GEMM] + ([GEMV] if M <= 16 else []) + ([BATCHED] if M <= 64 else [])
     for kern in kernels:
-        say("ragged", M, N, K, g, dt, "gemv" if kern == GEMV else "gemm")
+        say("ragged", M, N, K, g, dt, {GEMV: "gemv", GEMM: "gemm", BATCHED: "batched"}[kern])
         Y32 = out_to_f64(_run(X, dt, pd, g, kern, torch.float32))
         assert_close(Y32, ref, f"{M}x{N}x{K} fp32 out")
         Y16 = out_to_f64(_run(X, dt, pd, g, kern))          # same dtype as X
@@ -415,6 +417,32 @@ def test_batched_gemm_layers(case):
     assert_close(out_to_f64(_run(X, "f16", pd, case.group_size, 0)), ref, case.name)
 
 
+@pytest.mark.parametrize("case", wl.gemm_cases(Ms=(16, 64)), ids=lambda c: c.name)
+def test_batched_decode_kernel_layers(case):
+    """The batched-decode kernel on the 13B-class layers at M = 16 and 64,
+    K split (partials summed in split order), against the oracle; repeated
+    calls are bit-identical.  Without a workspace these K need more than one
+    split, and the call says so (AWQ_ERR_WORKSPACE) rather than running."""
+    torch = torch_mod()
+    awq = _awq()
+    W = case.weight()
+    X = case.activation()
+    qw, sc, zr, pd = _packed(W, case.group_size)
+    ref = linear64(X, qw, sc, zr, case.group_size)
+    Xd = to_dev(X)
+    say("batched kernel layer", case.name)
+    a = awq.awq_linear_ex(Xd, *pd, kernel=BATCHED, group_size=case.group_size,
+                          out_dtype=torch.float32)
+    b = awq.awq_linear_ex(Xd, *pd, kernel=BATCHED, group_size=case.group_size,
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert_close(out_to_f64(a), ref, case.name)
+    with pytest.raises(awq.AwqError) as e:
+        awq.awq_linear_ex(Xd, *pd, kernel=BATCHED, group_size=case.group_size, workspace=None)
+    assert e.value.status == 3      # AWQ_ERR_WORKSPACE
+
+
 @pytest.mark.parametrize("case", wl.prefill_cases(), ids=lambda c: c.name)
 def test_prefill_layers_sampled(case):
     """M=4096 prefill on 70B-class layers: every output is computed on the GPU;
@@ -531,7 +559,7 @@ def test_symmetric_ragged(M, N, K, g, dt):
     X = wl.gen_activation(M, K, 181 + M, 182, dt)
     qw, sc, zr, pd = _packed(W, g, zero_point=False)
     ref = linear64(_x_f64(X, dt), qw, sc, None, g)
-    for kern in [GEMM] + ([GEMV] if M <= 16 else []):
+    for kern in [GEMM] + ([GEMV] if M <= 16 else []) + ([BATCHED] if M <= 64 else []):
         say("symmetric ragged", M, N, K, g, dt, kern)
         Y = _run(X, dt, pd, g, kern, torch.float32)
         assert_close(out_to_f64(Y), ref, f"sym {M}x{N}x{K}")
