@@ -408,6 +408,12 @@ awq_status check_fused(const void *X, int32_t x_dtype, const awq_linear_part *pa
   return AWQ_OK;
 }
 
+// Whether a part of a fused call that does not run the GEMV runs the
+// batched-decode kernel (the automatic choice with scratch) or the GEMM.
+bool fused_part_batched(int64_t M, int64_t N, int64_t K, int gs, int32_t kernel) {
+  return kernel == AWQ_KERNEL_AUTO && auto_batched(M, N, K, gs);
+}
+
 FusedLayout fused_layout(const awq_linear_part *parts, int32_t n_parts, int64_t M, int64_t K,
                          awq_config cfg, awq::XType xt, int32_t epilogue, int32_t kernel) {
   FusedLayout L{};
@@ -424,7 +430,12 @@ FusedLayout fused_layout(const awq_linear_part *parts, int32_t n_parts, int64_t 
   if (L.gemv || M == 0 || ntot == 0) return L;
   for (int i = 0; i < n_parts; ++i) {
     if (parts[i].N == 0) continue;
-    const size_t b = awq::gemm_plan(M, parts[i].N, K, xt, awq::Scratch::Full).workspace_bytes;
+    // each part on its own: the batched-decode kernel where the automatic
+    // choice takes it, else the GEMM; the parts run in turn and share scratch
+    const size_t b =
+        fused_part_batched(M, parts[i].N, K, cfg.group_size, kernel)
+            ? awq::batched_gemv_plan(M, parts[i].N, K, cfg.group_size, awq::Scratch::Full).partial_bytes
+            : awq::gemm_plan(M, parts[i].N, K, xt, awq::Scratch::Full).workspace_bytes;
     L.gemm_ws = b > L.gemm_ws ? b : L.gemm_ws;
   }
   if (pair) {
@@ -486,10 +497,18 @@ awq_status awq_linear_fused(const void *X, int32_t x_dtype, const awq_linear_par
   hipError_t e = hipSuccess;
   for (int i = 0; i < n_parts && e == hipSuccess; ++i) {
     if (lp[i].N == 0) continue;
-    const awq::GemmPlan plan = awq::gemm_plan(M, lp[i].N, K, xt, awq::Scratch::Full);
     void *y = pair ? (void *)(ws + (i == 0 ? L.gate_off : L.up_off)) : lp[i].Y;
+    const awq::YType pyt = pair ? awq::YType::F32 : yt;
+    if (fused_part_batched(M, lp[i].N, K, cfg.group_size, kernel)) {
+      const awq::BatchedPlan bp =
+          awq::batched_gemv_plan(M, lp[i].N, K, cfg.group_size, awq::Scratch::Full);
+      e = awq::launch_batched_gemv(X, xt, lp[i].qweight, lp[i].scales, lp[i].zeros, M, lp[i].N,
+                                   K, cfg.group_size, y, pyt, bp, scratch, hs);
+      continue;
+    }
+    const awq::GemmPlan plan = awq::gemm_plan(M, lp[i].N, K, xt, awq::Scratch::Full);
     e = awq::launch_gemm(X, xt, lp[i].qweight, lp[i].scales, lp[i].zeros, M, lp[i].N, K,
-                         cfg.group_size, y, pair ? awq::YType::F32 : yt, plan, scratch, hs);
+                         cfg.group_size, y, pyt, plan, scratch, hs);
   }
   if (e == hipSuccess && pair)
     e = awq::launch_silu_mul(reinterpret_cast<const float *>(ws + L.gate_off),

@@ -593,11 +593,14 @@ def test_fused_qkv_parts(M, kernel, zp):
 
 
 @pytest.mark.parametrize("M,kernel,dt", [(1, 0, "f16"), (4, 0, "f16"), (4, 0, "bf16"), (16, GEMV, "f16"),
-                                         (64, 0, "f16"), (300, 0, "bf16"), (2, GEMM, "f16")])
+                                         (16, 0, "f16"), (24, 0, "bf16"), (64, 0, "f16"),
+                                         (300, 0, "bf16"), (2, GEMM, "f16")])
 def test_fused_gate_up_silu(M, kernel, dt):
     """The 7B-class MLP's gate and up projections (N = 11008, K = 4096) with
     the SiLU-mul epilogue: H = silu(X Wg^T) * (X Wu^T) against the fp64 oracle,
-    fp32 and 16-bit output (the 16-bit output is the fp32 result rounded once)."""
+    fp32 and 16-bit output (the 16-bit output is the fp32 result rounded once).
+    M = 16 and 24 with the automatic choice run each part on the batched-decode
+    kernel, then the SiLU-mul kernel."""
     torch = torch_mod()
     awq = _awq()
     K, N, g = 4096, 11008, 128
@@ -613,7 +616,8 @@ def test_fused_gate_up_silu(M, kernel, dt):
     got = out_to_f64(H32)
     assert torch.equal(H16, H32.to(H16.dtype))
     if M <= 32:
-        # the GEMV and the 32-row tile multiply by exact q - z
+        # the GEMV, the batched-decode kernel and the 32-row tile multiply by
+        # exact q - z
         rel, mx = assert_close(got, ref, f"gate/up M={M}")
         say("  rel_fro %.2e max_abs %.2e" % (rel, mx))
         return
