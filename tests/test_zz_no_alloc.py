@@ -28,9 +28,11 @@ def _call_noalloc(awq, Xd, pd, M, N, K, g, out):
 def test_noalloc_matches_workspace_call():
     import bit_weight_only_quantize_amd as awq
     torch = torch_mod()
-    # first call: bf16, K split 8 ways (partials and row factors in the static
-    # scratch); second, smaller: fp16 split K; third: the GEMV (no scratch)
-    shapes = [(48, 6000, 4096, 128, "bf16"), (20, 3000, 2048, 64, "f16"), (3, 2000, 1024, 128, "f16")]
+    # first call: the batched-decode kernel (its split-K partials in the
+    # static scratch); then bf16, K split 8 ways (partials and row factors);
+    # then, smaller: fp16 split K; last: the GEMV (no scratch)
+    shapes = [(16, 11008, 4096, 128, "f16"), (48, 6000, 4096, 128, "bf16"),
+              (20, 3000, 2048, 64, "f16"), (3, 2000, 1024, 128, "f16")]
     for (M, N, K, g, dt) in shapes:
         W = wl.gen_weight(N, K, 170 + M)
         X = wl.gen_activation(M, K, 171 + M, 172, dt)
