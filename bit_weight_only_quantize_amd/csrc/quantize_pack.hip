@@ -29,17 +29,21 @@
 
 namespace awq {
 
-// Min and max over the g/8 lanes of a group (aligned runs of 8 or 16 lanes)
+// Largest value over the g/8 lanes of a group (aligned runs of 8 or 16 lanes)
 // with DPP lane exchanges: swap neighbours, swap pairs, mirror within 8, then
 // (g = 128) mirror within 16.  Each step pairs every lane with one of the other
 // half of its current run, so after log2(g/8) steps every lane of a group
-// holds the group's extremes.
+// holds the group's maximum.  Applied to the bit patterns of floats of one
+// sign it is an exact float reduction: non-negative floats order like their
+// patterns, and non-positive ones in reverse (so the largest pattern is the
+// minimum).  Integer maxima need no NaN quieting before each exchange, which
+// a float min or max does (two more instructions per step).
 template <int LANES>
-__device__ __forceinline__ float group_min(float v) {
-  auto step = [](float x, auto ctrl_tag) {
+__device__ __forceinline__ uint32_t group_umax(uint32_t v) {
+  auto step = [](uint32_t x, auto ctrl_tag) {
     constexpr int kCtrl = decltype(ctrl_tag)::value;
-    const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true);
-    return __builtin_fminf(x, __builtin_bit_cast(float, y));
+    const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, true);
+    return x > y ? x : y;
   };
   v = step(v, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
   v = step(v, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
@@ -47,18 +51,15 @@ __device__ __forceinline__ float group_min(float v) {
   if constexpr (LANES == 16) v = step(v, std::integral_constant<int, 0x140>{});   // row_mirror
   return v;
 }
+// Minimum of non-positive floats and maximum of non-negative floats over the
+// group (lo <= 0 <= hi by construction).
 template <int LANES>
-__device__ __forceinline__ float group_max(float v) {
-  auto step = [](float x, auto ctrl_tag) {
-    constexpr int kCtrl = decltype(ctrl_tag)::value;
-    const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true);
-    return __builtin_fmaxf(x, __builtin_bit_cast(float, y));
-  };
-  v = step(v, std::integral_constant<int, 0xB1>{});
-  v = step(v, std::integral_constant<int, 0x4E>{});
-  v = step(v, std::integral_constant<int, 0x141>{});
-  if constexpr (LANES == 16) v = step(v, std::integral_constant<int, 0x140>{});
-  return v;
+__device__ __forceinline__ float group_min_nonpos(float v) {
+  return __builtin_bit_cast(float, group_umax<LANES>(__builtin_bit_cast(uint32_t, v)));
+}
+template <int LANES>
+__device__ __forceinline__ float group_max_nonneg(float v) {
+  return __builtin_bit_cast(float, group_umax<LANES>(__builtin_bit_cast(uint32_t, v)));
 }
 
 // Grid: x covers the words of one row in chunks of 256 (a multiple of the
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
-      amax = group_max<kLanesPerGroup>(amax);
+      amax = group_max_nonneg<kLanesPerGroup>(amax);
       step = amax / 7.0f;
     } else {
 #pragma unroll
@@ -117,8 +118,8 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
         lo = fminf(lo, v[i]);
         hi = fmaxf(hi, v[i]);
       }
-      lo = group_min<kLanesPerGroup>(lo);
-      hi = group_max<kLanesPerGroup>(hi);
+      lo = group_min_nonpos<kLanesPerGroup>(lo);
+      hi = group_max_nonneg<kLanesPerGroup>(hi);
 
       // (hi - lo) / 15, correctly rounded, from the product with RN(1/15)
       // and one exact-remainder correction (Markstein): checked against IEEE
