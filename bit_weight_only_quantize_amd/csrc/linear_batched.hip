@@ -18,8 +18,8 @@
 // holds its packed weights for the whole range in registers, so a split
 // costs one memory latency (a pipeline of several chunks per workgroup,
 // with a barrier each, measured slower: every chunk paid a latency of its
-// own).  Two workgroups fit a CU (at most 70 KiB of LDS and 128 VGPRs each),
-// and the splits are chosen so that every workgroup is resident at once.
+// own).  Two workgroups fit a CU (at most 70 KiB of LDS and 128 VGPRs each);
+// the split count balances the most loaded CU against the partials' cost.
 // Splits of K write fp32 partials that a second kernel sums in split order
 // (deterministic); a single split stores Y directly.
 
@@ -204,20 +204,36 @@ void batched_gemv_kernel(
   }
 }
 
-// Y[m][n] = sum over splits (in split order) of partial[split][m][n].
+// Y[m][n] = sum over splits (in split order) of partial[split][m][n]; one
+// thread per 4 consecutive outputs (16-byte partial loads: M * N is a
+// multiple of 4 here), or per output when it is not.
+template <int VEC>
 __global__ __launch_bounds__(256) void batched_gemv_reduce_kernel(const float *__restrict__ partial,
                                                                   int splits, int64_t MN,
                                                                   void *__restrict__ Y, int ytype) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * VEC;
   if (i >= MN) return;
-  float v = partial[i];
-  for (int s = 1; s < splits; ++s) v += partial[(int64_t)s * MN + i];
-  if (ytype == (int)YType::F16)
-    reinterpret_cast<uint16_t *>(Y)[i] = float_to_half_bits(v);
-  else if (ytype == (int)YType::BF16)
-    reinterpret_cast<uint16_t *>(Y)[i] = float_to_bf16_bits(v);
-  else
-    reinterpret_cast<float *>(Y)[i] = v;
+  float v[VEC];
+  if constexpr (VEC == 4) {
+    const float4 p0 = *reinterpret_cast<const float4 *>(partial + i);
+    v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+    for (int s = 1; s < splits; ++s) {
+      const float4 p = *reinterpret_cast<const float4 *>(partial + (int64_t)s * MN + i);
+      v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+    }
+  } else {
+    v[0] = partial[i];
+    for (int s = 1; s < splits; ++s) v[0] += partial[(int64_t)s * MN + i];
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    if (ytype == (int)YType::F16)
+      reinterpret_cast<uint16_t *>(Y)[i + e] = float_to_half_bits(v[e]);
+    else if (ytype == (int)YType::BF16)
+      reinterpret_cast<uint16_t *>(Y)[i + e] = float_to_bf16_bits(v[e]);
+    else
+      reinterpret_cast<float *>(Y)[i + e] = v[e];
+  }
 }
 
 namespace {
@@ -239,12 +255,30 @@ BatchedPlan batched_gemv_plan(int64_t M, int64_t N, int64_t K, int gs, Scratch s
   const int64_t G = K / gs;
   const int64_t mg = bg_max_groups(gs, bg_mt(M));
   const int64_t colblocks = (N + 16 * kBgWaves - 1) / (16 * kBgWaves);
-  // At least G / mg splits (a split stages at most mg groups); beyond that,
-  // as many as keep every workgroup resident at once (two per CU: 512).
+  // At least G / mg splits (a split stages at most mg groups).  Among the
+  // counts up to two rounds of resident workgroups, the one that minimizes
+  // the most loaded CU's groups (workgroups per CU, ceil(wgs / 256), times
+  // groups per split) plus 1.1 groups' time per split (each adds a partial
+  // to write and sum); ties to fewer splits.  Fitted to same-box sweeps of
+  // the split count: best or within 0.5 us of it on 11008 x 4096 (2 splits,
+  // 2 us faster than filling every slot), 13824 x 5120 and 5120 x 13824.
   const int64_t s_min = (G + mg - 1) / mg;
-  int64_t splits = 512 / colblocks;
-  if (splits > G) splits = G;
-  if (splits < s_min || sc == Scratch::None) splits = s_min;
+  int64_t best = s_min;
+  if (sc != Scratch::None) {
+    int64_t s_max = 1024 / colblocks;
+    if (s_max > G) s_max = G;
+    double best_cost = 1e30;
+    for (int64_t sp = s_min; sp <= (s_max > s_min ? s_max : s_min); ++sp) {
+      const int64_t gps = (G + sp - 1) / sp;
+      const int64_t waves = (colblocks * sp + 255) / 256;
+      const double cost = (double)(waves * gps) + 1.1 * (double)sp;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = sp;
+      }
+    }
+  }
+  int64_t splits = best;
   for (;;) {
     const int64_t gps = (G + splits - 1) / splits;
     const int64_t s2 = (G + gps - 1) / gps;
@@ -275,8 +309,12 @@ static hipError_t bg_go(const void *X, const uint32_t *qw, const uint16_t *sc, c
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t MN = M * N;
-  batched_gemv_reduce_kernel<<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(partial, p.splits, MN, Y,
-                                                                           (int)yt);
+  if (MN % 4 == 0)
+    batched_gemv_reduce_kernel<4><<<(unsigned)((MN / 4 + 255) / 256), 256, 0, st>>>(
+        partial, p.splits, MN, Y, (int)yt);
+  else
+    batched_gemv_reduce_kernel<1><<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(
+        partial, p.splits, MN, Y, (int)yt);
   return hipGetLastError();
 }
 
