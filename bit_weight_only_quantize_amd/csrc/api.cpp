@@ -52,19 +52,27 @@ bool auto_gemv(int64_t M, int64_t N, int64_t K, int g) {
 }
 
 // Automatic choice of the batched-decode kernel (with scratch for its
-// partials): where the GEMV cannot stage the activation rows, for 2 <= M <= 32
-// on layers of at least 4e7 weights and 5000 columns.  Same-box graph replays
-// (us; batched / GEMV / GEMM, g = 128 unless noted): 13824 x 5120 at M = 8
-// 17.0 / 21.2 / 20.5 and M = 16 17.4 / 28.0 / 20.9; 5120 x 13824 at M = 4
-// 18.7 / 22.4 / 21.1 and M = 16 19.0 / 34.5 / 21.6; g = 64, 13824 x 5120 at
-// M = 32 25.9 / - / 29.5; 11008 x 4096 at M = 16 15.3 / 17.9 / 16.6.  On 4096
-// x 4096 and 4096 x 11008 (N = 4096) the GEMV or the GEMM was as fast or
-// faster, and at M = 64 the GEMM (whose splits need fewer workgroups).
+// partials), for 2 <= M <= 32 on layers of at least 1.6e7 weights and 4096
+// columns, except where the GEMV stages the activation rows and either
+// M < 8 or the layer has under 2e7 weights (4096 x 4096, whose GEMV stages
+// up to 16 rows in 16-wave workgroups).  Same-box graph replays (us; GEMV /
+// batched / GEMM, g = 128 unless noted, N x K):
+//   11008 x 4096   M = 6: 10.1 / 11.2 / 16.0   M = 8: 12.6 / 11.3 / 16.1
+//                  M = 16: 17.8 / 11.6 / 16.6  M = 32: - / 15.5 / 17.9
+//   4096 x 11008   M = 4: 9.2 / 12.4 / 17.3    M = 8: 13.3 / 12.6 / 17.5
+//                  M = 16: 17.7 / 13.0 / 18.3  M = 32: - / 17.2 / 18.9
+//   13824 x 5120   M = 6: 15.8 / 16.1 / 20.4   M = 8: 20.9 / 16.2 / 20.4
+//                  M = 32: - / 20.2 / 21.6; g = 64, M = 32: - / 23.8 / 29.1
+//   5120 x 13824   M = 4: 22.0 / 17.4 / 21.0   M = 16: 34.1 / 17.9 / 21.5
+//   4096 x 4096    M = 16: 7.9 / 9.5 / 12.7    M = 24: - / 10.1 / 13.3
+// (the one loss: 4096 x 11008 at M = 6, unstaged, 12.5 against the GEMV's
+// 12.1).  At M = 64 the GEMM is faster (its splits need fewer workgroups).
 bool auto_batched(int64_t M, int64_t N, int64_t K, int g) {
-  if (M < 2 || M > 32 || N < 5000 || N * K < 40000000) return false;
+  if (M < 2 || M > 32 || N < 4096 || N * K < 16000000) return false;
   if (!awq::batched_gemv_supported(M, N, K, g)) return false;
-  return !(M <= AWQ_GEMV_MAX_M && awq::gemv_supported(M, N, K, g) &&
-           awq::gemv_stages_activations(M, N, K));
+  const bool staged = M <= AWQ_GEMV_MAX_M && awq::gemv_supported(M, N, K, g) &&
+                      awq::gemv_stages_activations(M, N, K);
+  return !(staged && (M < 8 || N * K < 20000000));
 }
 
 awq_status check_config(awq_config cfg, int64_t K) {

@@ -13,13 +13,15 @@
 // of weights.  Here a workgroup owns 128 columns (8 waves, wave w: 16 of
 // them, for all M rows) and a range of at most kMaxGroups groups of K (a
 // split); the range's activations, scales and zero points are staged once in
-// LDS and shared by the 8 waves, so X is read once per 128 columns.  Every
-// load of the workgroup is issued at once, before any arithmetic: each wave
-// holds its packed weights for the whole range in registers, so a split
-// costs one memory latency (a pipeline of several chunks per workgroup,
-// with a barrier each, measured slower: every chunk paid a latency of its
-// own).  Two workgroups fit a CU (at most 70 KiB of LDS and 128 VGPRs each);
-// the split count balances the most loaded CU against the partials' cost.
+// LDS and shared by the 8 waves, so X is read once per 128 columns.  The
+// staging loads are issued first, with one barrier after them (a pipeline of
+// several X chunks per workgroup, with a barrier each, measured slower: every
+// chunk paid a latency of its own).  Each wave streams its packed weights
+// with 64 bytes per lane in flight at M <= 16 and 32 above (the next group's
+// load is issued as a group is consumed): measured 5-14% faster than issuing
+// the whole range at once, bit-identical.  Two workgroups fit a
+// CU (at most 80 KiB of LDS and 128 VGPRs each); the split count balances
+// the most loaded CU against the partials' cost.
 // Splits of K write fp32 partials that a second kernel sums in split order
 // (deterministic); a single split stores Y directly.
 
@@ -37,14 +39,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
 
 constexpr int kBgWaves = 8;                  // waves per workgroup: 128 columns
 
-// Most groups per split (kMaxGroups): the range's activations and every
-// lane's packed weights for it (16 or 8 bytes per group) stay on chip.
+// Most groups per split (kMaxGroups): the range's activations (at most 64 KiB)
+// stay in LDS.
 template <int GS, int MT>
 struct BgGeom {
   static constexpr int kRows = 16 * MT;                 // padded activation rows
-  // at most 64 KiB of X and 16 groups (the staging and weight registers of
-  // 32 groups at g = 64 exceed the 128-VGPR budget)
-  static constexpr int kMaxGroups = 2048 / GS / MT < 16 ? 2048 / GS / MT : 16;
+  static constexpr int kMaxGroups = 2048 / GS / MT;
+  // groups of packed weights in flight per wave: 64 (M <= 16) or 32 bytes
+  // per lane times 128 / GS
+  static constexpr int kWin = (MT == 1 ? 4 : 2) * 128 / GS < kMaxGroups
+                                  ? (MT == 1 ? 4 : 2) * 128 / GS : kMaxGroups;
   static constexpr int kKR = kMaxGroups * GS;            // K values of a full range
   static constexpr int kRowBytes = kKR * 2 + 16;         // +16: rows start 4 banks apart
   static constexpr int kXBytes = kRows * kRowBytes;
@@ -114,20 +118,21 @@ void batched_gemv_kernel(
     zs[r] = __builtin_amdgcn_raw_buffer_load_b8(rZ, o, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // packed weights of this lane for every group of the range (groups past it
-  // read 0 and are not used)
+  // packed weights of this lane, group gl of the range (groups past it read 0
+  // and are not used); the first window now, the rest as groups are consumed
   const uint32_t q_lane = (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(kq * kWpl * 4);
   typedef uint32_t wvec_t __attribute__((ext_vector_type(kWpl)));
   wvec_t w[kMG];
-#pragma unroll
-  for (int gl = 0; gl < kMG; ++gl) {
+  auto load_group = [&](int gl) {
     const int g = g_begin + gl;
     const uint32_t qo = g < g_end ? q_lane + (uint32_t)g * (GS / 2) : 0x7FFFFFF0u;
     if constexpr (kWpl == 4)
       w[gl] = __builtin_bit_cast(wvec_t, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo, 0, 0));
     else
       w[gl] = __builtin_bit_cast(wvec_t, __builtin_amdgcn_raw_buffer_load_b64(rQ, qo, 0, 0));
-  }
+  };
+#pragma unroll
+  for (int gl = 0; gl < Geo::kWin; ++gl) load_group(gl);
   __builtin_amdgcn_sched_barrier(0);
   // the staging registers to LDS (the counted wait leaves the weight loads,
   // issued after them, in flight)
@@ -155,6 +160,11 @@ void batched_gemv_kernel(
   const DeqRegs dq;
 #pragma unroll
   for (int gl = 0; gl < kMG; ++gl) {
+    if (gl + Geo::kWin < kMG) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_group(gl + Geo::kWin);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // (a guarded body rather than an early exit: the loop stays fully
     // unrolled and w[] in registers)
     if (g_begin + gl >= g_end) continue;                // uniform
@@ -238,7 +248,7 @@ __global__ __launch_bounds__(256) void batched_gemv_reduce_kernel(const float *_
 
 namespace {
 int bg_mt(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
-int bg_max_groups(int gs, int mt) { return 2048 / gs / mt < 16 ? 2048 / gs / mt : 16; }
+int bg_max_groups(int gs, int mt) { return 2048 / gs / mt; }
 size_t bg_lds(int gs, int mt) {
   const int mg = bg_max_groups(gs, mt), cols = 16 * kBgWaves;
   return (size_t)16 * mt * (mg * gs * 2 + 16) + (size_t)cols * mg * 3;
@@ -256,12 +266,15 @@ BatchedPlan batched_gemv_plan(int64_t M, int64_t N, int64_t K, int gs, Scratch s
   const int64_t mg = bg_max_groups(gs, bg_mt(M));
   const int64_t colblocks = (N + 16 * kBgWaves - 1) / (16 * kBgWaves);
   // At least G / mg splits (a split stages at most mg groups).  Among the
-  // counts up to two rounds of resident workgroups, the one that minimizes
-  // the most loaded CU's groups (workgroups per CU, ceil(wgs / 256), times
-  // groups per split) plus 1.1 groups' time per split (each adds a partial
-  // to write and sum); ties to fewer splits.  Fitted to same-box sweeps of
-  // the split count: best or within 0.5 us of it on 11008 x 4096 (2 splits,
-  // 2 us faster than filling every slot), 13824 x 5120 and 5120 x 13824.
+  // counts up to four workgroups per CU, the one that minimizes the most
+  // loaded CU's groups (workgroups per CU, ceil(wgs / 256), times groups per
+  // split), plus 1.1 groups' time per split (each adds a partial to write
+  // and sum), plus 4 when the workgroups need a second residency round (more
+  // than 512); ties to fewer splits.  Fitted to same-box sweeps of every
+  // split count on 13824 x 5120, 5120 x 13824 (g = 64 and 128) and
+  // 11008 x 4096 at M = 4..32: the pick is the best or within 0.5 us of it
+  // (11008 x 4096: 2 splits, 2 us faster than filling every slot; 13824 x
+  // 5120 at g = 64: 4, 2 us faster than 7).
   const int64_t s_min = (G + mg - 1) / mg;
   int64_t best = s_min;
   if (sc != Scratch::None) {
@@ -270,8 +283,9 @@ BatchedPlan batched_gemv_plan(int64_t M, int64_t N, int64_t K, int gs, Scratch s
     double best_cost = 1e30;
     for (int64_t sp = s_min; sp <= (s_max > s_min ? s_max : s_min); ++sp) {
       const int64_t gps = (G + sp - 1) / sp;
-      const int64_t waves = (colblocks * sp + 255) / 256;
-      const double cost = (double)(waves * gps) + 1.1 * (double)sp;
+      const int64_t wgs = colblocks * ((G + gps - 1) / gps);
+      const double cost = (double)((wgs + 255) / 256 * gps) + 1.1 * (double)sp +
+                          (wgs > 512 ? 4.0 : 0.0);
       if (cost < best_cost) {
         best_cost = cost;
         best = sp;

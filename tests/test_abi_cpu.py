@@ -206,14 +206,15 @@ def test_noalloc_rejects_beyond_its_static_scratch():
 
 def test_linear_dispatch_rule():
     """The automatic kernel choice of a call with scratch (awq_linear_ws,
-    awq_linear_ex with a workspace; host logic, no GPU): the GEMV wherever its
-    activation rows fit in LDS (64 KiB, or 128 KiB when N <= 4096); else the
-    batched-decode kernel for 2 <= M <= 32 on layers of at least 4e7 weights
-    and 5000 columns; else, unstaged, the GEMM where a GEMV wave would walk
-    more than 8 groups, the GEMV up to M = 8 (12 on layers of at most 5e7
-    weights), the GEMM beyond.  The kernel is read off the workspace size
-    (bf16 activations: the GEMM always needs one, the GEMV none, the batched
-    kernel exactly its own)."""
+    awq_linear_ex with a workspace; host logic, no GPU): the batched-decode
+    kernel for 2 <= M <= 32 on layers of at least 1.6e7 weights and 4096
+    columns, unless the GEMV stages the activation rows (64 KiB, or 128 KiB
+    when N <= 4096) and M < 8 or the layer has under 2e7 weights; else the
+    GEMV wherever it stages the rows; else, unstaged, the GEMM where a GEMV
+    wave would walk more than 8 groups, the GEMV up to M = 8 (12 on layers
+    of at most 5e7 weights), the GEMM beyond.  The kernel is read off the
+    workspace size (bf16 activations: the GEMM always needs one, the GEMV
+    none, the batched kernel exactly its own)."""
     B = binding.AWQ_KERNEL_BATCHED
 
     def kind(M, N, K):
@@ -226,17 +227,22 @@ def test_linear_dispatch_rule():
         return "gemm"
     assert kind(2, 5120, 13824) == "gemv"       # 55 KiB of rows: staged
     assert kind(4, 5120, 13824) == "batched"    # unstaged, 7.1e7 weights
-    assert kind(8, 11008, 4096) == "gemv"       # 64 KiB: staged
-    assert kind(12, 11008, 4096) == "batched"   # unstaged, 4.5e7 weights, N >= 5000
+    assert kind(6, 11008, 4096) == "gemv"       # staged, M < 8
+    assert kind(8, 11008, 4096) == "batched"    # staged (64 KiB), but M >= 8
+    assert kind(12, 11008, 4096) == "batched"
     assert kind(8, 13824, 5120) == "batched"
     assert kind(32, 13824, 5120) == "batched"
     assert kind(33, 13824, 5120) == "gemm"      # beyond 32 rows
-    assert kind(16, 4096, 4096) == "gemv"       # 128 KiB: staged (16-wave workgroups)
-    assert kind(6, 4096, 11008) == "gemv"       # N < 5000: unstaged GEMV, M <= 8
-    assert kind(16, 4096, 11008) == "gemm"      # N < 5000, M > 12
-    assert kind(17, 4096, 4096) == "gemm"       # beyond the GEMV's 16 rows
-    assert kind(12, 3000, 20480) == "gemm"      # N < 5000: 10 groups per GEMV wave
-    assert kind(4, 6000, 4096) == "gemv"        # 2.5e7 weights: staged
+    assert kind(16, 4096, 4096) == "gemv"       # 128 KiB: staged, 1.7e7 weights
+    assert kind(17, 4096, 4096) == "batched"    # beyond the GEMV's 16 rows
+    assert kind(4, 4096, 11008) == "gemv"       # 88 KiB: staged (16-wave workgroups)
+    assert kind(6, 4096, 11008) == "batched"    # 132 KiB: unstaged
+    assert kind(16, 4096, 11008) == "batched"
+    assert kind(8, 4000, 5120) == "gemv"        # N < 4096: staged GEMV (80 KiB, 16 waves)
+    assert kind(16, 4000, 5120) == "gemm"       # N < 4096, unstaged, M > 12
+    assert kind(12, 3000, 20480) == "gemm"      # N < 4096: 10 groups per GEMV wave
+    assert kind(4, 6000, 4096) == "gemv"        # 2.5e7 weights: staged, M < 8
+    assert kind(16, 2048, 4096) == "gemv"       # N < 4096: staged GEMV
 
 
 def test_search_workspace_and_validation():
