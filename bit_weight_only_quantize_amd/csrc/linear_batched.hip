@@ -91,7 +91,7 @@ void batched_gemv_kernel(
   const rsrc_t rZ = make_rsrc(zeros, zeros ? (uint32_t)N * (uint32_t)G : 0u);
   const rsrc_t rX = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
 
-  // ---- every load of the split, issued before any arithmetic ----------------
+  // ---- staging loads first, then the first weight window ---------------------
   // Staging (registers, then LDS): X rows 0..kRows-1 over [k_begin, k_end)
   // (rows >= M and values past the range read 0), scales and zero points of
   // the 128 columns, [col][group] (columns >= N and groups past the range
