@@ -57,16 +57,15 @@ bool auto_gemv(int64_t M, int64_t N, int64_t K, int g) {
 // M < 8 or the layer has under 2e7 weights (4096 x 4096, whose GEMV stages
 // up to 16 rows in 16-wave workgroups).  Same-box graph replays (us; GEMV /
 // batched / GEMM, g = 128 unless noted, N x K):
-//   11008 x 4096   M = 6: 10.1 / 11.2 / 16.0   M = 8: 12.6 / 11.3 / 16.1
-//                  M = 16: 17.8 / 11.6 / 16.6  M = 32: - / 15.5 / 17.9
-//   4096 x 11008   M = 4: 9.2 / 12.4 / 17.3    M = 8: 13.3 / 12.6 / 17.5
-//                  M = 16: 17.7 / 13.0 / 18.3  M = 32: - / 17.2 / 18.9
-//   13824 x 5120   M = 6: 15.8 / 16.1 / 20.4   M = 8: 20.9 / 16.2 / 20.4
-//                  M = 32: - / 20.2 / 21.6; g = 64, M = 32: - / 23.8 / 29.1
-//   5120 x 13824   M = 4: 22.0 / 17.4 / 21.0   M = 16: 34.1 / 17.9 / 21.5
-//   4096 x 4096    M = 16: 7.9 / 9.5 / 12.7    M = 24: - / 10.1 / 13.3
-// (the one loss: 4096 x 11008 at M = 6, unstaged, 12.5 against the GEMV's
-// 12.1).  At M = 64 the GEMM is faster (its splits need fewer workgroups).
+//   11008 x 4096   M = 6: 10.0 / 10.8 / 16.1   M = 8: 12.7 / 11.1 / 16.0
+//                  M = 16: 17.7 / 11.5 / 16.5  M = 32: - / 15.3 / 17.9
+//   4096 x 11008   M = 4: 9.2 / 10.8 / 17.3    M = 6: 12.1 / 11.0 / 17.4
+//                  M = 16: 17.9 / 11.6 / 18.2  M = 32: - / 16.1 / 18.7
+//   13824 x 5120   M = 6: 15.7 / 15.5 / 20.3   M = 8: 20.9 / 15.7 / 20.4
+//                  M = 32: - / 19.6 / 21.7; g = 64, M = 32: - / 23.5 / 29.0
+//   5120 x 13824   M = 4: 22.0 / 15.3 / 21.0   M = 16: 34.3 / 16.1 / 21.5
+//   4096 x 4096    M = 16: 7.9 / 8.8 / 12.7    M = 24: - / 9.5 / 13.3
+// At M = 64 the GEMM is faster (its splits need fewer workgroups).
 bool auto_batched(int64_t M, int64_t N, int64_t K, int g) {
   if (M < 2 || M > 32 || N < 4096 || N * K < 16000000) return false;
   if (!awq::batched_gemv_supported(M, N, K, g)) return false;
