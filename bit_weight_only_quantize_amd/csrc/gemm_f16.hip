@@ -17,10 +17,12 @@
 // Work split, chosen from measured MI355X rates (one wave keeps the MFMA unit
 // busy when it issues about two VALU operations or fewer per 16x16x32 MFMA;
 // a CU's LDS delivers about 160 bytes per clock to ds_read_b128):
-//  * A 256-thread workgroup owns a BM x 256 tile of Y (BM = 16 * MT rows);
-//    wave v owns columns 64v .. 64v+63 over all BM rows.  Each packed weight
-//    word is loaded and dequantized by exactly one lane and feeds MT MFMAs;
-//    each activation fragment read from LDS feeds four.
+//  * A workgroup owns a BM x 256 tile of Y (BM = 16 * MT rows): four waves
+//    of 64 columns each for BM >= 128, eight of 32 columns for the 32- and
+//    64-row tiles (two waves per SIMD), each over all BM rows.  Each packed
+//    weight word is loaded and dequantized by exactly one lane and feeds MT
+//    MFMAs; each activation fragment read from LDS feeds four (two with
+//    eight waves).
 //  * Dequantizing costs 13 VALU operations per word (8 weights): 4 and-or
 //    into the mantissa of 1024.0 or 64.0, 4 packed subtractions of the biased
 //    zero point (exact), 4 packed multiplies by the scale (rounded once).  A
@@ -46,17 +48,21 @@
 
 #include "awq_internal.h"
 #include "device_common.h"
+#include <type_traits>
 
 namespace awq {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kNT = 4;            // 16-column MFMA tiles per wave
-constexpr int kBN = 64 * 4;       // columns per workgroup
+constexpr int kBN = 256;          // columns per workgroup
 constexpr int kBK = 128;          // input channels per K block
 constexpr int kSteps = kBK / 32;  // MFMA K steps per block
 constexpr int kGroupRows = 4;     // row tiles per tile group
+// Waves per workgroup: eight (32 columns each, two waves per SIMD) for the
+// 32- and 64-row tiles, four (64 columns each) for the larger ones, whose
+// registers hold one wave per SIMD.  Eight waves measured 3-9% faster at
+// M = 24-64, bit-identical; at 128 rows they spill and gain nothing.
+constexpr int gemm_waves(int mt) { return mt <= 4 ? 8 : 4; }
 // One workgroup per CU; K is split only when there are fewer tiles than
 // slots (CUs).
 constexpr int kSlots = 256;
@@ -120,7 +126,7 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 // the 32-row tile (batched decode, where the VALU work per MFMA is highest
 // anyway and exact products keep the error independent of the activations'
 // mean); larger tiles use fp16((q - z) * s).
-template <int GS, int YT, int MT, bool KTAIL, bool BF16X, int EPI>
+template <int GS, int YT, int MT, bool KTAIL, bool BF16X, int EPI, int NW>
 __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
                                               const uint32_t *__restrict__ qweight,
                                               const uint16_t *__restrict__ scales,
@@ -131,6 +137,9 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
                                               double *__restrict__ partials) {
   constexpr bool kExact = EPI == 1 || MT <= 2;
   constexpr int kBM = 16 * MT;
+  constexpr int kNTw = 16 / NW;      // 16-column MFMA tiles per wave
+  constexpr int kThr = 64 * NW;
+  using SZV = std::conditional_t<kNTw == 4, u32x4, u32x2>;
   constexpr int kWpl = GS / 32;      // packed words per lane per group and column
   constexpr int kGPB = kBK / GS;     // groups per K block
   // Chunk bit whose value flips bit 3 of the physical chunk: 2 for both group
@@ -139,11 +148,12 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // 2%: rocprofv3 SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE.)
   constexpr int kKqBit = 2;
   constexpr int kWin = MT >= 8 ? 2 : 4;   // weight blocks in flight (even: bq buffers alternate)
-  constexpr int kWords = kNT * kSteps;          // packed words per lane per block
+  constexpr int kWords = kNTw * kSteps;         // packed words per lane per block
   constexpr int kWordsPerTile = kWords / MT;    // dequantized alongside each row tile
   // The 256-row tile's 256 accumulators fill the AGPRs: its activations go to
   // LDS by DMA (buffer_load ... lds), without staging registers.
   constexpr bool kDMA = MT == 16;
+  static_assert(!kDMA || NW == 4, "the DMA tile runs four waves");
   // (bf16 input reaches it already scaled and converted to fp16 by the row
   // prescan; only the epilogue's row factors remain)
   static_assert(!(kDMA && kExact), "the 256-row tile stores Y");
@@ -178,11 +188,11 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // Lane (c, kq) holds, for column tile j, words kq*kWpl .. kq*kWpl+kWpl-1 of
   // each group of column col0 + 64*wave + 16*j + c: channels
   // 8*(kq*kWpl + w) .. +7 of the group, for MFMA step gi*kWpl + w.
-  const uint32_t lane_col = (uint32_t)(col0 + wave * 64 + c);
+  const uint32_t lane_col = (uint32_t)(col0 + wave * 16 * kNTw + c);
   const rsrc_t rQ = make_rsrc(qweight, (uint32_t)N * (uint32_t)K / 2u);
   const uint32_t q_lane = lane_col * (uint32_t)(K / 2) + (uint32_t)(kq * kWpl * 4);
   struct Raw {
-    uint32_t w[kNT][kGPB][kWpl];
+    uint32_t w[kNTw][kGPB][kWpl];
   };
   // Column tile j of block kb (one load).  With KTAIL (K % 128 == 64, g = 64)
   // a group past the end of K reads zero weights and, below, zero scale and
@@ -241,7 +251,9 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
       r.zr1 = __builtin_amdgcn_raw_buffer_load_b8(rZ, o1, 0, 0);
     }
   };
-  const int sz_slot = ((wave * 16 + c) * 4 + kq) * 4;   // this thread's column: j = kq
+  const bool sz_thread = NW == 4 || tid < 256;        // one thread per column of the tile
+  const int sz_slot = NW == 4 ? ((wave * 16 + c) * 4 + kq) * 4   // this thread's column: j = kq
+                              : (((tid / (16 * kNTw)) * 16 + (tid & 15)) * kNTw + (tid / 16) % kNTw) * 4;
   auto store_sz = [&](uint32_t *buf, const SZ &r) {
     if constexpr (kGPB == 1) {
       buf[sz_slot / 4] = (((uint32_t)(uint8_t)r.zr << 16) + zfix) | (uint16_t)r.sc;
@@ -255,7 +267,7 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   };
 
   // ---- dequantized B fragments of one block: bq[j][step] ------------------------
-  typedef u32x4 BQ[kNT][kSteps];
+  typedef u32x4 BQ[kNTw][kSteps];
   // Words (j, gi, *) of a block: fp16((q - z) * s) of 8 channels each, in the
   // MFMA B-operand order; sz is the column's (zero << 16 | scale).
   auto deq_word = [&](const Raw &r, uint32_t sz, int j, int gi, int w, BQ &out) {
@@ -277,14 +289,14 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
               __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, e3) * s2)};
   };
   auto read_sz = [&](const uint32_t *buf, int gi) {
-    return *reinterpret_cast<const u32x4 *>(buf + gi * 256 + (wave * 16 + c) * 4);
+    return *reinterpret_cast<const SZV *>(buf + gi * 256 + (wave * 16 + c) * kNTw);
   };
 
-  f32x4 acc[MT][kNT];
+  f32x4 acc[MT][kNTw];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kNTw; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // A fragment: 16-row tile i, logical 16-byte chunk ch of the block row.
   auto a_frag = [&](const uint16_t *buf, int i, int ch) {
@@ -299,10 +311,10 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   auto clampk = [&](int k) { return k < last ? k : last; };
 
   // ---- activations staged through registers ----------------------------------
-  constexpr int kARounds = kBM / 16;     // 16-byte chunks per thread per block
+  constexpr int kARounds = kBM * 16 / kThr;   // 16-byte chunks per thread per block
   u32x4 areg[kARounds];
   auto load_a1 = [&](int kb, int r) {
-    const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
+    const int q = tid + kThr * r, row = q >> 4, ch = q & 15;
     uint32_t off = (uint32_t)(row0 + row) * (uint32_t)K * 2u + (uint32_t)kb * (kBK * 2) +
                    (uint32_t)ch * 16u;
     if constexpr (KTAIL) off = kb * kBK + ch * 8 < K ? off : kNone;   // zeros past K
@@ -317,12 +329,12 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     const rsrc_t rR = make_rsrc(rowf, (uint32_t)M * 4u);
 #pragma unroll
     for (int r = 0; r < kARounds; ++r) {
-      const uint32_t row = (uint32_t)(row0 + ((tid + kThreads * r) >> 4));
+      const uint32_t row = (uint32_t)(row0 + ((tid + kThr * r) >> 4));
       rf[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, row * 4u, 0, 0));
     }
   }
   auto store_a1 = [&](uint16_t *buf, int r) {
-    const int q = tid + kThreads * r, row = q >> 4, ch = q & 15;
+    const int q = tid + kThr * r, row = q >> 4, ch = q & 15;
     u32x4 v = areg[r];
     if constexpr (BF16X) {
 #pragma unroll
@@ -368,14 +380,14 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // consumes it (given one, the compiler sinks the prefetch loads down to it,
   // right before the wait that then drains them); the last steps follow
   // unrolled.
-  constexpr int kLoads = kARounds + kNT + 1;      // prefetch loads per step
+  constexpr int kLoads = kARounds + kNTw + 1;     // prefetch loads per step
   // row tiles that issue them: all, or with the DMA the first half, so the
   // last ones still have half a step to land before the step's vmcnt(0)
   constexpr int kIssueTiles = kDMA ? MT / 2 : MT;
   Raw rw[kWin];
   BQ bq[2];
   SZ szr;
-  u32x4 szc[2][kGPB];                    // exact path: blocks' scales, by step parity
+  SZV szc[2][kGPB];                      // exact path: blocks' scales, by step parity
   // Load n of a step: scales first and activations next (both are needed at
   // the start of the next step), then the weight window's refill.  Each
   // activation chunk's register first goes to LDS (block k+1, into the
@@ -385,13 +397,13 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
       // weights first: every load of a step must land by its end (the DMA
       // is waited for with vmcnt(0)); then scales, then block k+1's
       // activations straight into the buffer this step does not read
-      if (n < kNT) load_w(clampk(k + kWin), n, rw[u]);
-      else if (n == kNT) load_sz(clampk(k + 3), szr);
-      else dma_a1(nbuf, clampk(k + 1), n - kNT - 1);
+      if (n < kNTw) load_w(clampk(k + kWin), n, rw[u]);
+      else if (n == kNTw) load_sz(clampk(k + 3), szr);
+      else dma_a1(nbuf, clampk(k + 1), n - kNTw - 1);
       return;
     }
     if (n == 0) {
-      load_sz(clampk(k + 3), szr);
+      if (sz_thread) load_sz(clampk(k + 3), szr);
     } else if (n <= kARounds) {
       store_a1(nbuf, n - 1);
       load_a1(clampk(k + 2), n - 1);
@@ -403,18 +415,18 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     const int p = u & 1;
     const bool odd = ((k - kb_begin) & 1) != 0;
     uint16_t *abuf = odd ? sA1 : sA0;
-    store_sz(((k - kb_begin) & 1) ? sSZ1 : sSZ0, szr);    // block k+2
+    if (sz_thread) store_sz(((k - kb_begin) & 1) ? sSZ1 : sSZ0, szr);    // block k+2
     const uint32_t *zbuf = ((k - kb_begin) & 1) ? sSZ0 : sSZ1;   // block k+1
-    u32x4 szv[kGPB];
+    SZV szv[kGPB];
 #pragma unroll
     for (int gi = 0; gi < kGPB; ++gi) szv[gi] = read_sz(zbuf, gi);
-    float sk[kGPB][kNT];                 // block k's scales (exact path)
+    float sk[kGPB][kNTw];                 // block k's scales (exact path)
     if constexpr (kExact) {
 #pragma unroll
       for (int gi = 0; gi < kGPB; ++gi) {
-        const u32x4 zz = szc[p][gi];
+        const SZV zz = szc[p][gi];
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) {
+        for (int j = 0; j < kNTw; ++j) {
           const uint32_t z1 = zz[j];
           sk[gi][j] = half_bits_to_float((uint16_t)(z1 & 0xFFFFu));
         }
@@ -436,16 +448,16 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
       if constexpr (kExact) {
 #pragma unroll
         for (int gi = 0; gi < kGPB; ++gi) {
-          f32x4 t[kNT];
+          f32x4 t[kNTw];
 #pragma unroll
-          for (int j = 0; j < kNT; ++j) t[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int j = 0; j < kNTw; ++j) t[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int w = 0; w < kWpl; ++w)
 #pragma unroll
-            for (int j = 0; j < kNT; ++j)
+            for (int j = 0; j < kNTw; ++j)
               t[j] = mfma32<TagF16>(a[cur][gi * kWpl + w], bq[p][j][gi * kWpl + w], t[j]);
 #pragma unroll
-          for (int j = 0; j < kNT; ++j)
+          for (int j = 0; j < kNTw; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               acc[i][j][e] = __builtin_fmaf(t[j][e], sk[gi][j], acc[i][j][e]);
@@ -454,14 +466,14 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 #pragma unroll
         for (int st = 0; st < kSteps; ++st)
 #pragma unroll
-          for (int j = 0; j < kNT; ++j)
+          for (int j = 0; j < kNTw; ++j)
             acc[i][j] = mfma32<TagF16>(a[cur][st], bq[p][j][st], acc[i][j]);
       }
       // dequantize words [i*kWordsPerTile, (i+1)*kWordsPerTile) of block k+1
 #pragma unroll
       for (int q = i * kWordsPerTile; q < (i + 1) * kWordsPerTile; ++q) {
         const int j = q / kSteps, st = q % kSteps, gi = st / kWpl, w = st % kWpl;
-        const u32x4 zz = szv[gi];
+        const SZV zz = szv[gi];
         const uint32_t sz = zz[j];
         deq_word(nx, sz, j, gi, w, bq[p ^ 1]);
       }
@@ -470,8 +482,8 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
         for (int n = i * kLoads / kIssueTiles; n < (i + 1) * kLoads / kIssueTiles; ++n)
           issue(n, k, u, odd ? sA0 : sA1);
       }
-      tile_order<kNT * kSteps, (kWordsPerTile * (kExact ? 9 : 13) + (kExact ? 4 * kNT * kGPB : 0) +
-                                kNT * kSteps - 1) / (kNT * kSteps) + 1>();
+      tile_order<kNTw * kSteps, (kWordsPerTile * (kExact ? 9 : 13) + (kExact ? 4 * kNTw * kGPB : 0) +
+                                kNTw * kSteps - 1) / (kNTw * kSteps) + 1>();
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (kDMA)
@@ -496,24 +508,28 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 #pragma unroll
     for (int u = 0; u < kWin; ++u)
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) load_w(clampk(kb0 + u), j, rw[u]);
+      for (int j = 0; j < kNTw; ++j) load_w(clampk(kb0 + u), j, rw[u]);
     SZ s0, s1;
-    load_sz(kb0, s0);
-    load_sz(clampk(kb0 + 1), s1);
-    load_sz(clampk(kb0 + 2), szr);
+    if (sz_thread) {
+      load_sz(kb0, s0);
+      load_sz(clampk(kb0 + 1), s1);
+      load_sz(clampk(kb0 + 2), szr);
+    }
     if constexpr (!kDMA) {
       store_a(sA0);
 #pragma unroll
       for (int r = 0; r < kARounds; ++r) load_a1(clampk(kb0 + 1), r);
     }
-    store_sz(sSZ0, s0);
-    store_sz(sSZ1, s1);
+    if (sz_thread) {
+      store_sz(sSZ0, s0);
+      store_sz(sSZ1, s1);
+    }
     if constexpr (kDMA)
       __builtin_amdgcn_s_waitcnt(0x0070);
     else
       wait_lds_all();
     __builtin_amdgcn_s_barrier();
-    u32x4 szv[kGPB];
+    SZV szv[kGPB];
 #pragma unroll
     for (int gi = 0; gi < kGPB; ++gi) szv[gi] = read_sz(sSZ0, gi);
 #pragma unroll
@@ -521,7 +537,7 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 #pragma unroll
     for (int q = 0; q < kWords; ++q) {
       const int j = q / kSteps, st = q % kSteps, gi = st / kWpl, w = st % kWpl;
-      const u32x4 zz = szv[gi];
+      const SZV zz = szv[gi];
       const uint32_t sz = zz[j];
       deq_word(rw[0], sz, j, gi, w, bq[0]);
     }
@@ -543,9 +559,9 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // at or past row M).  (Not compiled for the 256-row tile, which the plan
   // never splits.)
   if (!kDMA && sk.splits > 1) {
-    constexpr int kTiles = MT * kNT;     // f32x4 accumulators per lane
+    constexpr int kTiles = MT * kNTw;    // f32x4 accumulators per lane
     const uint32_t wave_bytes = (uint32_t)kTiles * 64u * 16u;
-    const uint32_t tile_bytes = 4u * wave_bytes;
+    const uint32_t tile_bytes = (uint32_t)NW * wave_bytes;
     const rsrc_t rP = make_rsrc(sk.partials, 0x7FFFFFF0u);
     const uint32_t mine = ((uint32_t)tile * (uint32_t)sk.splits + (uint32_t)split) * tile_bytes +
                           (uint32_t)wave * wave_bytes + (uint32_t)lane * 16u;
@@ -558,10 +574,10 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
       // cost more than it saved.
       const bool live = MT > 2 || row0 + i * 16 < M;   // uniform
 #pragma unroll
-      for (int j = 0; j < kNT; ++j)
+      for (int j = 0; j < kNTw; ++j)
         __builtin_amdgcn_raw_buffer_store_b128(
             __builtin_bit_cast(u32x4, acc[i][j]), rP,
-            live ? mine + (uint32_t)(i * kNT + j) * 1024u : 0x7FFFFFF0u, 0, 0);
+            live ? mine + (uint32_t)(i * kNTw + j) * 1024u : 0x7FFFFFF0u, 0, 0);
     }
     return;
   }
@@ -573,8 +589,8 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     const rsrc_t rR = make_rsrc(Yref, (uint32_t)M * (uint32_t)N * 4u);
     double sum = 0.0;
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) {
-      const int n = col0 + wave * 64 + j * 16 + c;
+    for (int j = 0; j < kNTw; ++j) {
+      const int n = col0 + wave * 16 * kNTw + j * 16 + c;
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -593,7 +609,12 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     double *wsum = reinterpret_cast<double *>(sA0);
     if (lane == 0) wsum[wave] = sum;
     __syncthreads();
-    if (tid == 0) partials[tile] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    if (tid == 0) {
+      double t = wsum[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) t += wsum[w];
+      partials[tile] = t;
+    }
     return;
   }
   if constexpr (BF16X) {
@@ -611,7 +632,7 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
         const float inv = fe > 0.0f ? __builtin_bit_cast(float, 0x7F000000u - __builtin_bit_cast(uint32_t, fe))
                                     : 1.0f;
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) acc[i][j][e] *= inv;
+        for (int j = 0; j < kNTw; ++j) acc[i][j][e] *= inv;
       }
     }
   }
@@ -626,19 +647,20 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     // start 16 banks apart) and stores them as whole 16-byte pieces, 8 lanes
     // per row.  Waves 0-1 use sA0, waves 2-3 sA1, once every wave is past
     // the main loop.
-    constexpr int kRowB = 64 * 2 + 16;
+    constexpr int kRowB = 16 * kNTw * 2 + 16;
+    constexpr int kLpr = 2 * kNTw;                      // lanes per row: 16 bytes each
     constexpr int kHalf = kBM / 2;
-    static_assert(2 * kHalf * kRowB <= kBM * kBK * 2, "epilogue staging exceeds the A buffers");
+    static_assert(NW / 2 * kHalf * kRowB <= kBM * kBK * 2, "epilogue staging exceeds the A buffers");
     __syncthreads();
-    char *region = reinterpret_cast<char *>(wave < 2 ? sA0 : sA1) + (wave & 1) * kHalf * kRowB;
-    const int nb = col0 + wave * 64;
+    char *region = reinterpret_cast<char *>(wave < NW / 2 ? sA0 : sA1) + (wave % (NW / 2)) * kHalf * kRowB;
+    const int nb = col0 + wave * 16 * kNTw;
     const bool vec = (N & 7) == 0;                      // 16-byte aligned rows of Y
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int i = h * (MT / 2); i < (h + 1) * (MT / 2); ++i)
 #pragma unroll
-        for (int j = 0; j < kNT; ++j)
+        for (int j = 0; j < kNTw; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = (i - h * (MT / 2)) * 16 + 4 * kq + e;
@@ -649,8 +671,8 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
       __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): this wave's writes landed
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int it = 0; it < kHalf / 8; ++it) {
-        const int r = it * 8 + (lane >> 3), q = lane & 7;
+      for (int it = 0; it < kHalf * kLpr / 64; ++it) {
+        const int r = it * (64 / kLpr) + lane / kLpr, q = lane % kLpr;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(region + r * kRowB + q * 16);
         const int m = row0 + h * kHalf + r, n = nb + 8 * q;
         if (m >= M || n >= N) continue;
@@ -671,8 +693,8 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     return;
   }
 #pragma unroll
-  for (int j = 0; j < kNT; ++j) {
-    const int n = col0 + wave * 64 + j * 16 + c;
+  for (int j = 0; j < kNTw; ++j) {
+    const int n = col0 + wave * 16 * kNTw + j * 16 + c;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -693,14 +715,14 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 
 // One wave per SIMD: accumulators, two dequantized blocks and the weight
 // window (two or four blocks) live in registers.
-template <int GS, int YT, int MT, bool KTAIL, bool BF16X, int EPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int GS, int YT, int MT, bool KTAIL, bool BF16X, int EPI, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_f16_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
                      const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
                      int M, int N, int K, void *__restrict__ Y, SplitK sk,
                      const float *__restrict__ rowf, const float *__restrict__ Yref,
                      double *__restrict__ partials) {
-  gemm_f16_body<GS, YT, MT, KTAIL, BF16X, EPI>(X, qweight, scales, zeros, M, N, K, Y, sk, rowf,
+  gemm_f16_body<GS, YT, MT, KTAIL, BF16X, EPI, NW>(X, qweight, scales, zeros, M, N, K, Y, sk, rowf,
                                                Yref, partials);
 }
 
@@ -710,12 +732,13 @@ void gemm_f16_kernel(const uint16_t *__restrict__ X, const uint32_t *__restrict_
 // l & 15).  Every CU takes a share of the partials: summing them in the GEMM
 // kernel's last workgroup of each tile was bound by that one CU's load
 // bandwidth (measured 25% slower at 6 splits, 3% at 2).
-template <int YT, int MT, bool BF16X, int NS>
+template <int YT, int MT, bool BF16X, int NS, int NW>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ partials,
                                                             int splits, int M, int N,
                                                             void *__restrict__ Y,
                                                             const float *__restrict__ rowf) {
-  constexpr int kTiles = MT * kNT;
+  constexpr int kNTw = 16 / NW;
+  constexpr int kTiles = MT * kNTw;    // fragments per GEMM wave
   constexpr int kBM = 16 * MT;
   const int tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM;
   // kTiles workgroups per output tile (4 GEMM waves x kTiles fragments x 64
@@ -723,12 +746,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
   // b / MT in row tile i = b % MT, its own wave j those of 16x16 tile (i, j).
   // Everything but j and the lane is uniform per workgroup, so the tile's
   // coordinates and the dead-row test are scalar work.
-  const int tile = (int)(blockIdx.x / kTiles);
+  const int tile = (int)(blockIdx.x / (4 * MT));
   if (tile >= tiles_m * tiles_n) return;
-  const int bt = (int)(blockIdx.x % kTiles);
-  const int wave = bt / MT, i = bt % MT;
-  const int j = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = i * kNT + j;
+  // fragment f of the tile, in the partials' [wave][i][j] order
+  const int f = (int)(blockIdx.x % (4 * MT)) * 4 + (threadIdx.x >> 6);
+  const int wave = f / kTiles, i = (f / kNTw) % MT, j = f % kNTw;
+  const int lane = threadIdx.x & 63;
+  const int t = i * kNTw + j;
   // one row of tiles (M within one tile: the common split-K case) needs no
   // division before the loads can start
   int tm = 0, tn = tile;
@@ -739,9 +763,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
   const int c = lane & 15, kq = lane >> 4;
   // [tile][split][wave][t][lane] of 16 bytes (below 32 MiB: K is split only
   // for fewer than kSlots tiles of at most 128 x 256)
-  constexpr uint32_t kSplitBytes = 4u * kTiles * 64u * 16u;
+  constexpr uint32_t kSplitBytes = (uint32_t)NW * kTiles * 64u * 16u;
   const rsrc_t rP = make_rsrc(partials, (uint32_t)(tiles_m * tiles_n) * (uint32_t)splits * kSplitBytes);
-  const uint32_t base = ((uint32_t)tile * (uint32_t)splits * 4u * kTiles +
+  const uint32_t base = ((uint32_t)tile * (uint32_t)splits * (uint32_t)(NW * kTiles) +
                          (uint32_t)(wave * kTiles + t)) * 1024u + (uint32_t)lane * 16u;
   // Every split's load is issued before the first is used (a loop adding
   // each as it arrived waited for them one by one).  NS >= splits is the
@@ -759,7 +783,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
   for (int sp = 1; sp < NS; ++sp)
 #pragma unroll
     for (int e = 0; e < 4; ++e) sum[e] = sp < splits ? sum[e] + part[sp][e] : sum[e];
-  const int n = tn * kBN + wave * 64 + j * 16 + c;
+  const int n = tn * kBN + wave * 16 * kNTw + j * 16 + c;
   if (n >= N) return;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -867,24 +891,25 @@ hipError_t f16_launch_mt(const uint16_t *X, const uint32_t *qw, const uint16_t *
     const int64_t tiles = ((mm + bm - 1) / bm) * ((N + kBN - 1) / kBN);
     const dim3 grid((unsigned)(tiles * sk.splits));
     void *y = reinterpret_cast<char *>(Y) + m0 * N * ysize;
-    gemm_f16_kernel<GS, YT, MT, KTAIL, BF16X, 0><<<grid, kThreads, 0, st>>>(
+    constexpr int NW = gemm_waves(MT);
+    gemm_f16_kernel<GS, YT, MT, KTAIL, BF16X, 0, NW><<<grid, 64 * NW, 0, st>>>(
         X + m0 * K, qw, sc, zr, (int)mm, (int)N, (int)K, y, sk, rowf ? rowf + m0 : nullptr,
         nullptr, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (MT < 16) {
       if (sk.splits > 1) {
-        // kTiles = MT * kNT reduction workgroups per output tile
-        const dim3 rgrid((unsigned)(tiles * MT * kNT));
+        // 4 * MT reduction workgroups per output tile (four fragments each)
+        const dim3 rgrid((unsigned)(tiles * MT * 4));
         const float *rf = rowf ? rowf + m0 : nullptr;
         if (sk.splits <= 2)
-          splitk_reduce_kernel<YT, MT, BF16X, 2><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
+          splitk_reduce_kernel<YT, MT, BF16X, 2, NW><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
         else if (sk.splits <= 4)
-          splitk_reduce_kernel<YT, MT, BF16X, 4><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
+          splitk_reduce_kernel<YT, MT, BF16X, 4, NW><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
         else if (sk.splits <= 8)
-          splitk_reduce_kernel<YT, MT, BF16X, 8><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
+          splitk_reduce_kernel<YT, MT, BF16X, 8, NW><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
         else
-          splitk_reduce_kernel<YT, MT, BF16X, kMaxSplits><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
+          splitk_reduce_kernel<YT, MT, BF16X, kMaxSplits, NW><<<rgrid, 256, 0, st>>>(sk.partials, sk.splits, (int)mm, (int)N, y, rf);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
       }
@@ -1021,7 +1046,7 @@ static hipError_t loss_go(const uint16_t *A, const uint32_t *qw, const uint16_t 
   for (int64_t m0 = 0; m0 < M; m0 += rows) {
     const int64_t mm = M - m0 < rows ? M - m0 : rows;
     const int64_t tiles = ((mm + bm - 1) / bm) * ((N + kBN - 1) / kBN);
-    gemm_f16_kernel<GS, (int)YType::F32, 8, KTAIL, false, 1><<<dim3((unsigned)tiles), kThreads, 0, st>>>(
+    gemm_f16_kernel<GS, (int)YType::F32, 8, KTAIL, false, 1, 4><<<dim3((unsigned)tiles), 256, 0, st>>>(
         A + m0 * K, qw, sc, zr, (int)mm, (int)N, (int)K, nullptr, SplitK{1, nullptr},
         nullptr, Yref + m0 * N, partials + tile_base);
     tile_base += tiles;
