@@ -713,7 +713,7 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   }
 }
 
-// One wave per SIMD: accumulators, two dequantized blocks and the weight
+// NW / 4 waves per SIMD: accumulators, two dequantized blocks and the weight
 // window (two or four blocks) live in registers.
 template <int GS, int YT, int MT, bool KTAIL, bool BF16X, int EPI, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
