@@ -186,7 +186,7 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
 
   // ---- packed weights of one K block (registers) ------------------------------
   // Lane (c, kq) holds, for column tile j, words kq*kWpl .. kq*kWpl+kWpl-1 of
-  // each group of column col0 + 64*wave + 16*j + c: channels
+  // each group of column col0 + 16*kNTw*wave + 16*j + c: channels
   // 8*(kq*kWpl + w) .. +7 of the group, for MFMA step gi*kWpl + w.
   const uint32_t lane_col = (uint32_t)(col0 + wave * 16 * kNTw + c);
   const rsrc_t rQ = make_rsrc(qweight, (uint32_t)N * (uint32_t)K / 2u);
@@ -220,8 +220,9 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
   // Thread t loads column col0 + t's scale(s) and zero point(s) of a block
   // (one or two loads instead of one per lane and column tile) and stores
   // them as u32 (zero << 16 | scale) at [group][wave][c][j] with
-  // t = 64 * wave + 16 * j + c, so that lane (c, kq) reads its four column
-  // tiles' values with one 16-byte LDS read per group.
+  // t = 16 * kNTw * wave + 16 * j + c, so that lane (c, kq) reads its kNTw
+  // column tiles' values with one LDS read per group.  (Eight waves: the
+  // first four load and store, one thread per column of the tile.)
   const rsrc_t rS = make_rsrc(scales, (uint32_t)N * (uint32_t)G * 2u);
   // no zeros (the symmetric grid): every zero load reads 0, and 8 is added
   const rsrc_t rZ = make_rsrc(zeros, zeros ? (uint32_t)N * (uint32_t)G : 0u);
@@ -642,11 +643,11 @@ __device__ __forceinline__ void gemm_f16_body(const uint16_t *__restrict__ X,
     // 16-bit output of the 128- and 256-row tiles through LDS: an MFMA result
     // lane holds 4 rows of one column, so direct stores write 32-byte pieces
     // of 4 rows each (measured about twice the bytes of Y reaching HBM).
-    // Each wave turns its 64 columns, half the rows at a time, into rows of
-    // 128 bytes in LDS (rows 144 bytes apart: the 4 row groups of a store
-    // start 16 banks apart) and stores them as whole 16-byte pieces, 8 lanes
-    // per row.  Waves 0-1 use sA0, waves 2-3 sA1, once every wave is past
-    // the main loop.
+    // Each wave turns its 16 * kNTw columns, half the rows at a time, into
+    // rows in LDS (with four waves: 128 bytes, 144 apart, so the 4 row groups
+    // of a store start 16 banks apart) and stores them as whole 16-byte
+    // pieces, kLpr lanes per row.  The first half of the waves use sA0, the
+    // rest sA1, once every wave is past the main loop.
     constexpr int kRowB = 16 * kNTw * 2 + 16;
     constexpr int kLpr = 2 * kNTw;                      // lanes per row: 16 bytes each
     constexpr int kHalf = kBM / 2;
