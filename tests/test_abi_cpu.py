@@ -204,6 +204,29 @@ def test_noalloc_rejects_beyond_its_static_scratch():
                                           FAKE, 2, NULL) == binding.AWQ_ERR_UNSUPPORTED
 
 
+def test_batched_split_plan():
+    """The batched-decode kernel's split count (host logic, read off its
+    workspace: splits x M x N fp32 partials).  The plan minimizes the busiest
+    CU's groups (workgroups per CU times groups per split) plus 1.1 per split
+    plus 4 for a second residency round; these are the picks that same-box
+    sweeps of every split count put at (or within 0.5 us of) the fastest."""
+    B = binding.AWQ_KERNEL_BATCHED
+
+    def splits(M, N, K, g):
+        w = _wsz(M, N, K, g, kernel=B)
+        assert w % (M * N * 4) == 0
+        return w // (M * N * 4)
+    assert splits(16, 11008, 4096, 128) == 2     # 172 workgroups, one round
+    assert splits(16, 13824, 5120, 128) == 4     # 432 workgroups
+    assert splits(16, 5120, 13824, 128) == 12    # 480 workgroups of 9 groups
+    assert splits(16, 13824, 5120, 64) == 4      # not 7: that needs a second round
+    assert splits(32, 13824, 5120, 128) == 7     # 8 groups per split at most
+    assert splits(8, 4096, 4096, 128) == 4
+    # a range of at most 2048 / (g * ceil(M/16)) groups: 4096 / 128 = 32
+    # groups at M = 64 need 8 splits even without a cost model
+    assert splits(64, 4096, 4096, 128) >= 8
+
+
 def test_linear_dispatch_rule():
     """The automatic kernel choice of a call with scratch (awq_linear_ws,
     awq_linear_ex with a workspace; host logic, no GPU): the batched-decode
