@@ -411,7 +411,7 @@ def awq_linear_noalloc(X, qweight, scales, zeros, group_size: int = 128, out_dty
     M, N, K, out, dev = _linear_args(X, qweight, scales, zeros, group_size, out_dtype, out)
     st = lib.awq_linear_noalloc(_ptr(X), _dtype_code(X.dtype), _ptr(qweight), _ptr(scales),
                                 _zp_ptr(zeros), M, N, K,
-                           config(group_size, zero_point=zeros is not None), _ptr(out),
+                                config(group_size, zero_point=zeros is not None), _ptr(out),
                                 _dtype_code(out.dtype), _stream(dev))
     check(st, "awq_linear_noalloc")
     return out
