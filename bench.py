@@ -11,12 +11,15 @@ before the timed region.  The steps are replayed from HIP graphs that hold the
 ten rotation steps back to back (the timed region runs exactly --steps steps).
 
 Also measured after the timed region ("rows"): quantize/pack, GEMV at M=4,
-GEMM at M=1 (for the GEMV-vs-GEMM comparison), batched GEMM at M=16/64/256
-(13B-class MLP, g64 and g128), prefill GEMM at M=4096 (70B-class, fp16 and
-bf16), fused QKV and gate/up projections at M=1, and the full alpha search on
-a 4096^3 layer (plain, with duo scaling, with weight clipping).
+GEMM at M=1 (for the GEMV-vs-GEMM comparison), batched rows at M=16/64/256
+(13B-class MLP, g64 and g128; the automatic choice with a workspace: the
+batched-decode kernel at M=16, the split-K GEMM above), prefill GEMM at
+M=4096 (70B-class, fp16 and bf16), fused QKV and gate/up projections at M=1,
+and the full alpha search on a 4096^3 layer (plain, with duo scaling, with
+weight clipping), each with the CPU oracle timed beside it.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows all|none]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows all|gemm|none]
+                       [--no-cpu-baseline] [--calibrate-copy]
 """
 
 from __future__ import annotations
