@@ -151,9 +151,13 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
     u32x4 a[U][kWpl];      // used only when activations are not staged
   };
   // Packed weights (and, without staging, activations) of groups
-  // g0, g0 + NW, ..., g0 + (U-1)*NW.  No load is issued for a group past the
-  // end (g is uniform across the wave, so this is a scalar branch): its
-  // registers keep stale values, which the zero scale of such a group cancels.
+  // g0, g0 + NW, ..., g0 + (U-1)*NW.  Every batch issues the same number of
+  // load instructions: a group past the end loads from an offset beyond every
+  // buffer, which the range check turns into zeros without a memory access
+  // (and the zero scale of such a group cancels whatever it computes).  A
+  // fixed count lets every wait for a batch be a counted vmcnt that leaves
+  // the next batch in flight; a conditional load between a load and its use
+  // makes the compiler wait for all loads instead.
   // Packed weights with the non-temporal hint when the workgroup owns its CU
   // (16 waves, at most 256 column tiles): 2-4% faster on those layers at
   // M = 1 and 4, while on layers of 688 and more workgroups the hint measured
@@ -163,8 +167,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int g = g0 + u * NW;
-      if (g >= G) continue;
-      const uint32_t qo = q_lane + (uint32_t)g * (GS / 2);
+      const uint32_t qo = g < G ? q_lane + (uint32_t)g * (GS / 2) : 0x7FFFFFF0u;
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         if constexpr (kWpl == 4) {
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
         }
       }
       if constexpr (!STAGE_X) {
-        const uint32_t xo = x_lane + (uint32_t)g * (GS * 2);
+        const uint32_t xo = g < G ? x_lane + (uint32_t)g * (GS * 2) : 0x7FFFFFF0u - 16u * kWpl;
 #pragma unroll
         for (int j = 0; j < kWpl; ++j)
           b.a[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, xo + 16u * j, 0, 0));
@@ -194,18 +197,71 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
   // barrier waits for the staging loads only (counted vmcnt), not for that
   // batch (an LDS DMA could only be waited for with vmcnt(0)):
   //  * activation rows, 16 bytes per thread and round (M*K*2 is a multiple
-  //    of 128 bytes, so no chunk straddles the end of X);
-  //  * scales and zero points of the 16 columns ([16][G], contiguous),
-  //    element by element (a 16-byte chunk could straddle the end of those
-  //    arrays, where the range check would zero it).
-  constexpr int kSZ = kGemvMaxSZ / (64 * NW);   // scale/zero elements per thread
+  //    of 128 bytes, so no chunk straddles the end of X); in a 16-wave
+  //    workgroup a wave whose chunks all lie past the end issues no load (in
+  //    the 8-wave kernel that skip made the compiler copy the staging
+  //    registers, and wait for their loads, before the first weight load);
+  //  * scales ([16][G] fp16, 32*G bytes) and zero points ([16][G] u8, 16*G
+  //    bytes) of the 16 columns, both contiguous.
+  // Every load instruction occupies the CU's address unit for the same ~16
+  // clocks whatever its width.  A 16-wave workgroup owns its CU, and its
+  // staging took 48-96 instructions element by element against 32-88 for
+  // its weights; it loads scales and zero points in 16-byte chunks instead
+  // (measured 0.2-0.5 us faster per layer).  8-wave workgroups share a CU
+  // two or three at a time, and there the 16-byte chunks measured 0.3 us
+  // slower per launch (4096 x 11008), so they keep one element per lane.
+  constexpr bool kVecSZ = NW == 16;
   constexpr int kXR = STAGE_X ? gemv_stage_budget(NW) / (64 * NW * 16) : 1;   // X chunks per thread
-  const int nsz = (16 * G + 64 * NW - 1) / (64 * NW);   // uniform: rounds needed
   const uint32_t xbytes = STAGE_X ? (uint32_t)M * L.xrow : 0u;
   const int nxr = (int)((xbytes + 64u * NW * 16u - 1u) / (64u * NW * 16u));
-  uint32_t sreg[NP][kSZ], zreg[NP][kSZ];
   u32x4 xreg[kXR];
-  {
+  // 16-byte chunks (16-wave workgroups).  The tile starts at element
+  // 16*tile*G, so both blocks are 16-byte aligned.  A chunk across the end of
+  // the arrays would read as zero under the range check; that happens only
+  // in a partial last tile with N*G not a multiple of 16, which stages
+  // element by element after the first weight batch instead.  The chunks are
+  // dealt out in wave-sized slots (slot v = wave + r * NW), each segment
+  // starting on a slot boundary, so every load instruction reads one array
+  // (a uniform buffer resource): per weight set, ceil(2G/64) slots of
+  // scales, then ceil(G/64) of zero points.
+  const int ws = (2 * G + 63) / 64, wz = (G + 63) / 64;
+  const bool sz_vec = kVecSZ && (n0 + 16 <= N || ((N * G) & 15) == 0);
+  constexpr int kSZV = kVecSZ ? (NP * (kGemvMaxSZ / 512 + kGemvMaxSZ / 1024) + NW - 1) / NW : 1;
+  const int nslots = NP * (ws + wz);
+  // slot v (uniform): weight set, array, and the byte offsets of this lane's
+  // chunk in global memory (beyond every buffer when past the segment) and LDS
+  auto sz_slot = [&](int v, int &set, bool &is_zero, uint32_t &gofs, uint32_t &lofs) {
+    set = v >= ws + wz ? 1 : 0;
+    const int u = v - set * (ws + wz);
+    is_zero = u >= ws;
+    const int j = (is_zero ? u - ws : u) * 64 + lane;
+    gofs = j < (is_zero ? G : 2 * G)
+               ? (uint32_t)n0 * (uint32_t)G * (is_zero ? 1u : 2u) + 16u * (uint32_t)j : 0x7FFFFFF0u;
+    // arithmetic on the layout of gemv_smem, not an index into L: a runtime
+    // index puts L in scratch memory, whose load waits for every load in flight
+    const uint32_t sbytes = kib_up(32u * (uint32_t)G), zbytes = kib_up(16u * (uint32_t)G);
+    lofs = L.soff[0] + (uint32_t)set * (sbytes + zbytes) + (is_zero ? sbytes : 0u) + 16u * (uint32_t)j;
+  };
+  u32x4 szreg[kSZV];
+  // One element per lane (8-wave workgroups).
+  constexpr int kSZ = kVecSZ ? 1 : kGemvMaxSZ / (64 * NW);   // scale/zero elements per thread
+  const int nsz = (16 * G + 64 * NW - 1) / (64 * NW);         // uniform: rounds needed
+  uint32_t sreg[NP][kSZ], zreg[NP][kSZ];
+  if constexpr (kVecSZ) {
+    if (sz_vec) {
+#pragma unroll
+      for (int r = 0; r < kSZV; ++r) {
+        const int v = wave + r * NW;
+        if (v >= nslots) break;
+        int set;
+        bool z;
+        uint32_t go, lo;
+        sz_slot(v, set, z, go, lo);
+        const rsrc_t rr = z ? (set ? rZ[NP - 1] : rZ[0]) : (set ? rS[NP - 1] : rS[0]);
+        szreg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, go, 0, 0));
+      }
+    }
+  } else {
     const uint32_t base = (uint32_t)n0 * (uint32_t)G;
 #pragma unroll
     for (int r = 0; r < kSZ; ++r) {
@@ -218,23 +274,49 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
         zreg[s][r] = __builtin_amdgcn_raw_buffer_load_b8(rZ[s], o, 0, 0);
       }
     }
-    if constexpr (STAGE_X) {
+  }
+  if constexpr (STAGE_X) {
 #pragma unroll
-      for (int r = 0; r < kXR; ++r) {
-        if (r >= nxr) break;
-        const uint32_t o = (uint32_t)(tid + r * 64 * NW) * 16u;
-        xreg[r] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, o < xbytes ? o : 0x7FFFFFF0u, 0, 0));
-      }
+    for (int r = 0; r < kXR; ++r) {
+      if (r >= nxr || (kVecSZ && (uint32_t)(wave * 64 + r * 64 * NW) * 16u >= xbytes)) break;
+      const uint32_t o = (uint32_t)(tid + r * 64 * NW) * 16u;
+      xreg[r] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, o < xbytes ? o : 0x7FFFFFF0u, 0, 0));
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // First batch of packed weights, behind the staging loads.
-  Batch cur, nxt;
-  load_batch(wave, cur);
+  Batch bA, bB;
+  load_batch(wave, bA);
   __builtin_amdgcn_sched_barrier(0);
-  {
+  if constexpr (kVecSZ) {
+    if (sz_vec) {
+#pragma unroll
+      for (int r = 0; r < kSZV; ++r) {
+        const int v = wave + r * NW;
+        if (v >= nslots) break;
+        int set;
+        bool z;
+        uint32_t go, lo;
+        sz_slot(v, set, z, go, lo);
+        if (go != 0x7FFFFFF0u) *reinterpret_cast<u32x4 *>(smem + lo) = szreg[r];
+      }
+    } else {
+      // partial last tile with a chunk across the end of the arrays
+      const uint32_t base = (uint32_t)n0 * (uint32_t)G;
+      for (int i = tid; i < 16 * G; i += 64 * NW) {
+        const uint32_t o = base + (uint32_t)i;
+#pragma unroll
+        for (int s = 0; s < NP; ++s) {
+          reinterpret_cast<uint16_t *>(smem + L.soff[s])[i] =
+              (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rS[s], o * 2u, 0, 0);
+          reinterpret_cast<uint8_t *>(smem + L.zoff[s])[i] =
+              (uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rZ[s], o, 0, 0);
+        }
+      }
+    }
+  } else {
 #pragma unroll
     for (int r = 0; r < kSZ; ++r) {
       if (r >= nsz) break;
@@ -247,13 +329,13 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
         }
       }
     }
-    if constexpr (STAGE_X) {
+  }
+  if constexpr (STAGE_X) {
 #pragma unroll
-      for (int r = 0; r < kXR; ++r) {
-        if (r >= nxr) break;
-        const uint32_t o = (uint32_t)(tid + r * 64 * NW) * 16u;
-        if (o < xbytes) *reinterpret_cast<u32x4 *>(smem + o) = xreg[r];
-      }
+    for (int r = 0; r < kXR; ++r) {
+      if (r >= nxr || (kVecSZ && (uint32_t)(wave * 64 + r * 64 * NW) * 16u >= xbytes)) break;
+      const uint32_t o = (uint32_t)(tid + r * 64 * NW) * 16u;
+      if (o < xbytes) *reinterpret_cast<u32x4 *>(smem + o) = xreg[r];
     }
   }
   __syncthreads();
@@ -269,11 +351,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
   for (int s = 0; s < NP; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const DeqRegs dq;
 
-  // Software pipeline: the next batch's loads are in flight while this batch
-  // is dequantized and multiplied.
-  for (int g0 = wave; g0 < G; g0 += NW * U) {
-    load_batch(g0 + NW * U, nxt);
-    __builtin_amdgcn_sched_barrier(0);
+  // Batch i of this wave holds groups wave + i*NW*U + u*NW (u < U).
+  auto compute = [&](const Batch &cur, int g0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int g = g0 + u * NW;
@@ -283,7 +362,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
       for (int j = 0; j < kWpl; ++j) {
         if constexpr (STAGE_X)
           a[j] = *reinterpret_cast<const u32x4 *>(xlds + (uint32_t)gs * (GS * 2) + 16u * j);
-        else  // a group past the end loaded nothing: its stale registers may hold any bits
+        else
           a[j] = g < G ? cur.a[u][j] : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
@@ -304,7 +383,32 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
         for (int e = 0; e < 4; ++e) acc[s][e] = __builtin_fmaf(t[e], sc, acc[s][e]);
       }
     }
-    cur = nxt;
+  };
+
+  // Software pipeline over two register sets: while one batch is dequantized
+  // and multiplied, the next one's loads are in flight.  The steady-state
+  // loop body issues exactly one batch before each computed batch, and the
+  // last one or two batches are peeled, so no load is ever conditional and
+  // no register copy forces a wait.
+  const int nb = wave < G ? (G - wave + NW * U - 1) / (NW * U) : 0;   // uniform
+  int i = 0;
+  for (; i + 2 < nb; i += 2) {
+    const int g0 = wave + i * NW * U;
+    load_batch(g0 + NW * U, bB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bA, g0);
+    load_batch(g0 + 2 * NW * U, bA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bB, g0 + NW * U);
+  }
+  if (nb - i == 2) {
+    const int g0 = wave + i * NW * U;
+    load_batch(g0 + NW * U, bB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bA, g0);
+    compute(bB, g0 + NW * U);
+  } else if (nb - i == 1) {
+    compute(bA, wave + i * NW * U);
   }
 
   __syncthreads();
@@ -351,8 +455,9 @@ static void gemv_launch(const uint16_t *X, const GemvParts &parts, int tiles, in
   // the reduction reuses the buffer: at least NP * NW * 64 * 16 bytes
   const uint32_t need = (uint32_t)NP * 64u * NW * 16u;
   const uint32_t bytes = L.total > need ? L.total : need;
-  // Two batches in flight once a wave walks more than 8 groups (measured 7%
-  // faster at 13.5 groups per wave, slower at 5 and below).
+  // Two groups per batch once a wave walks more than 8 groups (measured 7%
+  // faster at 13.5 groups per wave, slower at 5 and below: 4096 x 4096 and
+  // 4096 x 11008 at M = 1 and 4 took 1-10% longer with two).
   if (stage && G > 8 * NW)
     gemv_kernel<XT, GS, NW, 2, true, NP, MULTI><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
   else if (stage)
@@ -364,7 +469,7 @@ static void gemv_launch(const uint16_t *X, const GemvParts &parts, int tiles, in
 // Waves per workgroup.  Every workgroup of a launch should be resident at
 // once (a second partial round of workgroups costs a whole extra memory
 // latency): with at most one workgroup per CU (at most 256 column tiles) the
-// workgroup takes 16 waves, otherwise 8.  One group per wave is in flight ahead
+// workgroup takes 16 waves, otherwise 8.  One batch per wave is in flight ahead
 // of the one being computed: deeper windows were measured slower on MI355X
 // (every wave's staging loads then queue behind more weight traffic).
 template <class XT, int GS, int NP>

@@ -47,8 +47,8 @@ def test_host_code_under_asan_and_ubsan():
                         os.path.join(HERE, "host_abi_check.cpp"), "-o", drv],
                        check=True, capture_output=True, text=True)
         # the link line pulls in the sanitizer runtimes (host only)
-        link = subprocess.run([B.hipcc(), "-fsanitize=address", "-fsanitize=undefined",
-                               "-fno-gpu-sanitize", drv, lib, "-o", exe, f"-Wl,-rpath,{tmp}"],
+        link_flags = ["-fno-gpu-sanitize", "-fsanitize=address", "-fsanitize=undefined"]
+        link = subprocess.run([B.hipcc(), *link_flags, drv, lib, "-o", exe, f"-Wl,-rpath,{tmp}"],
                               capture_output=True, text=True)
         assert link.returncode == 0, link.stdout + link.stderr
         env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
