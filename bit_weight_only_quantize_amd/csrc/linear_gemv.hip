@@ -47,13 +47,16 @@ __host__ __device__ constexpr int gemv_waves(int64_t N) { return gemv_waves_for_
 __host__ __device__ constexpr uint32_t gemv_stage_budget(int nw) {
   return nw == 16 ? kGemvStageBytesSolo : kGemvStageBytes;
 }
+// LDS a workgroup may take: the CU's 160 KiB alone, or 80 KiB two per CU.
+__host__ __device__ constexpr uint32_t gemv_lds_cap(int nw) { return nw == 16 ? 160u * 1024u : 80u * 1024u; }
 
 // LDS layout (dynamic shared memory, byte offsets; every region starts on a
 // 1 KiB boundary):
 //   [0, xbytes)              activation rows 0..M-1 (when staged)
 //   [soff[i], ...)           scales of the 16 columns of weight set i, fp16 bits, [16][G]
 //   [zoff[i], ...)           zero points of those columns, u8, [16][G]
-// The cross-wave reduction reuses the start of the buffer after the loop.
+//   [total, ...)             cross-wave partials, [NP][M][16] outputs x (NW + 4) floats,
+//                            when they fit; else they reuse the start of the buffer
 
 struct GemvSmem {
   uint32_t xrow;     // bytes per activation row (K * 2)
@@ -411,37 +414,51 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
     compute(bA, wave + i * NW * U);
   }
 
-  __syncthreads();
-  f32x4 *red = reinterpret_cast<f32x4 *>(smem);
-#pragma unroll
-  for (int s = 0; s < NP; ++s) red[(s * NW + wave) * 64 + lane] = acc[s];
-  __syncthreads();
-  if (wave != 0) return;
-  f32x4 sum[NP];
+  // Cross-wave sum.  Wave w's partial of output (m, c) goes to
+  // red[(s*M*16 + m*16 + c) * kRS + w]: the NW partials of one output are
+  // contiguous (kRS = NW + 4 floats per output keeps rows 16-byte aligned and
+  // the 16 lanes of a row of outputs on distinct banks), so thread t < M*16
+  // sums output t with NW/4 16-byte reads, in wave order as before.  The
+  // partials have their own LDS region after the staged data when it fits
+  // (one barrier); otherwise they reuse the start of the buffer, after a
+  // barrier that waits for every wave to leave the loop.
+  constexpr int kRS = NW + 4;
+  const uint32_t red_bytes = (uint32_t)NP * (uint32_t)M * 16u * kRS * 4u;
+  const bool red_alias = L.total + red_bytes > gemv_lds_cap(NW);
+  if (red_alias) __syncthreads();
+  float *red = reinterpret_cast<float *>(smem + (red_alias ? 0u : L.total));
 #pragma unroll
   for (int s = 0; s < NP; ++s) {
-    sum[s] = red[s * NW * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      const f32x4 o = red[(s * NW + w) * 64 + lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sum[s][e] += o[e];
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * kq + e;
+      if (m < M) red[((s * M + m) * 16 + c) * kRS + wave] = acc[s][e];
     }
   }
-  if (n >= N) return;
+  __syncthreads();
+  if (tid >= M * 16) return;
+  const int om = tid >> 4, oc = tid & 15;
+  const int on = n0 + oc;
+  if (on >= N) return;
+  float sum[NP];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int m = 4 * kq + e;
-    if (m >= M) continue;
-    const int64_t o = (int64_t)m * N + n;
-    const float v = NP == 2 ? silu(sum[0][e]) * sum[1][e] : sum[0][e];
-    if (ytype == (int)YType::F16)
-      reinterpret_cast<uint16_t *>(Y)[o] = float_to_half_bits(v);
-    else if (ytype == (int)YType::BF16)
-      reinterpret_cast<uint16_t *>(Y)[o] = float_to_bf16_bits(v);
-    else
-      reinterpret_cast<float *>(Y)[o] = v;
+  for (int s = 0; s < NP; ++s) {
+    const f32x4 *row = reinterpret_cast<const f32x4 *>(red + ((s * M + om) * 16 + oc) * kRS);
+    f32x4 part[NW / 4];
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) part[i] = row[i];
+    sum[s] = part[0][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) sum[s] += part[w >> 2][w & 3];
   }
+  const int64_t o = (int64_t)om * N + on;
+  const float v = NP == 2 ? silu(sum[0]) * sum[1] : sum[0];
+  if (ytype == (int)YType::F16)
+    reinterpret_cast<uint16_t *>(Y)[o] = float_to_half_bits(v);
+  else if (ytype == (int)YType::BF16)
+    reinterpret_cast<uint16_t *>(Y)[o] = float_to_bf16_bits(v);
+  else
+    reinterpret_cast<float *>(Y)[o] = v;
 }
 
 
@@ -452,9 +469,10 @@ static void gemv_launch(const uint16_t *X, const GemvParts &parts, int tiles, in
   const int G = (int)(K / GS);
   const bool stage = (uint64_t)M * (uint64_t)K * 2u <= gemv_stage_budget(NW);
   const GemvSmem L = gemv_smem(M, (int)K, G, stage, NP);
-  // the reduction reuses the buffer: at least NP * NW * 64 * 16 bytes
-  const uint32_t need = (uint32_t)NP * 64u * NW * 16u;
-  const uint32_t bytes = L.total > need ? L.total : need;
+  // the cross-wave partials: after the staged data when that fits, else
+  // over its start (the kernel makes the same choice)
+  const uint32_t red = (uint32_t)NP * (uint32_t)M * 16u * (NW + 4) * 4u;
+  const uint32_t bytes = L.total + red <= gemv_lds_cap(NW) ? L.total + red : (L.total > red ? L.total : red);
   // Two groups per batch once a wave walks more than 8 groups (measured 7%
   // faster at 13.5 groups per wave, slower at 5 and below: 4096 x 4096 and
   // 4096 x 11008 at M = 1 and 4 took 1-10% longer with two).
@@ -502,8 +520,7 @@ bool gemv_supported(int64_t M, int64_t N, int64_t K, int gs, int np) {
   const int nw = np == 2 ? 8 : gemv_waves(N);
   const bool stage = (uint64_t)M * (uint64_t)K * 2u <= gemv_stage_budget(nw);
   const GemvSmem L = gemv_smem((int)M, (int)K, (int)G, stage, np);
-  const uint32_t lds = nw == 16 ? 160u * 1024u : 80u * 1024u;
-  return M <= 16 && 16 * G <= kGemvMaxSZ && L.total <= lds && N * K / 2 < 0x7FFFFFF0;
+  return M <= 16 && 16 * G <= kGemvMaxSZ && L.total <= gemv_lds_cap(nw) && N * K / 2 < 0x7FFFFFF0;
 }
 
 namespace {
