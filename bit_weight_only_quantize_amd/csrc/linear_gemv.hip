@@ -109,7 +109,11 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 //
 // MULTI: more than one part (a single part reads its pointers at fixed
 // argument offsets, with no dependent lookup before the first load).
-template <class XT, int GS, int NW, int U, bool STAGE_X, int NP, bool MULTI>
+// SMALL: the staging needs at most two activation rounds and one scale/zero
+// round; the staging loops then unroll to that, not to the LDS budget's
+// maximum (8 rounds), and the kernel's code shrinks by up to a third
+// (measured 0.1-0.3 us per launch on the decode layers).
+template <class XT, int GS, int NW, int U, bool STAGE_X, int NP, bool MULTI, bool SMALL>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restrict__ X,
                                                        GemvParts parts, int M, int K, int ytype,
                                                        uint32_t zfix) {
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
   // two or three at a time, and there the 16-byte chunks measured 0.3 us
   // slower per launch (4096 x 11008), so they keep one element per lane.
   constexpr bool kVecSZ = NW == 16;
-  constexpr int kXR = STAGE_X ? gemv_stage_budget(NW) / (64 * NW * 16) : 1;   // X chunks per thread
+  constexpr int kXR = !STAGE_X ? 1 : SMALL ? 2 : gemv_stage_budget(NW) / (64 * NW * 16);   // X chunks per thread
   const uint32_t xbytes = STAGE_X ? (uint32_t)M * L.xrow : 0u;
   const int nxr = (int)((xbytes + 64u * NW * 16u - 1u) / (64u * NW * 16u));
   u32x4 xreg[kXR];
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
   // scales, then ceil(G/64) of zero points.
   const int ws = (2 * G + 63) / 64, wz = (G + 63) / 64;
   const bool sz_vec = kVecSZ && (n0 + 16 <= N || ((N * G) & 15) == 0);
-  constexpr int kSZV = kVecSZ ? (NP * (kGemvMaxSZ / 512 + kGemvMaxSZ / 1024) + NW - 1) / NW : 1;
+  constexpr int kSZV = kVecSZ && !SMALL ? (NP * (kGemvMaxSZ / 512 + kGemvMaxSZ / 1024) + NW - 1) / NW : 1;
   const int nslots = NP * (ws + wz);
   // slot v (uniform): weight set, array, and the byte offsets of this lane's
   // chunk in global memory (beyond every buffer when past the segment) and LDS
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
   };
   u32x4 szreg[kSZV];
   // One element per lane (8-wave workgroups).
-  constexpr int kSZ = kVecSZ ? 1 : kGemvMaxSZ / (64 * NW);   // scale/zero elements per thread
+  constexpr int kSZ = kVecSZ || SMALL ? 1 : kGemvMaxSZ / (64 * NW);   // scale/zero elements per thread
   const int nsz = (16 * G + 64 * NW - 1) / (64 * NW);         // uniform: rounds needed
   uint32_t sreg[NP][kSZ], zreg[NP][kSZ];
   if constexpr (kVecSZ) {
@@ -476,12 +480,20 @@ static void gemv_launch(const uint16_t *X, const GemvParts &parts, int tiles, in
   // Two groups per batch once a wave walks more than 8 groups (measured 7%
   // faster at 13.5 groups per wave, slower at 5 and below: 4096 x 4096 and
   // 4096 x 11008 at M = 1 and 4 took 1-10% longer with two).
+  // staging rounds: activations (16 bytes per thread), and scale/zero slots
+  // (16-wave: one wave-slot of 16-byte chunks per wave) or elements (8-wave)
+  const uint32_t xr = (uint32_t)(((uint64_t)M * (uint64_t)K * 2u + 64u * NW * 16u - 1u) / (64u * NW * 16u));
+  const int szr = NW == 16 ? (NP * ((2 * G + 63) / 64 + (G + 63) / 64) + NW - 1) / NW
+                           : (16 * G + 64 * NW - 1) / (64 * NW);
+  const bool small = xr <= 2 && szr <= 1;
   if (stage && G > 8 * NW)
-    gemv_kernel<XT, GS, NW, 2, true, NP, MULTI><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
+    gemv_kernel<XT, GS, NW, 2, true, NP, MULTI, false><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
+  else if (stage && small && NP == 1)
+    gemv_kernel<XT, GS, NW, 1, true, NP, MULTI, true><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
   else if (stage)
-    gemv_kernel<XT, GS, NW, 1, true, NP, MULTI><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
+    gemv_kernel<XT, GS, NW, 1, true, NP, MULTI, false><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
   else
-    gemv_kernel<XT, GS, NW, 2, false, NP, MULTI><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
+    gemv_kernel<XT, GS, NW, 2, false, NP, MULTI, false><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
 }
 
 // Waves per workgroup.  Every workgroup of a launch should be resident at
