@@ -488,7 +488,7 @@ static void gemv_launch(const uint16_t *X, const GemvParts &parts, int tiles, in
   const bool small = xr <= 2 && szr <= 1;
   if (stage && G > 8 * NW)
     gemv_kernel<XT, GS, NW, 2, true, NP, MULTI, false><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
-  else if (stage && small && NP == 1)
+  else if (stage && small)
     gemv_kernel<XT, GS, NW, 1, true, NP, MULTI, true><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
   else if (stage)
     gemv_kernel<XT, GS, NW, 1, true, NP, MULTI, false><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
