@@ -255,7 +255,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
   const int nsz = (16 * G + 64 * NW - 1) / (64 * NW);         // uniform: rounds needed
   uint32_t sreg[NP][kSZ], zreg[NP][kSZ];
   if constexpr (kVecSZ) {
-    if (sz_vec) {
+    if (__builtin_expect(sz_vec, 1)) {
 #pragma unroll
       for (int r = 0; r < kSZV; ++r) {
         const int v = wave + r * NW;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
   load_batch(wave, bA);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (kVecSZ) {
-    if (sz_vec) {
+    if (__builtin_expect(sz_vec, 1)) {
 #pragma unroll
       for (int r = 0; r < kSZV; ++r) {
         const int v = wave + r * NW;
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
   constexpr int kRS = NW + 4;
   const uint32_t red_bytes = (uint32_t)NP * (uint32_t)M * 16u * kRS * 4u;
   const bool red_alias = L.total + red_bytes > gemv_lds_cap(NW);
-  if (red_alias) __syncthreads();
+  if (__builtin_expect(red_alias, 0)) __syncthreads();
   float *red = reinterpret_cast<float *>(smem + (red_alias ? 0u : L.total));
 #pragma unroll
   for (int s = 0; s < NP; ++s) {
