@@ -215,9 +215,11 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const uint16_t *__restric
   // staging took 48-96 instructions element by element against 32-88 for
   // its weights; it loads scales and zero points in 16-byte chunks instead
   // (measured 0.2-0.5 us faster per layer).  8-wave workgroups share a CU
-  // two or three at a time, and there the 16-byte chunks measured 0.3 us
-  // slower per launch (4096 x 11008), so they keep one element per lane.
-  constexpr bool kVecSZ = NW == 16;
+  // two or three at a time, and there the 16-byte chunks measured 0.1-0.3 us
+  // slower per launch (4096 x 11008), so they keep one element per lane,
+  // except the gate/up pair in the compact variant (two weight sets to
+  // stage: 12.05 -> 11.59 us on 2 x 11008 x 4096 at M = 1).
+  constexpr bool kVecSZ = NW == 16 || (SMALL && NP == 2);
   constexpr int kXR = !STAGE_X ? 1 : SMALL ? 2 : gemv_stage_budget(NW) / (64 * NW * 16);   // X chunks per thread
   const uint32_t xbytes = STAGE_X ? (uint32_t)M * L.xrow : 0u;
   const int nxr = (int)((xbytes + 64u * NW * 16u - 1u) / (64u * NW * 16u));
@@ -483,8 +485,10 @@ static void gemv_launch(const uint16_t *X, const GemvParts &parts, int tiles, in
   // staging rounds: activations (16 bytes per thread), and scale/zero slots
   // (16-wave: one wave-slot of 16-byte chunks per wave) or elements (8-wave)
   const uint32_t xr = (uint32_t)(((uint64_t)M * (uint64_t)K * 2u + 64u * NW * 16u - 1u) / (64u * NW * 16u));
-  const int szr = NW == 16 ? (NP * ((2 * G + 63) / 64 + (G + 63) / 64) + NW - 1) / NW
-                           : (16 * G + 64 * NW - 1) / (64 * NW);
+  // (16-wave workgroups and the 8-wave gate/up pair stage them in 16-byte
+  // wave slots, single 8-wave sets element by element: gemv_kernel's kVecSZ)
+  const int szr = NW == 16 || NP == 2 ? (NP * ((2 * G + 63) / 64 + (G + 63) / 64) + NW - 1) / NW
+                                      : (16 * G + 64 * NW - 1) / (64 * NW);
   const bool small = xr <= 2 && szr <= 1;
   if (stage && G > 8 * NW)
     gemv_kernel<XT, GS, NW, 2, true, NP, MULTI, false><<<grid, 64 * NW, bytes, st>>>(X, parts, M, (int)K, (int)yt, zfix);
