@@ -382,21 +382,30 @@ def main():
     log(f"decode step: wall {ms_per_step * 1e3:.2f} us, GPU {gpu_step * 1e6:.2f} us per step")
 
     # per-layer kernel time: a graph of launches over >= 512 MB of copies of
-    # that layer alone, so no launch finds its weights in the Infinity Cache
+    # that layer alone, so no launch finds its weights in the Infinity Cache.
+    # Every layer's extra copies are written first, then the device idles
+    # briefly before the timing: right after writing a few hundred MB of
+    # copies, the same launches measured 5-10% slower for about 0.2 s (a
+    # graph built and timed once the device had settled did not), and
+    # decode weights are not freshly written memory.
     per_layer = []
+    layer_copies = []
     for (c, Xd, copies, Yd) in layers:
         Rl = copies_for(c.weight_bytes)
         more = [tuple(t.clone() for t in copies[0]) for _ in range(max(0, Rl - R))]
-        lc = list(copies) + more
-
+        layer_copies.append(list(copies) + more)
+    torch.cuda.synchronize()
+    time.sleep(0.5)
+    for (c, Xd, copies, Yd), lc in zip(layers, layer_copies):
         def f(c=c, Xd=Xd, lc=lc, Yd=Yd):
             for cp in lc:
                 L.linear(Xd, cp, Yd, 128, awq.AWQ_KERNEL_AUTO)
         g = make_graph(torch, f)
         t = time_graph(torch, g, 10, len(lc))
-        del g, more, lc
+        del g
         per_layer.append({"layer": c.name, "us": round(t * 1e6, 3),
                           "GB/s": round(c.io_bytes / t / 1e9, 1)})
+    del layer_copies
 
     # roofline of the GEMV kernel: algorithmic bytes of one launch of each
     # layer over that launch's average duration, byte-weighted over the layers
