@@ -156,6 +156,15 @@ def copies_for(nbytes):
     return max(2, -(-ROTATE_BYTES // max(1, nbytes)))
 
 
+def settle(torch):
+    """Wait for the work queued so far and idle briefly: launches right after
+    a few hundred MB of weight copies have been written measured 5-10% slower
+    for about 0.2 s.  Called after writing copies, before building the graphs
+    that time them."""
+    torch.cuda.synchronize()
+    time.sleep(0.5)
+
+
 def packed_copies(awq, torch, W_np, g, R):
     W = torch.from_numpy(W_np).cuda()
     base = awq.awq_quantize_pack(W, g)
@@ -394,8 +403,7 @@ def main():
         Rl = copies_for(c.weight_bytes)
         more = [tuple(t.clone() for t in copies[0]) for _ in range(max(0, Rl - R))]
         layer_copies.append(list(copies) + more)
-    torch.cuda.synchronize()
-    time.sleep(0.5)
+    settle(torch)
     for (c, Xd, copies, Yd), lc in zip(layers, layer_copies):
         def f(c=c, Xd=Xd, lc=lc, Yd=Yd):
             for cp in lc:
@@ -492,6 +500,7 @@ def measure_fused_rows(awq, torch, wl, L):
         nbytes = sum(qw.numel() * 4 + sc.numel() * 2 + zr.numel() for (qw, sc, zr) in base)
         R = copies_for(nbytes)
         copies = [base] + [[tuple(t.clone() for t in p) for p in base] for _ in range(R - 1)]
+        settle(torch)
         torch.cuda.synchronize()
         if epi == "none":
             outs = [torch.empty((1, N), dtype=torch.float16, device="cuda") for N in Ns]
@@ -530,6 +539,7 @@ def measure_decode_extra_rows(awq, torch, wl, L, decode_layers, R_dec):
             Rl = copies_for(c.weight_bytes)
             lc = list(copies) + [tuple(t.clone() for t in copies[0])
                                  for _ in range(max(0, Rl - R_dec))]
+            settle(torch)
 
             def f(Xd=Xd, Yd=Yd, lc=lc):
                 for cp in lc:
@@ -550,6 +560,7 @@ def measure_decode_extra_rows(awq, torch, wl, L, decode_layers, R_dec):
     Rq = copies_for(qbytes)
     Wd += [Wd[0].clone() for _ in range(Rq - 1)]
     outs = [awq.empty_packed(c.N, c.K, 128, "cuda") for _ in range(Rq)]
+    settle(torch)
 
     def fq():
         for r in range(Rq):
@@ -577,6 +588,7 @@ def measure_gemm_rows(awq, torch, wl, L):
             Rg = copies_for(case.weight_bytes)
             cache.clear()
             cache[key] = (packed_copies(awq, torch, case.weight(), case.group_size, Rg), Rg)
+            settle(torch)
         copies, Rg = cache[key]
         Xd = torch.from_numpy(case.activation()).cuda()
         Yd = torch.empty((case.M, case.N), dtype=torch.float16, device="cuda")
