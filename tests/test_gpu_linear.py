@@ -655,3 +655,23 @@ def test_fused_ragged_and_symmetric_pair():
                                  kernel=kernel)
         torch.cuda.synchronize()
         assert_close(out_to_f64(H), gate_up_silu64(X, gate[:3], up[:3], g), f"pair M={M}")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_fused_pair_partials_over_staged_rows(dt):
+    """The GEMV's cross-wave partials reuse the start of LDS when they do not
+    fit beside the staged data: the gate/up pair at M = 16, K = 2048 stages
+    64 KiB of activation rows, and its partials (24 KiB) would take an
+    8-wave workgroup past 80 KiB.  Ragged N, forced GEMV, against the fp64
+    oracle."""
+    torch = torch_mod()
+    awq = _awq()
+    M, K, N, g = 16, 2048, 1000, 128
+    X = wl.gen_activation(M, K, 220, 221, dt)
+    gate = _packed(wl.gen_weight(N, K, 222), g)
+    up = _packed(wl.gen_weight(N, K, 223), g)
+    say("fused pair, partials over staged rows", dt)
+    H = awq.awq_linear_fused(to_dev(X, bf16=(dt == "bf16")), [gate[3], up[3]], "silu_mul", g,
+                             torch.float32, kernel=GEMV)
+    torch.cuda.synchronize()
+    assert_close(out_to_f64(H), gate_up_silu64(_x_f64(X, dt), gate[:3], up[:3], g), f"pair {dt}")
