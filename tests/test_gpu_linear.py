@@ -93,6 +93,9 @@ RAGGED = [
     # 50 and 64 KiB with 8-wave workgroups (N > 4096)
     (4, 4096, 11008, 128, "f16"), (16, 4000, 4096, 64, "bf16"),
     (5, 6000, 5120, 64, "bf16"), (8, 5000, 4096, 128, "f16"),
+    # GEMV with unstaged rows (over 64 KiB) on 8-wave workgroups: two groups
+    # per batch, the pipelined loop and its one- and two-batch tails
+    (12, 4200, 4096, 128, "f16"), (16, 4100, 5120, 64, "bf16"),
 ]
 
 
