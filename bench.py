@@ -9,6 +9,10 @@ every launch streams its weights from HBM rather than the 256 MB Infinity
 Cache.  Inputs are seeded synthetic tensors (workloads/), resident in HBM
 before the timed region.  The steps are replayed from HIP graphs that hold the
 ten rotation steps back to back (the timed region runs exactly --steps steps).
+The roofline's per-layer launch times (and the extra rows) are taken from
+graphs over their own weight copies, after the copies are written and the
+device has idled briefly (freshly written copies measured 5-10% slower for
+about 0.2 s).
 
 Also measured after the timed region ("rows"): quantize/pack, GEMV at M=4,
 GEMM at M=1 (for the GEMV-vs-GEMM comparison), batched rows at M=16/64/256
