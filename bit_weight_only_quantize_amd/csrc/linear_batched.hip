@@ -17,9 +17,10 @@
 // staging loads are issued first, with one barrier after them (a pipeline of
 // several X chunks per workgroup, with a barrier each, measured slower: every
 // chunk paid a latency of its own).  Each wave streams its packed weights
-// with 64 bytes per lane in flight at M <= 16 and 32 above (the next group's
-// load is issued as a group is consumed): measured 5-14% faster than issuing
-// the whole range at once, bit-identical.  Two workgroups fit a
+// with 48-64 bytes per lane in flight at M <= 16 and 32 above (the next
+// groups' loads are issued as groups are consumed): measured 5-14% faster
+// than issuing the whole range at once, bit-identical; windows of 2, 3, 6
+// and 8 groups at g = 128 were no faster than 4.  Two workgroups fit a
 // CU (at most 80 KiB of LDS and 128 VGPRs each); the split count balances
 // the most loaded CU against the partials' cost.
 // Splits of K write fp32 partials that a second kernel sums in split order
@@ -45,10 +46,15 @@ template <int GS, int MT>
 struct BgGeom {
   static constexpr int kRows = 16 * MT;                 // padded activation rows
   static constexpr int kMaxGroups = 2048 / GS / MT;
-  // groups of packed weights in flight per wave: 64 (M <= 16) or 32 bytes
-  // per lane times 128 / GS
-  static constexpr int kWin = (MT == 1 ? 4 : 2) * 128 / GS < kMaxGroups
-                                  ? (MT == 1 ? 4 : 2) * 128 / GS : kMaxGroups;
+  // Groups of packed weights in flight per wave.  M <= 16: four (64 bytes
+  // per lane) at g = 128; six (48 bytes) at g = 64, refilled two at a time
+  // so that each column's refill is one 64-byte run (measured 2-7% faster
+  // than one 32-byte group at a time on 13B-class layers at M = 8 and 16,
+  // bit-identical; at g = 128, whose groups are 64-byte runs already, pairs
+  // gained nothing).  Above M = 16: 32 bytes per lane.
+  static constexpr int kWinWant = MT == 1 ? (GS == 64 ? 6 : 4) : 2 * 128 / GS;
+  static constexpr int kWin = kWinWant < kMaxGroups ? kWinWant : kMaxGroups;
+  static constexpr int kRefill = MT == 1 && GS == 64 ? 2 : 1;   // groups per refill
   static constexpr int kKR = kMaxGroups * GS;            // K values of a full range
   static constexpr int kRowBytes = kKR * 2 + 16;         // +16: rows start 4 banks apart
   static constexpr int kXBytes = kRows * kRowBytes;
@@ -160,9 +166,11 @@ void batched_gemv_kernel(
   const DeqRegs dq;
 #pragma unroll
   for (int gl = 0; gl < kMG; ++gl) {
-    if (gl + Geo::kWin < kMG) {
+    if (gl % Geo::kRefill == 0 && gl + Geo::kWin < kMG) {
       __builtin_amdgcn_sched_barrier(0);
-      load_group(gl + Geo::kWin);
+#pragma unroll
+      for (int u = 0; u < Geo::kRefill; ++u)
+        if (gl + Geo::kWin + u < kMG) load_group(gl + Geo::kWin + u);
       __builtin_amdgcn_sched_barrier(0);
     }
     // (a guarded body rather than an early exit: the loop stays fully
