@@ -47,14 +47,15 @@ struct BgGeom {
   static constexpr int kRows = 16 * MT;                 // padded activation rows
   static constexpr int kMaxGroups = 2048 / GS / MT;
   // Groups of packed weights in flight per wave.  M <= 16: four (64 bytes
-  // per lane) at g = 128; six (48 bytes) at g = 64, refilled two at a time
-  // so that each column's refill is one 64-byte run (measured 2-7% faster
-  // than one 32-byte group at a time on 13B-class layers at M = 8 and 16,
-  // bit-identical; at g = 128, whose groups are 64-byte runs already, pairs
-  // gained nothing).  Above M = 16: 32 bytes per lane.
+  // per lane) at g = 128, six (48 bytes) at g = 64.  Above M = 16: 32 bytes
+  // per lane.  At g = 64 and M <= 32 they are refilled two at a time, so
+  // that each column's refill is one 64-byte run: measured 2-7% faster at
+  // M = 8 and 16 and 1-4% at M = 24 and 32 than one 32-byte group at a time
+  // on 13B-class layers, bit-identical (no gain at M = 48; at g = 128,
+  // whose groups are 64-byte runs already, none either).
   static constexpr int kWinWant = MT == 1 ? (GS == 64 ? 6 : 4) : 2 * 128 / GS;
   static constexpr int kWin = kWinWant < kMaxGroups ? kWinWant : kMaxGroups;
-  static constexpr int kRefill = MT == 1 && GS == 64 ? 2 : 1;   // groups per refill
+  static constexpr int kRefill = MT <= 2 && GS == 64 ? 2 : 1;   // groups per refill
   static constexpr int kKR = kMaxGroups * GS;            // K values of a full range
   static constexpr int kRowBytes = kKR * 2 + 16;         // +16: rows start 4 banks apart
   static constexpr int kXBytes = kRows * kRowBytes;

@@ -96,6 +96,10 @@ RAGGED = [
     # GEMV with unstaged rows (over 64 KiB) on 8-wave workgroups: two groups
     # per batch, the pipelined loop and its one- and two-batch tails
     (12, 4200, 4096, 128, "f16"), (16, 4100, 5120, 64, "bf16"),
+    # batched-decode kernel at g = 64, whose weight loads are refilled two
+    # groups at a time: an odd group count (45) and a partial column block,
+    # with one and two row tiles
+    (9, 4200, 2880, 64, "f16"), (24, 4200, 2880, 64, "bf16"),
 ]
 
 
