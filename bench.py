@@ -320,7 +320,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              f"(this build has no multi-GPU path; run with --gpus 1)", file=sys.stderr)
+              f"(this library has no multi-GPU path; run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     if args.calibrate_copy:

@@ -60,7 +60,7 @@ typedef struct awq_config {
 typedef enum awq_status {
     AWQ_OK = 0,
     AWQ_ERR_INVALID_ARG = 1, /* bad shape, NULL pointer, misalignment, bad enum */
-    AWQ_ERR_UNSUPPORTED = 2, /* a config this build does not implement */
+    AWQ_ERR_UNSUPPORTED = 2, /* a config the library does not implement */
     AWQ_ERR_WORKSPACE = 3,   /* workspace smaller than required */
     AWQ_ERR_HIP = 4,         /* the HIP runtime reported an error (incl. no device) */
     AWQ_ERR_NONFINITE = 5    /* reserved: non-finite input detected */
