@@ -424,9 +424,10 @@ def test_batched_gemm_layers(case):
     assert_close(out_to_f64(_run(X, "f16", pd, case.group_size, 0)), ref, case.name)
 
 
-@pytest.mark.parametrize("case", wl.gemm_cases(Ms=(16, 64)), ids=lambda c: c.name)
+@pytest.mark.parametrize("case", wl.gemm_cases(Ms=(16, 32, 64)), ids=lambda c: c.name)
 def test_batched_decode_kernel_layers(case):
-    """The batched-decode kernel on the 13B-class layers at M = 16 and 64,
+    """The batched-decode kernel on the 13B-class layers at M = 16, 32 and 64
+    (one, two and four row tiles),
     K split (partials summed in split order), against the oracle; repeated
     calls are bit-identical.  Without a workspace these K need more than one
     split, and the call says so (AWQ_ERR_WORKSPACE) rather than running."""
