@@ -48,14 +48,10 @@ struct BgGeom {
   static constexpr int kMaxGroups = 2048 / GS / MT;
   // Groups of packed weights in flight per wave.  M <= 16: four (64 bytes
   // per lane) at g = 128, six (48 bytes) at g = 64.  Above M = 16: 32 bytes
-  // per lane.  At g = 64 and M <= 32 they are refilled two at a time, so
-  // that each column's refill is one 64-byte run: measured 2-7% faster at
-  // M = 8 and 16 and 1-4% at M = 24 and 32 than one 32-byte group at a time
-  // on 13B-class layers, bit-identical (no gain at M = 48; at g = 128,
-  // whose groups are 64-byte runs already, none either).
+  // per lane.  The kernel's REFILL is how many are requested at a time (see
+  // bg_refill).
   static constexpr int kWinWant = MT == 1 ? (GS == 64 ? 6 : 4) : 2 * 128 / GS;
   static constexpr int kWin = kWinWant < kMaxGroups ? kWinWant : kMaxGroups;
-  static constexpr int kRefill = MT <= 2 && GS == 64 ? 2 : 1;   // groups per refill
   static constexpr int kKR = kMaxGroups * GS;            // K values of a full range
   static constexpr int kRowBytes = kKR * 2 + 16;         // +16: rows start 4 banks apart
   static constexpr int kXBytes = kRows * kRowBytes;
@@ -70,7 +66,7 @@ struct BgGeom {
 };
 
 // (four waves per SIMD: two workgroups per CU)
-template <class XT, int GS, int MT>
+template <class XT, int GS, int MT, int REFILL>
 __global__ __launch_bounds__(64 * kBgWaves) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void batched_gemv_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ qweight,
@@ -167,10 +163,10 @@ void batched_gemv_kernel(
   const DeqRegs dq;
 #pragma unroll
   for (int gl = 0; gl < kMG; ++gl) {
-    if (gl % Geo::kRefill == 0 && gl + Geo::kWin < kMG) {
+    if (gl % REFILL == 0 && gl + Geo::kWin < kMG) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < Geo::kRefill; ++u)
+      for (int u = 0; u < REFILL; ++u)
         if (gl + Geo::kWin + u < kMG) load_group(gl + Geo::kWin + u);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -330,6 +326,20 @@ BatchedPlan batched_gemv_plan(int64_t M, int64_t N, int64_t K, int gs, Scratch s
   return p;
 }
 
+// Weight groups requested at a time.  Pairs make each column's refill one
+// run of two groups: at g = 64 and M <= 32 (a 64-byte run instead of two
+// 32-byte ones) measured 2-7% faster at M = 8 and 16 and 1-4% at M = 24 and
+// 32 on 13B-class layers (no gain at M = 48); at g = 128 and M <= 16, 1.5-5%
+// faster where a split holds an even number of groups (10 or 16) and 1-3%
+// slower where it holds an odd number (9 or 11), hence the choice by the
+// plan's groups per split.  Same box, bit-identical either way.
+template <int GS, int MT>
+static int bg_refill(const BatchedPlan &p) {
+  if (GS == 64 && MT <= 2) return 2;
+  if (GS == 128 && MT == 1 && p.gps % 2 == 0) return 2;
+  return 1;
+}
+
 template <class XT, int GS, int MT>
 static hipError_t bg_go(const void *X, const uint32_t *qw, const uint16_t *sc, const uint8_t *zr,
                         int64_t M, int64_t N, int64_t K, void *Y, YType yt,
@@ -338,9 +348,19 @@ static hipError_t bg_go(const void *X, const uint32_t *qw, const uint16_t *sc, c
   const dim3 grid((unsigned)((N + Geo::kCols - 1) / Geo::kCols), (unsigned)p.splits);
   const uint32_t zfix = zr ? 0u : 8u;
   float *part = p.splits > 1 ? partial : nullptr;
-  batched_gemv_kernel<XT, GS, MT><<<grid, Geo::kThreads, Geo::kBytes, st>>>(
-      reinterpret_cast<const uint16_t *>(X), qw, sc, zr, (int)M, (int)N, (int)K, p.gps, Y, (int)yt,
-      zfix, part);
+  const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
+  constexpr bool kPairs = (GS == 64 && MT <= 2) || (GS == 128 && MT == 1);
+  if constexpr (kPairs) {
+    if (bg_refill<GS, MT>(p) == 2)
+      batched_gemv_kernel<XT, GS, MT, 2><<<grid, Geo::kThreads, Geo::kBytes, st>>>(
+          x, qw, sc, zr, (int)M, (int)N, (int)K, p.gps, Y, (int)yt, zfix, part);
+    else
+      batched_gemv_kernel<XT, GS, MT, 1><<<grid, Geo::kThreads, Geo::kBytes, st>>>(
+          x, qw, sc, zr, (int)M, (int)N, (int)K, p.gps, Y, (int)yt, zfix, part);
+  } else {
+    batched_gemv_kernel<XT, GS, MT, 1><<<grid, Geo::kThreads, Geo::kBytes, st>>>(
+        x, qw, sc, zr, (int)M, (int)N, (int)K, p.gps, Y, (int)yt, zfix, part);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t MN = M * N;
