@@ -329,7 +329,9 @@ BatchedPlan batched_gemv_plan(int64_t M, int64_t N, int64_t K, int gs, Scratch s
 // Weight groups requested at a time.  Pairs make each column's refill one
 // run of two groups: at g = 64 and M <= 32 (a 64-byte run instead of two
 // 32-byte ones) measured 2-7% faster at M = 8 and 16 and 1-4% at M = 24 and
-// 32 on 13B-class layers (no gain at M = 48); at g = 128 and M <= 16, 1.5-5%
+// 32 on 13B-class layers (no gain at M = 48), and no slower with an odd
+// number of groups per split (13 or 11 on 7B-class layers, within 1%); at
+// g = 128 and M <= 16, 1.5-5%
 // faster where a split holds an even number of groups (10 or 16) and 1-3%
 // slower where it holds an odd number (9 or 11), hence the choice by the
 // plan's groups per split.  Same box, bit-identical either way.
